@@ -1,0 +1,397 @@
+"""Plain CPU oracle of one layer-streamed training step (TEST INFRASTRUCTURE).
+
+This module is test infrastructure.  Only ``tests/``, ``__graft_entry__.smoke()``
+and the ``cpu_baseline`` leg of ``bench.py`` may import it.  The product path
+(the HIP library and its Python binding) never calls it and shares no code with
+it; the only shared module is ``synth`` (seeded inputs, no training arithmetic).
+
+What it computes.  The method -- host memory as the authoritative store,
+per-layer streaming of weights, block checkpointing with recompute, gradient
+offload, host-side Adam -- is a *schedule*: it reaches exactly the result of
+one ordinary training step of the model (MegaTrain paper page, section 3
+"MegaTrain System", execution workflow: block checkpoints only trade extra
+forward compute for bounded memory; hyper.ai summary, experiments: no
+numerical drift against the standard baselines).  So this oracle is the plain
+definition: a forward pass, an analytic backward pass written out by hand (no
+autodiff) and an Adam step in the method's storage format (bf16 weights, bf16
+gradients, fp32 moments; paper page, section 2 "Preliminaries", the 12 bytes
+per parameter accounting).  A second mode, ``streamed``, follows the method's
+own order (keep only block-start activations, recompute a block, run its
+backward top-down, update each layer as soon as its gradient exists) and exists
+only to check that the schedule leaves the result unchanged.
+
+Every function is generic over numpy float32 / float64 (``dt``); arithmetic is
+done in that precision on weights that are exact bf16 values.
+
+Readings taken where the pages are silent (each listed in the design doc):
+Llama-style pre-norm RMSNorm with eps inside the square root and the gain after
+normalising; fused QKV; rotate-half RoPE with cos/sin tables computed in fp64
+and rounded to fp32; causal softmax attention with scale 1/sqrt(hd); SwiGLU
+silu(gate) * up; untied LM head behind a final RMSNorm; mean next-token cross
+entropy over the B*(S-1) labelled positions; PyTorch-form Adam with bias
+correction, no master fp32 weights.
+"""
+import numpy as np
+
+from synth import bf16_bits_to_f32, f32_to_bf16_bits, layer_tensor_shapes
+
+
+# ----------------------------------------------------------------------------
+# helpers
+# ----------------------------------------------------------------------------
+
+def bf16_round(x):
+    """Round-to-nearest-even to bf16, returned widened to float32."""
+    return bf16_bits_to_f32(f32_to_bf16_bits(np.asarray(x, dtype=np.float32)))
+
+
+def to_float(bits_tree, dt):
+    """Convert a (nested) dict/list of bf16 bit arrays into float arrays of dtype dt."""
+    if isinstance(bits_tree, dict):
+        return {k: to_float(v, dt) for k, v in bits_tree.items()}
+    if isinstance(bits_tree, list):
+        return [to_float(v, dt) for v in bits_tree]
+    return bf16_bits_to_f32(bits_tree).astype(dt)
+
+
+# ----------------------------------------------------------------------------
+# building blocks of the layer template (paper page, appendix A.4: templates
+# hold attention and MLP kernels; the pages leave their math to the model)
+# ----------------------------------------------------------------------------
+
+def rmsnorm_fwd(x, g, eps):
+    """y = x * (mean_j x_j^2 + eps)^(-1/2) * g, row-wise over the last axis."""
+    dt = x.dtype
+    r = (1.0 / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + dt.type(eps))).astype(dt)
+    xh = x * r
+    return xh * g, xh, r
+
+
+def rmsnorm_bwd(dy, xh, r, g):
+    """Gradient of rmsnorm_fwd.  Returns (dx, dg)."""
+    dg = np.sum(dy * xh, axis=tuple(range(dy.ndim - 1)))
+    gy = dy * g
+    dx = r * (gy - xh * np.mean(gy * xh, axis=-1, keepdims=True))
+    return dx, dg
+
+
+def rope_tables(S, hd, base):
+    """cos/sin of the angle s * base^(-2i/hd), i < hd/2, in fp64 rounded to fp32."""
+    i = np.arange(hd // 2, dtype=np.float64)
+    theta = base ** (-2.0 * i / hd)
+    ang = np.arange(S, dtype=np.float64)[:, None] * theta[None, :]
+    return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+
+
+def rope_fwd(a, cos, sin):
+    """Rotate pairs (i, i + hd/2) of the last axis by the position angle.
+
+    ``a`` has shape [..., S, hd]; cos/sin have shape [S, hd/2]."""
+    half = a.shape[-1] // 2
+    c = cos.astype(a.dtype)
+    s = sin.astype(a.dtype)
+    a1, a2 = a[..., :half], a[..., half:]
+    return np.concatenate([a1 * c - a2 * s, a2 * c + a1 * s], axis=-1)
+
+
+def rope_bwd(da, cos, sin):
+    """Gradient of rope_fwd: the rotation by the opposite angle."""
+    half = da.shape[-1] // 2
+    c = cos.astype(da.dtype)
+    s = sin.astype(da.dtype)
+    d1, d2 = da[..., :half], da[..., half:]
+    return np.concatenate([d1 * c + d2 * s, d2 * c - d1 * s], axis=-1)
+
+
+def attention_fwd(q, k, v):
+    """Causal softmax attention per (batch, head).
+
+    q, k, v: [B, nh, S, hd].  Returns o [B, nh, S, hd] and the row softmax
+    P [B, nh, S, S] (zeros above the diagonal)."""
+    dt = q.dtype
+    B, nh, S, hd = q.shape
+    scale = dt.type(1.0 / np.sqrt(hd))
+    mask = np.triu(np.ones((S, S), dtype=bool), 1)
+    o = np.empty_like(q)
+    P = np.empty((B, nh, S, S), dtype=dt)
+    for b in range(B):
+        for hh in range(nh):
+            A = (q[b, hh] @ k[b, hh].T) * scale
+            A[mask] = -np.inf
+            A = A - A.max(axis=-1, keepdims=True)
+            E = np.exp(A)
+            Pb = E / E.sum(axis=-1, keepdims=True)
+            P[b, hh] = Pb
+            o[b, hh] = Pb @ v[b, hh]
+    return o, P
+
+
+def attention_bwd(do, q, k, v, o, P):
+    """Gradient of attention_fwd.  Returns (dq, dk, dv)."""
+    dt = q.dtype
+    hd = q.shape[-1]
+    scale = dt.type(1.0 / np.sqrt(hd))
+    dq = np.empty_like(q)
+    dk = np.empty_like(k)
+    dv = np.empty_like(v)
+    B, nh = q.shape[:2]
+    for b in range(B):
+        for hh in range(nh):
+            Pb = P[b, hh]
+            dv[b, hh] = Pb.T @ do[b, hh]
+            dP = do[b, hh] @ v[b, hh].T
+            Drow = np.sum(do[b, hh] * o[b, hh], axis=-1, keepdims=True)
+            dA = Pb * (dP - Drow)
+            dq[b, hh] = (dA @ k[b, hh]) * scale
+            dk[b, hh] = (dA.T @ q[b, hh]) * scale
+    return dq, dk, dv
+
+
+def silu(z):
+    return z / (1.0 + np.exp(-z))
+
+
+def swiglu_fwd(gate, up):
+    return silu(gate) * up
+
+
+def swiglu_bwd(da, gate, up):
+    """Gradient of silu(gate) * up.  Returns (dgate, dup)."""
+    sig = 1.0 / (1.0 + np.exp(-gate))
+    dgate = da * up * sig * (1.0 + gate * (1.0 - sig))
+    dup = da * (gate * sig)
+    return dgate, dup
+
+
+# ----------------------------------------------------------------------------
+# one decoder layer (the stateless template applied to bound weights)
+# ----------------------------------------------------------------------------
+
+def _heads(t, B, S, nh, hd):
+    return t.reshape(B, S, nh, hd).transpose(0, 2, 1, 3)
+
+
+def _tokens(t, B, S, h):
+    return t.transpose(0, 2, 1, 3).reshape(B * S, h)
+
+
+def layer_fwd(x, W, cfg, cos, sin):
+    """x [T, h] -> (y [T, h], cache).  W: dict of float arrays of one layer."""
+    B, S, nh, hd, h, f = cfg.batch, cfg.seq, cfg.heads, cfg.head_dim, cfg.hidden, cfg.ffn
+    n1, xh1, r1 = rmsnorm_fwd(x, W["g_attn"], cfg.eps)
+    qkv = n1 @ W["wqkv"].T
+    q = rope_fwd(_heads(qkv[:, :h], B, S, nh, hd), cos, sin)
+    k = rope_fwd(_heads(qkv[:, h:2 * h], B, S, nh, hd), cos, sin)
+    v = _heads(qkv[:, 2 * h:], B, S, nh, hd)
+    oh, P = attention_fwd(q, k, v)
+    o = _tokens(oh, B, S, h)
+    xm = x + o @ W["wo"].T
+    n2, xh2, r2 = rmsnorm_fwd(xm, W["g_mlp"], cfg.eps)
+    gu = n2 @ W["wgu"].T
+    gate, up = gu[:, :f], gu[:, f:]
+    a = swiglu_fwd(gate, up)
+    y = xm + a @ W["wd"].T
+    cache = dict(x=x, n1=n1, xh1=xh1, r1=r1, q=q, k=k, v=v, oh=oh, P=P, o=o, xm=xm,
+                 n2=n2, xh2=xh2, r2=r2, gate=gate, up=up, a=a)
+    return y, cache
+
+
+def layer_bwd(dy, c, W, cfg, cos, sin):
+    """Analytic backward of layer_fwd.  Returns (dx, dW dict)."""
+    B, S, nh, hd, h = cfg.batch, cfg.seq, cfg.heads, cfg.head_dim, cfg.hidden
+    dW = {}
+    # down projection and residual
+    dW["wd"] = dy.T @ c["a"]
+    da = dy @ W["wd"]
+    dgate, dup = swiglu_bwd(da, c["gate"], c["up"])
+    dgu = np.concatenate([dgate, dup], axis=1)
+    dW["wgu"] = dgu.T @ c["n2"]
+    dn2 = dgu @ W["wgu"]
+    dxm_norm, dW["g_mlp"] = rmsnorm_bwd(dn2, c["xh2"], c["r2"], W["g_mlp"])
+    dxm = dy + dxm_norm
+    # attention block
+    dW["wo"] = dxm.T @ c["o"]
+    do = _heads(dxm @ W["wo"], B, S, nh, hd)
+    dq, dk, dv = attention_bwd(do, c["q"], c["k"], c["v"], c["oh"], c["P"])
+    dq = rope_bwd(dq, cos, sin)
+    dk = rope_bwd(dk, cos, sin)
+    dqkv = np.concatenate([_tokens(dq, B, S, h), _tokens(dk, B, S, h), _tokens(dv, B, S, h)], axis=1)
+    dW["wqkv"] = dqkv.T @ c["n1"]
+    dn1 = dqkv @ W["wqkv"]
+    dx_norm, dW["g_attn"] = rmsnorm_bwd(dn1, c["xh1"], c["r1"], W["g_attn"])
+    return dxm + dx_norm, dW
+
+
+# ----------------------------------------------------------------------------
+# head: final RMSNorm, LM head, next-token cross entropy
+# ----------------------------------------------------------------------------
+
+def labels_of(tok):
+    """label[b, s] = tok[b, s+1]; the last position of each row has no label."""
+    return tok[:, 1:]
+
+
+def head_fwd_bwd(x, g_final, w_head, tok, cfg):
+    """Loss and gradients of the head.  Returns (loss, per_pos_loss, dx, dg_final, dw_head)."""
+    B, S, V = cfg.batch, cfg.seq, cfg.vocab
+    dt = x.dtype
+    xf, xhf, rf = rmsnorm_fwd(x, g_final, cfg.eps)
+    z = (xf @ w_head.T).reshape(B, S, V)
+    zmax = z.max(axis=-1, keepdims=True)
+    lse = (zmax + np.log(np.sum(np.exp(z - zmax), axis=-1, keepdims=True)))[..., 0]
+    lab = labels_of(tok)
+    N = B * (S - 1)
+    zl = np.take_along_axis(z[:, :-1], lab[..., None].astype(np.int64), axis=-1)[..., 0]
+    per_pos = lse[:, :-1] - zl
+    loss = per_pos.sum() / dt.type(N)
+    dz = np.exp(z - lse[..., None]) / dt.type(N)
+    dz[:, -1, :] = 0
+    bi, si = np.meshgrid(np.arange(B), np.arange(S - 1), indexing="ij")
+    dz[bi, si, lab] -= dt.type(1.0) / dt.type(N)
+    dz = dz.reshape(B * S, V)
+    dw_head = dz.T @ xf
+    dxf = dz @ w_head
+    dx, dg = rmsnorm_bwd(dxf, xhf, rf, g_final)
+    return loss, per_pos, dx, dg, dw_head
+
+
+# ----------------------------------------------------------------------------
+# Adam in the method's storage format (paper page, section 3: CPU-side Adam,
+# moments never leave host memory; section 2: bf16 weights and grads, fp32
+# moments)
+# ----------------------------------------------------------------------------
+
+def adam_consts(adam, t):
+    """Scalar constants, each computed in fp64 and rounded once to fp32."""
+    f = np.float32
+    return dict(b1=f(adam.beta1), b2=f(adam.beta2), omb1=f(1.0 - adam.beta1), omb2=f(1.0 - adam.beta2),
+                c1=f(1.0 - adam.beta1 ** t), c2=f(1.0 - adam.beta2 ** t), lr=f(adam.lr), eps=f(adam.eps),
+                decay=f(1.0 - adam.lr * adam.weight_decay))
+
+
+def adam_update(w_bits, g_fp32, m, v, adam, t):
+    """One Adam step on one tensor, all in fp32, one IEEE rounding per operation.
+
+    w_bits: bf16 weights (uint16); g_fp32: gradient as computed; m, v: fp32
+    moments (updated in place).  The gradient is first stored as bf16, as the
+    method keeps bf16 gradients on the host.  Returns (new bf16 bits, the fp32
+    weight before its bf16 rounding)."""
+    k = adam_consts(adam, t)
+    w = bf16_bits_to_f32(w_bits)
+    if adam.weight_decay != 0.0:
+        w = w * k["decay"]
+    gh = bf16_round(g_fp32)
+    m[...] = k["b1"] * m + k["omb1"] * gh
+    v[...] = k["b2"] * v + k["omb2"] * (gh * gh)
+    mhat = m / k["c1"]
+    vhat = v / k["c2"]
+    denom = np.sqrt(vhat) + k["eps"]
+    step = k["lr"] * mhat
+    w_new = (w - step / denom).astype(np.float32)
+    return f32_to_bf16_bits(w_new), w_new
+
+
+# ----------------------------------------------------------------------------
+# full step
+# ----------------------------------------------------------------------------
+
+def embed_fwd(embed, tok):
+    return embed[tok.reshape(-1)]
+
+
+def embed_bwd(dx0, tok, V):
+    """dE[v] = sum over positions t with tok_t == v of dx0[t], accumulated in ascending t."""
+    dE = np.zeros((V, dx0.shape[1]), dtype=dx0.dtype)
+    np.add.at(dE, tok.reshape(-1), dx0)
+    return dE
+
+
+def forward_backward(Wf, tok, cfg, mode="resident", ckpt_every=None, on_layer_grad=None):
+    """Loss and all gradients of one step.
+
+    Wf: dict of float weights (embed, g_final, head, layers[list of dicts]).
+    mode 'resident' keeps every layer's internals; mode 'streamed' keeps only
+    the block-start activations (one every ``ckpt_every`` layers), recomputes a
+    block's internals in the backward, and visits layers in the method's
+    order.  ``on_layer_grad(l, dW)`` is called as soon as a layer's gradient
+    exists (the hook where the method runs that layer's Adam)."""
+    dt = Wf["embed"].dtype
+    L = cfg.layers
+    cos, sin = rope_tables(cfg.seq, cfg.head_dim, cfg.rope_base)
+    x = embed_fwd(Wf["embed"], tok)
+    K = ckpt_every or cfg.ckpt_every
+    caches, ckpts = [], {}
+    for l in range(L):
+        if mode == "streamed" and l % K == 0:
+            ckpts[l] = x
+        x, c = layer_fwd(x, Wf["layers"][l], cfg, cos, sin)
+        if mode == "resident":
+            caches.append(c)
+    loss, per_pos, dx, dg_final, dw_head = head_fwd_bwd(x, Wf["g_final"], Wf["head"], tok, cfg)
+    grads = {"g_final": dg_final, "head": dw_head, "layers": [None] * L}
+    if mode == "resident":
+        for l in reversed(range(L)):
+            dx, dW = layer_bwd(dx, caches[l], Wf["layers"][l], cfg, cos, sin)
+            grads["layers"][l] = dW
+            if on_layer_grad:
+                on_layer_grad(l, dW)
+    else:
+        for b0 in reversed(range(0, L, K)):
+            xb = ckpts[b0]
+            block = []
+            for l in range(b0, min(L, b0 + K)):
+                xb, c = layer_fwd(xb, Wf["layers"][l], cfg, cos, sin)
+                block.append(c)
+            for l in reversed(range(b0, min(L, b0 + K))):
+                dx, dW = layer_bwd(dx, block[l - b0], Wf["layers"][l], cfg, cos, sin)
+                grads["layers"][l] = dW
+                if on_layer_grad:
+                    on_layer_grad(l, dW)
+    grads["embed"] = embed_bwd(dx, tok, cfg.vocab)
+    return loss, per_pos, grads, dx
+
+
+class HostState:
+    """Host-resident training state of the oracle: bf16 weights + fp32 moments."""
+
+    def __init__(self, bits):
+        self.bits = {"embed": bits["embed"].copy(), "g_final": bits["g_final"].copy(),
+                     "head": bits["head"].copy(),
+                     "layers": [{k: v.copy() for k, v in lw.items()} for lw in bits["layers"]]}
+        z = lambda a: np.zeros(a.shape, dtype=np.float32)
+        self.m = {k: z(self.bits[k]) for k in ("embed", "g_final", "head")}
+        self.v = {k: z(self.bits[k]) for k in ("embed", "g_final", "head")}
+        self.m["layers"] = [{k: z(a) for k, a in lw.items()} for lw in self.bits["layers"]]
+        self.v["layers"] = [{k: z(a) for k, a in lw.items()} for lw in self.bits["layers"]]
+        self.t = 0
+
+
+def train_step(state, tok, cfg, adam, mode="resident", dt=np.float32, ckpt_every=None):
+    """One training step on ``state`` (updated in place).
+
+    Returns dict(loss, grads (float, as computed), w_fp32 (pre-rounding fp32
+    weights after Adam, same tree as the weights))."""
+    state.t += 1
+    t = state.t
+    Wf = to_float(state.bits, dt)
+    w_fp32 = {"layers": [dict() for _ in range(cfg.layers)]}
+
+    def upd_layer(l, dW):
+        for name in layer_tensor_shapes(cfg):
+            nb, wf = adam_update(state.bits["layers"][l][name], dW[name].astype(np.float32),
+                                 state.m["layers"][l][name], state.v["layers"][l][name], adam, t)
+            state.bits["layers"][l][name] = nb
+            w_fp32["layers"][l][name] = wf
+
+    loss, per_pos, grads, _ = forward_backward(
+        Wf, tok, cfg, mode=mode, ckpt_every=ckpt_every,
+        on_layer_grad=upd_layer if mode == "streamed" else None)
+    if mode == "resident":
+        for l in range(cfg.layers):
+            upd_layer(l, grads["layers"][l])
+    for name in ("head", "g_final", "embed"):
+        nb, wf = adam_update(state.bits[name], grads[name].astype(np.float32),
+                             state.m[name], state.v[name], adam, t)
+        state.bits[name] = nb
+        w_fp32[name] = wf
+    return dict(loss=loss, per_pos=per_pos, grads=grads, w_fp32=w_fp32)
