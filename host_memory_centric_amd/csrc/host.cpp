@@ -1,0 +1,540 @@
+// Host side of the layer-streamed trainer: unit layout, the pageable master
+// store, the just-in-time packer, pinned buffers and asynchronous copies, the
+// SIMD host Adam, the embedding gather/scatter and the RoPE tables.
+//
+// Design notes (MegaTrain paper page, appendix A.1 "Host (CPU) Memory
+// Management" and A.3 "GPU Buffer Management"; hyper.ai summary, method):
+// every unit's state is one contiguous block with 4 KB-aligned regions so a
+// layer moves in one DMA burst; the store itself is pageable and only a few
+// fixed-size staging buffers are pinned, so pinned memory does not grow with
+// depth.
+#include <hip/hip_runtime_api.h>
+#include <immintrin.h>
+#include <sys/mman.h>
+
+#include <algorithm>
+#include <atomic>
+#include <cmath>
+#include <cstdarg>
+#include <cstring>
+#include <mutex>
+#include <thread>
+#include <vector>
+
+#include "common.h"
+
+namespace mt {
+
+// ---------------------------------------------------------------------------
+// errors
+// ---------------------------------------------------------------------------
+static thread_local char g_err[512] = "";
+
+void set_error(const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+}
+
+static void hip_check(hipError_t e, const char* what) {
+    if (e != hipSuccess) MT_FAIL(MT_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// ---------------------------------------------------------------------------
+// layout
+// ---------------------------------------------------------------------------
+void check_cfg(const mt_model_cfg* cfg) {
+    MT_CHECK_ARG(cfg != nullptr, "cfg is NULL");
+    if (cfg->layers < 1 || cfg->hidden < 8 || cfg->heads < 1 || cfg->head_dim < 8 || cfg->ffn < 8 ||
+        cfg->vocab < 8)
+        MT_FAIL(MT_E_SHAPE, "non-positive model dimension");
+    if ((int64_t)cfg->heads * cfg->head_dim != cfg->hidden)
+        MT_FAIL(MT_E_SHAPE, "hidden (%d) != heads (%d) * head_dim (%d)", cfg->hidden, cfg->heads,
+                cfg->head_dim);
+    if (cfg->hidden % 8 || cfg->ffn % 8 || cfg->vocab % 8 || cfg->head_dim % 8)
+        MT_FAIL(MT_E_SHAPE, "hidden, ffn, vocab and head_dim must be multiples of 8");
+    if (!(cfg->eps > 0.f) || !(cfg->rope_base > 1.f)) MT_FAIL(MT_E_ARG, "bad eps or rope_base");
+}
+
+mt_unit_layout layout_of(const mt_model_cfg* cfg, int unit) {
+    check_cfg(cfg);
+    mt_unit_layout L;
+    memset(&L, 0, sizeof(L));
+    const uint64_t h = cfg->hidden, f = cfg->ffn, V = cfg->vocab;
+    uint64_t numel[6] = {0, 0, 0, 0, 0, 0};
+    if (unit >= 0) {
+        MT_CHECK_ARG(unit < cfg->layers, "unit %d out of range", unit);
+        L.n_tensors = 6;
+        numel[0] = h;          // attention RMSNorm gain
+        numel[1] = 3 * h * h;  // fused QKV
+        numel[2] = h * h;      // output projection
+        numel[3] = h;          // MLP RMSNorm gain
+        numel[4] = 2 * f * h;  // fused gate/up
+        numel[5] = h * f;      // down projection
+    } else if (unit == MT_UNIT_EMBED) {
+        L.n_tensors = 1;
+        numel[0] = V * h;
+    } else if (unit == MT_UNIT_HEAD) {
+        L.n_tensors = 2;
+        numel[0] = h;      // final RMSNorm gain
+        numel[1] = V * h;  // LM head
+    } else {
+        MT_FAIL(MT_E_ARG, "unknown unit %d", unit);
+    }
+    uint64_t off = 0;
+    for (int j = 0; j < L.n_tensors; ++j) {
+        L.tensor_off[j] = off;
+        L.tensor_numel[j] = numel[j];
+        L.params += numel[j];
+        off = round_up(off + 2 * numel[j], MT_TENSOR_ALIGN);
+    }
+    L.w_bytes = off;
+    const uint64_t elems = L.w_bytes / 2;
+    const uint64_t rb[4] = {L.w_bytes, L.w_bytes, 4 * elems, 4 * elems};
+    uint64_t pos = 0;
+    for (int r = 0; r < 4; ++r) {
+        L.region_off[r] = pos;
+        L.region_bytes[r] = round_up(rb[r], MT_BLOCK_ALIGN);
+        pos += L.region_bytes[r];
+    }
+    L.block_bytes = pos;
+    return L;
+}
+
+// ---------------------------------------------------------------------------
+// host worker threads: a blocking parallel-for over [0, n)
+// ---------------------------------------------------------------------------
+static std::atomic<int> g_threads{0};
+
+static int n_threads() {
+    int t = g_threads.load();
+    if (t > 0) return t;
+    cpu_set_t set;
+    if (sched_getaffinity(0, sizeof(set), &set) == 0) t = CPU_COUNT(&set);
+    if (t <= 0) t = (int)std::thread::hardware_concurrency();
+    return std::max(1, t);
+}
+
+template <class F>
+static void parallel_for(uint64_t n, uint64_t grain, F&& fn) {
+    if (n == 0) return;
+    const uint64_t chunks = (n + grain - 1) / grain;
+    const int nt = (int)std::min<uint64_t>(chunks, (uint64_t)n_threads());
+    if (nt <= 1) {
+        fn(0, n);
+        return;
+    }
+    std::atomic<uint64_t> next{0};
+    std::exception_ptr err;
+    std::mutex err_mu;
+    auto work = [&]() {
+        try {
+            for (;;) {
+                const uint64_t c = next.fetch_add(1);
+                if (c >= chunks) break;
+                fn(c * grain, std::min(n, (c + 1) * grain));
+            }
+        } catch (...) {
+            std::lock_guard<std::mutex> lk(err_mu);
+            if (!err) err = std::current_exception();
+        }
+    };
+    std::vector<std::thread> ts;
+    ts.reserve(nt - 1);
+    for (int i = 0; i < nt - 1; ++i) ts.emplace_back(work);
+    work();
+    for (auto& t : ts) t.join();
+    if (err) std::rethrow_exception(err);
+}
+
+static void par_memcpy(void* dst, const void* src, uint64_t bytes) {
+    const uint64_t grain = 4ull << 20;
+    parallel_for(bytes, grain, [&](uint64_t b, uint64_t e) {
+        memcpy((char*)dst + b, (const char*)src + b, e - b);
+    });
+}
+
+// ---------------------------------------------------------------------------
+// store
+// ---------------------------------------------------------------------------
+}  // namespace mt
+
+struct mt_store {
+    mt_model_cfg cfg;
+    std::vector<void*> blocks;           // index: unit + 2 (embed, head, layers...)
+    std::vector<uint64_t> mapped_bytes;  // mmap lengths
+    std::vector<mt_unit_layout> layouts;
+    std::vector<float> embed_acc;        // fp32 embedding-gradient accumulator
+};
+
+namespace mt {
+
+static int unit_index(const mt_store* st, int unit) {
+    MT_CHECK_ARG(st != nullptr, "store is NULL");
+    MT_CHECK_ARG(unit >= MT_UNIT_HEAD && unit < st->cfg.layers, "unit %d out of range", unit);
+    return unit + 2;
+}
+
+static void* map_block(uint64_t bytes) {
+    void* p = mmap(nullptr, bytes, PROT_READ | PROT_WRITE, MAP_PRIVATE | MAP_ANONYMOUS | MAP_NORESERVE, -1,
+                   0);
+    if (p == MAP_FAILED) MT_FAIL(MT_E_NOMEM, "mmap of %llu bytes failed", (unsigned long long)bytes);
+    madvise(p, bytes, MADV_HUGEPAGE);
+    return p;
+}
+
+// ---------------------------------------------------------------------------
+// seeded generator (SplitMix64 in counter form; Box-Muller normals)
+// ---------------------------------------------------------------------------
+static inline uint64_t mix64(uint64_t z) {
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return z ^ (z >> 31);
+}
+static inline uint64_t rng_u(uint32_t seed, uint32_t stream, uint64_t i) {
+    const uint64_t key = ((uint64_t)seed << 48) | ((uint64_t)stream << 32) | i;
+    return mix64(key * 0x9E3779B97F4A7C15ull);
+}
+static inline uint16_t f32_to_bf16(float f) {
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+static inline float bf16_to_f32(uint16_t b) {
+    const uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return f;
+}
+
+static void fill_normal(uint16_t* dst, uint64_t n, uint32_t seed, uint32_t stream, double std) {
+    parallel_for(n, 1 << 16, [&](uint64_t b, uint64_t e) {
+        for (uint64_t i = b; i < e; ++i) {
+            const uint64_t a = rng_u(seed, stream, 2 * i), c = rng_u(seed, stream, 2 * i + 1);
+            const double u1 = (double)((a >> 11) + 1) * 0x1.0p-53;
+            const double u2 = (double)(c >> 11) * 0x1.0p-53;
+            const double z = std::sqrt(-2.0 * std::log(u1)) * std::cos(2.0 * M_PI * u2);
+            dst[i] = f32_to_bf16((float)(std * z));
+        }
+    });
+}
+
+// ---------------------------------------------------------------------------
+// Adam (fp32, one IEEE rounding per operation; no contraction)
+// ---------------------------------------------------------------------------
+struct AdamK {
+    float b1, b2, omb1, omb2, c1, c2, lr, eps, decay;
+    bool wd;
+};
+
+static AdamK adam_consts(const mt_adam_cfg* a, int64_t t) {
+    AdamK k;
+    k.b1 = (float)a->beta1;
+    k.b2 = (float)a->beta2;
+    k.omb1 = (float)(1.0 - a->beta1);
+    k.omb2 = (float)(1.0 - a->beta2);
+    k.c1 = (float)(1.0 - std::pow(a->beta1, (double)t));
+    k.c2 = (float)(1.0 - std::pow(a->beta2, (double)t));
+    k.lr = (float)a->lr;
+    k.eps = (float)a->eps;
+    k.decay = (float)(1.0 - a->lr * a->weight_decay);
+    k.wd = a->weight_decay != 0.0;
+    return k;
+}
+
+#pragma clang fp contract(off)
+static void adam_scalar(uint16_t* W, uint16_t* G, float* M, float* Vv, const uint16_t* src, float* wout,
+                        uint64_t b, uint64_t e, const AdamK& k) {
+    for (uint64_t i = b; i < e; ++i) {
+        if (src) G[i] = src[i];
+        float w = bf16_to_f32(W[i]);
+        if (k.wd) w = w * k.decay;
+        const float g = bf16_to_f32(G[i]);
+        const float m = k.b1 * M[i] + k.omb1 * g;
+        const float v = k.b2 * Vv[i] + k.omb2 * (g * g);
+        M[i] = m;
+        Vv[i] = v;
+        const float mhat = m / k.c1;
+        const float vhat = v / k.c2;
+        const float denom = std::sqrt(vhat) + k.eps;
+        const float step = k.lr * mhat;
+        const float wn = w - step / denom;
+        if (wout) wout[i] = wn;
+        W[i] = f32_to_bf16(wn);
+    }
+}
+
+__attribute__((target("avx512f,avx512bw"))) static void adam_avx512(uint16_t* W, uint16_t* G, float* M,
+                                                                      float* Vv, const uint16_t* src,
+                                                                      float* wout, uint64_t b, uint64_t e,
+                                                                      const AdamK& k) {
+    const __m512 b1 = _mm512_set1_ps(k.b1), b2 = _mm512_set1_ps(k.b2), omb1 = _mm512_set1_ps(k.omb1),
+                 omb2 = _mm512_set1_ps(k.omb2), c1 = _mm512_set1_ps(k.c1), c2 = _mm512_set1_ps(k.c2),
+                 lr = _mm512_set1_ps(k.lr), eps = _mm512_set1_ps(k.eps), dec = _mm512_set1_ps(k.decay);
+    const __m512i rnd = _mm512_set1_epi32(0x7fff), one = _mm512_set1_epi32(1);
+    uint64_t i = b;
+    for (; i + 16 <= e; i += 16) {
+        __m256i gb;
+        if (src) {
+            gb = _mm256_loadu_si256((const __m256i*)(src + i));
+            _mm256_storeu_si256((__m256i*)(G + i), gb);
+        } else {
+            gb = _mm256_loadu_si256((const __m256i*)(G + i));
+        }
+        const __m256i wb = _mm256_loadu_si256((const __m256i*)(W + i));
+        __m512 w = _mm512_castsi512_ps(_mm512_slli_epi32(_mm512_cvtepu16_epi32(wb), 16));
+        if (k.wd) w = _mm512_mul_ps(w, dec);
+        const __m512 g = _mm512_castsi512_ps(_mm512_slli_epi32(_mm512_cvtepu16_epi32(gb), 16));
+        const __m512 m = _mm512_add_ps(_mm512_mul_ps(b1, _mm512_loadu_ps(M + i)), _mm512_mul_ps(omb1, g));
+        const __m512 v = _mm512_add_ps(_mm512_mul_ps(b2, _mm512_loadu_ps(Vv + i)),
+                                       _mm512_mul_ps(omb2, _mm512_mul_ps(g, g)));
+        _mm512_storeu_ps(M + i, m);
+        _mm512_storeu_ps(Vv + i, v);
+        const __m512 mhat = _mm512_div_ps(m, c1);
+        const __m512 vhat = _mm512_div_ps(v, c2);
+        const __m512 denom = _mm512_add_ps(_mm512_sqrt_ps(vhat), eps);
+        const __m512 step = _mm512_mul_ps(lr, mhat);
+        const __m512 wn = _mm512_sub_ps(w, _mm512_div_ps(step, denom));
+        if (wout) _mm512_storeu_ps(wout + i, wn);
+        // round to nearest even (weights are finite)
+        __m512i u = _mm512_castps_si512(wn);
+        u = _mm512_add_epi32(u, _mm512_add_epi32(rnd, _mm512_and_si512(_mm512_srli_epi32(u, 16), one)));
+        _mm256_storeu_si256((__m256i*)(W + i), _mm512_cvtepi32_epi16(_mm512_srli_epi32(u, 16)));
+    }
+    if (i < e) adam_scalar(W, G, M, Vv, src, wout, i, e, k);
+}
+#pragma clang fp contract(on)
+
+static bool have_avx512() {
+    static const bool ok = __builtin_cpu_supports("avx512f") && __builtin_cpu_supports("avx512bw") &&
+                           getenv("MT_NO_AVX512") == nullptr;
+    return ok;
+}
+
+}  // namespace mt
+
+using namespace mt;
+
+// ===========================================================================
+// C ABI
+// ===========================================================================
+extern "C" {
+
+const char* mt_last_error(void) { return g_err; }
+
+int mt_set_threads(int n) {
+    return guard([&] {
+        MT_CHECK_ARG(n >= 0 && n <= 4096, "bad thread count %d", n);
+        g_threads.store(n);
+    });
+}
+
+int mt_unit_layout_get(const mt_model_cfg* cfg, int unit, mt_unit_layout* out) {
+    return guard([&] {
+        MT_CHECK_ARG(out != nullptr, "out is NULL");
+        *out = layout_of(cfg, unit);
+    });
+}
+
+int mt_store_create(const mt_model_cfg* cfg, mt_store** out) {
+    return guard([&] {
+        MT_CHECK_ARG(out != nullptr, "out is NULL");
+        check_cfg(cfg);
+        auto* st = new mt_store();
+        st->cfg = *cfg;
+        try {
+            for (int u = MT_UNIT_HEAD; u < cfg->layers; ++u) {
+                mt_unit_layout L = layout_of(cfg, u);
+                const uint64_t len = round_up(L.block_bytes, 2ull << 20);
+                st->layouts.push_back(L);
+                st->blocks.push_back(map_block(len));
+                st->mapped_bytes.push_back(len);
+            }
+        } catch (...) {
+            mt_store_destroy(st);
+            throw;
+        }
+        *out = st;
+    });
+}
+
+void mt_store_destroy(mt_store* st) {
+    if (!st) return;
+    for (size_t i = 0; i < st->blocks.size(); ++i)
+        if (st->blocks[i]) munmap(st->blocks[i], st->mapped_bytes[i]);
+    delete st;
+}
+
+int mt_store_block(mt_store* st, int unit, void** block) {
+    return guard([&] {
+        MT_CHECK_ARG(block != nullptr, "block is NULL");
+        *block = st->blocks[unit_index(st, unit)];
+    });
+}
+
+int mt_store_bytes(const mt_store* st, uint64_t* out) {
+    return guard([&] {
+        MT_CHECK_ARG(st && out, "NULL argument");
+        uint64_t s = 0;
+        for (auto& L : st->layouts) s += L.block_bytes;
+        *out = s;
+    });
+}
+
+int mt_store_fill_normal(mt_store* st, uint32_t seed, double std_) {
+    return guard([&] {
+        MT_CHECK_ARG(st != nullptr, "store is NULL");
+        MT_CHECK_ARG(seed < 65536, "seed must fit in 16 bits");
+        for (int u = MT_UNIT_HEAD; u < st->cfg.layers; ++u) {
+            const int idx = unit_index(st, u);
+            const mt_unit_layout& L = st->layouts[idx];
+            char* blk = (char*)st->blocks[idx];
+            // zero every region first (first touch happens here, in parallel)
+            parallel_for(L.block_bytes, 8ull << 20, [&](uint64_t b, uint64_t e) { memset(blk + b, 0, e - b); });
+            for (int j = 0; j < L.n_tensors; ++j) {
+                uint16_t* t = (uint16_t*)(blk + L.tensor_off[j]);
+                const uint64_t n = L.tensor_numel[j];
+                const bool gain = (u >= 0 && (j == 0 || j == 3)) || (u == MT_UNIT_HEAD && j == 0);
+                if (gain) {
+                    for (uint64_t i = 0; i < n; ++i) t[i] = 0x3F80;  // 1.0
+                } else {
+                    uint32_t stream = u >= 0 ? 16u + 8u * (uint32_t)u + (uint32_t)j
+                                             : (u == MT_UNIT_EMBED ? 1u : 3u);
+                    fill_normal(t, n, seed, stream, std_);
+                }
+            }
+        }
+    });
+}
+
+int mt_pack_layer(mt_store* st, int unit, void* dst, size_t dst_bytes) {
+    return guard([&] {
+        const int idx = unit_index(st, unit);
+        const mt_unit_layout& L = st->layouts[idx];
+        MT_CHECK_ARG(dst != nullptr, "dst is NULL");
+        MT_CHECK_ARG(dst_bytes >= L.w_bytes, "dst holds %zu bytes, unit needs %llu", dst_bytes,
+                     (unsigned long long)L.w_bytes);
+        par_memcpy(dst, (const char*)st->blocks[idx] + L.region_off[0], L.w_bytes);
+    });
+}
+
+int mt_pinned_alloc(size_t bytes, void** out) {
+    return guard([&] {
+        MT_CHECK_ARG(out != nullptr && bytes > 0, "bad arguments");
+        void* p = nullptr;
+        hip_check(hipHostMalloc(&p, bytes, hipHostMallocDefault), "hipHostMalloc");
+        *out = p;
+    });
+}
+
+int mt_pinned_free(void* p) {
+    return guard([&] {
+        if (p) hip_check(hipHostFree(p), "hipHostFree");
+    });
+}
+
+int mt_copy_h2d(void* dst_dev, const void* src_host, size_t bytes, void* stream) {
+    return guard([&] {
+        MT_CHECK_ARG(dst_dev && src_host, "NULL pointer");
+        hip_check(hipMemcpyAsync(dst_dev, src_host, bytes, hipMemcpyHostToDevice, (hipStream_t)stream),
+                  "hipMemcpyAsync H2D");
+    });
+}
+
+int mt_copy_d2h(void* dst_host, const void* src_dev, size_t bytes, void* stream) {
+    return guard([&] {
+        MT_CHECK_ARG(dst_host && src_dev, "NULL pointer");
+        hip_check(hipMemcpyAsync(dst_host, src_dev, bytes, hipMemcpyDeviceToHost, (hipStream_t)stream),
+                  "hipMemcpyAsync D2H");
+    });
+}
+
+int mt_step(mt_store* st, int unit, const void* grad_src, const mt_adam_cfg* adam, int64_t t,
+            float* w_fp32_out) {
+    return guard([&] {
+        const int idx = unit_index(st, unit);
+        MT_CHECK_ARG(adam != nullptr, "adam is NULL");
+        MT_CHECK_ARG(t >= 1, "step counter must be >= 1");
+        const mt_unit_layout& L = st->layouts[idx];
+        char* blk = (char*)st->blocks[idx];
+        uint16_t* W = (uint16_t*)(blk + L.region_off[0]);
+        uint16_t* G = (uint16_t*)(blk + L.region_off[1]);
+        float* M = (float*)(blk + L.region_off[2]);
+        float* Vv = (float*)(blk + L.region_off[3]);
+        const AdamK k = adam_consts(adam, t);
+        const uint64_t n = L.w_bytes / 2;
+        const uint16_t* src = (const uint16_t*)grad_src;
+        const bool simd = have_avx512();
+        parallel_for(n, 1 << 18, [&](uint64_t b, uint64_t e) {
+            if (simd)
+                adam_avx512(W, G, M, Vv, src, w_fp32_out, b, e, k);
+            else
+                adam_scalar(W, G, M, Vv, src, w_fp32_out, b, e, k);
+        });
+    });
+}
+
+int mt_embed_gather(mt_store* st, const int32_t* tok, int64_t T, void* dst) {
+    return guard([&] {
+        const int idx = unit_index(st, MT_UNIT_EMBED);
+        MT_CHECK_ARG(tok && dst && T >= 0, "bad arguments");
+        const uint64_t h = st->cfg.hidden;
+        const uint16_t* E = (const uint16_t*)((const char*)st->blocks[idx] + st->layouts[idx].region_off[0]);
+        for (int64_t t = 0; t < T; ++t)
+            MT_CHECK_ARG(tok[t] >= 0 && tok[t] < st->cfg.vocab, "token %d at %lld out of range", tok[t],
+                         (long long)t);
+        parallel_for((uint64_t)T, 256, [&](uint64_t b, uint64_t e) {
+            for (uint64_t t = b; t < e; ++t) memcpy((uint16_t*)dst + t * h, E + (uint64_t)tok[t] * h, 2 * h);
+        });
+    });
+}
+
+int mt_embed_grad(mt_store* st, const int32_t* tok, int64_t T, const float* dx0) {
+    return guard([&] {
+        const int idx = unit_index(st, MT_UNIT_EMBED);
+        MT_CHECK_ARG(tok && dx0 && T >= 0, "bad arguments");
+        const uint64_t h = st->cfg.hidden, V = st->cfg.vocab;
+        for (int64_t t = 0; t < T; ++t)
+            MT_CHECK_ARG(tok[t] >= 0 && tok[t] < st->cfg.vocab, "token out of range");
+        if (st->embed_acc.size() != V * h) st->embed_acc.assign(V * h, 0.f);
+        float* acc = st->embed_acc.data();
+        uint16_t* G = (uint16_t*)((char*)st->blocks[idx] + st->layouts[idx].region_off[1]);
+        // Columns are split across threads; every element is summed over t in
+        // ascending order, so the result does not depend on the thread count.
+        const uint64_t cgrain = 64;
+        parallel_for(h, cgrain, [&](uint64_t c0, uint64_t c1) {
+            for (uint64_t v = 0; v < V; ++v) memset(acc + v * h + c0, 0, 4 * (c1 - c0));
+            for (int64_t t = 0; t < T; ++t) {
+                float* row = acc + (uint64_t)tok[t] * h;
+                const float* src = dx0 + (uint64_t)t * h;
+                for (uint64_t c = c0; c < c1; ++c) row[c] += src[c];
+            }
+            for (uint64_t v = 0; v < V; ++v)
+                for (uint64_t c = c0; c < c1; ++c) G[v * h + c] = f32_to_bf16(acc[v * h + c]);
+        });
+    });
+}
+
+int mt_rope_tables(const mt_model_cfg* cfg, int32_t seq, float* cos_out, float* sin_out) {
+    return guard([&] {
+        check_cfg(cfg);
+        MT_CHECK_ARG(seq >= 1 && cos_out && sin_out, "bad arguments");
+        const int half = cfg->head_dim / 2;
+        std::vector<double> theta(half);
+        for (int i = 0; i < half; ++i)
+            theta[i] = std::pow((double)cfg->rope_base, (-2.0 * (double)i) / (double)cfg->head_dim);
+        parallel_for((uint64_t)seq, 1024, [&](uint64_t b, uint64_t e) {
+            for (uint64_t s = b; s < e; ++s)
+                for (int i = 0; i < half; ++i) {
+                    const double a = (double)s * theta[i];
+                    cos_out[s * half + i] = (float)std::cos(a);
+                    sin_out[s * half + i] = (float)std::sin(a);
+                }
+        });
+    });
+}
+
+}  // extern "C"

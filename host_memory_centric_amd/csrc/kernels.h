@@ -1,0 +1,68 @@
+// Host-side launchers of the gfx950 kernels used by the layer template.
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+
+#include "common.h"
+
+namespace mt {
+
+// Check the last launch (and, with MT_SYNC_CHECK=1, synchronise the stream).
+void launch_check(const char* what, hipStream_t s = nullptr);
+
+struct GemmDesc {
+    int64_t M = 0, N = 0, K = 0;
+    const void* A = nullptr;
+    int64_t lda = 0;
+    bool a_kmajor = true;
+    const void* B = nullptr;
+    int64_t ldb = 0;
+    bool b_kmajor = true;
+    float* Cf = nullptr;        // fp32 output (optional)
+    void* Cb = nullptr;         // bf16 output (optional)
+    const void* R = nullptr;    // bf16 residual added before storing (optional)
+    int64_t ldc = 0;
+    int accumulate = 0;         // Cf += result
+    void* ws = nullptr;         // split-K scratch (fp32)
+    size_t ws_bytes = 0;
+};
+void gemm(const GemmDesc& d, hipStream_t s);
+int gemm_pick_splits(int64_t M, int64_t N, int64_t K);
+size_t gemm_splitk_bytes(int64_t M, int64_t N, int64_t K);
+
+// RMSNorm over rows of length h: y = x * rstd * g (bf16 out), rstd fp32 [T].
+void rmsnorm_fwd(const uint16_t* x, const uint16_t* g, uint16_t* y, float* rstd, int64_t T, int h, float eps,
+                 hipStream_t s);
+// Backward: dx = resid + rstd * (dy*g - xh * mean(dy*g*xh)); writes fp32 and
+// bf16 dx (either may be NULL), and per-row-block partials of dg.
+int64_t rmsnorm_bwd_blocks(int64_t T);
+void rmsnorm_bwd(const float* dy, const uint16_t* x, const float* rstd, const uint16_t* g, const float* resid,
+                 float* dx, uint16_t* dx_b, float* dg_part, int64_t T, int h, hipStream_t s);
+// dg[j] = sum over blocks (in order) of part[b][j], stored bf16.
+void colsum_to_bf16(const float* part, int64_t nblk, int h, uint16_t* out, hipStream_t s);
+
+// RoPE on the q and k parts of a fused [T, 3h] buffer (in place); inverse
+// rotation when `inverse`.
+void rope_apply(uint16_t* qkv, const float* cos, const float* sin, int64_t T, int S, int heads, int hd,
+                bool inverse, hipStream_t s);
+
+// SwiGLU: a = silu(gate) * up from gu [T, 2f]; and its backward.
+void swiglu_fwd(const uint16_t* gu, uint16_t* a, int64_t T, int f, hipStream_t s);
+void swiglu_bwd(const uint16_t* da, const uint16_t* gu, uint16_t* dgu, int64_t T, int f, hipStream_t s);
+
+// Causal flash attention on a fused qkv buffer.
+void attention_fwd(const uint16_t* qkv, uint16_t* o, float* lse, int B, int S, int heads, int hd, hipStream_t s);
+void attention_bwd(const uint16_t* qkv, const uint16_t* o, const float* lse, const uint16_t* dout, uint16_t* dqkv,
+                   float* dvec, int B, int S, int heads, int hd, hipStream_t s);
+
+// Cross entropy over a chunk of logits z [rows, V] (fp32) for tokens
+// t0..t0+rows-1 of the batch: per-row loss and dz (bf16) = (softmax - onehot)/N.
+void cross_entropy(const float* z, const int32_t* tokens, int64_t t0, int64_t rows, int S, int V, float inv_n,
+                   float* row_loss, uint16_t* dz, hipStream_t s);
+// loss = sum(row_loss[0..n)) * scale, summed in a fixed order.
+void sum_scaled(const float* v, int64_t n, float scale, float* out, hipStream_t s);
+void f32_to_bf16(const float* x, uint16_t* y, int64_t n, hipStream_t s);
+
+}  // namespace mt

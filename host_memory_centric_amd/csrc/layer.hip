@@ -1,0 +1,472 @@
+// The stateless layer template (MegaTrain paper page, appendix A.4: templates
+// hold the attention and MLP kernels but no weight pointers; weights are bound
+// right before execution) and the head.  Every entry point here only enqueues
+// kernels on the caller's stream; all device memory (weight slot, gradient
+// slot, activations, saved internals, workspace) is the caller's.
+#include <cstdlib>
+#include <cstring>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace mt {
+
+namespace {
+
+// Bump allocator over a caller buffer (256-byte aligned pieces).
+struct Carve {
+    char* base;
+    size_t off = 0;
+    explicit Carve(void* b) : base((char*)b) {}
+    template <class T>
+    T* take(size_t count) {
+        T* p = base ? (T*)(base + off) : nullptr;
+        off = round_up(off + count * sizeof(T), 256);
+        return p;
+    }
+};
+
+// Internals of one layer's forward that its backward reads.
+struct Saved {
+    uint16_t* n1;    // RMSNorm output before attention [T, h]
+    float* rstd1;    // [T]
+    uint16_t* qkv;   // fused projection, q and k rotated [T, 3h]
+    uint16_t* o;     // attention output [T, h]
+    float* lse;      // [B, heads, S]
+    uint16_t* xm;    // residual stream after attention [T, h]
+    uint16_t* n2;    // RMSNorm output before the MLP [T, h]
+    float* rstd2;    // [T]
+    uint16_t* gu;    // gate | up [T, 2f]
+    uint16_t* a;     // silu(gate) * up [T, f]
+};
+
+Saved carve_saved(Carve& c, const mt_model_cfg* cfg, int64_t B, int64_t S) {
+    const int64_t T = B * S, h = cfg->hidden, f = cfg->ffn;
+    Saved s;
+    s.n1 = c.take<uint16_t>(T * h);
+    s.rstd1 = c.take<float>(T);
+    s.qkv = c.take<uint16_t>(T * 3 * h);
+    s.o = c.take<uint16_t>(T * h);
+    s.lse = c.take<float>(B * cfg->heads * S);
+    s.xm = c.take<uint16_t>(T * h);
+    s.n2 = c.take<uint16_t>(T * h);
+    s.rstd2 = c.take<float>(T);
+    s.gu = c.take<uint16_t>(T * 2 * f);
+    s.a = c.take<uint16_t>(T * f);
+    return s;
+}
+
+struct BwdWs {
+    Saved sv;         // internals when the caller keeps none
+    uint16_t* xtmp;   // forward output during recompute [T, h]
+    uint16_t* da;     // [T, f]
+    uint16_t* dgu;    // [T, 2f]
+    float* dn;        // gradient at a RMSNorm output [T, h]
+    float* dxm;       // gradient of the mid residual stream [T, h]
+    uint16_t* dxm_b;  // its bf16 copy
+    uint16_t* dout;   // gradient of the attention output [T, h]
+    float* dvec;      // [B, heads, S]
+    uint16_t* dqkv;   // [T, 3h]
+    float* dg_part;   // RMSNorm gain partials [blocks, h]
+    void* splitk;     // split-K partials
+    size_t splitk_bytes;
+};
+
+size_t splitk_need(const mt_model_cfg* cfg, int64_t T) {
+    const int64_t h = cfg->hidden, f = cfg->ffn;
+    size_t m = 0;
+    m = std::max(m, gemm_splitk_bytes(h, f, T));
+    m = std::max(m, gemm_splitk_bytes(2 * f, h, T));
+    m = std::max(m, gemm_splitk_bytes(h, h, T));
+    m = std::max(m, gemm_splitk_bytes(3 * h, h, T));
+    return m;
+}
+
+BwdWs carve_ws(Carve& c, const mt_model_cfg* cfg, int64_t B, int64_t S) {
+    const int64_t T = B * S, h = cfg->hidden, f = cfg->ffn;
+    BwdWs w;
+    w.sv = carve_saved(c, cfg, B, S);
+    w.xtmp = c.take<uint16_t>(T * h);
+    w.da = c.take<uint16_t>(T * f);
+    w.dgu = c.take<uint16_t>(T * 2 * f);
+    w.dn = c.take<float>(T * h);
+    w.dxm = c.take<float>(T * h);
+    w.dxm_b = c.take<uint16_t>(T * h);
+    w.dout = c.take<uint16_t>(T * h);
+    w.dvec = c.take<float>(B * cfg->heads * S);
+    w.dqkv = c.take<uint16_t>(T * 3 * h);
+    w.dg_part = c.take<float>(rmsnorm_bwd_blocks(T) * h);
+    w.splitk_bytes = splitk_need(cfg, T);
+    w.splitk = c.take<char>(w.splitk_bytes);
+    return w;
+}
+
+void check_act_shape(const mt_model_cfg* cfg, int32_t B, int32_t S) {
+    check_cfg(cfg);
+    if (B < 1 || S < 1) MT_FAIL(MT_E_SHAPE, "batch and seq must be positive");
+    if ((int64_t)B * S % 8) MT_FAIL(MT_E_SHAPE, "batch*seq must be a multiple of 8");
+    if (cfg->head_dim != 64 && cfg->head_dim != 128) MT_FAIL(MT_E_SHAPE, "head_dim must be 64 or 128");
+}
+
+template <class T>
+void need(const T* p, const char* what) {
+    if (!p) MT_FAIL(MT_E_ARG, "%s is NULL", what);
+    if ((uintptr_t)p & 15) MT_FAIL(MT_E_ALIGN, "%s must be 16-byte aligned", what);
+}
+
+GemmDesc gd(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, bool ak, const void* Bm, int64_t ldb,
+            bool bk, int64_t ldc) {
+    GemmDesc d;
+    d.M = M;
+    d.N = N;
+    d.K = K;
+    d.A = A;
+    d.lda = lda;
+    d.a_kmajor = ak;
+    d.B = Bm;
+    d.ldb = ldb;
+    d.b_kmajor = bk;
+    d.ldc = ldc;
+    return d;
+}
+
+// Forward of one layer: x -> y, internals into sv.
+void layer_forward(const mt_layer_view* v, const mt_model_cfg* cfg, int B, int S, const uint16_t* x, uint16_t* y,
+                   const float* cs, const float* sn, const Saved& sv, hipStream_t s) {
+    const int64_t T = (int64_t)B * S, h = cfg->hidden, f = cfg->ffn;
+    const uint16_t* g_attn = (const uint16_t*)v->w[0];
+    const uint16_t* wqkv = (const uint16_t*)v->w[1];
+    const uint16_t* wo = (const uint16_t*)v->w[2];
+    const uint16_t* g_mlp = (const uint16_t*)v->w[3];
+    const uint16_t* wgu = (const uint16_t*)v->w[4];
+    const uint16_t* wd = (const uint16_t*)v->w[5];
+
+    rmsnorm_fwd(x, g_attn, sv.n1, sv.rstd1, T, (int)h, cfg->eps, s);
+    GemmDesc d = gd(T, 3 * h, h, sv.n1, h, true, wqkv, h, true, 3 * h);
+    d.Cb = sv.qkv;
+    gemm(d, s);
+    rope_apply(sv.qkv, cs, sn, T, S, cfg->heads, cfg->head_dim, false, s);
+    attention_fwd(sv.qkv, sv.o, sv.lse, B, S, cfg->heads, cfg->head_dim, s);
+    d = gd(T, h, h, sv.o, h, true, wo, h, true, h);
+    d.R = x;
+    d.Cb = sv.xm;
+    gemm(d, s);
+    rmsnorm_fwd(sv.xm, g_mlp, sv.n2, sv.rstd2, T, (int)h, cfg->eps, s);
+    d = gd(T, 2 * f, h, sv.n2, h, true, wgu, h, true, 2 * f);
+    d.Cb = sv.gu;
+    gemm(d, s);
+    swiglu_fwd(sv.gu, sv.a, T, (int)f, s);
+    d = gd(T, h, f, sv.a, f, true, wd, f, true, h);
+    d.R = sv.xm;
+    d.Cb = y;
+    gemm(d, s);
+}
+
+void layer_backward(const mt_layer_view* v, const mt_model_cfg* cfg, const mt_act* io, const Saved& sv, BwdWs& w,
+                    hipStream_t s) {
+    const int B = io->batch, S = io->seq;
+    const int64_t T = (int64_t)B * S, h = cfg->hidden, f = cfg->ffn;
+    const uint16_t* wqkv = (const uint16_t*)v->w[1];
+    const uint16_t* wo = (const uint16_t*)v->w[2];
+    const uint16_t* wgu = (const uint16_t*)v->w[4];
+    const uint16_t* wd = (const uint16_t*)v->w[5];
+    const uint16_t* dyb = (const uint16_t*)io->dy_bf16;
+
+    // down projection
+    GemmDesc d = gd(h, f, T, dyb, h, false, sv.a, f, false, f);
+    d.Cb = v->g[5];
+    d.ws = w.splitk;
+    d.ws_bytes = w.splitk_bytes;
+    gemm(d, s);
+    d = gd(T, f, h, dyb, h, true, wd, f, false, f);
+    d.Cb = w.da;
+    gemm(d, s);
+    swiglu_bwd(w.da, sv.gu, w.dgu, T, (int)f, s);
+    // gate/up projection
+    d = gd(2 * f, h, T, w.dgu, 2 * f, false, sv.n2, h, false, h);
+    d.Cb = v->g[4];
+    d.ws = w.splitk;
+    d.ws_bytes = w.splitk_bytes;
+    gemm(d, s);
+    d = gd(T, h, 2 * f, w.dgu, 2 * f, true, wgu, h, false, h);
+    d.Cf = w.dn;
+    gemm(d, s);
+    // MLP RMSNorm (+ residual)
+    rmsnorm_bwd(w.dn, sv.xm, sv.rstd2, (const uint16_t*)v->w[3], io->dy, w.dxm, w.dxm_b, w.dg_part, T, (int)h, s);
+    colsum_to_bf16(w.dg_part, rmsnorm_bwd_blocks(T), (int)h, (uint16_t*)v->g[3], s);
+    // output projection
+    d = gd(h, h, T, w.dxm_b, h, false, sv.o, h, false, h);
+    d.Cb = v->g[2];
+    d.ws = w.splitk;
+    d.ws_bytes = w.splitk_bytes;
+    gemm(d, s);
+    d = gd(T, h, h, w.dxm_b, h, true, wo, h, false, h);
+    d.Cb = w.dout;
+    gemm(d, s);
+    // attention and RoPE
+    attention_bwd(sv.qkv, sv.o, sv.lse, w.dout, w.dqkv, w.dvec, B, S, cfg->heads, cfg->head_dim, s);
+    rope_apply(w.dqkv, io->rope_cos, io->rope_sin, T, S, cfg->heads, cfg->head_dim, true, s);
+    // QKV projection
+    d = gd(3 * h, h, T, w.dqkv, 3 * h, false, sv.n1, h, false, h);
+    d.Cb = v->g[1];
+    d.ws = w.splitk;
+    d.ws_bytes = w.splitk_bytes;
+    gemm(d, s);
+    d = gd(T, h, 3 * h, w.dqkv, 3 * h, true, wqkv, h, false, h);
+    d.Cf = w.dn;
+    gemm(d, s);
+    // attention RMSNorm (+ residual)
+    rmsnorm_bwd(w.dn, (const uint16_t*)io->x_in, sv.rstd1, (const uint16_t*)v->w[0], w.dxm, io->dx,
+                (uint16_t*)io->dx_bf16, w.dg_part, T, (int)h, s);
+    colsum_to_bf16(w.dg_part, rmsnorm_bwd_blocks(T), (int)h, (uint16_t*)v->g[0], s);
+}
+
+struct HeadWs {
+    uint16_t* xf;
+    float* rstd;
+    float* z;
+    uint16_t* dz;
+    float* dxf;
+    float* row_loss;
+    float* dwh;
+    float* dg_part;
+    void* splitk;
+    size_t splitk_bytes;
+};
+
+constexpr int64_t HEAD_CHUNK = 8192;
+
+HeadWs carve_head(Carve& c, const mt_model_cfg* cfg, int64_t B, int64_t S) {
+    const int64_t T = B * S, h = cfg->hidden, V = cfg->vocab;
+    const int64_t Tc = std::min(T, HEAD_CHUNK);
+    HeadWs w;
+    w.xf = c.take<uint16_t>(Tc * h);
+    w.rstd = c.take<float>(Tc);
+    w.z = c.take<float>(Tc * V);
+    w.dz = c.take<uint16_t>(Tc * V);
+    w.dxf = c.take<float>(Tc * h);
+    w.row_loss = c.take<float>(T);
+    w.dwh = c.take<float>(V * h);
+    w.dg_part = c.take<float>(((T + HEAD_CHUNK - 1) / HEAD_CHUNK) * rmsnorm_bwd_blocks(Tc) * h);
+    w.splitk_bytes = gemm_splitk_bytes(V, h, Tc);
+    w.splitk = c.take<char>(w.splitk_bytes);
+    return w;
+}
+
+hipStream_t as_stream(void* s) { return (hipStream_t)s; }
+
+}  // namespace
+
+}  // namespace mt
+
+using namespace mt;
+
+extern "C" {
+
+int mt_bind(const mt_model_cfg* cfg, int unit, const void* dev_w_slot, void* dev_g_slot, mt_layer_view* out) {
+    return guard([&] {
+        MT_CHECK_ARG(out != nullptr && dev_w_slot != nullptr, "NULL argument");
+        if (((uintptr_t)dev_w_slot | (uintptr_t)dev_g_slot) & 255)
+            MT_FAIL(MT_E_ALIGN, "device slots must be 256-byte aligned");
+        const mt_unit_layout L = layout_of(cfg, unit);
+        memset(out, 0, sizeof(*out));
+        for (int j = 0; j < L.n_tensors; ++j) {
+            out->w[j] = (const char*)dev_w_slot + L.tensor_off[j];
+            out->g[j] = dev_g_slot ? (char*)dev_g_slot + L.tensor_off[j] : nullptr;
+        }
+    });
+}
+
+int mt_layer_saved_bytes(const mt_model_cfg* cfg, int32_t batch, int32_t seq, size_t* out) {
+    return guard([&] {
+        MT_CHECK_ARG(out != nullptr, "out is NULL");
+        check_act_shape(cfg, batch, seq);
+        Carve c(nullptr);
+        carve_saved(c, cfg, batch, seq);
+        *out = c.off;
+    });
+}
+
+int mt_layer_workspace_bytes(const mt_model_cfg* cfg, int32_t batch, int32_t seq, size_t* out) {
+    return guard([&] {
+        MT_CHECK_ARG(out != nullptr, "out is NULL");
+        check_act_shape(cfg, batch, seq);
+        Carve c(nullptr);
+        carve_ws(c, cfg, batch, seq);
+        *out = c.off;
+    });
+}
+
+int mt_layer_fwd(const mt_layer_view* v, const mt_model_cfg* cfg, const mt_act* io, void* stream) {
+    return guard([&] {
+        MT_CHECK_ARG(v && io, "NULL argument");
+        check_act_shape(cfg, io->batch, io->seq);
+        need(io->x_in, "x_in");
+        need(io->x_out, "x_out");
+        need(io->rope_cos, "rope_cos");
+        need(io->rope_sin, "rope_sin");
+        for (int j = 0; j < 6; ++j) need(v->w[j], "weight view");
+        Saved sv;
+        if (io->saved) {
+            size_t nb;
+            mt_layer_saved_bytes(cfg, io->batch, io->seq, &nb);
+            if (io->saved_bytes < nb) MT_FAIL(MT_E_ARG, "saved buffer holds %zu bytes, needs %zu", io->saved_bytes, nb);
+            need(io->saved, "saved");
+            Carve c(io->saved);
+            sv = carve_saved(c, cfg, io->batch, io->seq);
+        } else {
+            size_t nb;
+            mt_layer_workspace_bytes(cfg, io->batch, io->seq, &nb);
+            if (io->workspace_bytes < nb)
+                MT_FAIL(MT_E_ARG, "workspace holds %zu bytes, needs %zu", io->workspace_bytes, nb);
+            need(io->workspace, "workspace");
+            Carve c(io->workspace);
+            sv = carve_saved(c, cfg, io->batch, io->seq);
+        }
+        layer_forward(v, cfg, io->batch, io->seq, (const uint16_t*)io->x_in, (uint16_t*)io->x_out, io->rope_cos,
+                      io->rope_sin, sv, as_stream(stream));
+    });
+}
+
+int mt_layer_recompute_bwd(const mt_layer_view* v, const mt_model_cfg* cfg, const mt_act* io, void* stream) {
+    return guard([&] {
+        MT_CHECK_ARG(v && io, "NULL argument");
+        check_act_shape(cfg, io->batch, io->seq);
+        need(io->x_in, "x_in");
+        need(io->dy, "dy");
+        need(io->dy_bf16, "dy_bf16");
+        need(io->dx, "dx");
+        need(io->dx_bf16, "dx_bf16");
+        need(io->rope_cos, "rope_cos");
+        need(io->rope_sin, "rope_sin");
+        for (int j = 0; j < 6; ++j) {
+            need(v->w[j], "weight view");
+            need(v->g[j], "gradient view");
+        }
+        size_t nb;
+        mt_layer_workspace_bytes(cfg, io->batch, io->seq, &nb);
+        if (io->workspace_bytes < nb) MT_FAIL(MT_E_ARG, "workspace holds %zu bytes, needs %zu", io->workspace_bytes, nb);
+        need(io->workspace, "workspace");
+        Carve c(io->workspace);
+        BwdWs w = carve_ws(c, cfg, io->batch, io->seq);
+        const hipStream_t s = as_stream(stream);
+        Saved sv = w.sv;
+        if (io->saved) {
+            size_t sb;
+            mt_layer_saved_bytes(cfg, io->batch, io->seq, &sb);
+            if (io->saved_bytes < sb) MT_FAIL(MT_E_ARG, "saved buffer holds %zu bytes, needs %zu", io->saved_bytes, sb);
+            need(io->saved, "saved");
+            Carve cs(io->saved);
+            sv = carve_saved(cs, cfg, io->batch, io->seq);
+        } else {
+            layer_forward(v, cfg, io->batch, io->seq, (const uint16_t*)io->x_in, w.xtmp, io->rope_cos, io->rope_sin, sv,
+                          s);
+        }
+        layer_backward(v, cfg, io, sv, w, s);
+    });
+}
+
+int mt_head_workspace_bytes(const mt_model_cfg* cfg, int32_t batch, int32_t seq, size_t* out) {
+    return guard([&] {
+        MT_CHECK_ARG(out != nullptr, "out is NULL");
+        check_act_shape(cfg, batch, seq);
+        Carve c(nullptr);
+        carve_head(c, cfg, batch, seq);
+        *out = c.off;
+    });
+}
+
+int mt_head_fwd_bwd(const mt_layer_view* v, const mt_model_cfg* cfg, const mt_head_io* io, void* stream) {
+    return guard([&] {
+        MT_CHECK_ARG(v && io, "NULL argument");
+        check_act_shape(cfg, io->batch, io->seq);
+        if (io->seq < 2) MT_FAIL(MT_E_SHAPE, "seq must be >= 2 for next-token loss");
+        need(io->x, "x");
+        need(io->dx, "dx");
+        need(io->dx_bf16, "dx_bf16");
+        need(io->loss, "loss");
+        MT_CHECK_ARG(io->tokens != nullptr, "tokens is NULL");
+        for (int j = 0; j < 2; ++j) {
+            need(v->w[j], "head weight view");
+            need(v->g[j], "head gradient view");
+        }
+        size_t nb;
+        mt_head_workspace_bytes(cfg, io->batch, io->seq, &nb);
+        if (io->workspace_bytes < nb) MT_FAIL(MT_E_ARG, "workspace holds %zu bytes, needs %zu", io->workspace_bytes, nb);
+        need(io->workspace, "workspace");
+        Carve c(io->workspace);
+        HeadWs w = carve_head(c, cfg, io->batch, io->seq);
+        const hipStream_t s = as_stream(stream);
+        const int64_t T = (int64_t)io->batch * io->seq, h = cfg->hidden, V = cfg->vocab;
+        const float inv_n = 1.0f / (float)((int64_t)io->batch * (io->seq - 1));
+        const uint16_t* gf = (const uint16_t*)v->w[0];
+        const uint16_t* wh = (const uint16_t*)v->w[1];
+        const uint16_t* x = (const uint16_t*)io->x;
+        const int64_t Tc = std::min(T, HEAD_CHUNK);
+        const int64_t bpc = rmsnorm_bwd_blocks(Tc);
+        int64_t nblk = 0;
+        for (int64_t t0 = 0, ci = 0; t0 < T; t0 += Tc, ++ci) {
+            const int64_t rows = std::min(Tc, T - t0);
+            rmsnorm_fwd(x + t0 * h, gf, w.xf, w.rstd, rows, (int)h, cfg->eps, s);
+            GemmDesc d = gd(rows, V, h, w.xf, h, true, wh, h, true, V);
+            d.Cf = w.z;
+            gemm(d, s);
+            cross_entropy(w.z, io->tokens, t0, rows, io->seq, (int)V, inv_n, w.row_loss + t0, w.dz, s);
+            d = gd(V, h, rows, w.dz, V, false, w.xf, h, false, h);
+            d.Cf = w.dwh;
+            d.accumulate = ci > 0;
+            d.ws = w.splitk;
+            d.ws_bytes = w.splitk_bytes;
+            gemm(d, s);
+            d = gd(rows, h, V, w.dz, V, true, wh, h, false, h);
+            d.Cf = w.dxf;
+            gemm(d, s);
+            rmsnorm_bwd(w.dxf, x + t0 * h, w.rstd, gf, nullptr, io->dx + t0 * h, (uint16_t*)io->dx_bf16 + t0 * h,
+                        w.dg_part + ci * bpc * h, rows, (int)h, s);
+            nblk = ci * bpc + rmsnorm_bwd_blocks(rows);
+        }
+        colsum_to_bf16(w.dg_part, nblk, (int)h, (uint16_t*)v->g[0], s);
+        f32_to_bf16(w.dwh, (uint16_t*)v->g[1], V * h, s);
+        sum_scaled(w.row_loss, T, inv_n, io->loss, s);
+    });
+}
+
+int mt_op_gemm(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, int a_kmajor, const void* B, int64_t ldb,
+               int b_kmajor, float* c_f32, void* c_bf16, const void* resid_bf16, int64_t ldc, int accumulate, void* ws,
+               size_t ws_bytes, void* stream) {
+    return guard([&] {
+        GemmDesc d = gd(M, N, K, A, lda, a_kmajor != 0, B, ldb, b_kmajor != 0, ldc);
+        d.Cf = c_f32;
+        d.Cb = c_bf16;
+        d.R = resid_bf16;
+        d.accumulate = accumulate;
+        d.ws = ws;
+        d.ws_bytes = ws_bytes;
+        gemm(d, as_stream(stream));
+    });
+}
+
+int mt_op_attention_fwd(int32_t batch, int32_t seq, int32_t heads, int32_t hd, const void* qkv, void* o, float* lse,
+                        void* stream) {
+    return guard([&] {
+        need(qkv, "qkv");
+        need(o, "o");
+        MT_CHECK_ARG(lse != nullptr, "lse is NULL");
+        attention_fwd((const uint16_t*)qkv, (uint16_t*)o, lse, batch, seq, heads, hd, as_stream(stream));
+    });
+}
+
+int mt_op_attention_bwd(int32_t batch, int32_t seq, int32_t heads, int32_t hd, const void* qkv, const void* o,
+                        const float* lse, const void* d_o, void* dqkv, float* dvec, void* stream) {
+    return guard([&] {
+        need(qkv, "qkv");
+        need(o, "o");
+        need(d_o, "d_o");
+        need(dqkv, "dqkv");
+        MT_CHECK_ARG(lse && dvec, "NULL argument");
+        attention_bwd((const uint16_t*)qkv, (const uint16_t*)o, lse, (const uint16_t*)d_o, (uint16_t*)dqkv, dvec, batch,
+                      seq, heads, hd, as_stream(stream));
+    });
+}
+
+}  // extern "C"

@@ -1,0 +1,431 @@
+"""Layer-streamed training engine (the schedule around the C ABI).
+
+One training step, in the method's order (MegaTrain paper page, section 3 and
+appendix A.2; hyper.ai summary, method; the author blog's block figure):
+
+* forward: for each layer, the packer thread copies its W region from the
+  pageable host store into a pinned staging buffer, the weight stream copies
+  it into a device slot and records *weights-ready*; the compute stream waits
+  for that event, binds the slot to the stateless template and runs the layer;
+  an event after the layer marks the slot *buffer-free* for the next copy.
+  Block-start activations (one every ``ckpt_every`` layers) stay on the device;
+  the last block also keeps its layer internals.
+* head: final RMSNorm, LM head and cross entropy with their backward.
+* backward, block by block from the top: re-stream and recompute the block's
+  layers from its checkpoint (keeping their internals), then run their
+  backward top-down.  After each layer's backward (*backward-done*) the
+  gradient stream copies its gradient slot into a pinned gradient slab; a host
+  optimizer thread waits for that copy, lands the slab into the store and runs
+  Adam on the layer, then recycles the slab.
+* the embedding gradient is scattered on the host and the embedding's Adam
+  runs last.
+
+Which device slot receives which weight load is planned for the whole step
+before it starts: since the sequence of layer uses is known, each load evicts
+the slot whose unit is needed furthest in the future.  With two slots this is
+the pages' double buffering; with more slots a recomputed block can stay
+resident for its backward.  ``resident`` mode is the same schedule with a
+single block covering all layers and one slot per unit (no recompute, no
+re-streaming), which must give bit-identical results.
+
+PyTorch provides device memory, streams and events only; every step of the
+computation runs in libmt.so.
+"""
+import ctypes
+import queue
+import time
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+import torch
+
+from . import _lib
+from ._lib import MT_UNIT_EMBED, MT_UNIT_HEAD, MtAct, MtHeadIO, MtLayerView, call
+from .store import HostStore
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+class PinnedBuffer:
+    """Library-owned pinned host memory with a numpy view."""
+
+    def __init__(self, nbytes):
+        p = ctypes.c_void_p()
+        call("mt_pinned_alloc", nbytes, ctypes.byref(p))
+        self.ptr = p
+        self.nbytes = nbytes
+
+    def view(self, dtype, count=None):
+        n = self.nbytes // np.dtype(dtype).itemsize if count is None else count
+        buf = (ctypes.c_char * (n * np.dtype(dtype).itemsize)).from_address(self.ptr.value)
+        return np.frombuffer(buf, dtype=dtype, count=n)
+
+    def free(self):
+        if self.ptr is not None and self.ptr.value:
+            call("mt_pinned_free", self.ptr)
+        self.ptr = None
+
+
+def plan_step(L, K, resident):
+    """Ops of one step: (kind, layer, saved_index).  kind in fwd/head/refwd/bwd."""
+    if resident:
+        K = L
+    nblk = (L + K - 1) // K
+    last0 = (nblk - 1) * K
+    ops = []
+    for l in range(L):
+        ops.append(("fwd", l, (l - last0) if l >= last0 else None))
+    ops.append(("head", None, None))
+    for b in reversed(range(nblk)):
+        lo, hi = b * K, min(L, (b + 1) * K)
+        if b != nblk - 1:
+            for l in range(lo, hi):
+                ops.append(("refwd", l, l - lo))
+        for l in reversed(range(lo, hi)):
+            ops.append(("bwd", l, l - lo))
+    return ops
+
+
+def plan_slots(units, n_slots):
+    """Assign a device slot to every use; returns (slot per use, load flag per use).
+
+    A use of a unit already resident is a hit.  Otherwise the load may not go
+    into the slot of the op just before it (that copy would have to wait for
+    that op, so nothing would overlap); among the other slots an empty one is
+    taken, else the one whose unit is next needed furthest in the future
+    (ties: the least recently used)."""
+    content = [None] * n_slots
+    last_used = [-1] * n_slots
+    slot_of, load = [], []
+    for i, u in enumerate(units):
+        if u in content:
+            s = content.index(u)
+            slot_of.append(s)
+            load.append(False)
+            last_used[s] = i
+            continue
+        cands = [k for k in range(n_slots) if n_slots == 1 or i == 0 or k != slot_of[i - 1]]
+        empty = [k for k in cands if content[k] is None]
+        if empty:
+            s = empty[0]
+        else:
+            def next_use(x):
+                for j in range(i + 1, len(units)):
+                    if units[j] == x:
+                        return j
+                return len(units) + 1
+            s = max(cands, key=lambda k: (next_use(content[k]), -last_used[k]))
+        content[s] = u
+        last_used[s] = i
+        slot_of.append(s)
+        load.append(True)
+    return slot_of, load
+
+
+class Trainer:
+    """Host-memory-centric trainer on one GPU.
+
+    cfg: model shape + batch/seq (``synth.ModelCfg``-like); adam: optimizer
+    settings; mode: 'streamed' or 'resident'; n_slots: device weight slots
+    (2 = the pages' double buffering); n_grad_slabs: pinned gradient slabs;
+    weights: None (seeded fill by the library) or bf16 bit arrays;
+    capture_w32: keep each unit's updated fp32 weights before their bf16
+    rounding (``self.w32[unit]``, W-region indexing) for parity checks."""
+
+    def __init__(self, cfg, adam, mode="streamed", n_slots=2, n_grad_slabs=12, ckpt_every=None, weights=None,
+                 device="cuda:0", capture_w32=False):
+        if mode not in ("streamed", "resident"):
+            raise ValueError("mode must be 'streamed' or 'resident'")
+        _lib.load()
+        self.cfg, self.adam_cfg, self.mode = cfg, adam, mode
+        self.dev = torch.device(device)
+        self.L = cfg.layers
+        self.K = self.L if mode == "resident" else (ckpt_every or cfg.ckpt_every)
+        self.n_slots = self.L + 1 if mode == "resident" else max(2, n_slots)
+        self.B, self.S = cfg.batch, cfg.seq
+        self.T = self.B * self.S
+        h = cfg.hidden
+        self.mcfg = _lib.model_cfg(cfg)
+        self.madam = _lib.adam_cfg(adam)
+        self.t = 0
+
+        self.store = HostStore(cfg)
+        if weights is None:
+            self.store.fill_normal()
+        else:
+            self.store.load_bits(weights)
+        self.lay = self.store.layout_of(0)
+        self.lay_head = self.store.layout_of(MT_UNIT_HEAD)
+        self.slot_bytes = max(self.lay.w_bytes, self.lay_head.w_bytes)
+
+        self.ops = plan_step(self.L, self.K, mode == "resident")
+        units = [MT_UNIT_HEAD if k == "head" else l for (k, l, _) in self.ops]
+        self.op_unit = units
+        self.op_slot, self.op_load = plan_slots(units, self.n_slots)
+
+        d, T = self.dev, self.T
+        bf, f32 = torch.bfloat16, torch.float32
+        self.slots = [torch.empty(self.slot_bytes, dtype=torch.uint8, device=d) for _ in range(self.n_slots)]
+        self.gslots = [torch.empty(self.lay.w_bytes, dtype=torch.uint8, device=d) for _ in range(2)]
+        self.head_g = torch.empty(self.lay_head.w_bytes, dtype=torch.uint8, device=d)
+        nblk = (self.L + self.K - 1) // self.K
+        self.ckpt = [torch.empty((T, h), dtype=bf, device=d) for _ in range(nblk)]
+        self.blockx = [None] + [torch.empty((T, h), dtype=bf, device=d) for _ in range(1, self.K)]
+        self.xscratch = torch.empty((T, h), dtype=bf, device=d)
+        self.xL = torch.empty((T, h), dtype=bf, device=d)
+        self.dgrad = [torch.empty((T, h), dtype=f32, device=d) for _ in range(2)]
+        self.dgrad_b = [torch.empty((T, h), dtype=bf, device=d) for _ in range(2)]
+        self.saved_bytes = _lib.size_query("mt_layer_saved_bytes", self.mcfg, self.B, self.S)
+        self.saved = [torch.empty(self.saved_bytes, dtype=torch.uint8, device=d) for _ in range(min(self.K, self.L))]
+        ws = max(_lib.size_query("mt_layer_workspace_bytes", self.mcfg, self.B, self.S),
+                 _lib.size_query("mt_head_workspace_bytes", self.mcfg, self.B, self.S))
+        self.ws = torch.empty(ws, dtype=torch.uint8, device=d)
+        self.ws_bytes = ws
+        cs = np.empty((self.S, cfg.head_dim // 2), dtype=np.float32)
+        sn = np.empty_like(cs)
+        call("mt_rope_tables", ctypes.byref(self.mcfg), self.S, cs.ctypes.data_as(ctypes.c_void_p),
+             sn.ctypes.data_as(ctypes.c_void_p))
+        self.rope_cos = torch.from_numpy(cs).to(d)
+        self.rope_sin = torch.from_numpy(sn).to(d)
+        self.tok_dev = torch.empty((self.B, self.S), dtype=torch.int32, device=d)
+        self.loss_dev = torch.zeros(1, dtype=f32, device=d)
+
+        self.wslab = [PinnedBuffer(self.slot_bytes) for _ in range(2)]
+        self.gslab = [PinnedBuffer(self.lay.w_bytes) for _ in range(max(1, n_grad_slabs))]
+        self.head_gslab = PinnedBuffer(self.lay_head.w_bytes)
+        self.x0_pin = PinnedBuffer(T * h * 2)
+        self.dx0_pin = PinnedBuffer(T * h * 4)
+        self.tok_pin = PinnedBuffer(T * 4)
+
+        self.s_comp = torch.cuda.Stream(device=d)
+        self.s_h2d = torch.cuda.Stream(device=d)
+        self.s_d2h = torch.cuda.Stream(device=d)
+        self.packer = ThreadPoolExecutor(1, thread_name_prefix="mt-pack")
+        self.optimizer = ThreadPoolExecutor(1, thread_name_prefix="mt-adam")
+        self.stats = {}
+        self.w32 = {}
+        if capture_w32:
+            for u in self.store.units:
+                self.w32[u] = np.zeros(self.store.layout_of(u).w_bytes // 2, dtype=np.float32)
+
+    def _w32_ptr(self, unit):
+        a = self.w32.get(unit)
+        return a.ctypes.data_as(ctypes.c_void_p) if a is not None else None
+
+    # ------------------------------------------------------------------
+    def close(self):
+        torch.cuda.synchronize(self.dev)
+        self.packer.shutdown(wait=True)
+        self.optimizer.shutdown(wait=True)
+        for b in self.wslab + self.gslab + [self.head_gslab, self.x0_pin, self.dx0_pin, self.tok_pin]:
+            b.free()
+        self.store.close()
+
+    def n_weight_loads(self):
+        return sum(self.op_load)
+
+    def _x(self, l):
+        if l == self.L:
+            return self.xL
+        if l % self.K == 0:
+            return self.ckpt[l // self.K]
+        return self.blockx[l % self.K]
+
+    def _bind(self, slot, gslot, unit):
+        v = MtLayerView()
+        call("mt_bind", ctypes.byref(self.mcfg), unit, _ptr(self.slots[slot]),
+             _ptr(gslot) if gslot is not None else None, ctypes.byref(v))
+        return v
+
+    def _act(self, x_in, x_out=None, saved=None, dy=None, dyb=None, dx=None, dxb=None):
+        a = MtAct()
+        a.batch, a.seq = self.B, self.S
+        a.x_in = x_in.data_ptr()
+        a.x_out = x_out.data_ptr() if x_out is not None else None
+        a.dy = dy.data_ptr() if dy is not None else None
+        a.dy_bf16 = dyb.data_ptr() if dyb is not None else None
+        a.dx = dx.data_ptr() if dx is not None else None
+        a.dx_bf16 = dxb.data_ptr() if dxb is not None else None
+        a.rope_cos = self.rope_cos.data_ptr()
+        a.rope_sin = self.rope_sin.data_ptr()
+        a.saved = saved.data_ptr() if saved is not None else None
+        a.saved_bytes = self.saved_bytes if saved is not None else 0
+        a.workspace = self.ws.data_ptr()
+        a.workspace_bytes = self.ws_bytes
+        return a
+
+    # ------------------------------------------------------------------
+    def step(self, tokens):
+        """One training step on int32 tokens [B, S].  Returns the loss."""
+        tokens = np.ascontiguousarray(tokens, dtype=np.int32)
+        if tokens.shape != (self.B, self.S):
+            raise ValueError(f"tokens must have shape {(self.B, self.S)}")
+        self.t += 1
+        t = self.t
+        h = self.cfg.hidden
+        cs, hs, ds = self.s_comp, self.s_h2d, self.s_d2h
+        sc, sh, sd = (ctypes.c_void_p(s.cuda_stream) for s in (cs, hs, ds))
+        t0 = time.perf_counter()
+
+        # embedding gather + tokens (host) -> device
+        tok_host = self.tok_pin.view(np.int32)
+        tok_host[:] = tokens.reshape(-1)
+        call("mt_embed_gather", self.store.ptr, self.tok_pin.ptr, self.T, self.x0_pin.ptr)
+        inputs_ready = torch.cuda.Event()
+        with torch.cuda.stream(hs):
+            call("mt_copy_h2d", _ptr(self.ckpt[0]), self.x0_pin.ptr, self.T * h * 2, sh)
+            call("mt_copy_h2d", _ptr(self.tok_dev), self.tok_pin.ptr, self.T * 4, sh)
+            inputs_ready.record(hs)
+        cs.wait_event(inputs_ready)
+
+        # weight loads of this step, in order
+        loads = [i for i, ld in enumerate(self.op_load) if ld]
+        load_of_op = {i: j for j, i in enumerate(loads)}
+        ready_ev = [torch.cuda.Event() for _ in loads]
+        op_done = [None] * len(self.ops)
+        # previous op that used the same slot (the copy into the slot waits for it)
+        slot_prev = [None] * len(self.ops)
+        last = {}
+        for i, s in enumerate(self.op_slot):
+            slot_prev[i] = last.get(s)
+            last[s] = i
+
+        def pack(j):
+            if j >= 2:
+                ready_ev[j - 2].synchronize()  # the copy that read this staging buffer is done
+            call("mt_pack_layer", self.store.ptr, self.op_unit[loads[j]], self.wslab[j % 2].ptr, self.slot_bytes)
+
+        pack_fut = {j: self.packer.submit(pack, j) for j in range(min(2, len(loads)))}
+        next_load = [0]
+
+        def issue_load(j):
+            i = loads[j]
+            pack_fut.pop(j).result()
+            unit = self.op_unit[i]
+            nbytes = (self.lay_head if unit == MT_UNIT_HEAD else self.lay).w_bytes
+            with torch.cuda.stream(hs):
+                if slot_prev[i] is not None:
+                    hs.wait_event(op_done[slot_prev[i]])  # buffer-free
+                call("mt_copy_h2d", _ptr(self.slots[self.op_slot[i]]), self.wslab[j % 2].ptr, nbytes, sh)
+                ready_ev[j].record(hs)  # weights-ready
+            if j + 2 < len(loads):
+                pack_fut[j + 2] = self.packer.submit(pack, j + 2)
+
+        def issue_ready_loads(upto):
+            # prefetch: issue the next loads whose slot is no longer needed by an
+            # op that is still to be enqueued, as long as their packing is done
+            while next_load[0] < len(loads):
+                j = next_load[0]
+                pu = slot_prev[loads[j]]
+                if pu is not None and pu > upto:
+                    break
+                if not pack_fut[j].done():
+                    break
+                issue_load(j)
+                next_load[0] += 1
+
+        slab_free = queue.Queue()
+        for k in range(len(self.gslab)):
+            slab_free.put(k)
+        gslot_d2h = [None, None]
+        adam_futs = []
+        cur = 0
+        n_bwd = 0
+
+        def adam_layer(ev, unit, slab):
+            ev.synchronize()
+            call("mt_step", self.store.ptr, unit, slab.ptr, ctypes.byref(self.madam), t, self._w32_ptr(unit))
+
+        def adam_layer_slab(ev, unit, k):
+            try:
+                adam_layer(ev, unit, self.gslab[k])
+            finally:
+                slab_free.put(k)
+
+        def adam_embed(ev):
+            ev.synchronize()
+            call("mt_embed_grad", self.store.ptr, self.tok_pin.ptr, self.T, self.dx0_pin.ptr)
+            call("mt_step", self.store.ptr, MT_UNIT_EMBED, None, ctypes.byref(self.madam), t,
+                 self._w32_ptr(MT_UNIT_EMBED))
+
+        issue_ready_loads(-1)
+        for i, (kind, l, si) in enumerate(self.ops):
+            if self.op_load[i]:
+                while next_load[0] <= load_of_op[i]:
+                    issue_load(next_load[0])
+                    next_load[0] += 1
+                cs.wait_event(ready_ev[load_of_op[i]])
+            slot = self.op_slot[i]
+            with torch.cuda.stream(cs):
+                if kind == "fwd":
+                    v = self._bind(slot, None, l)
+                    a = self._act(self._x(l), self._x(l + 1), self.saved[si] if si is not None else None)
+                    call("mt_layer_fwd", ctypes.byref(v), ctypes.byref(self.mcfg), ctypes.byref(a), sc)
+                elif kind == "refwd":
+                    out = self._x(l + 1) if (l + 1) % self.K != 0 else self.xscratch
+                    v = self._bind(slot, None, l)
+                    a = self._act(self._x(l), out, self.saved[si])
+                    call("mt_layer_fwd", ctypes.byref(v), ctypes.byref(self.mcfg), ctypes.byref(a), sc)
+                elif kind == "head":
+                    v = self._bind(slot, self.head_g, MT_UNIT_HEAD)
+                    io = MtHeadIO()
+                    io.batch, io.seq = self.B, self.S
+                    io.x = self.xL.data_ptr()
+                    io.tokens = self.tok_dev.data_ptr()
+                    io.dx = self.dgrad[cur].data_ptr()
+                    io.dx_bf16 = self.dgrad_b[cur].data_ptr()
+                    io.loss = self.loss_dev.data_ptr()
+                    io.workspace = self.ws.data_ptr()
+                    io.workspace_bytes = self.ws_bytes
+                    call("mt_head_fwd_bwd", ctypes.byref(v), ctypes.byref(self.mcfg), ctypes.byref(io), sc)
+                else:  # bwd
+                    g = n_bwd % 2
+                    if gslot_d2h[g] is not None:
+                        cs.wait_event(gslot_d2h[g])
+                    v = self._bind(slot, self.gslots[g], l)
+                    a = self._act(self._x(l), None, self.saved[si], dy=self.dgrad[cur], dyb=self.dgrad_b[cur],
+                                  dx=self.dgrad[1 - cur], dxb=self.dgrad_b[1 - cur])
+                    call("mt_layer_recompute_bwd", ctypes.byref(v), ctypes.byref(self.mcfg), ctypes.byref(a), sc)
+                    cur = 1 - cur
+                ev = torch.cuda.Event()
+                ev.record(cs)
+                op_done[i] = ev
+            if kind == "head":
+                d2h = torch.cuda.Event()
+                with torch.cuda.stream(ds):
+                    ds.wait_event(ev)
+                    call("mt_copy_d2h", self.head_gslab.ptr, _ptr(self.head_g), self.lay_head.w_bytes, sd)
+                    d2h.record(ds)
+                adam_futs.append(self.optimizer.submit(adam_layer, d2h, MT_UNIT_HEAD, self.head_gslab))
+            elif kind == "bwd":
+                g = n_bwd % 2
+                n_bwd += 1
+                k = slab_free.get()
+                d2h = torch.cuda.Event()
+                with torch.cuda.stream(ds):
+                    ds.wait_event(ev)
+                    call("mt_copy_d2h", self.gslab[k].ptr, _ptr(self.gslots[g]), self.lay.w_bytes, sd)
+                    if l == 0:
+                        call("mt_copy_d2h", self.dx0_pin.ptr, _ptr(self.dgrad[cur]), self.T * h * 4, sd)
+                    d2h.record(ds)
+                gslot_d2h[g] = d2h
+                adam_futs.append(self.optimizer.submit(adam_layer_slab, d2h, l, k))
+                if l == 0:
+                    adam_futs.append(self.optimizer.submit(adam_embed, d2h))
+            issue_ready_loads(i)
+
+        for f in adam_futs:
+            f.result()
+        for f in list(pack_fut.values()):
+            f.result()
+        cs.synchronize()
+        loss = float(self.loss_dev.item())
+        self.stats = {"step_s": time.perf_counter() - t0, "weight_loads": len(loads)}
+        return loss
+
+    # ------------------------------------------------------------------
+    def weights(self):
+        """bf16 bit arrays of all weights (host store)."""
+        return self.store.read_bits()

@@ -1,0 +1,102 @@
+"""Host store wrapper: the library-owned, layer-contiguous master copy.
+
+numpy views over a unit's regions are provided for filling weights and for
+inspection; all arithmetic on the store happens inside the library
+(``mt_step``, ``mt_embed_grad``, ``mt_pack_layer``).
+"""
+import ctypes
+
+import numpy as np
+
+from ._lib import MT_UNIT_EMBED, MT_UNIT_HEAD, call, load, model_cfg, unit_layout
+
+REGION_W, REGION_G, REGION_M, REGION_V = 0, 1, 2, 3
+LAYER_TENSORS = ("g_attn", "wqkv", "wo", "g_mlp", "wgu", "wd")
+
+
+def tensor_shapes(cfg, unit):
+    h, f, V = cfg.hidden, cfg.ffn, cfg.vocab
+    if unit == MT_UNIT_EMBED:
+        return [("embed", (V, h))]
+    if unit == MT_UNIT_HEAD:
+        return [("g_final", (h,)), ("head", (V, h))]
+    return [("g_attn", (h,)), ("wqkv", (3 * h, h)), ("wo", (h, h)), ("g_mlp", (h,)), ("wgu", (2 * f, h)),
+            ("wd", (h, f))]
+
+
+class HostStore:
+    def __init__(self, cfg):
+        load()
+        self.cfg = cfg
+        self.mcfg = model_cfg(cfg)
+        p = ctypes.c_void_p()
+        call("mt_store_create", ctypes.byref(self.mcfg), ctypes.byref(p))
+        self.ptr = p
+        self.units = [MT_UNIT_HEAD, MT_UNIT_EMBED] + list(range(cfg.layers))
+        self.layout = {u: unit_layout(self.mcfg, u) for u in (MT_UNIT_HEAD, MT_UNIT_EMBED, 0)}
+
+    def layout_of(self, unit):
+        return self.layout[unit if unit < 0 else 0]
+
+    def close(self):
+        if self.ptr is not None and self.ptr.value:
+            load().mt_store_destroy(self.ptr)
+        self.ptr = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def total_bytes(self):
+        out = ctypes.c_uint64()
+        call("mt_store_bytes", self.ptr, ctypes.byref(out))
+        return out.value
+
+    def block_addr(self, unit):
+        p = ctypes.c_void_p()
+        call("mt_store_block", self.ptr, unit, ctypes.byref(p))
+        return p.value
+
+    def region(self, unit, r):
+        """numpy view of a region over the W indexing (uint16 for W/G, float32 for M/V)."""
+        L = self.layout_of(unit)
+        n = L.w_bytes // 2
+        dt = np.uint16 if r in (REGION_W, REGION_G) else np.float32
+        addr = self.block_addr(unit) + L.region_off[r]
+        buf = (ctypes.c_char * (n * np.dtype(dt).itemsize)).from_address(addr)
+        return np.frombuffer(buf, dtype=dt, count=n)
+
+    def tensor(self, unit, name, r=REGION_W):
+        L = self.layout_of(unit)
+        reg = self.region(unit, r)
+        for j, (nm, shape) in enumerate(tensor_shapes(self.cfg, unit)):
+            if nm == name:
+                off = L.tensor_off[j] // 2
+                return reg[off:off + int(np.prod(shape))].reshape(shape)
+        raise KeyError(name)
+
+    def fill_normal(self, seed=None, std=0.02):
+        call("mt_store_fill_normal", self.ptr, self.cfg.seed if seed is None else seed, std)
+
+    def load_bits(self, bits):
+        """Copy weights given as bf16 bit arrays (the synth layout) into the W regions; zero G, M, V."""
+        for u in self.units:
+            for r in (REGION_G, REGION_M, REGION_V):
+                self.region(u, r)[:] = 0
+        self.tensor(MT_UNIT_EMBED, "embed")[:] = bits["embed"]
+        self.tensor(MT_UNIT_HEAD, "g_final")[:] = bits["g_final"]
+        self.tensor(MT_UNIT_HEAD, "head")[:] = bits["head"]
+        for l, lw in enumerate(bits["layers"]):
+            for name in LAYER_TENSORS:
+                self.tensor(l, name)[:] = lw[name]
+
+    def read_bits(self):
+        """Copy of all weights as bf16 bit arrays (the synth layout)."""
+        out = {"embed": self.tensor(MT_UNIT_EMBED, "embed").copy(),
+               "g_final": self.tensor(MT_UNIT_HEAD, "g_final").copy(),
+               "head": self.tensor(MT_UNIT_HEAD, "head").copy(), "layers": []}
+        for l in range(self.cfg.layers):
+            out["layers"].append({n: self.tensor(l, n).copy() for n in LAYER_TENSORS})
+        return out

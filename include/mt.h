@@ -1,0 +1,281 @@
+/*
+ * mt.h -- C ABI of the layer-streamed trainer (host-memory-centric training,
+ * MI355X / gfx950).
+ *
+ * The method (MegaTrain paper page, section 3 "MegaTrain System" and appendix
+ * A): host memory is the authoritative store of every layer's weights,
+ * gradients and Adam moments; each layer streams through a bounded device
+ * staging area, runs on a stateless layer template, is block-checkpointed and
+ * recomputed in the backward pass; its gradients are offloaded and a host
+ * Adam updates it.
+ *
+ * Conventions for every entry point
+ *  - returns int: MT_OK (0) or a negative MT_E_* code; mt_last_error() gives a
+ *    thread-local message for the last failure of the calling thread;
+ *  - no C++ exception crosses this boundary;
+ *  - device entry points validate arguments, enqueue work on the given HIP
+ *    stream and return; faults surface at the caller's next synchronisation
+ *    (set MT_SYNC_CHECK=1 in the environment to synchronise after every call);
+ *  - the library never allocates or frees device memory on the training path
+ *    and never creates streams or events: the caller owns device buffers,
+ *    workspaces, streams and events.  The host store, pinned buffers from
+ *    mt_pinned_alloc and the host worker threads belong to the library;
+ *  - all bf16 data is stored as raw 16-bit patterns (uint16), row-major;
+ *    floating-point roundings to bf16 are round-to-nearest-even.
+ */
+#ifndef MT_H
+#define MT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    MT_OK = 0,
+    MT_E_ARG = -1,    /* bad pointer, size or enum value */
+    MT_E_SHAPE = -2,  /* shape the kernels do not support (see each call) */
+    MT_E_ALIGN = -3,  /* pointer not aligned as documented */
+    MT_E_NOMEM = -4,  /* host allocation failed */
+    MT_E_HIP = -5,    /* a HIP runtime call failed (message holds its error) */
+    MT_E_STATE = -6   /* call out of order */
+};
+
+/* Units of the host store: layers are 0..layers-1. */
+enum { MT_UNIT_EMBED = -1, MT_UNIT_HEAD = -2 };
+
+#define MT_BLOCK_ALIGN 4096 /* region alignment inside a block (4 KB pages) */
+#define MT_TENSOR_ALIGN 256 /* tensor alignment inside a W/G region */
+
+/* Model shape.  Llama-style decoder: per layer RMSNorm gain [h], fused QKV
+ * weight [3h, h], output projection [h, h], RMSNorm gain [h], fused gate/up
+ * weight [2f, h] (gate rows first), down projection [h, f]; untied embedding
+ * [V, h]; final RMSNorm gain [h] and LM head [V, h].  Weights are [out, in]. */
+typedef struct mt_model_cfg {
+    int32_t layers, hidden, heads, head_dim, ffn, vocab;
+    float eps;       /* RMSNorm epsilon (inside the square root) */
+    float rope_base; /* RoPE base (rotate-half pairs (i, i + hd/2)) */
+} mt_model_cfg;
+
+/* Layout of one unit's block.  Layer-contiguous tiling (paper page, appendix
+ * A.1; hyper.ai summary, method): one block per unit holding, in order, the
+ * bf16 weight region W, the bf16 gradient region G, and the fp32 Adam moment
+ * regions M and V, each starting on a 4 KB boundary.  Tensors sit in W (and
+ * at the same offsets in G and in the device staging slot) at 256-byte
+ * aligned offsets; M and V use the same element indexing as W (4 bytes per
+ * element).  Padding elements are zero and stay zero under Adam. */
+typedef struct mt_unit_layout {
+    int32_t n_tensors;        /* 6 per layer; 1 for the embedding; 2 for the head */
+    int32_t pad_;
+    uint64_t tensor_off[6];   /* byte offset of tensor j inside W */
+    uint64_t tensor_numel[6]; /* element count of tensor j */
+    uint64_t w_bytes;         /* bytes of W incl. inter-tensor padding (== G's) */
+    uint64_t region_off[4];   /* W, G, M, V byte offsets inside the block */
+    uint64_t region_bytes[4]; /* their 4 KB-padded sizes */
+    uint64_t block_bytes;     /* total block size */
+    uint64_t params;          /* real parameter count of the unit */
+} mt_unit_layout;
+
+/* Pure function: the layout of `unit`.  MT_E_SHAPE if hidden != heads *
+ * head_dim, or a dimension is not a positive multiple of 8. */
+int mt_unit_layout_get(const mt_model_cfg* cfg, int unit, mt_unit_layout* out);
+
+/* ------------------------------------------------------------------------ */
+/* Host store (the authoritative copy of all training state).               */
+/* ------------------------------------------------------------------------ */
+typedef struct mt_store mt_store;
+
+/* Allocates one page-aligned, zero-filled block per unit (pageable memory;
+ * 2 MB huge pages are requested).  Owned by the library; free with
+ * mt_store_destroy. */
+int mt_store_create(const mt_model_cfg* cfg, mt_store** out);
+void mt_store_destroy(mt_store* st);
+/* Base address of a unit's block (layout as mt_unit_layout_get). */
+int mt_store_block(mt_store* st, int unit, void** block);
+/* Total bytes of all blocks. */
+int mt_store_bytes(const mt_store* st, uint64_t* out);
+/* Fills every W region from the seeded SplitMix64 generator: matrices
+ * bf16(fp32(std * N(0,1))) via Box-Muller, RMSNorm gains = 1.  Streams:
+ * embedding 1, final gain 2, LM head 3, layer l tensor j 16 + 8 l + j.
+ * Multithreaded.  Zeroes G, M and V. */
+int mt_store_fill_normal(mt_store* st, uint32_t seed, double std);
+
+/* Number of host worker threads used by pack, Adam, fill and embedding
+ * (default: the process's CPU affinity count). */
+int mt_set_threads(int n);
+
+/* ------------------------------------------------------------------------ */
+/* Transfer engine                                                          */
+/* ------------------------------------------------------------------------ */
+
+/* Just-in-time packer (hyper.ai summary, method: a dedicated CPU worker
+ * copies a layer from the pageable store into a pinned buffer from which DMA
+ * runs at full bandwidth).  Copies the unit's W region (w_bytes) to dst,
+ * which must hold at least w_bytes.  Multithreaded; safe to call for
+ * distinct units concurrently; must not overlap mt_step on the same unit. */
+int mt_pack_layer(mt_store* st, int unit, void* dst, size_t dst_bytes);
+
+/* Pinned (page-locked) host memory, hipHostMalloc-backed, owned by the
+ * library.  Used for the two weight staging buffers and the gradient slabs
+ * (paper page, appendix A.3: two pinned staging buffers sized to the largest
+ * layer; K pinned gradient slabs). */
+int mt_pinned_alloc(size_t bytes, void** out);
+int mt_pinned_free(void* p);
+
+/* Asynchronous copies on a caller stream (hipStream_t passed as void*):
+ * host->device weight stream and device->host gradient evacuation (paper
+ * page, appendix A.2: weight and gradient streams beside the compute stream).
+ * src/dst on the host side should be pinned for asynchronous DMA. */
+int mt_copy_h2d(void* dst_dev, const void* src_host, size_t bytes, void* stream);
+int mt_copy_d2h(void* dst_host, const void* src_dev, size_t bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Host optimizer                                                           */
+/* ------------------------------------------------------------------------ */
+typedef struct mt_adam_cfg {
+    double lr, beta1, beta2, eps, weight_decay;
+} mt_adam_cfg;
+
+/* CPU-side Adam over one unit (paper page, section 3: optimizer state never
+ * leaves host memory; appendix A: SIMD-accelerated optimizer).  If grad_src
+ * is non-NULL it holds the unit's bf16 gradient in W-region layout (w_bytes,
+ * e.g. a pinned gradient slab) and is first landed into G; then for every
+ * element, in fp32 with one rounding per operation:
+ *   w = bf16 W (times (1 - lr*wd) if wd != 0); g = bf16 G;
+ *   m = b1*m + (1-b1)*g;  v = b2*v + (1-b2)*(g*g);
+ *   w' = w - (lr * (m/c1)) / (sqrt(v/c2) + eps),  c1 = 1-b1^t, c2 = 1-b2^t;
+ *   W = bf16(w').
+ * Scalar constants are computed in fp64 and rounded once to fp32.  t >= 1.
+ * If w_fp32_out is non-NULL it receives w' (w_bytes/2 floats, W indexing)
+ * before rounding.  Multithreaded, deterministic. */
+int mt_step(mt_store* st, int unit, const void* grad_src, const mt_adam_cfg* adam, int64_t t,
+            float* w_fp32_out);
+
+/* Embedding on the host: dst[t, :] = E[tok[t], :] (bf16, [T, h]). */
+int mt_embed_gather(mt_store* st, const int32_t* tok, int64_t T, void* dst);
+/* Embedding gradient: dE[v] = sum over t with tok[t] == v of dx0[t]
+ * (fp32, accumulated in ascending t), rounded once to bf16 into the
+ * embedding unit's G region.  dx0: fp32 [T, h] on the host. */
+int mt_embed_grad(mt_store* st, const int32_t* tok, int64_t T, const float* dx0);
+
+/* RoPE tables computed on the host in fp64 (angle s * base^(-2i/hd)) and
+ * rounded to fp32: cos_out, sin_out are [seq, head_dim/2]. */
+int mt_rope_tables(const mt_model_cfg* cfg, int32_t seq, float* cos_out, float* sin_out);
+
+/* ------------------------------------------------------------------------ */
+/* Stateless layer template on the device                                   */
+/* ------------------------------------------------------------------------ */
+
+/* Views of one unit's tensors inside a device weight slot and gradient slot
+ * (same offsets as the host W region). */
+typedef struct mt_layer_view {
+    const void* w[6];
+    void* g[6];
+} mt_layer_view;
+
+/* Bind (paper page, appendix A.4; hyper.ai summary, method: a Bind primitive
+ * maps views of the streaming buffer onto the template's input slots).  Pure
+ * pointer arithmetic over the unit layout: no copy, no launch.  dev_g_slot may
+ * be NULL (forward only).  MT_E_ALIGN unless both slots are 256-byte
+ * aligned. */
+int mt_bind(const mt_model_cfg* cfg, int unit, const void* dev_w_slot, void* dev_g_slot,
+            mt_layer_view* out);
+
+/* Activations of one layer call.  T = batch * seq tokens, row-major [T, h]
+ * with token t = b * seq + s.  Positions restart at 0 in every batch row. */
+typedef struct mt_act {
+    int32_t batch, seq;
+    const void* x_in;      /* bf16 [T, h]: layer input */
+    void* x_out;           /* bf16 [T, h]: layer output (forward) */
+    const float* dy;       /* fp32 [T, h]: gradient of the layer output */
+    const void* dy_bf16;   /* bf16 copy of dy */
+    float* dx;             /* fp32 [T, h]: gradient of the layer input */
+    void* dx_bf16;         /* bf16 copy of dx */
+    const float* rope_cos; /* fp32 [seq, head_dim/2] (device) */
+    const float* rope_sin;
+    void* saved;           /* layer internals (mt_layer_saved_bytes) or NULL */
+    void* workspace;       /* mt_layer_workspace_bytes, 256-byte aligned */
+    size_t saved_bytes, workspace_bytes;
+} mt_act;
+
+int mt_layer_saved_bytes(const mt_model_cfg* cfg, int32_t batch, int32_t seq, size_t* out);
+int mt_layer_workspace_bytes(const mt_model_cfg* cfg, int32_t batch, int32_t seq, size_t* out);
+
+/* Layer forward (paper page, section 3, execution workflow: bind streamed
+ * weights to a template and compute): RMSNorm, QKV GEMM, RoPE, causal
+ * attention, output projection + residual, RMSNorm, gate/up GEMM, SwiGLU,
+ * down projection + residual.  x_out = layer(x_in).  When io->saved is
+ * non-NULL the internals needed by the backward are stored there; otherwise
+ * the workspace is used as scratch.  Needs x_in, x_out, rope tables,
+ * workspace.  MT_E_SHAPE unless head_dim is 64 or 128. */
+int mt_layer_fwd(const mt_layer_view* v, const mt_model_cfg* cfg, const mt_act* io, void* stream);
+
+/* Layer backward with recompute (paper page, section 3: block checkpoints,
+ * activations recomputed in the backward, gradients offloaded right away):
+ * if io->saved is NULL the layer's internals are first recomputed from x_in
+ * into the workspace; otherwise they are read from io->saved (written by an
+ * earlier mt_layer_fwd of the same x_in and weights).  The same kernels run in
+ * both cases, so the results are bit-identical.  Writes dx, dx_bf16 and the
+ * bf16 weight gradients into v->g (the device gradient slot). */
+int mt_layer_recompute_bwd(const mt_layer_view* v, const mt_model_cfg* cfg, const mt_act* io,
+                           void* stream);
+
+/* Head: final RMSNorm, LM head, mean next-token cross entropy over the
+ * batch*(seq-1) labelled positions (label of token (b, s) is tok[b, s+1]),
+ * and its backward, processed in token chunks of at most 8192. */
+typedef struct mt_head_io {
+    int32_t batch, seq;
+    const void* x;         /* bf16 [T, h]: output of the last layer */
+    const int32_t* tokens; /* device int32 [batch, seq] */
+    float* dx;             /* fp32 [T, h]: gradient of x */
+    void* dx_bf16;         /* bf16 copy of dx */
+    float* loss;           /* device fp32 scalar */
+    void* workspace;       /* mt_head_workspace_bytes */
+    size_t workspace_bytes;
+} mt_head_io;
+
+int mt_head_workspace_bytes(const mt_model_cfg* cfg, int32_t batch, int32_t seq, size_t* out);
+/* v binds the head unit: w[0] = final gain [h], w[1] = LM head [V, h];
+ * g[0], g[1] receive their bf16 gradients. */
+int mt_head_fwd_bwd(const mt_layer_view* v, const mt_model_cfg* cfg, const mt_head_io* io,
+                    void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Single-operation entry points (the template's kernels, for tests)        */
+/* ------------------------------------------------------------------------ */
+
+/* C = op(A) * op(B), bf16 inputs, fp32 accumulation on MFMA.
+ * a_kmajor: A is [M, K] (row stride lda) if nonzero, else [K, M].
+ * b_kmajor: B is [N, K] (row stride ldb) if nonzero, else [K, N].
+ * Outputs (any may be NULL, at least one not): c_f32 [M, N] fp32 (accumulated
+ * into when accumulate != 0), c_bf16 [M, N] bf16, optional resid_bf16 [M, N]
+ * added before rounding to c_bf16 / storing c_f32.  ldc is the row stride of
+ * all of C's arrays.  M, N, K, lda, ldb, ldc must be positive multiples of 8
+ * (MT_E_SHAPE otherwise); pointers 16-byte aligned.  ws/ws_bytes: fp32
+ * scratch for deterministic split-K (may be NULL: no split). */
+int mt_op_gemm(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, int a_kmajor,
+               const void* B, int64_t ldb, int b_kmajor, float* c_f32, void* c_bf16,
+               const void* resid_bf16, int64_t ldc, int accumulate, void* ws, size_t ws_bytes,
+               void* stream);
+
+/* Causal attention forward on a fused QKV buffer: qkv bf16 [batch*seq, 3*heads*hd]
+ * (q | k | v, head-major inside each), o bf16 [batch*seq, heads*hd],
+ * lse fp32 [batch, heads, seq] (natural-log row logsumexp of the scaled
+ * scores).  Scale 1/sqrt(hd).  hd in {64, 128}. */
+int mt_op_attention_fwd(int32_t batch, int32_t seq, int32_t heads, int32_t hd, const void* qkv,
+                        void* o, float* lse, void* stream);
+/* Its backward: writes dq | dk | dv into dqkv (same layout as qkv).
+ * dvec: fp32 scratch [batch, heads, seq]. */
+int mt_op_attention_bwd(int32_t batch, int32_t seq, int32_t heads, int32_t hd, const void* qkv,
+                        const void* o, const float* lse, const void* d_o, void* dqkv, float* dvec,
+                        void* stream);
+
+/* Thread-local message of the calling thread's last failure. */
+const char* mt_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MT_H */

@@ -1,0 +1,168 @@
+"""GPU parity of the single-operation entry points (C ABI) against the oracle.
+
+GEMM: small-integer bf16 inputs make every fp32 partial sum exact, so the
+MFMA kernels must match a brute-force integer product bit for bit, in all
+three operand orientations, both tile paths, split-K, ragged edges and each
+epilogue.  Attention: forward and backward against the oracle's plain
+softmax attention on the same bf16 inputs, within tolerances derived from
+bf16 probabilities.
+"""
+import ctypes
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from host_memory_centric_amd import _lib
+from host_memory_centric_amd._lib import MtError, call
+
+pytestmark = pytest.mark.gpu
+
+
+def _dev(a, gpu):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a)).to(gpu)
+
+
+def _p(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _stream():
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _int_bf16(shape, stream):
+    n = int(np.prod(shape))
+    return synth.uniform_int_bf16_bits(0, stream, n).reshape(shape)
+
+
+def _run_gemm(gpu, M, N, K, ak, bk, epi, seed, ws_mb=64):
+    import torch
+    A = _int_bf16((M, K) if ak else (K, M), 100 + seed)
+    B = _int_bf16((N, K) if bk else (K, N), 200 + seed)
+    Af = synth.bf16_bits_to_f32(A).astype(np.int64)
+    Bf = synth.bf16_bits_to_f32(B).astype(np.int64)
+    ref = (Af if ak else Af.T) @ (Bf.T if bk else Bf)
+    dA, dB = _dev(A.view(np.int16), gpu), _dev(B.view(np.int16), gpu)
+    cf = torch.full((M, N), 7.0, dtype=torch.float32, device=gpu)
+    cb = torch.zeros((M, N), dtype=torch.int16, device=gpu)
+    R = _int_bf16((M, N), 300 + seed)
+    dR = _dev(R.view(np.int16), gpu)
+    ws = torch.empty(ws_mb << 20, dtype=torch.uint8, device=gpu)
+    use_f, use_b, use_r, acc = {"f32": (1, 0, 0, 0), "bf16": (0, 1, 0, 0), "resid": (1, 1, 1, 0),
+                                "accum": (1, 0, 0, 1)}[epi]
+    call("mt_op_gemm", M, N, K, _p(dA), K if ak else M, int(ak), _p(dB), K if bk else N, int(bk),
+         _p(cf) if use_f else None, _p(cb) if use_b else None, _p(dR) if use_r else None, N, acc, _p(ws),
+         ws.numel(), _stream())
+    torch.cuda.synchronize()
+    exp = ref.astype(np.float64)
+    if use_r:
+        exp = exp + synth.bf16_bits_to_f32(R)
+    if acc:
+        exp = exp + 7.0
+    if use_f:
+        assert np.array_equal(cf.cpu().numpy(), exp.astype(np.float32))
+    if use_b:
+        assert np.array_equal(cb.cpu().numpy().view(np.uint16), synth.f32_to_bf16_bits(exp.astype(np.float32)))
+
+
+@pytest.mark.parametrize("ak,bk", [(True, True), (True, False), (False, False), (False, True)])
+@pytest.mark.parametrize("M,N,K", [(136, 264, 200), (8, 8, 8), (1032, 1288, 520)])
+def test_gemm_integer_exact(gpu, ak, bk, M, N, K):
+    _run_gemm(gpu, M, N, K, ak, bk, "f32", seed=M + N + K)
+
+
+@pytest.mark.parametrize("epi", ["bf16", "resid", "accum"])
+def test_gemm_epilogues(gpu, epi):
+    _run_gemm(gpu, 264, 136, 128, True, True, epi, seed=3)
+    _run_gemm(gpu, 1040, 1024, 64, True, False, epi, seed=4)
+
+
+@pytest.mark.parametrize("ak,bk", [(False, False), (True, False)])
+def test_gemm_split_k_exact(gpu, ak, bk):
+    # 4 output tiles over K = 16384 -> split into slices, summed in order
+    _run_gemm(gpu, 256, 256, 16384, ak, bk, "bf16", seed=5)
+    _run_gemm(gpu, 256, 256, 16384, ak, bk, "resid", seed=6)
+
+
+def test_gemm_rejects_bad_shapes(gpu):
+    import torch
+    t = torch.zeros(64, dtype=torch.int16, device=gpu)
+    with pytest.raises(MtError) as e:
+        call("mt_op_gemm", 12, 8, 8, _p(t), 8, 1, _p(t), 8, 1, _p(t), None, None, 8, 0, None, 0, _stream())
+    assert e.value.code == -2
+
+
+def _attn_inputs(B, S, nh, hd, seed):
+    rng = np.random.default_rng(seed)
+    qkv = (rng.standard_normal((B * S, 3 * nh * hd)) * 0.9).astype(np.float32)
+    return synth.f32_to_bf16_bits(qkv)
+
+
+def _split_heads(a, B, S, nh, hd):
+    return a.reshape(B, S, nh, hd).transpose(0, 2, 1, 3)
+
+
+def _metrics(got, ref):
+    got = got.astype(np.float64).reshape(-1)
+    ref = ref.astype(np.float64).reshape(-1)
+    mar = np.abs(got - ref).max() / max(np.abs(ref).max(), 1e-30)
+    cos = got @ ref / max(np.linalg.norm(got) * np.linalg.norm(ref), 1e-300)
+    return mar, cos
+
+
+@pytest.mark.parametrize("hd", [64, 128])
+@pytest.mark.parametrize("B,S,nh", [(2, 200, 3), (1, 1, 2), (1, 37, 1), (1, 384, 2)])
+def test_attention_fwd_bwd_vs_oracle(gpu, hd, B, S, nh):
+    import torch
+    H = nh * hd
+    qkv = _attn_inputs(B, S, nh, hd, seed=S + hd)
+    rng = np.random.default_rng(S * 7 + hd)
+    do = synth.f32_to_bf16_bits(rng.standard_normal((B * S, H)).astype(np.float32))
+    dq = _dev(qkv.view(np.int16), gpu)
+    o = torch.zeros((B * S, H), dtype=torch.int16, device=gpu)
+    lse = torch.zeros((B, nh, S), dtype=torch.float32, device=gpu)
+    call("mt_op_attention_fwd", B, S, nh, hd, _p(dq), _p(o), _p(lse), _stream())
+    ddo = _dev(do.view(np.int16), gpu)
+    dqkv = torch.zeros((B * S, 3 * H), dtype=torch.int16, device=gpu)
+    dvec = torch.zeros((B, nh, S), dtype=torch.float32, device=gpu)
+    call("mt_op_attention_bwd", B, S, nh, hd, _p(dq), _p(o), _p(lse), _p(ddo), _p(dqkv), _p(dvec), _stream())
+    torch.cuda.synchronize()
+
+    f = synth.bf16_bits_to_f32(qkv)
+    q = _split_heads(f[:, :H], B, S, nh, hd)
+    k = _split_heads(f[:, H:2 * H], B, S, nh, hd)
+    v = _split_heads(f[:, 2 * H:], B, S, nh, hd)
+    o_ref, P = oracle.attention_fwd(q, k, v)
+    o_gpu = _split_heads(synth.bf16_bits_to_f32(o.cpu().numpy().view(np.uint16)), B, S, nh, hd)
+    mar, cos = _metrics(o_gpu, o_ref)
+    assert mar < 2e-2 and cos > 0.9998, (mar, cos)
+    s = np.einsum("bhqd,bhkd->bhqk", q.astype(np.float64), k.astype(np.float64)) / np.sqrt(hd)
+    s = np.where(np.triu(np.ones((S, S), bool), 1), -np.inf, s)
+    lse_ref = np.log(np.exp(s - s.max(-1, keepdims=True)).sum(-1)) + s.max(-1)
+    assert np.abs(lse.cpu().numpy() - lse_ref).max() < 2e-3
+
+    dof = _split_heads(synth.bf16_bits_to_f32(do), B, S, nh, hd)
+    # the backward is checked at the kernel's own forward output (bf16 o)
+    dq_ref, dk_ref, dv_ref = oracle.attention_bwd(dof, q, k, v, o_gpu, P)
+    g = synth.bf16_bits_to_f32(dqkv.cpu().numpy().view(np.uint16))
+    for name, ref, got in (("dq", dq_ref, g[:, :H]), ("dk", dk_ref, g[:, H:2 * H]), ("dv", dv_ref, g[:, 2 * H:])):
+        got = _split_heads(got, B, S, nh, hd)
+        if np.abs(ref).max() < 1e-5:
+            # a single key (S = 1) has no softmax gradient: dq and dk vanish
+            assert np.abs(got).max() < 1e-4, name
+            continue
+        mar, cos = _metrics(got, ref)
+        assert mar < 3e-2 and cos > 0.9995, (name, mar, cos)
+
+
+def test_attention_rejects_head_dim(gpu):
+    import torch
+    t = torch.zeros(1 << 16, dtype=torch.int16, device=gpu)
+    lse = torch.zeros(64, dtype=torch.float32, device=gpu)
+    with pytest.raises(MtError) as e:
+        call("mt_op_attention_fwd", 1, 8, 1, 96, _p(t), _p(t), _p(lse), _stream())
+    assert e.value.code == -2

@@ -1,0 +1,313 @@
+"""Host-side parts of libmt.so, on the CPU (no GPU needed).
+
+The library must load and export every entry point the header declares; the
+host store layout must follow the layer-contiguous, 4 KB-aligned block format;
+the seeded filler must reproduce the synthetic-input generator bit for bit;
+the packer must copy the W region; the host Adam must equal the oracle's Adam
+bit for bit; the embedding gather/scatter and RoPE tables must match the
+oracle.  The schedule planner (pure Python) is checked for the number of
+weight loads the method implies.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from host_memory_centric_amd import _lib
+from host_memory_centric_amd._lib import MT_UNIT_EMBED, MT_UNIT_HEAD, MtError, call
+from host_memory_centric_amd.engine import plan_slots, plan_step
+from host_memory_centric_amd.store import REGION_G, REGION_M, REGION_V, REGION_W, HostStore, tensor_shapes
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    hdr = open(os.path.join(ROOT, "include", "mt.h")).read()
+    declared = set(re.findall(r"\b(mt_[a-z0-9_]+)\s*\(", hdr))
+    assert len(declared) >= 25
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert declared == set(_lib.EXPORTED)
+
+
+def _units(cfg):
+    return [MT_UNIT_HEAD, MT_UNIT_EMBED] + list(range(cfg.layers))
+
+
+@pytest.mark.parametrize("name", ["tiny", "7b", "14b", "depth180", "width5x"])
+def test_layout_alignment_and_accounting(lib, name):
+    cfg = synth.preset(name)
+    m = _lib.model_cfg(cfg)
+    total_params = 0
+    total_bytes = 0
+    for u in (MT_UNIT_HEAD, MT_UNIT_EMBED, 0):
+        L = _lib.unit_layout(m, u)
+        shapes = tensor_shapes(cfg, u)
+        assert L.n_tensors == len(shapes)
+        for j, (_, shp) in enumerate(shapes):
+            assert L.tensor_off[j] % 256 == 0
+            assert L.tensor_numel[j] == int(np.prod(shp))
+            if j:
+                assert L.tensor_off[j] >= L.tensor_off[j - 1] + 2 * L.tensor_numel[j - 1]
+        for r in range(4):
+            assert L.region_off[r] % 4096 == 0 and L.region_bytes[r] % 4096 == 0
+        assert L.region_off[1] == L.region_bytes[0] and L.region_bytes[1] == L.region_bytes[0]
+        assert L.region_bytes[2] >= 2 * L.w_bytes and L.region_bytes[3] == L.region_bytes[2]
+        assert L.block_bytes == sum(L.region_bytes)
+        mult = cfg.layers if u == 0 else 1
+        total_params += mult * L.params
+        total_bytes += mult * L.block_bytes
+    per_param = total_bytes / total_params
+    assert 12.0 <= per_param < 12.0 + 0.05 if name != "tiny" else per_param < 12.3
+
+
+def test_state_accounting_matches_pages(lib):
+    rows = {}
+    for line in open(os.path.join(ROOT, "tests", "golden", "state_accounting.txt")):
+        if line.strip() and not line.startswith("#"):
+            k, v = line.split()
+            rows[k] = int(v)
+    # bytes per real parameter of the block format, padding excluded
+    cfg = synth.preset("7b")
+    L = _lib.unit_layout(_lib.model_cfg(cfg), 0)
+    per = (2 * L.w_bytes + 2 * 4 * (L.w_bytes // 2)) / L.params  # W + G + M + V over the W indexing
+    assert round(per) == rows["bytes_per_param"]
+    assert rows["bytes_per_param"] * rows["params"] == rows["bytes"]
+
+
+def test_shape_errors(lib):
+    cfg = synth.preset("tiny").with_(heads=3)
+    with pytest.raises(MtError) as e:
+        _lib.unit_layout(_lib.model_cfg(cfg), 0)
+    assert e.value.code == -2
+    with pytest.raises(MtError) as e:
+        _lib.unit_layout(_lib.model_cfg(synth.preset("tiny")), 7)
+    assert e.value.code == -1
+
+
+def _bits_cfg():
+    # wide enough that every tensor spans many generator chunks
+    return synth.ModelCfg("host", 2, 512, 8, 64, 1376, 2048, 1, 16)
+
+
+def test_store_fill_matches_synth_generator(lib):
+    cfg = _bits_cfg()
+    st = HostStore(cfg)
+    try:
+        st.fill_normal(seed=0)
+        ref = synth.make_weights(cfg)
+        assert np.array_equal(st.tensor(MT_UNIT_EMBED, "embed"), ref["embed"])
+        assert np.array_equal(st.tensor(MT_UNIT_HEAD, "head"), ref["head"])
+        assert np.array_equal(st.tensor(MT_UNIT_HEAD, "g_final"), ref["g_final"])
+        for l in range(cfg.layers):
+            for k, a in ref["layers"][l].items():
+                assert np.array_equal(st.tensor(l, k), a), (l, k)
+        for u in _units(cfg):
+            for r in (REGION_G, REGION_M, REGION_V):
+                assert not st.region(u, r).any()
+    finally:
+        st.close()
+
+
+def test_store_fill_sampled_large_indices(lib):
+    """Elements near the end of a 7B-sized fused gate/up tensor (index ~9e7)."""
+    cfg = synth.ModelCfg("probe", 1, 4096, 32, 128, 11008, 8, 1, 8)
+    st = HostStore(cfg)
+    try:
+        st.fill_normal(seed=0)
+        wgu = st.tensor(0, "wgu").reshape(-1)
+        n = wgu.size
+        for start in (0, n // 3, n - 4096):
+            ref = synth.normal_bf16_bits(0, synth.layer_stream(0, 4), 4096, start=start)
+            assert np.array_equal(wgu[start:start + 4096], ref)
+    finally:
+        st.close()
+
+
+def test_pack_copies_w_region(lib):
+    cfg = synth.preset("tiny")
+    st = HostStore(cfg)
+    try:
+        st.fill_normal()
+        L = st.layout_of(0)
+        dst = np.zeros(L.w_bytes // 2 + 100, dtype=np.uint16)
+        call("mt_pack_layer", st.ptr, 1, dst.ctypes.data_as(ctypes.c_void_p), dst.nbytes)
+        assert np.array_equal(dst[: L.w_bytes // 2], st.region(1, REGION_W))
+        with pytest.raises(MtError):
+            call("mt_pack_layer", st.ptr, 1, dst.ctypes.data_as(ctypes.c_void_p), 16)
+    finally:
+        st.close()
+
+
+@pytest.mark.parametrize("wd", [0.0, 0.1])
+def test_host_adam_bitwise_equals_oracle(lib, wd):
+    cfg = synth.preset("tiny")
+    adam = synth.AdamCfg(weight_decay=wd)
+    st = HostStore(cfg)
+    try:
+        bits = synth.make_weights(cfg)
+        st.load_bits(bits)
+        rng = np.random.default_rng(0)
+        L = st.layout_of(0)
+        n = L.w_bytes // 2
+        m_ref = {k: np.zeros(a.shape, np.float32) for k, a in bits["layers"][1].items()}
+        v_ref = {k: np.zeros(a.shape, np.float32) for k, a in bits["layers"][1].items()}
+        w_bits = {k: a.copy() for k, a in bits["layers"][1].items()}
+        for t in (1, 2, 3):
+            g32 = {k: (rng.standard_normal(a.shape) * 10 ** rng.uniform(-7, -2)).astype(np.float32)
+                   for k, a in bits["layers"][1].items()}
+            slab = np.zeros(n, dtype=np.uint16)
+            for j, (name, shp) in enumerate(tensor_shapes(cfg, 1)):
+                off = L.tensor_off[j] // 2
+                slab[off:off + int(np.prod(shp))] = synth.f32_to_bf16_bits(g32[name]).reshape(-1)
+            wout = np.zeros(n, dtype=np.float32)
+            call("mt_step", st.ptr, 1, slab.ctypes.data_as(ctypes.c_void_p), ctypes.byref(_lib.adam_cfg(adam)), t,
+                 wout.ctypes.data_as(ctypes.c_void_p))
+            for j, (name, shp) in enumerate(tensor_shapes(cfg, 1)):
+                off = L.tensor_off[j] // 2
+                cnt = int(np.prod(shp))
+                nb, wf = oracle.adam_update(w_bits[name], g32[name], m_ref[name], v_ref[name], adam, t)
+                w_bits[name] = nb
+                assert np.array_equal(wout[off:off + cnt].view(np.uint32), wf.reshape(-1).view(np.uint32)), name
+                assert np.array_equal(st.tensor(1, name), nb), name
+                assert np.array_equal(st.tensor(1, name, REGION_M), m_ref[name]), name
+                assert np.array_equal(st.tensor(1, name, REGION_V), v_ref[name]), name
+                assert np.array_equal(st.tensor(1, name, REGION_G).reshape(-1),
+                                      slab[off:off + cnt]), name
+        # padding elements stay zero
+        wreg = st.region(1, REGION_W)
+        mask = np.ones(n, dtype=bool)
+        for j in range(L.n_tensors):
+            mask[L.tensor_off[j] // 2: L.tensor_off[j] // 2 + L.tensor_numel[j]] = False
+        assert not wreg[mask].any()
+    finally:
+        st.close()
+
+
+def test_host_adam_scalar_path_equals_simd(lib, monkeypatch):
+    """The AVX-512 and scalar paths give identical bits (checked in a subprocess)."""
+    import subprocess
+    import sys
+    code = r'''
+import ctypes, numpy as np, synth
+from host_memory_centric_amd import _lib
+from host_memory_centric_amd.store import HostStore
+cfg = synth.preset("tiny")
+st = HostStore(cfg); st.fill_normal()
+n = st.layout_of(0).w_bytes // 2
+g = synth.f32_to_bf16_bits((np.random.default_rng(1).standard_normal(n) * 1e-3).astype(np.float32))
+out = np.zeros(n, np.float32)
+_lib.call("mt_step", st.ptr, 0, g.ctypes.data_as(ctypes.c_void_p), ctypes.byref(_lib.adam_cfg(synth.AdamCfg())), 1,
+          out.ctypes.data_as(ctypes.c_void_p))
+import sys; sys.stdout.write(out.view(np.uint32).tobytes().hex()[:200000])
+'''
+    env = dict(os.environ, PYTHONPATH=ROOT)
+    a = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=env, cwd=ROOT)
+    env["MT_NO_AVX512"] = "1"
+    b = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=env, cwd=ROOT)
+    assert a.returncode == 0 and b.returncode == 0, a.stderr + b.stderr
+    assert a.stdout == b.stdout and len(a.stdout) > 1000
+
+
+def test_embed_gather_and_grad(lib):
+    cfg = synth.preset("tiny")
+    st = HostStore(cfg)
+    try:
+        bits = synth.make_weights(cfg)
+        st.load_bits(bits)
+        tok = synth.make_tokens(cfg).reshape(-1).astype(np.int32)
+        T = tok.size
+        x0 = np.zeros((T, cfg.hidden), np.uint16)
+        call("mt_embed_gather", st.ptr, tok.ctypes.data_as(ctypes.c_void_p), T, x0.ctypes.data_as(ctypes.c_void_p))
+        assert np.array_equal(x0, bits["embed"][tok])
+        # repeated tokens exercise the ordered accumulation
+        tok[::3] = tok[0]
+        dx0 = np.random.default_rng(2).standard_normal((T, cfg.hidden)).astype(np.float32)
+        call("mt_embed_grad", st.ptr, tok.ctypes.data_as(ctypes.c_void_p), T, dx0.ctypes.data_as(ctypes.c_void_p))
+        ref = synth.f32_to_bf16_bits(oracle.embed_bwd(dx0, tok, cfg.vocab))
+        assert np.array_equal(st.tensor(MT_UNIT_EMBED, "embed", REGION_G), ref)
+        bad = tok.copy()
+        bad[5] = cfg.vocab
+        with pytest.raises(MtError):
+            call("mt_embed_gather", st.ptr, bad.ctypes.data_as(ctypes.c_void_p), T, x0.ctypes.data_as(ctypes.c_void_p))
+    finally:
+        st.close()
+
+
+@pytest.mark.parametrize("name,seq", [("tiny", 128), ("lc512k", 524288)])
+def test_rope_tables_match_oracle(lib, name, seq):
+    cfg = synth.preset(name)
+    half = cfg.head_dim // 2
+    cs = np.empty((seq, half), np.float32)
+    sn = np.empty_like(cs)
+    call("mt_rope_tables", ctypes.byref(_lib.model_cfg(cfg)), seq, cs.ctypes.data_as(ctypes.c_void_p),
+         sn.ctypes.data_as(ctypes.c_void_p))
+    rc, rs = oracle.rope_tables(seq, cfg.head_dim, cfg.rope_base)
+    # independent fp64 evaluations (two libms) rounded to fp32: they may differ
+    # by one fp32 rounding step, i.e. at most one ulp of 1.0, and rarely
+    assert np.abs(cs - rc).max() <= 2.0 ** -23 and np.abs(sn - rs).max() <= 2.0 ** -23
+    assert (cs != rc).mean() < 1e-3 and (sn != rs).mean() < 1e-3
+
+
+# ----------------------------------------------------------------------------
+# schedule planning (host logic)
+# ----------------------------------------------------------------------------
+
+def _loads(L, K, slots, resident=False):
+    ops = plan_step(L, K, resident)
+    units = [-2 if k == "head" else l for k, l, _ in ops]
+    slot_of, load = plan_slots(units, slots)
+    return ops, units, slot_of, load
+
+
+def test_plan_orders_ops_as_the_method():
+    ops, units, slot_of, load = _loads(8, 4, 2)
+    kinds = [(k, l) for k, l, _ in ops]
+    assert kinds[:8] == [("fwd", l) for l in range(8)]
+    assert kinds[8] == ("head", None)
+    # last block: backward straight away (internals kept in the forward)
+    assert kinds[9:13] == [("bwd", 7), ("bwd", 6), ("bwd", 5), ("bwd", 4)]
+    # earlier block: recompute, then backward top-down
+    assert kinds[13:] == [("refwd", 0), ("refwd", 1), ("refwd", 2), ("refwd", 3),
+                          ("bwd", 3), ("bwd", 2), ("bwd", 1), ("bwd", 0)]
+
+
+@pytest.mark.parametrize("L,K", [(32, 4), (48, 4), (180, 4), (24, 4), (4, 1), (2, 1)])
+def test_two_slot_load_count(L, K):
+    _, units, slot_of, load = _loads(L, K, 2)
+    nblk = L // K
+    # forward L + head; the last block's backward reloads all but its top layer
+    # (the head took the other slot); every other block streams K layers for
+    # the recompute and K - 2 more for the backward (its top two are resident)
+    if K >= 2:
+        expect = L + 1 + (K - 1) + (nblk - 1) * (2 * K - 2)
+    else:
+        expect = L + 1 + 0 + (nblk - 1) * 1
+    assert sum(load) == expect
+    # no two consecutive uses evict each other's slot while both are needed
+    for i in range(1, len(units)):
+        if units[i] != units[i - 1]:
+            assert slot_of[i] != slot_of[i - 1]
+
+
+def test_k_slot_keeps_recomputed_block_resident():
+    L, K = 32, 4
+    _, units, slot_of, load = _loads(L, K, K + 1)
+    # at most: forward + head + the recompute of every block but the last
+    assert sum(load) <= L + 1 + (L // K - 1) * K
+    assert sum(load) < sum(_loads(L, K, 2)[3])
+
+
+def test_resident_loads_each_unit_once():
+    ops, units, slot_of, load = _loads(6, 6, 7, resident=True)
+    assert sum(load) == 7
+    assert not any(k == "refwd" for k, _, _ in ops)
