@@ -1,0 +1,181 @@
+"""Throughput of layer-streamed full-parameter training on one MI355X.
+
+One step = one full training step of the workload (streamed forward, head,
+block recompute + backward, gradient offload, host Adam for every unit) over
+one batch of seeded synthetic tokens.  Prints one JSON line:
+tokens/s (value), executed and model TFLOPS against the bf16 dense MFMA peak,
+host-link GB/s, the live-measured roofline of the dominant kernel, and the
+CPU oracle timed on a bounded sample of the same workload.
+
+    python bench.py [--steps K] [--warmup W] [--workload 7b] [--mode streamed]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "training tokens/s + TFLOPS (% bf16 MFMA peak), host-link GB/s, 1 MI355X"
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA (no sparsity)
+
+WORKLOAD_TEXT = {
+    "7b": "7B-shaped dense decoder (32 layers, hidden 4096, 32 heads x 128, SwiGLU ffn 11008, vocab 32000), "
+          "batch 4 x seq 2048, checkpoint every 4 layers, 2 device staging slots",
+    "14b": "14B-shaped dense decoder (48 layers, hidden 5120, 40 heads x 128, SwiGLU ffn 13824, vocab 32000), "
+           "batch 8 x seq 1024, checkpoint every 4 layers",
+    "tiny": "tiny decoder (2 layers, hidden 256, 4 heads x 64, ffn 688, vocab 1024), batch 2 x seq 128",
+}
+
+
+def flops_per_step(cfg, ops):
+    T, h, f, V, B, S = cfg.tokens, cfg.hidden, cfg.ffn, cfg.vocab, cfg.batch, cfg.seq
+    lin = 2.0 * T * (4 * h * h + 3 * h * f)
+    attn = 2.0 * B * S * (S + 1) * h  # causal: scores and products on and below the diagonal
+    head = 2.0 * T * h * V
+    n_fwd = sum(1 for k, _, _ in ops if k in ("fwd", "refwd"))
+    n_bwd = sum(1 for k, _, _ in ops if k == "bwd")
+    exec_ = n_fwd * (lin + attn) + n_bwd * (2 * lin + 2.5 * attn) + 3 * head
+    model = 3.0 * (cfg.layers * (lin + 2.0 * B * S * S * h) + head)
+    return exec_, model
+
+
+def cpu_baseline(cfg, seconds_hint=""):
+    """Time the oracle (fp32 numpy) on one sequence through one layer
+    (forward + backward), the head, and one layer's Adam; scale to the step."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import oracle
+    import synth
+
+    rng = np.random.default_rng(0)
+    S, h, V = cfg.seq, cfg.hidden, cfg.vocab
+    sub = cfg.with_(batch=1)
+    std = 0.02
+    W = {k: (rng.standard_normal(shp, dtype=np.float32) * std if not k.startswith("g_") else np.ones(shp, np.float32))
+         for k, shp in synth.layer_tensor_shapes(cfg).items()}
+    W = {k: oracle.bf16_round(v) for k, v in W.items()}
+    x = oracle.bf16_round(rng.standard_normal((S, h), dtype=np.float32))
+    dy = rng.standard_normal((S, h), dtype=np.float32) * 1e-3
+    cos, sin = oracle.rope_tables(S, cfg.head_dim, cfg.rope_base)
+    t0 = time.perf_counter()
+    y, cache = oracle.layer_fwd(x, W, sub, cos, sin)
+    oracle.layer_bwd(dy, cache, W, sub, cos, sin)
+    t_layer = time.perf_counter() - t0
+    del cache
+    head = oracle.bf16_round(rng.standard_normal((V, h), dtype=np.float32) * std)
+    tok = synth.tokens(0, V, 1, S)
+    t0 = time.perf_counter()
+    oracle.head_fwd_bwd(y, np.ones(h, np.float32), head, tok, sub)
+    t_head = time.perf_counter() - t0
+    P_L = sum(v.size for v in W.values())
+    t0 = time.perf_counter()
+    for k, v in W.items():
+        oracle.adam_update(synth.f32_to_bf16_bits(v), dy.reshape(-1)[: v.size].reshape(v.shape) if v.size <= dy.size
+                           else np.full(v.shape, 1e-3, np.float32), np.zeros(v.shape, np.float32),
+                           np.zeros(v.shape, np.float32), synth.AdamCfg(), 1)
+    t_adam = time.perf_counter() - t0
+    sample_s = t_layer + t_head + t_adam
+    scale_b = cfg.batch  # the sample is one of the batch's sequences
+    t_step = cfg.layers * (t_layer * scale_b + t_adam) + t_head * scale_b + t_adam * (2 * V * h + h) / P_L
+    blas = [i.get("num_threads") for i in threadpool_info() if i.get("user_api") == "blas"]
+    cores = max(blas) if blas else 1
+    return {"value": round(cfg.tokens / t_step, 3), "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": (f"fp32 oracle on 1 of {cfg.batch} sequences ({S} tokens): one layer forward+backward "
+                       f"{t_layer:.2f} s, head forward+backward {t_head:.2f} s, one layer's Adam {t_adam:.2f} s "
+                       f"(total {sample_s:.1f} s), scaled to {cfg.layers} layers x {cfg.batch} sequences plus "
+                       f"embedding/head Adam"),
+            "step_s_est": round(t_step, 2)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="7b", choices=sorted(WORKLOAD_TEXT))
+    ap.add_argument("--mode", default="streamed", choices=["streamed", "resident"])
+    ap.add_argument("--slots", type=int, default=2)
+    ap.add_argument("--grad-slabs", type=int, default=12)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this path has no multi-GPU sharding (see DESIGN.md, 'How it "
+              "would shard'); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import synth
+    from host_memory_centric_amd import _lib
+    from host_memory_centric_amd.engine import Trainer
+
+    cfg = synth.preset(args.workload)
+    adam = synth.AdamCfg()
+    t_init = time.perf_counter()
+    tr = Trainer(cfg, adam, mode=args.mode, n_slots=args.slots, n_grad_slabs=args.grad_slabs, device="cuda:0")
+    t_init = time.perf_counter() - t_init
+    print(f"[bench] init {t_init:.1f} s, weight loads/step {tr.n_weight_loads()}", file=sys.stderr, flush=True)
+    step = 0
+    for _ in range(args.warmup):
+        loss = tr.step(synth.make_tokens(cfg, step))
+        step += 1
+        print(f"[bench] warmup step {step}: loss {loss:.4f} {tr.stats['step_s']:.3f} s", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    _lib.prof_collect(reset=True)
+    _lib.call("mt_prof_enable", 1)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        loss = tr.step(synth.make_tokens(cfg, step))
+        step += 1
+        print(f"[bench] step {step}: loss {loss:.4f} {tr.stats['step_s']:.3f} s", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    _lib.call("mt_prof_enable", 0)
+    prof = _lib.prof_collect(reset=True)
+
+    T = cfg.tokens
+    ms_step = 1e3 * dt / args.steps
+    f_exec, f_model = flops_per_step(cfg, tr.ops)
+    tflops_exec = f_exec / (dt / args.steps) / 1e12
+    tflops_model = f_model / (dt / args.steps) / 1e12
+    lay, lay_h = tr.lay, tr.lay_head
+    n_loads = tr.n_weight_loads()
+    h2d = (n_loads - 1) * lay.w_bytes + lay_h.w_bytes + T * cfg.hidden * 2 + T * 4
+    d2h = cfg.layers * lay.w_bytes + lay_h.w_bytes + T * cfg.hidden * 4
+    dom = max(prof.items(), key=lambda kv: kv[1][1]) if prof else None
+    roof = None
+    if dom:
+        name, (n, ms, fl) = dom
+        ach = fl / (ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "kernel": name, "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "avg_launch_ms": round(ms / n, 4), "launches": n}
+    kernels = {k: {"launches": n, "avg_ms": round(ms / n, 4), "tflops": round(fl / (ms * 1e-3) / 1e12, 1),
+                   "share_of_step": round(ms / (1e3 * dt), 3)} for k, (n, ms, fl) in prof.items()}
+    out = {
+        "metric": METRIC, "value": round(T * args.steps / dt, 2), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 2), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": WORKLOAD_TEXT[args.workload], "name": cfg.name, "global_batch": cfg.batch,
+                   "seq_len": cfg.seq, "mode": args.mode, "slots": tr.n_slots, "ckpt_every": tr.K,
+                   "parallelism": "none (1 GPU)"},
+        "tflops_exec": round(tflops_exec, 1), "tflops_model": round(tflops_model, 1),
+        "pct_peak_exec": round(100 * tflops_exec / PEAK_BF16_TFLOPS, 2),
+        "pct_peak_model": round(100 * tflops_model / PEAK_BF16_TFLOPS, 2),
+        "h2d_GBps": round(h2d * args.steps / dt / 1e9, 2), "d2h_GBps": round(d2h * args.steps / dt / 1e9, 2),
+        "weight_loads_per_step": n_loads, "dev_peak_bytes": int(torch.cuda.max_memory_allocated()),
+        "host_store_bytes": int(tr.store.total_bytes()), "loss": round(loss, 5), "kernels": kernels,
+        "roofline": roof,
+    }
+    tr.close()
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(cfg)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -56,6 +56,10 @@ class MtHeadIO(ctypes.Structure):
                 ("dx_bf16", c_void_p), ("loss", c_void_p), ("workspace", c_void_p), ("workspace_bytes", c_size_t)]
 
 
+class MtProfEntry(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 24), ("launches", c_int64), ("ms", c_double), ("flops", c_double)]
+
+
 # name -> (argtypes)
 _SIGS = {
     "mt_unit_layout_get": [POINTER(MtModelCfg), c_int, POINTER(MtUnitLayout)],
@@ -82,6 +86,8 @@ _SIGS = {
     "mt_head_fwd_bwd": [POINTER(MtLayerView), POINTER(MtModelCfg), POINTER(MtHeadIO), c_void_p],
     "mt_op_gemm": [c_int64, c_int64, c_int64, c_void_p, c_int64, c_int, c_void_p, c_int64, c_int, c_void_p, c_void_p,
                    c_void_p, c_int64, c_int, c_void_p, c_size_t, c_void_p],
+    "mt_prof_enable": [c_int],
+    "mt_prof_collect": [POINTER(MtProfEntry), c_int, POINTER(c_int), c_int],
     "mt_op_attention_fwd": [c_int32, c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p],
     "mt_op_attention_bwd": [c_int32, c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                             c_void_p, c_void_p],
@@ -143,3 +149,11 @@ def size_query(name, mcfg, batch, seq):
     out = c_size_t()
     call(name, ctypes.byref(mcfg), batch, seq, ctypes.byref(out))
     return out.value
+
+
+def prof_collect(reset=True):
+    """{class: (launches, ms, flops)} of the timed kernel classes."""
+    out = (MtProfEntry * 8)()
+    n = c_int()
+    call("mt_prof_collect", out, 8, ctypes.byref(n), int(reset))
+    return {out[i].name.decode(): (out[i].launches, out[i].ms, out[i].flops) for i in range(n.value)}

@@ -21,7 +21,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmt.so")
 ARCH = os.environ.get("MT_OFFLOAD_ARCH", "gfx950")
 
-HIP_SOURCES = ["gemm.hip", "attention.hip", "elementwise.hip", "layer.hip"]
+HIP_SOURCES = ["gemm.hip", "attention.hip", "elementwise.hip", "layer.hip", "prof.hip"]
 HOST_SOURCES = ["host.cpp"]
 COMMON = ["-O3", "-fPIC", "-std=c++17", "-I", INCLUDE, "-I", CSRC, "-Wall", "-Wno-unused-function",
           "-Wno-unused-variable"]

@@ -450,6 +450,8 @@ void attention_fwd(const uint16_t* qkv, uint16_t* o, float* lse, int B, int S, i
     check_attn(B, S, heads, hd);
     const float sl2 = LOG2E / sqrtf((float)hd);
     const dim3 grid((S + ATT_BQ - 1) / ATT_BQ, B * heads);
+    // causal: S(S+1)/2 score entries, each 2*hd flops for QK^T and 2*hd for PV
+    ProfScope prof(PROF_ATTN_FWD, 4.0 * hd * (double)B * heads * ((double)S * (S + 1) / 2), s);
     if (hd == 128)
         hipLaunchKernelGGL(attn_fwd_kernel<128>, grid, dim3(ATT_THREADS), 0, s, qkv, o, lse, S, heads, sl2);
     else
@@ -465,6 +467,8 @@ void attention_bwd(const uint16_t* qkv, const uint16_t* o, const float* lse, con
     const int64_t T = (int64_t)B * S;
     const int64_t n = T * heads;
     const dim3 gq((S + ATT_BQ - 1) / ATT_BQ, B * heads), gk((S + ATT_BK - 1) / ATT_BK, B * heads);
+    // causal entries x (QK^T recompute, dP, dV, dK, dQ) at 2*hd flops each
+    ProfScope prof(PROF_ATTN_BWD, 10.0 * hd * (double)B * heads * ((double)S * (S + 1) / 2), s);
     if (hd == 128) {
         hipLaunchKernelGGL(attn_bwd_pre_kernel<128>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, o, dout, dvec,
                            T, S, heads);

@@ -332,6 +332,8 @@ void gemm(const GemmDesc& d, hipStream_t s) {
         splits = (int)((d.K + kps - 1) / kps);
     }
     float* part = splits > 1 ? (float*)d.ws : nullptr;
+    const ProfClass pc = d.a_kmajor ? (d.b_kmajor ? PROF_GEMM_NT : PROF_GEMM_NN) : PROF_GEMM_TN;
+    ProfScope prof(pc, 2.0 * (double)d.M * (double)d.N * (double)d.K, s);
     if (use_big(d.M, d.N))
         launch_tiles<256, 256, 64, 2, 4>(d, s, part, splits, kps);
     else

@@ -12,6 +12,16 @@ namespace mt {
 // Check the last launch (and, with MT_SYNC_CHECK=1, synchronise the stream).
 void launch_check(const char* what, hipStream_t s = nullptr);
 
+// Kernel timing (see mt_prof_enable): a scope that records a start event on
+// construction and an end event on destruction, when timing is on.
+enum ProfClass { PROF_GEMM_NT = 0, PROF_GEMM_NN, PROF_GEMM_TN, PROF_ATTN_FWD, PROF_ATTN_BWD, PROF_N };
+struct ProfScope {
+    ProfScope(ProfClass c, double flops, hipStream_t s);
+    ~ProfScope();
+    int idx = -1;
+    hipStream_t s;
+};
+
 struct GemmDesc {
     int64_t M = 0, N = 0, K = 0;
     const void* A = nullptr;

@@ -272,6 +272,30 @@ int mt_op_attention_bwd(int32_t batch, int32_t seq, int32_t heads, int32_t hd, c
                         const void* o, const float* lse, const void* d_o, void* dqkv, float* dvec,
                         void* stream);
 
+/* ------------------------------------------------------------------------ */
+/* Kernel timing                                                            */
+/* ------------------------------------------------------------------------ */
+
+/* One kernel class: GEMMs by operand orientation ("gemm_nt" forward,
+ * "gemm_nn" input gradient, "gemm_tn" weight gradient, each including its
+ * split-K reduction) and attention ("attn_fwd", "attn_bwd").  flops are the
+ * algorithmic flops of the recorded launches (2*M*N*K per GEMM; causal
+ * attention counts the scores and products on and below the diagonal). */
+typedef struct mt_prof_entry {
+    char name[24];
+    int64_t launches;
+    double ms;
+    double flops;
+} mt_prof_entry;
+
+/* on != 0: from now on every launch of a timed class is bracketed by two HIP
+ * events recorded on the launch's own stream; on == 0 stops recording. */
+int mt_prof_enable(int on);
+/* Waits for the recorded events, adds their elapsed times into per-class
+ * totals, and copies up to max entries (classes with launches) to out;
+ * *n receives the number written.  reset != 0 clears the totals afterwards. */
+int mt_prof_collect(mt_prof_entry* out, int max, int* n, int reset);
+
 /* Thread-local message of the calling thread's last failure. */
 const char* mt_last_error(void);
 
