@@ -88,9 +88,11 @@ _SIGS = {
                    c_void_p, c_int64, c_int, c_void_p, c_size_t, c_void_p],
     "mt_prof_enable": [c_int],
     "mt_prof_collect": [POINTER(MtProfEntry), c_int, POINTER(c_int), c_int],
-    "mt_op_attention_fwd": [c_int32, c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p],
+    "mt_op_attention_fwd": [c_int32, c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
+                            c_void_p],
     "mt_op_attention_bwd": [c_int32, c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
-                            c_void_p, c_void_p],
+                            c_void_p, c_size_t, c_void_p],
+    "mt_op_attention_ws_bytes": [c_int32, c_int32, c_int32, c_int32, POINTER(c_size_t)],
 }
 VOID_FUNCS = {"mt_store_destroy": [c_void_p]}
 EXPORTED = sorted(list(_SIGS) + list(VOID_FUNCS) + ["mt_last_error"])

@@ -22,6 +22,7 @@ LIB = os.path.join(HERE, "libmt.so")
 ARCH = os.environ.get("MT_OFFLOAD_ARCH", "gfx950")
 
 HIP_SOURCES = ["gemm.hip", "attention.hip", "elementwise.hip", "layer.hip", "prof.hip"]
+EXTRA = {}  # per-source extra flags
 HOST_SOURCES = ["host.cpp"]
 COMMON = ["-O3", "-fPIC", "-std=c++17", "-I", INCLUDE, "-I", CSRC, "-Wall", "-Wno-unused-function",
           "-Wno-unused-variable"]
@@ -51,7 +52,7 @@ def build(verbose=False, jobs=None):
     cmds, objs = [], []
     for src in HIP_SOURCES:
         obj = os.path.join(BUILD, src + ".o")
-        cmds.append([hipcc, *COMMON, *HIP_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        cmds.append([hipcc, *COMMON, *HIP_FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
     for src in HOST_SOURCES:
         obj = os.path.join(BUILD, src + ".o")

@@ -62,10 +62,14 @@ void rope_apply(uint16_t* qkv, const float* cos, const float* sin, int64_t T, in
 void swiglu_fwd(const uint16_t* gu, uint16_t* a, int64_t T, int f, hipStream_t s);
 void swiglu_bwd(const uint16_t* da, const uint16_t* gu, uint16_t* dgu, int64_t T, int f, hipStream_t s);
 
-// Causal flash attention on a fused qkv buffer.
-void attention_fwd(const uint16_t* qkv, uint16_t* o, float* lse, int B, int S, int heads, int hd, hipStream_t s);
+// Causal flash attention on a fused qkv buffer (scratch: transposed operand
+// copies, and the backward's row dot products).
+size_t attention_fwd_ws_bytes(int B, int S, int heads, int hd);
+size_t attention_bwd_ws_bytes(int B, int S, int heads, int hd);
+void attention_fwd(const uint16_t* qkv, uint16_t* o, float* lse, int B, int S, int heads, int hd, void* ws,
+                   size_t ws_bytes, hipStream_t s);
 void attention_bwd(const uint16_t* qkv, const uint16_t* o, const float* lse, const uint16_t* dout, uint16_t* dqkv,
-                   float* dvec, int B, int S, int heads, int hd, hipStream_t s);
+                   int B, int S, int heads, int hd, void* ws, size_t ws_bytes, hipStream_t s);
 
 // Cross entropy over a chunk of logits z [rows, V] (fp32) for tokens
 // t0..t0+rows-1 of the batch: per-row loss and dz (bf16) = (softmax - onehot)/N.

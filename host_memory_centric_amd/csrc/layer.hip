@@ -65,8 +65,9 @@ struct BwdWs {
     float* dxm;       // gradient of the mid residual stream [T, h]
     uint16_t* dxm_b;  // its bf16 copy
     uint16_t* dout;   // gradient of the attention output [T, h]
-    float* dvec;      // [B, heads, S]
     uint16_t* dqkv;   // [T, 3h]
+    void* attn;       // attention scratch (transposed operands, row dot products)
+    size_t attn_bytes;
     float* dg_part;   // RMSNorm gain partials [blocks, h]
     void* splitk;     // split-K partials
     size_t splitk_bytes;
@@ -93,8 +94,10 @@ BwdWs carve_ws(Carve& c, const mt_model_cfg* cfg, int64_t B, int64_t S) {
     w.dxm = c.take<float>(T * h);
     w.dxm_b = c.take<uint16_t>(T * h);
     w.dout = c.take<uint16_t>(T * h);
-    w.dvec = c.take<float>(B * cfg->heads * S);
     w.dqkv = c.take<uint16_t>(T * 3 * h);
+    w.attn_bytes = std::max(attention_fwd_ws_bytes((int)B, (int)S, cfg->heads, cfg->head_dim),
+                            attention_bwd_ws_bytes((int)B, (int)S, cfg->heads, cfg->head_dim));
+    w.attn = c.take<char>(w.attn_bytes);
     w.dg_part = c.take<float>(rmsnorm_bwd_blocks(T) * h);
     w.splitk_bytes = splitk_need(cfg, T);
     w.splitk = c.take<char>(w.splitk_bytes);
@@ -132,7 +135,7 @@ GemmDesc gd(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, bool ak
 
 // Forward of one layer: x -> y, internals into sv.
 void layer_forward(const mt_layer_view* v, const mt_model_cfg* cfg, int B, int S, const uint16_t* x, uint16_t* y,
-                   const float* cs, const float* sn, const Saved& sv, hipStream_t s) {
+                   const float* cs, const float* sn, const Saved& sv, void* attn_ws, size_t attn_bytes, hipStream_t s) {
     const int64_t T = (int64_t)B * S, h = cfg->hidden, f = cfg->ffn;
     const uint16_t* g_attn = (const uint16_t*)v->w[0];
     const uint16_t* wqkv = (const uint16_t*)v->w[1];
@@ -146,7 +149,7 @@ void layer_forward(const mt_layer_view* v, const mt_model_cfg* cfg, int B, int S
     d.Cb = sv.qkv;
     gemm(d, s);
     rope_apply(sv.qkv, cs, sn, T, S, cfg->heads, cfg->head_dim, false, s);
-    attention_fwd(sv.qkv, sv.o, sv.lse, B, S, cfg->heads, cfg->head_dim, s);
+    attention_fwd(sv.qkv, sv.o, sv.lse, B, S, cfg->heads, cfg->head_dim, attn_ws, attn_bytes, s);
     d = gd(T, h, h, sv.o, h, true, wo, h, true, h);
     d.R = x;
     d.Cb = sv.xm;
@@ -204,7 +207,7 @@ void layer_backward(const mt_layer_view* v, const mt_model_cfg* cfg, const mt_ac
     d.Cb = w.dout;
     gemm(d, s);
     // attention and RoPE
-    attention_bwd(sv.qkv, sv.o, sv.lse, w.dout, w.dqkv, w.dvec, B, S, cfg->heads, cfg->head_dim, s);
+    attention_bwd(sv.qkv, sv.o, sv.lse, w.dout, w.dqkv, B, S, cfg->heads, cfg->head_dim, w.attn, w.attn_bytes, s);
     rope_apply(w.dqkv, io->rope_cos, io->rope_sin, T, S, cfg->heads, cfg->head_dim, true, s);
     // QKV projection
     d = gd(3 * h, h, T, w.dqkv, 3 * h, false, sv.n1, h, false, h);
@@ -306,25 +309,23 @@ int mt_layer_fwd(const mt_layer_view* v, const mt_model_cfg* cfg, const mt_act* 
         need(io->rope_cos, "rope_cos");
         need(io->rope_sin, "rope_sin");
         for (int j = 0; j < 6; ++j) need(v->w[j], "weight view");
-        Saved sv;
+        size_t nb;
+        mt_layer_workspace_bytes(cfg, io->batch, io->seq, &nb);
+        if (io->workspace_bytes < nb) MT_FAIL(MT_E_ARG, "workspace holds %zu bytes, needs %zu", io->workspace_bytes, nb);
+        need(io->workspace, "workspace");
+        Carve c(io->workspace);
+        BwdWs w = carve_ws(c, cfg, io->batch, io->seq);
+        Saved sv = w.sv;
         if (io->saved) {
-            size_t nb;
-            mt_layer_saved_bytes(cfg, io->batch, io->seq, &nb);
-            if (io->saved_bytes < nb) MT_FAIL(MT_E_ARG, "saved buffer holds %zu bytes, needs %zu", io->saved_bytes, nb);
+            size_t sb;
+            mt_layer_saved_bytes(cfg, io->batch, io->seq, &sb);
+            if (io->saved_bytes < sb) MT_FAIL(MT_E_ARG, "saved buffer holds %zu bytes, needs %zu", io->saved_bytes, sb);
             need(io->saved, "saved");
-            Carve c(io->saved);
-            sv = carve_saved(c, cfg, io->batch, io->seq);
-        } else {
-            size_t nb;
-            mt_layer_workspace_bytes(cfg, io->batch, io->seq, &nb);
-            if (io->workspace_bytes < nb)
-                MT_FAIL(MT_E_ARG, "workspace holds %zu bytes, needs %zu", io->workspace_bytes, nb);
-            need(io->workspace, "workspace");
-            Carve c(io->workspace);
-            sv = carve_saved(c, cfg, io->batch, io->seq);
+            Carve cs(io->saved);
+            sv = carve_saved(cs, cfg, io->batch, io->seq);
         }
         layer_forward(v, cfg, io->batch, io->seq, (const uint16_t*)io->x_in, (uint16_t*)io->x_out, io->rope_cos,
-                      io->rope_sin, sv, as_stream(stream));
+                      io->rope_sin, sv, w.attn, w.attn_bytes, as_stream(stream));
     });
 }
 
@@ -360,7 +361,7 @@ int mt_layer_recompute_bwd(const mt_layer_view* v, const mt_model_cfg* cfg, cons
             sv = carve_saved(cs, cfg, io->batch, io->seq);
         } else {
             layer_forward(v, cfg, io->batch, io->seq, (const uint16_t*)io->x_in, w.xtmp, io->rope_cos, io->rope_sin, sv,
-                          s);
+                          w.attn, w.attn_bytes, s);
         }
         layer_backward(v, cfg, io, sv, w, s);
     });
@@ -447,25 +448,34 @@ int mt_op_gemm(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, int 
 }
 
 int mt_op_attention_fwd(int32_t batch, int32_t seq, int32_t heads, int32_t hd, const void* qkv, void* o, float* lse,
-                        void* stream) {
+                        void* ws, size_t ws_bytes, void* stream) {
     return guard([&] {
         need(qkv, "qkv");
         need(o, "o");
+        need(ws, "ws");
         MT_CHECK_ARG(lse != nullptr, "lse is NULL");
-        attention_fwd((const uint16_t*)qkv, (uint16_t*)o, lse, batch, seq, heads, hd, as_stream(stream));
+        attention_fwd((const uint16_t*)qkv, (uint16_t*)o, lse, batch, seq, heads, hd, ws, ws_bytes, as_stream(stream));
     });
 }
 
 int mt_op_attention_bwd(int32_t batch, int32_t seq, int32_t heads, int32_t hd, const void* qkv, const void* o,
-                        const float* lse, const void* d_o, void* dqkv, float* dvec, void* stream) {
+                        const float* lse, const void* d_o, void* dqkv, void* ws, size_t ws_bytes, void* stream) {
     return guard([&] {
         need(qkv, "qkv");
         need(o, "o");
         need(d_o, "d_o");
         need(dqkv, "dqkv");
-        MT_CHECK_ARG(lse && dvec, "NULL argument");
-        attention_bwd((const uint16_t*)qkv, (const uint16_t*)o, lse, (const uint16_t*)d_o, (uint16_t*)dqkv, dvec, batch,
-                      seq, heads, hd, as_stream(stream));
+        need(ws, "ws");
+        MT_CHECK_ARG(lse != nullptr, "lse is NULL");
+        attention_bwd((const uint16_t*)qkv, (const uint16_t*)o, lse, (const uint16_t*)d_o, (uint16_t*)dqkv, batch, seq,
+                      heads, hd, ws, ws_bytes, as_stream(stream));
+    });
+}
+
+int mt_op_attention_ws_bytes(int32_t batch, int32_t seq, int32_t heads, int32_t hd, size_t* out) {
+    return guard([&] {
+        MT_CHECK_ARG(out != nullptr, "out is NULL");
+        *out = std::max(attention_fwd_ws_bytes(batch, seq, heads, hd), attention_bwd_ws_bytes(batch, seq, heads, hd));
     });
 }
 

@@ -263,14 +263,16 @@ int mt_op_gemm(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, int 
 /* Causal attention forward on a fused QKV buffer: qkv bf16 [batch*seq, 3*heads*hd]
  * (q | k | v, head-major inside each), o bf16 [batch*seq, heads*hd],
  * lse fp32 [batch, heads, seq] (natural-log row logsumexp of the scaled
- * scores).  Scale 1/sqrt(hd).  hd in {64, 128}. */
-int mt_op_attention_fwd(int32_t batch, int32_t seq, int32_t heads, int32_t hd, const void* qkv,
-                        void* o, float* lse, void* stream);
-/* Its backward: writes dq | dk | dv into dqkv (same layout as qkv).
- * dvec: fp32 scratch [batch, heads, seq]. */
+ * scores).  Scale 1/sqrt(hd).  hd in {64, 128}.  ws: device scratch of at
+ * least mt_op_attention_ws_bytes (transposed operand copies). */
+int mt_op_attention_fwd(int32_t batch, int32_t seq, int32_t heads, int32_t hd, const void* qkv, void* o,
+                        float* lse, void* ws, size_t ws_bytes, void* stream);
+/* Its backward: writes dq | dk | dv into dqkv (same layout as qkv). */
 int mt_op_attention_bwd(int32_t batch, int32_t seq, int32_t heads, int32_t hd, const void* qkv,
-                        const void* o, const float* lse, const void* d_o, void* dqkv, float* dvec,
-                        void* stream);
+                        const void* o, const float* lse, const void* d_o, void* dqkv, void* ws,
+                        size_t ws_bytes, void* stream);
+/* Scratch bytes either attention call needs. */
+int mt_op_attention_ws_bytes(int32_t batch, int32_t seq, int32_t heads, int32_t hd, size_t* out);
 
 /* ------------------------------------------------------------------------ */
 /* Kernel timing                                                            */

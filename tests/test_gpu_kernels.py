@@ -115,7 +115,7 @@ def _metrics(got, ref):
 
 
 @pytest.mark.parametrize("hd", [64, 128])
-@pytest.mark.parametrize("B,S,nh", [(2, 200, 3), (1, 1, 2), (1, 37, 1), (1, 384, 2)])
+@pytest.mark.parametrize("B,S,nh", [(2, 200, 3), (1, 1, 2), (1, 37, 1), (1, 384, 2), (2, 67, 2), (1, 1000, 1)])
 def test_attention_fwd_bwd_vs_oracle(gpu, hd, B, S, nh):
     import torch
     H = nh * hd
@@ -125,11 +125,13 @@ def test_attention_fwd_bwd_vs_oracle(gpu, hd, B, S, nh):
     dq = _dev(qkv.view(np.int16), gpu)
     o = torch.zeros((B * S, H), dtype=torch.int16, device=gpu)
     lse = torch.zeros((B, nh, S), dtype=torch.float32, device=gpu)
-    call("mt_op_attention_fwd", B, S, nh, hd, _p(dq), _p(o), _p(lse), _stream())
+    nws = ctypes.c_size_t()
+    call("mt_op_attention_ws_bytes", B, S, nh, hd, ctypes.byref(nws))
+    ws = torch.empty(nws.value, dtype=torch.uint8, device=gpu)
+    call("mt_op_attention_fwd", B, S, nh, hd, _p(dq), _p(o), _p(lse), _p(ws), nws.value, _stream())
     ddo = _dev(do.view(np.int16), gpu)
     dqkv = torch.zeros((B * S, 3 * H), dtype=torch.int16, device=gpu)
-    dvec = torch.zeros((B, nh, S), dtype=torch.float32, device=gpu)
-    call("mt_op_attention_bwd", B, S, nh, hd, _p(dq), _p(o), _p(lse), _p(ddo), _p(dqkv), _p(dvec), _stream())
+    call("mt_op_attention_bwd", B, S, nh, hd, _p(dq), _p(o), _p(lse), _p(ddo), _p(dqkv), _p(ws), nws.value, _stream())
     torch.cuda.synchronize()
 
     f = synth.bf16_bits_to_f32(qkv)
@@ -164,5 +166,5 @@ def test_attention_rejects_head_dim(gpu):
     t = torch.zeros(1 << 16, dtype=torch.int16, device=gpu)
     lse = torch.zeros(64, dtype=torch.float32, device=gpu)
     with pytest.raises(MtError) as e:
-        call("mt_op_attention_fwd", 1, 8, 1, 96, _p(t), _p(t), _p(lse), _stream())
+        call("mt_op_attention_fwd", 1, 8, 1, 96, _p(t), _p(t), _p(lse), _p(t), t.numel() * 2, _stream())
     assert e.value.code == -2
