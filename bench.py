@@ -42,6 +42,27 @@ def flops_per_step(cfg, ops):
     return exec_, model
 
 
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch of a GEMM class from the committed rocprofv3 PMC
+    summary (profiles/gemm_7b_traffic.md), or None if that summary is for
+    another workload or the GEMM sources changed since it was taken."""
+    import hashlib
+    import re
+    path = os.path.join(ROOT, "profiles", "gemm_7b_traffic.md")
+    if workload != "7b" or not os.path.exists(path):
+        return None
+    m = re.search(r"```json\n(.*?)\n```", open(path).read(), re.S)
+    if not m:
+        return None
+    data = json.loads(m.group(1))
+    csrc = os.path.join(ROOT, "host_memory_centric_amd", "csrc")
+    src = open(os.path.join(csrc, "gemm.hip")).read() + open(os.path.join(csrc, "gemm_kernel.h")).read()
+    if hashlib.sha256(src.encode()).hexdigest()[:16] != data.get("source_sha256_16"):
+        return None
+    k = data.get("kernels", {}).get(kernel)
+    return k["hbm_bytes"] if k else None
+
+
 def cpu_baseline(cfg, seconds_hint=""):
     """Time the oracle (fp32 numpy) on one sequence through one layer
     (forward + backward), the head, and one layer's Adam; scale to the step."""
@@ -152,7 +173,8 @@ def main():
         name, (n, ms, fl) = dom
         ach = fl / (ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "kernel": name, "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+                "traffic": measured_traffic(name, args.workload), "traffic_unit": "HBM bytes per launch",
                 "avg_launch_ms": round(ms / n, 4), "launches": n}
     kernels = {k: {"launches": n, "avg_ms": round(ms / n, 4), "tflops": round(fl / (ms * 1e-3) / 1e12, 1),
                    "share_of_step": round(ms / (1e3 * dt), 3)} for k, (n, ms, fl) in prof.items()}
