@@ -147,6 +147,38 @@ def attention_bwd(do, q, k, v, o, P):
     return dq, dk, dv
 
 
+def attention_suffix(q, k, v, do, r0, o_rows=None):
+    """Causal attention of one head, evaluated only for the query rows s >= r0.
+
+    q, k, v, do: [S, hd] of one (batch, head).  Every query s attends to keys
+    0..s, so the outputs of the rows s >= r0 need only those rows' scores; and
+    key j is attended only by queries s >= j, so for j >= r0 the suffix rows
+    hold every term of dk_j and dv_j.  Returns, for rows / keys r0..S-1:
+    o, lse (natural-log logsumexp of the scaled scores), dq, dk, dv.  Used to
+    check long sequences where the full S x S probabilities do not fit.
+    ``o_rows`` (optional) is the forward output at which the backward is
+    evaluated (its rows enter rowsum(dO * O)); by default the rows' own o."""
+    dt = q.dtype
+    S, hd = q.shape
+    scale = dt.type(1.0 / np.sqrt(hd))
+    A = (q[r0:] @ k.T) * scale
+    future = np.arange(S)[None, :] > np.arange(r0, S)[:, None]
+    A[future] = -np.inf
+    amax = A.max(axis=-1, keepdims=True)
+    E = np.exp(A - amax)
+    l = E.sum(axis=-1, keepdims=True)
+    P = E / l
+    lse = (amax + np.log(l))[:, 0]
+    o = P @ v
+    dP = do[r0:] @ v.T
+    Drow = np.sum(do[r0:] * (o if o_rows is None else o_rows), axis=-1, keepdims=True)
+    dA = P * (dP - Drow)
+    dq = (dA @ k) * scale
+    dk = (dA[:, r0:].T @ q[r0:]) * scale
+    dv = P[:, r0:].T @ do[r0:]
+    return o, lse, dq, dk, dv
+
+
 def silu(z):
     return z / (1.0 + np.exp(-z))
 

@@ -20,13 +20,19 @@ mix, ``key = seed << 48 | stream << 32 | i``.
 * Streams: tokens 0, embedding 1, final-norm gain 2, LM head 3, layer l
   tensor j = 16 + 8 l + j, tensor order (gain_attn, Wqkv, Wo, gain_mlp, Wgu,
   Wd).  RMSNorm gains are 1 and are not drawn.
+
+Full-size kernel tests (hundreds of millions of elements) draw their inputs
+from torch's seeded CPU generator instead (``torch_normal_bf16_bits``,
+``torch_int_bf16_bits``): same bits on both sides, much faster than numpy.
 """
 from .gen import (mix64, u64, normal_bf16_bits, tokens, bf16_bits_to_f32,
-                  f32_to_bf16_bits, uniform_int_bf16_bits)
+                  f32_to_bf16_bits, uniform_int_bf16_bits, torch_normal_bf16_bits, torch_int_bf16_bits,
+                  torch_normal_bf16_device, torch_int_bf16_device)
 from .configs import ModelCfg, AdamCfg, PRESETS, preset, layer_tensor_shapes, STREAM_TOKENS, \
     STREAM_EMBED, STREAM_FINAL_NORM, STREAM_HEAD, layer_stream, make_weights, make_layer_weights, make_tokens, LAYER_TENSORS, BF16_ONE
 
 __all__ = ["mix64", "u64", "normal_bf16_bits", "tokens", "bf16_bits_to_f32", "f32_to_bf16_bits",
-           "uniform_int_bf16_bits", "ModelCfg", "AdamCfg", "PRESETS", "preset", "layer_tensor_shapes",
+           "uniform_int_bf16_bits", "torch_normal_bf16_bits", "torch_int_bf16_bits",
+           "torch_normal_bf16_device", "torch_int_bf16_device", "ModelCfg", "AdamCfg", "PRESETS", "preset", "layer_tensor_shapes",
            "STREAM_TOKENS", "STREAM_EMBED", "STREAM_FINAL_NORM", "STREAM_HEAD", "layer_stream",
            "make_weights", "make_layer_weights", "make_tokens", "LAYER_TENSORS", "BF16_ONE"]

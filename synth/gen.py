@@ -107,3 +107,45 @@ def uniform_int_bf16_bits(seed, stream, n, lo_val=-4, hi_val=4):
         t = (hi * span + ((lo * span) >> np.uint64(32))) >> np.uint64(32)
     vals = t.astype(np.int64) + lo_val
     return f32_to_bf16_bits(vals.astype(np.float32))
+
+
+def torch_normal_bf16_bits(seed, shape, std=1.0, mean=0.0):
+    """bf16 bits (uint16 numpy) of N(mean, std^2) samples for full-size tests.
+
+    Drawn with torch's CPU generator (Mersenne Twister seeded with ``seed``),
+    scaled in fp32 and rounded to bf16 to nearest-even.  Used where the
+    counter-based generator above would be too slow in numpy (hundreds of
+    millions of elements); both sides of a comparison read the same bits."""
+    import torch
+    g = torch.Generator().manual_seed(int(seed))
+    t = torch.randn(tuple(shape), generator=g, dtype=torch.float32)
+    t = t * float(std) + float(mean)
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def torch_int_bf16_bits(seed, shape, lo_val=-4, hi_val=4):
+    """bf16 bits of integers uniform in [lo_val, hi_val] from torch's CPU
+    generator; exact in bf16 (full-size GEMM tests)."""
+    import torch
+    g = torch.Generator().manual_seed(int(seed))
+    t = torch.randint(lo_val, hi_val + 1, tuple(shape), generator=g, dtype=torch.int32)
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def torch_normal_bf16_device(seed, shape, std=1.0, device="cuda:0"):
+    """Like ``torch_normal_bf16_bits`` but drawn on the device with torch's
+    seeded device generator (Philox) and returned as an int16 device tensor of
+    bf16 bits; for inputs of several GB whose sampled parts are copied back."""
+    import torch
+    g = torch.Generator(device=device).manual_seed(int(seed))
+    t = torch.empty(tuple(shape), dtype=torch.bfloat16, device=device)
+    t.normal_(0.0, float(std), generator=g)
+    return t.view(torch.int16)
+
+
+def torch_int_bf16_device(seed, shape, lo_val=-4, hi_val=4, device="cuda:0"):
+    """Integers uniform in [lo_val, hi_val] as bf16 bits (int16 device tensor)."""
+    import torch
+    g = torch.Generator(device=device).manual_seed(int(seed))
+    t = torch.randint(lo_val, hi_val + 1, tuple(shape), generator=g, dtype=torch.int8, device=device)
+    return t.to(torch.bfloat16).view(torch.int16)

@@ -239,6 +239,40 @@ def test_attention_against_torch_sdpa_and_autograd():
         np.testing.assert_allclose(a, t.grad.numpy(), rtol=1e-11, atol=1e-11)
 
 
+@pytest.mark.parametrize("S,r0", [(41, 0), (41, 29), (41, 40), (7, 3)])
+def test_attention_suffix_against_torch_sdpa(S, r0):
+    """The suffix evaluation used for long sequences: its rows, logsumexp and
+    the gradients of keys >= r0 against torch's SDPA + autograd over the
+    whole sequence, and against the full-matrix oracle."""
+    torch = pytest.importorskip("torch")
+    import torch.nn.functional as F
+    rng = np.random.default_rng(7 + S + r0)
+    hd = 16
+    q, k, v, do = (rng.standard_normal((S, hd)) for _ in range(4))
+    o, lse, dq, dk, dv = oracle.attention_suffix(q, k, v, do, r0)
+    qt, kt, vt = (torch.tensor(a[None, None], requires_grad=True) for a in (q, k, v))
+    ot = F.scaled_dot_product_attention(qt, kt, vt, is_causal=True)
+    ot.backward(torch.tensor(do[None, None]))
+    np.testing.assert_allclose(o, ot.detach().numpy()[0, 0, r0:], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(dq, qt.grad.numpy()[0, 0, r0:], rtol=1e-11, atol=1e-11)
+    np.testing.assert_allclose(dk, kt.grad.numpy()[0, 0, r0:], rtol=1e-11, atol=1e-11)
+    np.testing.assert_allclose(dv, vt.grad.numpy()[0, 0, r0:], rtol=1e-11, atol=1e-11)
+    sc = torch.tensor(q @ k.T / np.sqrt(hd))
+    sc = sc.masked_fill(torch.triu(torch.ones(S, S, dtype=torch.bool), 1), float("-inf"))
+    np.testing.assert_allclose(lse, torch.logsumexp(sc, dim=-1).numpy()[r0:], rtol=1e-13, atol=1e-13)
+    of, P = oracle.attention_fwd(q[None, None], k[None, None], v[None, None])
+    dqf, dkf, dvf = oracle.attention_bwd(do[None, None], q[None, None], k[None, None], v[None, None], of, P)
+    np.testing.assert_allclose(dk, dkf[0, 0, r0:], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(dv, dvf[0, 0, r0:], rtol=1e-12, atol=1e-12)
+    # the backward evaluated at a given forward output (rounded o)
+    o_given = of + 1e-3 * rng.standard_normal(of.shape)
+    _, _, dq2, dk2, _ = oracle.attention_suffix(q, k, v, do, r0, o_rows=o_given[0, 0, r0:])
+    dqg, dkg, _ = oracle.attention_bwd(do[None, None], q[None, None], k[None, None], v[None, None], o_given, P)
+    np.testing.assert_allclose(dq2, dqg[0, 0, r0:], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(dk2, dkg[0, 0, r0:], rtol=1e-12, atol=1e-12)
+    assert not np.allclose(dq2, dq, rtol=1e-9, atol=0)
+
+
 def test_rope_identities():
     rng = np.random.default_rng(2)
     S, hd = 40, 16
