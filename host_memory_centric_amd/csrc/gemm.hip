@@ -7,7 +7,9 @@
 //   weight grad  dW[out,in] = dY[T, out]^T * X[T, in]   A M-major, B N-major
 // 256x256 output tiles, 8 waves each computing 128x64 with 32x32x16 MFMAs;
 // operand tiles go straight from global memory into a double-buffered LDS
-// ring (global_load_lds_dwordx4), one barrier per K step of 64.  An operand
+// ring (global_load_lds_dwordx4), one barrier per K step of 64; the loads of
+// the next tile overlap the MFMAs of the current one (see the restrict note in
+// gemm_kernel.h).  An operand
 // whose contraction index is strided (the N-major weight in dX, both
 // operands of dW) is copied into LDS as it lies and read with the
 // transposing ds_read_b64_tr_b16, so no orientation needs register staging

@@ -226,17 +226,25 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(GemmArgs p) {
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfm[j], acc[i][j], 0, 0, 0);
     };
 
+    // One K step: start the direct loads of the next tile into the other
+    // buffer, then consume this one.  The two buffers are passed as
+    // restrict-qualified pointers: the compiler's wait insertion otherwise
+    // assumes the in-flight global->LDS loads may alias this step's LDS reads
+    // and waits for them (vmcnt(0)) before the first read, which serialises
+    // the copy and the MFMAs.  The loads are waited for explicitly below.
+    auto step = [&](const uint16_t* __restrict__ cur, uint16_t* __restrict__ nxt, bool more, int64_t knext) {
+        if (more) issue(knext, nxt);
+#pragma unroll
+        for (int kk = 0; kk < GBK / 16; ++kk) mfma_k(cur, cur + BM * GBK, kk);
+    };
+
     if (nk > 0) issue(kbeg, smem[0]);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     for (int kt = 0; kt < nk; ++kt) {
         const int cur = kt & 1;
         // the other buffer was last read in the previous step, before the barrier
-        if (kt + 1 < nk) issue(kbeg + (int64_t)(kt + 1) * GBK, smem[cur ^ 1]);
-        const uint16_t* As = smem[cur];
-        const uint16_t* Bs = smem[cur] + BM * GBK;
-#pragma unroll
-        for (int kk = 0; kk < GBK / 16; ++kk) mfma_k(As, Bs, kk);
+        step(smem[cur], smem[cur ^ 1], kt + 1 < nk, kbeg + (int64_t)(kt + 1) * GBK);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     }
