@@ -63,6 +63,94 @@ def measured_traffic(kernel, workload):
     return k["hbm_bytes"] if k else None
 
 
+def _union(iv):
+    out = []
+    for a, b in sorted(iv):
+        if out and a <= out[-1][1]:
+            out[-1][1] = max(out[-1][1], b)
+        else:
+            out.append([a, b])
+    return out
+
+
+def _total(u):
+    return sum(b - a for a, b in u)
+
+
+def _inter(u, w):
+    i = j = 0
+    t = 0.0
+    while i < len(u) and j < len(w):
+        a, b = max(u[i][0], w[j][0]), min(u[i][1], w[j][1])
+        if a < b:
+            t += b - a
+        if u[i][1] < w[j][1]:
+            i += 1
+        else:
+            j += 1
+    return t
+
+
+def overlap_report(tl):
+    """Busy and overlap fractions of one step from its event timeline: the
+    share of host-to-device and device-to-host copy time during which the
+    compute stream is running a layer, head or backward op."""
+    comp = _union([(a, b) for _, a, b in tl["ops"]])
+    h2d, d2h = _union(tl["h2d"]), _union(tl["d2h"])
+    copies = _union(tl["h2d"] + tl["d2h"])
+    span = max([b for _, _, b in tl["ops"]] + [b for _, b in tl["h2d"] + tl["d2h"]])
+
+    def frac(x, y):
+        return round(x / y, 4) if y > 0 else None
+    return {"step_ms": round(span, 2), "compute_busy_frac": frac(_total(comp), span),
+            "h2d_busy_frac": frac(_total(h2d), span), "d2h_busy_frac": frac(_total(d2h), span),
+            "h2d_overlap_frac": frac(_inter(h2d, comp), _total(h2d)),
+            "d2h_overlap_frac": frac(_inter(d2h, comp), _total(d2h)),
+            "copy_overlap_frac": frac(_inter(copies, comp), _total(copies)),
+            "gpu_idle_ms": round(span - _total(comp), 2)}
+
+
+def link_probe(tr, nbytes=1 << 30, reps=3):
+    """Pinned host <-> device copy rates on this machine: each direction alone and
+    both at once (the trainer's weight and gradient streams)."""
+    import torch
+
+    from host_memory_centric_amd import _lib
+    from host_memory_centric_amd.engine import PinnedBuffer
+    hb = [PinnedBuffer(nbytes) for _ in range(2)]
+    db = [torch.empty(nbytes, dtype=torch.uint8, device=tr.dev) for _ in range(2)]
+    sh, sd = tr.s_h2d, tr.s_d2h
+    import ctypes
+
+    def run(h2d, d2h):
+        torch.cuda.synchronize()
+        evs = {}
+        for name, on, st in (("h2d", h2d, sh), ("d2h", d2h, sd)):
+            if not on:
+                continue
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(st)
+            for _ in range(reps):
+                if name == "h2d":
+                    _lib.call("mt_copy_h2d", ctypes.c_void_p(db[0].data_ptr()), hb[0].ptr, nbytes,
+                              ctypes.c_void_p(st.cuda_stream))
+                else:
+                    _lib.call("mt_copy_d2h", hb[1].ptr, ctypes.c_void_p(db[1].data_ptr()), nbytes,
+                              ctypes.c_void_p(st.cuda_stream))
+            e1.record(st)
+            evs[name] = (e0, e1)
+        torch.cuda.synchronize()
+        return {k: round(reps * nbytes / (a.elapsed_time(b) * 1e-3) / 1e9, 2) for k, (a, b) in evs.items()}
+    try:
+        run(True, True)  # warm up
+        alone_h, alone_d, both = run(True, False), run(False, True), run(True, True)
+    finally:
+        for b in hb:
+            b.free()
+    return {"h2d_GBps": alone_h["h2d"], "d2h_GBps": alone_d["d2h"], "bidir_h2d_GBps": both["h2d"],
+            "bidir_d2h_GBps": both["d2h"], "probe_bytes": nbytes}
+
+
 def cpu_baseline(cfg, seconds_hint=""):
     """Time the oracle (fp32 numpy) on one sequence through one layer
     (forward + backward), the head, and one layer's Adam; scale to the step."""
@@ -122,10 +210,11 @@ def main():
     ap.add_argument("--slots", type=int, default=2)
     ap.add_argument("--grad-slabs", type=int, default=12)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--timeline-out", default=None, help="write the event timeline of one step as JSON")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this path has no multi-GPU sharding (see DESIGN.md, 'How it "
-              "would shard'); run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU only: this build has no multi-GPU sharding or collectives; "
+              "run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -153,10 +242,23 @@ def main():
         loss = tr.step(synth.make_tokens(cfg, step))
         step += 1
         print(f"[bench] step {step}: loss {loss:.4f} {tr.stats['step_s']:.3f} s", file=sys.stderr, flush=True)
+    tr.finish()  # the last step's host updates belong to the timed work
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
     _lib.call("mt_prof_enable", 0)
     prof = _lib.prof_collect(reset=True)
+
+    # one more (untimed) step with an event timeline: copy/compute overlap
+    tr.record_timeline = True
+    tr.step(synth.make_tokens(cfg, step))
+    tr.finish()
+    tl = tr.timeline()
+    tr.record_timeline = False
+    overlap = overlap_report(tl)
+    if args.timeline_out:
+        with open(args.timeline_out, "w") as fh:
+            json.dump(tl, fh)
+    link = link_probe(tr)
 
     T = cfg.tokens
     ms_step = 1e3 * dt / args.steps
@@ -192,6 +294,10 @@ def main():
         "weight_loads_per_step": n_loads, "dev_peak_bytes": int(torch.cuda.max_memory_allocated()),
         "host_store_bytes": int(tr.store.total_bytes()), "loss": round(loss, 5), "kernels": kernels,
         "roofline": roof,
+        "overlap": overlap,
+        "link": dict(link, h2d_bytes_per_step=int(h2d), d2h_bytes_per_step=int(d2h),
+                     h2d_link_frac=round(h2d / (ms_step * 1e-3) / (link["h2d_GBps"] * 1e9), 4),
+                     h2d_active_GBps=round(h2d / 1e9 / (overlap["h2d_busy_frac"] * overlap["step_ms"] * 1e-3), 2)),
     }
     tr.close()
     if not args.no_cpu_baseline:

@@ -165,7 +165,6 @@ struct mt_store {
     std::vector<void*> blocks;           // index: unit + 2 (embed, head, layers...)
     std::vector<uint64_t> mapped_bytes;  // mmap lengths
     std::vector<mt_unit_layout> layouts;
-    std::vector<float> embed_acc;        // fp32 embedding-gradient accumulator
 };
 
 namespace mt {
@@ -499,21 +498,34 @@ int mt_embed_grad(mt_store* st, const int32_t* tok, int64_t T, const float* dx0)
         const uint64_t h = st->cfg.hidden, V = st->cfg.vocab;
         for (int64_t t = 0; t < T; ++t)
             MT_CHECK_ARG(tok[t] >= 0 && tok[t] < st->cfg.vocab, "token out of range");
-        if (st->embed_acc.size() != V * h) st->embed_acc.assign(V * h, 0.f);
-        float* acc = st->embed_acc.data();
         uint16_t* G = (uint16_t*)((char*)st->blocks[idx] + st->layouts[idx].region_off[1]);
-        // Columns are split across threads; every element is summed over t in
-        // ascending order, so the result does not depend on the thread count.
-        const uint64_t cgrain = 64;
-        parallel_for(h, cgrain, [&](uint64_t c0, uint64_t c1) {
-            for (uint64_t v = 0; v < V; ++v) memset(acc + v * h + c0, 0, 4 * (c1 - c0));
-            for (int64_t t = 0; t < T; ++t) {
-                float* row = acc + (uint64_t)tok[t] * h;
-                const float* src = dx0 + (uint64_t)t * h;
-                for (uint64_t c = c0; c < c1; ++c) row[c] += src[c];
+        // Positions grouped by token id, ascending position inside a group
+        // (a stable counting sort): row v of the gradient is the sum of the
+        // rows dx0[t] with tok[t] = v taken in ascending t, accumulated in
+        // fp32 and rounded once to bf16; rows of absent tokens are zero.
+        std::vector<int64_t> start(V + 1, 0), pos(T);
+        for (int64_t t = 0; t < T; ++t) ++start[tok[t] + 1];
+        for (uint64_t v = 0; v < V; ++v) start[v + 1] += start[v];
+        {
+            std::vector<int64_t> fill(start.begin(), start.end() - 1);
+            for (int64_t t = 0; t < T; ++t) pos[fill[tok[t]]++] = t;
+        }
+        parallel_for(V, 64, [&](uint64_t v0, uint64_t v1) {
+            std::vector<float> acc(h);
+            for (uint64_t v = v0; v < v1; ++v) {
+                uint16_t* g = G + v * h;
+                const int64_t b = start[v], e = start[v + 1];
+                if (b == e) {
+                    memset(g, 0, 2 * h);
+                    continue;
+                }
+                std::fill(acc.begin(), acc.end(), 0.f);
+                for (int64_t i = b; i < e; ++i) {
+                    const float* src = dx0 + (uint64_t)pos[i] * h;
+                    for (uint64_t c = 0; c < h; ++c) acc[c] += src[c];
+                }
+                for (uint64_t c = 0; c < h; ++c) g[c] = f32_to_bf16(acc[c]);
             }
-            for (uint64_t v = 0; v < V; ++v)
-                for (uint64_t c = c0; c < c1; ++c) G[v * h + c] = f32_to_bf16(acc[v * h + c]);
         });
     });
 }

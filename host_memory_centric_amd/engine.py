@@ -20,6 +20,13 @@ appendix A.2; hyper.ai summary, method; the author blog's block figure):
 * the embedding gradient is scattered on the host and the embedding's Adam
   runs last.
 
+``step()`` returns once the GPU work of the step is done and the loss is
+known; the host Adam updates still running continue in the background.  Each
+unit's pending update is tracked, and the next step's packer waits for a
+unit's update before copying its weights (the embedding gather likewise waits
+for the embedding's update), so the next step's front end overlaps the tail
+of the previous step's optimizer work.  ``finish()`` waits for everything.
+
 Which device slot receives which weight load is planned for the whole step
 before it starts: since the sequence of layer uses is known, each load evicts
 the slot whose unit is needed furthest in the future.  With two slots this is
@@ -135,7 +142,7 @@ class Trainer:
     rounding (``self.w32[unit]``, W-region indexing) for parity checks."""
 
     def __init__(self, cfg, adam, mode="streamed", n_slots=2, n_grad_slabs=12, ckpt_every=None, weights=None,
-                 device="cuda:0", capture_w32=False):
+                 device="cuda:0", capture_w32=False, timeline=False):
         if mode not in ("streamed", "resident"):
             raise ValueError("mode must be 'streamed' or 'resident'")
         _lib.load()
@@ -204,6 +211,15 @@ class Trainer:
         self.s_d2h = torch.cuda.Stream(device=d)
         self.packer = ThreadPoolExecutor(1, thread_name_prefix="mt-pack")
         self.optimizer = ThreadPoolExecutor(1, thread_name_prefix="mt-adam")
+        self.embed_opt = ThreadPoolExecutor(1, thread_name_prefix="mt-adam-embed")
+        self.slab_free = queue.Queue()
+        for k in range(len(self.gslab)):
+            self.slab_free.put(k)
+        self.pending = {}              # unit -> future of its host update still running
+        self.gslot_d2h = [None, None]  # last copy out of each device gradient slot
+        self.head_d2h = None           # last copy out of the head's gradient buffer
+        self.record_timeline = timeline
+        self._tl = None
         self.stats = {}
         self.w32 = {}
         if capture_w32:
@@ -215,10 +231,24 @@ class Trainer:
         return a.ctypes.data_as(ctypes.c_void_p) if a is not None else None
 
     # ------------------------------------------------------------------
+    def finish(self):
+        """Wait for every host update of the previous steps."""
+        for u in list(self.pending):
+            self._wait_unit(u)
+
+    def _wait_unit(self, unit):
+        f = self.pending.pop(unit, None)
+        if f is not None:
+            f.result()
+
     def close(self):
-        torch.cuda.synchronize(self.dev)
-        self.packer.shutdown(wait=True)
-        self.optimizer.shutdown(wait=True)
+        try:
+            self.finish()
+        finally:
+            torch.cuda.synchronize(self.dev)
+            self.packer.shutdown(wait=True)
+            self.optimizer.shutdown(wait=True)
+            self.embed_opt.shutdown(wait=True)
         for b in self.wslab + self.gslab + [self.head_gslab, self.x0_pin, self.dx0_pin, self.tok_pin]:
             b.free()
         self.store.close()
@@ -269,7 +299,11 @@ class Trainer:
         sc, sh, sd = (ctypes.c_void_p(s.cuda_stream) for s in (cs, hs, ds))
         t0 = time.perf_counter()
 
-        # embedding gather + tokens (host) -> device
+        tl = self._timeline_begin(cs) if self.record_timeline else None
+
+        # embedding gather + tokens (host) -> device, after the embedding's
+        # update of the previous step (which also still reads the token buffer)
+        self._wait_unit(MT_UNIT_EMBED)
         tok_host = self.tok_pin.view(np.int32)
         tok_host[:] = tokens.reshape(-1)
         call("mt_embed_gather", self.store.ptr, self.tok_pin.ptr, self.T, self.x0_pin.ptr)
@@ -283,7 +317,7 @@ class Trainer:
         # weight loads of this step, in order
         loads = [i for i, ld in enumerate(self.op_load) if ld]
         load_of_op = {i: j for j, i in enumerate(loads)}
-        ready_ev = [torch.cuda.Event() for _ in loads]
+        ready_ev = [torch.cuda.Event(enable_timing=self.record_timeline) for _ in loads]
         op_done = [None] * len(self.ops)
         # previous op that used the same slot (the copy into the slot waits for it)
         slot_prev = [None] * len(self.ops)
@@ -292,10 +326,16 @@ class Trainer:
             slot_prev[i] = last.get(s)
             last[s] = i
 
+        pending = dict(self.pending)  # updates of the previous step still running
+
         def pack(j):
             if j >= 2:
                 ready_ev[j - 2].synchronize()  # the copy that read this staging buffer is done
-            call("mt_pack_layer", self.store.ptr, self.op_unit[loads[j]], self.wslab[j % 2].ptr, self.slot_bytes)
+            unit = self.op_unit[loads[j]]
+            f = pending.get(unit)
+            if f is not None:
+                f.result()  # the unit's update of the previous step has landed
+            call("mt_pack_layer", self.store.ptr, unit, self.wslab[j % 2].ptr, self.slot_bytes)
 
         pack_fut = {j: self.packer.submit(pack, j) for j in range(min(2, len(loads)))}
         next_load = [0]
@@ -308,6 +348,8 @@ class Trainer:
             with torch.cuda.stream(hs):
                 if slot_prev[i] is not None:
                     hs.wait_event(op_done[slot_prev[i]])  # buffer-free
+                if tl is not None:
+                    tl["h2d"].append([self._ev(hs), ready_ev[j]])
                 call("mt_copy_h2d", _ptr(self.slots[self.op_slot[i]]), self.wslab[j % 2].ptr, nbytes, sh)
                 ready_ev[j].record(hs)  # weights-ready
             if j + 2 < len(loads):
@@ -326,11 +368,8 @@ class Trainer:
                 issue_load(j)
                 next_load[0] += 1
 
-        slab_free = queue.Queue()
-        for k in range(len(self.gslab)):
-            slab_free.put(k)
-        gslot_d2h = [None, None]
-        adam_futs = []
+        slab_free = self.slab_free
+        gslot_d2h = self.gslot_d2h
         cur = 0
         n_bwd = 0
 
@@ -359,6 +398,12 @@ class Trainer:
                 cs.wait_event(ready_ev[load_of_op[i]])
             slot = self.op_slot[i]
             with torch.cuda.stream(cs):
+                if kind == "head" and self.head_d2h is not None:
+                    cs.wait_event(self.head_d2h)  # previous step's copy out of the head gradient
+                if kind == "bwd" and gslot_d2h[n_bwd % 2] is not None:
+                    cs.wait_event(gslot_d2h[n_bwd % 2])  # buffer-free (gradient slot)
+                if tl is not None:
+                    tl["ops"].append([kind, self._ev(cs), None])
                 if kind == "fwd":
                     v = self._bind(slot, None, l)
                     a = self._act(self._x(l), self._x(l + 1), self.saved[si] if si is not None else None)
@@ -382,50 +427,91 @@ class Trainer:
                     call("mt_head_fwd_bwd", ctypes.byref(v), ctypes.byref(self.mcfg), ctypes.byref(io), sc)
                 else:  # bwd
                     g = n_bwd % 2
-                    if gslot_d2h[g] is not None:
-                        cs.wait_event(gslot_d2h[g])
                     v = self._bind(slot, self.gslots[g], l)
                     a = self._act(self._x(l), None, self.saved[si], dy=self.dgrad[cur], dyb=self.dgrad_b[cur],
                                   dx=self.dgrad[1 - cur], dxb=self.dgrad_b[1 - cur])
                     call("mt_layer_recompute_bwd", ctypes.byref(v), ctypes.byref(self.mcfg), ctypes.byref(a), sc)
                     cur = 1 - cur
-                ev = torch.cuda.Event()
+                ev = torch.cuda.Event(enable_timing=self.record_timeline)
                 ev.record(cs)
                 op_done[i] = ev
+                if tl is not None:
+                    tl["ops"][-1][2] = ev
             if kind == "head":
-                d2h = torch.cuda.Event()
+                self._wait_unit(MT_UNIT_HEAD)  # the previous update still reads the head's slab
+                d2h = torch.cuda.Event(enable_timing=self.record_timeline)
                 with torch.cuda.stream(ds):
                     ds.wait_event(ev)
+                    if tl is not None:
+                        tl["d2h"].append([self._ev(ds), d2h])
                     call("mt_copy_d2h", self.head_gslab.ptr, _ptr(self.head_g), self.lay_head.w_bytes, sd)
                     d2h.record(ds)
-                adam_futs.append(self.optimizer.submit(adam_layer, d2h, MT_UNIT_HEAD, self.head_gslab))
+                self.head_d2h = d2h
+                self.pending[MT_UNIT_HEAD] = self.optimizer.submit(adam_layer, d2h, MT_UNIT_HEAD, self.head_gslab)
             elif kind == "bwd":
                 g = n_bwd % 2
                 n_bwd += 1
                 k = slab_free.get()
-                d2h = torch.cuda.Event()
+                self._wait_unit(l)  # (finished long ago: the previous step's update of this layer)
+                d2h = torch.cuda.Event(enable_timing=self.record_timeline)
                 with torch.cuda.stream(ds):
                     ds.wait_event(ev)
+                    if tl is not None:
+                        tl["d2h"].append([self._ev(ds), d2h])
                     call("mt_copy_d2h", self.gslab[k].ptr, _ptr(self.gslots[g]), self.lay.w_bytes, sd)
-                    if l == 0:
-                        call("mt_copy_d2h", self.dx0_pin.ptr, _ptr(self.dgrad[cur]), self.T * h * 4, sd)
                     d2h.record(ds)
+                    if l == 0:
+                        d2h_x = torch.cuda.Event(enable_timing=self.record_timeline)
+                        if tl is not None:
+                            tl["d2h"].append([self._ev(ds), d2h_x])
+                        call("mt_copy_d2h", self.dx0_pin.ptr, _ptr(self.dgrad[cur]), self.T * h * 4, sd)
+                        d2h_x.record(ds)
                 gslot_d2h[g] = d2h
-                adam_futs.append(self.optimizer.submit(adam_layer_slab, d2h, l, k))
+                self.pending[l] = self.optimizer.submit(adam_layer_slab, d2h, l, k)
                 if l == 0:
-                    adam_futs.append(self.optimizer.submit(adam_embed, d2h))
+                    self.pending[MT_UNIT_EMBED] = self.embed_opt.submit(adam_embed, d2h_x)
             issue_ready_loads(i)
 
-        for f in adam_futs:
-            f.result()
         for f in list(pack_fut.values()):
             f.result()
         cs.synchronize()
         loss = float(self.loss_dev.item())
         self.stats = {"step_s": time.perf_counter() - t0, "weight_loads": len(loads)}
+        if tl is not None:
+            self._tl = tl
         return loss
 
     # ------------------------------------------------------------------
+    @staticmethod
+    def _ev(stream):
+        e = torch.cuda.Event(enable_timing=True)
+        e.record(stream)
+        return e
+
+    def _timeline_begin(self, cs):
+        ref = torch.cuda.Event(enable_timing=True)
+        ref.record(cs)
+        return {"ref": ref, "ops": [], "h2d": [], "d2h": []}
+
+    def timeline(self):
+        """Intervals (ms from the step's start) of the last step recorded with
+        timeline=True: {'ops': [(kind, start, end)], 'h2d': [(start, end)],
+        'd2h': [(start, end)]}.  Waits for the step's copies to finish."""
+        tl = self._tl
+        if tl is None:
+            return None
+        for _, _, e in tl["ops"]:
+            e.synchronize()
+        for _, e in tl["h2d"] + tl["d2h"]:
+            e.synchronize()
+        ref = tl["ref"]
+        rel = ref.elapsed_time
+        return {"ops": [(k, rel(a), rel(b)) for k, a, b in tl["ops"]],
+                "h2d": [(rel(a), rel(b)) for a, b in tl["h2d"]],
+                "d2h": [(rel(a), rel(b)) for a, b in tl["d2h"]]}
+
+    # ------------------------------------------------------------------
     def weights(self):
-        """bf16 bit arrays of all weights (host store)."""
+        """bf16 bit arrays of all weights (host store), after every pending update."""
+        self.finish()
         return self.store.read_bits()

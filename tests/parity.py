@@ -55,6 +55,7 @@ def oracle_w32(res, unit, name):
 
 def check_step(trainer, loss, res, cfg, report=None):
     """Assert the trainer's step matches the oracle result ``res``."""
+    trainer.finish()  # the host updates of the step have landed
     rep = {"loss_rel": abs(loss - float(res["loss"])) / abs(float(res["loss"]))}
     assert rep["loss_rel"] <= LOSS_RTOL, rep
     worst = (0.0, 1.0, 0.0)
@@ -77,6 +78,7 @@ def check_step(trainer, loss, res, cfg, report=None):
 def sync_from_oracle(trainer, state, cfg):
     """Copy the oracle's weights and moments into the trainer's host store so
     that the next step of both starts from identical state."""
+    trainer.finish()
     from host_memory_centric_amd.store import REGION_M, REGION_V, REGION_W
     st = trainer.store
     for unit in st.units:

@@ -366,6 +366,7 @@ def test_head_full_shape_vs_oracle(gpu, name):
 def _digest(tr):
     import xxhash
     from host_memory_centric_amd.store import REGION_G, REGION_M, REGION_V, REGION_W
+    tr.finish()
     out = {}
     for u in tr.store.units:
         for r in (REGION_W, REGION_G, REGION_M, REGION_V):

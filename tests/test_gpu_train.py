@@ -19,6 +19,7 @@ def _trainer(cfg, bits, **kw):
 
 
 def _store_regions(tr):
+    tr.finish()
     return {(u, r): tr.store.region(u, r).copy() for u in tr.store.units
             for r in (REGION_W, REGION_G, REGION_M, REGION_V)}
 
@@ -71,6 +72,7 @@ def test_run_twice_deterministic(gpu):
         tr = _trainer(cfg, bits)
         try:
             l = tr.step(synth.make_tokens(cfg, 0))
+            tr.finish()
             out.append((l, tr.store.region(0, REGION_W).copy()))
         finally:
             tr.close()
