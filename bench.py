@@ -21,13 +21,16 @@ sys.path.insert(0, ROOT)
 METRIC = "training tokens/s + TFLOPS (% bf16 MFMA peak), host-link GB/s, 1 MI355X"
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA (no sparsity)
 
-WORKLOAD_TEXT = {
-    "7b": "7B-shaped dense decoder (32 layers, hidden 4096, 32 heads x 128, SwiGLU ffn 11008, vocab 32000), "
-          "batch 4 x seq 2048, checkpoint every 4 layers, 2 device staging slots",
-    "14b": "14B-shaped dense decoder (48 layers, hidden 5120, 40 heads x 128, SwiGLU ffn 13824, vocab 32000), "
-           "batch 8 x seq 1024, checkpoint every 4 layers",
-    "tiny": "tiny decoder (2 layers, hidden 256, 4 heads x 64, ffn 688, vocab 1024), batch 2 x seq 128",
-}
+WORKLOADS = ("7b", "14b", "depth180", "width5x", "lc128k", "lc256k", "lc512k", "tiny")
+
+
+def workload_text(cfg, slots):
+    kind = {"7b": "7B-shaped", "14b": "14B-shaped", "depth180": "depth-stress", "width5x": "width-stress",
+            "lc128k": "long-context 7B-layer", "lc256k": "long-context 7B-layer",
+            "lc512k": "long-context 7B-layer", "tiny": "tiny"}.get(cfg.name, cfg.name)
+    return (f"{kind} dense decoder ({cfg.layers} layers, hidden {cfg.hidden}, {cfg.heads} heads x {cfg.head_dim}, "
+            f"SwiGLU ffn {cfg.ffn}, vocab {cfg.vocab}), batch {cfg.batch} x seq {cfg.seq}, checkpoint every "
+            f"{cfg.ckpt_every} layers, {slots} device staging slots")
 
 
 def flops_per_step(cfg, ops):
@@ -205,7 +208,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--workload", default="7b", choices=sorted(WORKLOAD_TEXT))
+    ap.add_argument("--workload", default="7b", choices=WORKLOADS)
     ap.add_argument("--mode", default="streamed", choices=["streamed", "resident"])
     ap.add_argument("--slots", type=int, default=2)
     ap.add_argument("--grad-slabs", type=int, default=12)
@@ -284,7 +287,9 @@ def main():
         "metric": METRIC, "value": round(T * args.steps / dt, 2), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 2), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": WORKLOAD_TEXT[args.workload], "name": cfg.name, "global_batch": cfg.batch,
+        "config": {"workload": workload_text(cfg, tr.n_slots) if args.mode == "streamed" else
+                   workload_text(cfg, tr.n_slots).replace(f"{tr.n_slots} device staging slots",
+                                                          "all layers resident on the device"), "name": cfg.name, "global_batch": cfg.batch,
                    "seq_len": cfg.seq, "mode": args.mode, "slots": tr.n_slots, "ckpt_every": tr.K,
                    "parallelism": "none (1 GPU)"},
         "tflops_exec": round(tflops_exec, 1), "tflops_model": round(tflops_model, 1),

@@ -224,21 +224,26 @@ static void fill_normal(uint16_t* dst, uint64_t n, uint32_t seed, uint32_t strea
 // ---------------------------------------------------------------------------
 // Adam (fp32, one IEEE rounding per operation; no contraction)
 // ---------------------------------------------------------------------------
+// Adam constants, each computed in fp64 and rounded once to fp32.  The bias
+// corrections are folded into the step size and epsilon:
+// alpha = lr * sqrt(c2) / c1, eps_hat = eps * sqrt(c2) with c1 = 1 - beta1^t,
+// c2 = 1 - beta2^t, which is the bias-corrected update
+// lr * (m / c1) / (sqrt(v / c2) + eps) rewritten with one division and one
+// square root per element.
 struct AdamK {
-    float b1, b2, omb1, omb2, c1, c2, lr, eps, decay;
+    float b1, b2, omb1, omb2, alpha, eps_hat, decay;
     bool wd;
 };
 
 static AdamK adam_consts(const mt_adam_cfg* a, int64_t t) {
     AdamK k;
+    const double c1 = 1.0 - std::pow(a->beta1, (double)t), c2 = 1.0 - std::pow(a->beta2, (double)t);
     k.b1 = (float)a->beta1;
     k.b2 = (float)a->beta2;
     k.omb1 = (float)(1.0 - a->beta1);
     k.omb2 = (float)(1.0 - a->beta2);
-    k.c1 = (float)(1.0 - std::pow(a->beta1, (double)t));
-    k.c2 = (float)(1.0 - std::pow(a->beta2, (double)t));
-    k.lr = (float)a->lr;
-    k.eps = (float)a->eps;
+    k.alpha = (float)(a->lr * std::sqrt(c2) / c1);
+    k.eps_hat = (float)(a->eps * std::sqrt(c2));
     k.decay = (float)(1.0 - a->lr * a->weight_decay);
     k.wd = a->weight_decay != 0.0;
     return k;
@@ -256,10 +261,8 @@ static void adam_scalar(uint16_t* W, uint16_t* G, float* M, float* Vv, const uin
         const float v = k.b2 * Vv[i] + k.omb2 * (g * g);
         M[i] = m;
         Vv[i] = v;
-        const float mhat = m / k.c1;
-        const float vhat = v / k.c2;
-        const float denom = std::sqrt(vhat) + k.eps;
-        const float step = k.lr * mhat;
+        const float denom = std::sqrt(v) + k.eps_hat;
+        const float step = k.alpha * m;
         const float wn = w - step / denom;
         if (wout) wout[i] = wn;
         W[i] = f32_to_bf16(wn);
@@ -271,8 +274,8 @@ __attribute__((target("avx512f,avx512bw"))) static void adam_avx512(uint16_t* W,
                                                                       float* wout, uint64_t b, uint64_t e,
                                                                       const AdamK& k) {
     const __m512 b1 = _mm512_set1_ps(k.b1), b2 = _mm512_set1_ps(k.b2), omb1 = _mm512_set1_ps(k.omb1),
-                 omb2 = _mm512_set1_ps(k.omb2), c1 = _mm512_set1_ps(k.c1), c2 = _mm512_set1_ps(k.c2),
-                 lr = _mm512_set1_ps(k.lr), eps = _mm512_set1_ps(k.eps), dec = _mm512_set1_ps(k.decay);
+                 omb2 = _mm512_set1_ps(k.omb2), alpha = _mm512_set1_ps(k.alpha), eps = _mm512_set1_ps(k.eps_hat),
+                 dec = _mm512_set1_ps(k.decay);
     const __m512i rnd = _mm512_set1_epi32(0x7fff), one = _mm512_set1_epi32(1);
     uint64_t i = b;
     for (; i + 16 <= e; i += 16) {
@@ -292,10 +295,8 @@ __attribute__((target("avx512f,avx512bw"))) static void adam_avx512(uint16_t* W,
                                        _mm512_mul_ps(omb2, _mm512_mul_ps(g, g)));
         _mm512_storeu_ps(M + i, m);
         _mm512_storeu_ps(Vv + i, v);
-        const __m512 mhat = _mm512_div_ps(m, c1);
-        const __m512 vhat = _mm512_div_ps(v, c2);
-        const __m512 denom = _mm512_add_ps(_mm512_sqrt_ps(vhat), eps);
-        const __m512 step = _mm512_mul_ps(lr, mhat);
+        const __m512 denom = _mm512_add_ps(_mm512_sqrt_ps(v), eps);
+        const __m512 step = _mm512_mul_ps(alpha, m);
         const __m512 wn = _mm512_sub_ps(w, _mm512_div_ps(step, denom));
         if (wout) _mm512_storeu_ps(wout + i, wn);
         // round to nearest even (weights are finite)

@@ -145,9 +145,12 @@ typedef struct mt_adam_cfg {
  * element, in fp32 with one rounding per operation:
  *   w = bf16 W (times (1 - lr*wd) if wd != 0); g = bf16 G;
  *   m = b1*m + (1-b1)*g;  v = b2*v + (1-b2)*(g*g);
- *   w' = w - (lr * (m/c1)) / (sqrt(v/c2) + eps),  c1 = 1-b1^t, c2 = 1-b2^t;
- *   W = bf16(w').
- * Scalar constants are computed in fp64 and rounded once to fp32.  t >= 1.
+ *   w' = w - (alpha*m) / (sqrt(v) + eps_hat);   W = bf16(w'),
+ * with alpha = lr*sqrt(c2)/c1, eps_hat = eps*sqrt(c2), c1 = 1-b1^t,
+ * c2 = 1-b2^t: the bias-corrected update lr*(m/c1)/(sqrt(v/c2)+eps) with
+ * the corrections folded into two scalars (one division, one square root
+ * per element).  Scalar constants are computed in fp64 and rounded once to
+ * fp32.  t >= 1.
  * If w_fp32_out is non-NULL it receives w' (w_bytes/2 floats, W indexing)
  * before rounding.  Multithreaded, deterministic. */
 int mt_step(mt_store* st, int unit, const void* grad_src, const mt_adam_cfg* adam, int64_t t,

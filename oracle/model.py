@@ -294,10 +294,19 @@ def head_fwd_bwd(x, g_final, w_head, tok, cfg):
 # ----------------------------------------------------------------------------
 
 def adam_consts(adam, t):
-    """Scalar constants, each computed in fp64 and rounded once to fp32."""
+    """Scalar constants, each computed in fp64 and rounded once to fp32.
+
+    The bias corrections c1 = 1 - beta1^t and c2 = 1 - beta2^t are folded into
+    the step size and epsilon: alpha = lr * sqrt(c2) / c1 and
+    eps_hat = eps * sqrt(c2).  In exact arithmetic
+    lr * (m / c1) / (sqrt(v / c2) + eps) = alpha * m / (sqrt(v) + eps_hat),
+    so this is the bias-corrected Adam update itself, in the form that needs
+    one division and one square root per element."""
     f = np.float32
+    c1 = 1.0 - adam.beta1 ** t
+    c2 = 1.0 - adam.beta2 ** t
     return dict(b1=f(adam.beta1), b2=f(adam.beta2), omb1=f(1.0 - adam.beta1), omb2=f(1.0 - adam.beta2),
-                c1=f(1.0 - adam.beta1 ** t), c2=f(1.0 - adam.beta2 ** t), lr=f(adam.lr), eps=f(adam.eps),
+                alpha=f(adam.lr * np.sqrt(c2) / c1), eps_hat=f(adam.eps * np.sqrt(c2)),
                 decay=f(1.0 - adam.lr * adam.weight_decay))
 
 
@@ -306,8 +315,10 @@ def adam_update(w_bits, g_fp32, m, v, adam, t):
 
     w_bits: bf16 weights (uint16); g_fp32: gradient as computed; m, v: fp32
     moments (updated in place).  The gradient is first stored as bf16, as the
-    method keeps bf16 gradients on the host.  Returns (new bf16 bits, the fp32
-    weight before its bf16 rounding)."""
+    method keeps bf16 gradients on the host.  Operation order:
+    m = b1*m + (1-b1)*g;  v = b2*v + (1-b2)*(g*g);
+    w' = w - (alpha*m) / (sqrt(v) + eps_hat)   (constants of adam_consts).
+    Returns (new bf16 bits, the fp32 weight before its bf16 rounding)."""
     k = adam_consts(adam, t)
     w = bf16_bits_to_f32(w_bits)
     if adam.weight_decay != 0.0:
@@ -315,10 +326,8 @@ def adam_update(w_bits, g_fp32, m, v, adam, t):
     gh = bf16_round(g_fp32)
     m[...] = k["b1"] * m + k["omb1"] * gh
     v[...] = k["b2"] * v + k["omb2"] * (gh * gh)
-    mhat = m / k["c1"]
-    vhat = v / k["c2"]
-    denom = np.sqrt(vhat) + k["eps"]
-    step = k["lr"] * mhat
+    denom = np.sqrt(v) + k["eps_hat"]
+    step = k["alpha"] * m
     w_new = (w - step / denom).astype(np.float32)
     return f32_to_bf16_bits(w_new), w_new
 
