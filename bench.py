@@ -211,7 +211,7 @@ def main():
     ap.add_argument("--workload", default="7b", choices=WORKLOADS)
     ap.add_argument("--mode", default="streamed", choices=["streamed", "resident"])
     ap.add_argument("--slots", type=int, default=2)
-    ap.add_argument("--grad-slabs", type=int, default=12)
+    ap.add_argument("--grad-slabs", type=int, default=16)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--timeline-out", default=None, help="write the event timeline of one step as JSON")
     args = ap.parse_args()

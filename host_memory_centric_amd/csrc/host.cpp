@@ -148,10 +148,33 @@ static void parallel_for(uint64_t n, uint64_t grain, F&& fn) {
     if (err) std::rethrow_exception(err);
 }
 
+static bool have_avx512();
+
+// Copy with non-temporal stores: the destination (a pinned staging buffer read
+// next by the DMA engine) is not read back into the caches first, which saves
+// a third of the copy's DRAM traffic.
+__attribute__((target("avx512f"))) static void stream_copy(char* dst, const char* src, uint64_t n) {
+    uint64_t i = 0;
+    for (; i + 256 <= n; i += 256) {
+        const __m512i a = _mm512_loadu_si512(src + i), b = _mm512_loadu_si512(src + i + 64),
+                      c = _mm512_loadu_si512(src + i + 128), d = _mm512_loadu_si512(src + i + 192);
+        _mm512_stream_si512((__m512i*)(dst + i), a);
+        _mm512_stream_si512((__m512i*)(dst + i + 64), b);
+        _mm512_stream_si512((__m512i*)(dst + i + 128), c);
+        _mm512_stream_si512((__m512i*)(dst + i + 192), d);
+    }
+    if (i < n) memcpy(dst + i, src + i, n - i);
+    _mm_sfence();
+}
+
 static void par_memcpy(void* dst, const void* src, uint64_t bytes) {
     const uint64_t grain = 4ull << 20;
+    const bool nt = have_avx512() && ((uintptr_t)dst & 63) == 0;
     parallel_for(bytes, grain, [&](uint64_t b, uint64_t e) {
-        memcpy((char*)dst + b, (const char*)src + b, e - b);
+        if (nt)
+            stream_copy((char*)dst + b, (const char*)src + b, e - b);
+        else
+            memcpy((char*)dst + b, (const char*)src + b, e - b);
     });
 }
 
@@ -277,12 +300,16 @@ __attribute__((target("avx512f,avx512bw"))) static void adam_avx512(uint16_t* W,
                  omb2 = _mm512_set1_ps(k.omb2), alpha = _mm512_set1_ps(k.alpha), eps = _mm512_set1_ps(k.eps_hat),
                  dec = _mm512_set1_ps(k.decay);
     const __m512i rnd = _mm512_set1_epi32(0x7fff), one = _mm512_set1_epi32(1);
+    const bool g_aligned = ((uintptr_t)(G + b) & 31) == 0;
     uint64_t i = b;
     for (; i + 16 <= e; i += 16) {
         __m256i gb;
         if (src) {
             gb = _mm256_loadu_si256((const __m256i*)(src + i));
-            _mm256_storeu_si256((__m256i*)(G + i), gb);
+            if (g_aligned)
+                _mm256_stream_si256((__m256i*)(G + i), gb);  // G is not read again here
+            else
+                _mm256_storeu_si256((__m256i*)(G + i), gb);
         } else {
             gb = _mm256_loadu_si256((const __m256i*)(G + i));
         }
@@ -304,6 +331,7 @@ __attribute__((target("avx512f,avx512bw"))) static void adam_avx512(uint16_t* W,
         u = _mm512_add_epi32(u, _mm512_add_epi32(rnd, _mm512_and_si512(_mm512_srli_epi32(u, 16), one)));
         _mm256_storeu_si256((__m256i*)(W + i), _mm512_cvtepi32_epi16(_mm512_srli_epi32(u, 16)));
     }
+    if (src && g_aligned) _mm_sfence();
     if (i < e) adam_scalar(W, G, M, Vv, src, wout, i, e, k);
 }
 #pragma clang fp contract(on)

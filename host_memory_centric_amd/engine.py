@@ -15,8 +15,9 @@ appendix A.2; hyper.ai summary, method; the author blog's block figure):
   layers from its checkpoint (keeping their internals), then run their
   backward top-down.  After each layer's backward (*backward-done*) the
   gradient stream copies its gradient slot into a pinned gradient slab; a host
-  optimizer thread waits for that copy, lands the slab into the store and runs
-  Adam on the layer, then recycles the slab.
+  optimizer thread lands the slab into the store and runs Adam on the layer
+  once that copy is done, then recycles the slab (most urgent update first,
+  see ``UpdateScheduler``).
 * the embedding gradient is scattered on the host and the embedding's Adam
   runs last.
 
@@ -40,8 +41,9 @@ computation runs in libmt.so.
 """
 import ctypes
 import queue
+import threading
 import time
-from concurrent.futures import ThreadPoolExecutor
+from concurrent.futures import Future, ThreadPoolExecutor
 
 import numpy as np
 import torch
@@ -53,6 +55,60 @@ from .store import HostStore
 
 def _ptr(t):
     return ctypes.c_void_p(t.data_ptr())
+
+
+class UpdateScheduler:
+    """One host thread running optimizer updates, most urgent first.
+
+    Each job carries an event (its gradient copy) and a priority: the order
+    in which the next step's forward needs the unit's weights (embedding,
+    then layers bottom-up, then the head).  Among the jobs whose copy has
+    completed, the thread always runs the most urgent one.  The backward
+    produces gradients top-down while the next forward consumes weights
+    bottom-up, so this lets the updates of the upper layers wait and overlap
+    the next step's forward instead of delaying its first layers."""
+
+    def __init__(self):
+        self._cv = threading.Condition()
+        self._jobs = []
+        self._seq = 0
+        self._stop = False
+        self._thread = threading.Thread(target=self._run, name="mt-adam", daemon=True)
+        self._thread.start()
+
+    def submit(self, priority, event, fn, *args):
+        fut = Future()
+        with self._cv:
+            self._jobs.append((priority, self._seq, event, fut, fn, args))
+            self._seq += 1
+            self._cv.notify()
+        return fut
+
+    def _run(self):
+        while True:
+            with self._cv:
+                while True:
+                    if self._stop and not self._jobs:
+                        return
+                    ready = [j for j in self._jobs if j[2] is None or j[2].query()]
+                    if ready:
+                        job = min(ready, key=lambda j: (j[0], j[1]))
+                        self._jobs.remove(job)
+                        break
+                    self._cv.wait(timeout=2e-4 if self._jobs else None)
+            _, _, _, fut, fn, args = job
+            if not fut.set_running_or_notify_cancel():
+                continue
+            try:
+                fut.set_result(fn(*args))
+            except BaseException as e:  # propagated to whoever waits on the future
+                fut.set_exception(e)
+
+    def shutdown(self):
+        with self._cv:
+            self._stop = True
+            self._cv.notify()
+        self._thread.join()
 
 
 class PinnedBuffer:
@@ -141,7 +197,7 @@ class Trainer:
     capture_w32: keep each unit's updated fp32 weights before their bf16
     rounding (``self.w32[unit]``, W-region indexing) for parity checks."""
 
-    def __init__(self, cfg, adam, mode="streamed", n_slots=2, n_grad_slabs=12, ckpt_every=None, weights=None,
+    def __init__(self, cfg, adam, mode="streamed", n_slots=2, n_grad_slabs=16, ckpt_every=None, weights=None,
                  device="cuda:0", capture_w32=False, timeline=False):
         if mode not in ("streamed", "resident"):
             raise ValueError("mode must be 'streamed' or 'resident'")
@@ -210,8 +266,7 @@ class Trainer:
         self.s_h2d = torch.cuda.Stream(device=d)
         self.s_d2h = torch.cuda.Stream(device=d)
         self.packer = ThreadPoolExecutor(1, thread_name_prefix="mt-pack")
-        self.optimizer = ThreadPoolExecutor(1, thread_name_prefix="mt-adam")
-        self.embed_opt = ThreadPoolExecutor(1, thread_name_prefix="mt-adam-embed")
+        self.optimizer = UpdateScheduler()
         self.slab_free = queue.Queue()
         for k in range(len(self.gslab)):
             self.slab_free.put(k)
@@ -247,8 +302,7 @@ class Trainer:
         finally:
             torch.cuda.synchronize(self.dev)
             self.packer.shutdown(wait=True)
-            self.optimizer.shutdown(wait=True)
-            self.embed_opt.shutdown(wait=True)
+            self.optimizer.shutdown()
         for b in self.wslab + self.gslab + [self.head_gslab, self.x0_pin, self.dx0_pin, self.tok_pin]:
             b.free()
         self.store.close()
@@ -447,7 +501,8 @@ class Trainer:
                     call("mt_copy_d2h", self.head_gslab.ptr, _ptr(self.head_g), self.lay_head.w_bytes, sd)
                     d2h.record(ds)
                 self.head_d2h = d2h
-                self.pending[MT_UNIT_HEAD] = self.optimizer.submit(adam_layer, d2h, MT_UNIT_HEAD, self.head_gslab)
+                self.pending[MT_UNIT_HEAD] = self.optimizer.submit(self._urgency(MT_UNIT_HEAD), d2h, adam_layer, d2h,
+                                                                   MT_UNIT_HEAD, self.head_gslab)
             elif kind == "bwd":
                 g = n_bwd % 2
                 n_bwd += 1
@@ -467,9 +522,10 @@ class Trainer:
                         call("mt_copy_d2h", self.dx0_pin.ptr, _ptr(self.dgrad[cur]), self.T * h * 4, sd)
                         d2h_x.record(ds)
                 gslot_d2h[g] = d2h
-                self.pending[l] = self.optimizer.submit(adam_layer_slab, d2h, l, k)
+                self.pending[l] = self.optimizer.submit(self._urgency(l), d2h, adam_layer_slab, d2h, l, k)
                 if l == 0:
-                    self.pending[MT_UNIT_EMBED] = self.embed_opt.submit(adam_embed, d2h_x)
+                    self.pending[MT_UNIT_EMBED] = self.optimizer.submit(self._urgency(MT_UNIT_EMBED), d2h_x,
+                                                                        adam_embed, d2h_x)
             issue_ready_loads(i)
 
         for f in list(pack_fut.values()):
@@ -480,6 +536,14 @@ class Trainer:
         if tl is not None:
             self._tl = tl
         return loss
+
+    def _urgency(self, unit):
+        """Order in which the next step needs a unit's updated weights."""
+        if unit == MT_UNIT_EMBED:
+            return -1
+        if unit == MT_UNIT_HEAD:
+            return self.L
+        return unit
 
     # ------------------------------------------------------------------
     @staticmethod
