@@ -57,7 +57,6 @@ Saved carve_saved(Carve& c, const mt_model_cfg* cfg, int64_t B, int64_t S) {
 }
 
 struct BwdWs {
-    Saved sv;         // internals when the caller keeps none
     uint16_t* xtmp;   // forward output during recompute [T, h]
     uint16_t* da;     // [T, f]
     uint16_t* dgu;    // [T, 2f]
@@ -83,10 +82,11 @@ size_t splitk_need(const mt_model_cfg* cfg, int64_t T) {
     return m;
 }
 
+// Workspace of a layer call that is given a saved-internals buffer; a call
+// without one carves the internals right after these pieces.
 BwdWs carve_ws(Carve& c, const mt_model_cfg* cfg, int64_t B, int64_t S) {
     const int64_t T = B * S, h = cfg->hidden, f = cfg->ffn;
     BwdWs w;
-    w.sv = carve_saved(c, cfg, B, S);
     w.xtmp = c.take<uint16_t>(T * h);
     w.da = c.take<uint16_t>(T * f);
     w.dgu = c.take<uint16_t>(T * 2 * f);
@@ -258,6 +258,29 @@ HeadWs carve_head(Carve& c, const mt_model_cfg* cfg, int64_t B, int64_t S) {
 
 hipStream_t as_stream(void* s) { return (hipStream_t)s; }
 
+// Workspace pieces and the internals of a layer call: from io->saved when
+// given, else carved in the workspace after the backward temporaries.
+void carve_call(const mt_model_cfg* cfg, const mt_act* io, BwdWs& w, Saved& sv) {
+    size_t wb, sb;
+    mt_layer_workspace_bytes(cfg, io->batch, io->seq, &wb);
+    mt_layer_saved_bytes(cfg, io->batch, io->seq, &sb);
+    const size_t need_ws = io->saved ? wb : wb + sb;
+    if (io->workspace_bytes < need_ws)
+        MT_FAIL(MT_E_ARG, "workspace holds %zu bytes, needs %zu%s", io->workspace_bytes, need_ws,
+                io->saved ? "" : " (no saved buffer: workspace + saved bytes)");
+    need(io->workspace, "workspace");
+    Carve c(io->workspace);
+    w = carve_ws(c, cfg, io->batch, io->seq);
+    if (io->saved) {
+        if (io->saved_bytes < sb) MT_FAIL(MT_E_ARG, "saved buffer holds %zu bytes, needs %zu", io->saved_bytes, sb);
+        need(io->saved, "saved");
+        Carve cs(io->saved);
+        sv = carve_saved(cs, cfg, io->batch, io->seq);
+    } else {
+        sv = carve_saved(c, cfg, io->batch, io->seq);
+    }
+}
+
 }  // namespace
 
 }  // namespace mt
@@ -309,21 +332,9 @@ int mt_layer_fwd(const mt_layer_view* v, const mt_model_cfg* cfg, const mt_act* 
         need(io->rope_cos, "rope_cos");
         need(io->rope_sin, "rope_sin");
         for (int j = 0; j < 6; ++j) need(v->w[j], "weight view");
-        size_t nb;
-        mt_layer_workspace_bytes(cfg, io->batch, io->seq, &nb);
-        if (io->workspace_bytes < nb) MT_FAIL(MT_E_ARG, "workspace holds %zu bytes, needs %zu", io->workspace_bytes, nb);
-        need(io->workspace, "workspace");
-        Carve c(io->workspace);
-        BwdWs w = carve_ws(c, cfg, io->batch, io->seq);
-        Saved sv = w.sv;
-        if (io->saved) {
-            size_t sb;
-            mt_layer_saved_bytes(cfg, io->batch, io->seq, &sb);
-            if (io->saved_bytes < sb) MT_FAIL(MT_E_ARG, "saved buffer holds %zu bytes, needs %zu", io->saved_bytes, sb);
-            need(io->saved, "saved");
-            Carve cs(io->saved);
-            sv = carve_saved(cs, cfg, io->batch, io->seq);
-        }
+        BwdWs w;
+        Saved sv;
+        carve_call(cfg, io, w, sv);
         layer_forward(v, cfg, io->batch, io->seq, (const uint16_t*)io->x_in, (uint16_t*)io->x_out, io->rope_cos,
                       io->rope_sin, sv, w.attn, w.attn_bytes, as_stream(stream));
     });
@@ -344,22 +355,11 @@ int mt_layer_recompute_bwd(const mt_layer_view* v, const mt_model_cfg* cfg, cons
             need(v->w[j], "weight view");
             need(v->g[j], "gradient view");
         }
-        size_t nb;
-        mt_layer_workspace_bytes(cfg, io->batch, io->seq, &nb);
-        if (io->workspace_bytes < nb) MT_FAIL(MT_E_ARG, "workspace holds %zu bytes, needs %zu", io->workspace_bytes, nb);
-        need(io->workspace, "workspace");
-        Carve c(io->workspace);
-        BwdWs w = carve_ws(c, cfg, io->batch, io->seq);
+        BwdWs w;
+        Saved sv;
+        carve_call(cfg, io, w, sv);
         const hipStream_t s = as_stream(stream);
-        Saved sv = w.sv;
-        if (io->saved) {
-            size_t sb;
-            mt_layer_saved_bytes(cfg, io->batch, io->seq, &sb);
-            if (io->saved_bytes < sb) MT_FAIL(MT_E_ARG, "saved buffer holds %zu bytes, needs %zu", io->saved_bytes, sb);
-            need(io->saved, "saved");
-            Carve cs(io->saved);
-            sv = carve_saved(cs, cfg, io->batch, io->seq);
-        } else {
+        if (!io->saved) {
             layer_forward(v, cfg, io->batch, io->seq, (const uint16_t*)io->x_in, w.xtmp, io->rope_cos, io->rope_sin, sv,
                           w.attn, w.attn_bytes, s);
         }

@@ -460,7 +460,9 @@ class Trainer:
                     tl["ops"].append([kind, self._ev(cs), None])
                 if kind == "fwd":
                     v = self._bind(slot, None, l)
-                    a = self._act(self._x(l), self._x(l + 1), self.saved[si] if si is not None else None)
+                    # layers before the last block keep nothing: the first saved
+                    # buffer (written again by the last block) is their scratch
+                    a = self._act(self._x(l), self._x(l + 1), self.saved[si if si is not None else 0])
                     call("mt_layer_fwd", ctypes.byref(v), ctypes.byref(self.mcfg), ctypes.byref(a), sc)
                 elif kind == "refwd":
                     out = self._x(l + 1) if (l + 1) % self.K != 0 else self.xscratch

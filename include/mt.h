@@ -199,10 +199,15 @@ typedef struct mt_act {
     const float* rope_cos; /* fp32 [seq, head_dim/2] (device) */
     const float* rope_sin;
     void* saved;           /* layer internals (mt_layer_saved_bytes) or NULL */
-    void* workspace;       /* mt_layer_workspace_bytes, 256-byte aligned */
+    void* workspace;       /* scratch, 256-byte aligned (see below) */
     size_t saved_bytes, workspace_bytes;
 } mt_act;
 
+/* Bytes of a layer's saved internals (n1, rstd1, qkv, o, lse, x_mid, n2,
+ * rstd2, gate|up, a).  Workspace of a layer call: mt_layer_workspace_bytes
+ * when io->saved is given; a call without a saved buffer keeps the internals
+ * in the workspace too and needs workspace + saved bytes.  MT_E_ARG when a
+ * buffer is too small. */
 int mt_layer_saved_bytes(const mt_model_cfg* cfg, int32_t batch, int32_t seq, size_t* out);
 int mt_layer_workspace_bytes(const mt_model_cfg* cfg, int32_t batch, int32_t seq, size_t* out);
 
@@ -211,7 +216,7 @@ int mt_layer_workspace_bytes(const mt_model_cfg* cfg, int32_t batch, int32_t seq
  * attention, output projection + residual, RMSNorm, gate/up GEMM, SwiGLU,
  * down projection + residual.  x_out = layer(x_in).  When io->saved is
  * non-NULL the internals needed by the backward are stored there; otherwise
- * the workspace is used as scratch.  Needs x_in, x_out, rope tables,
+ * the workspace holds them as scratch.  Needs x_in, x_out, rope tables,
  * workspace.  MT_E_SHAPE unless head_dim is 64 or 128. */
 int mt_layer_fwd(const mt_layer_view* v, const mt_model_cfg* cfg, const mt_act* io, void* stream);
 

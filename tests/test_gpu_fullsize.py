@@ -318,6 +318,63 @@ def test_layer_full_shape_vs_oracle(gpu, name):
     assert not fails, fails
 
 
+@pytest.mark.parametrize("name", ["tiny", "7b"])
+def test_layer_recompute_path_equals_saved_path(gpu, name):
+    """mt_layer_recompute_bwd without a saved buffer recomputes the internals
+    in the workspace; with one it reads them from an earlier mt_layer_fwd.
+    Both run the same kernels: the gradients must be bit-identical."""
+    import torch
+    cfg = synth.preset(name)
+    B, S, h = cfg.batch, cfg.seq, cfg.hidden
+    T = B * S
+    W, x, dy = _layer_inputs(cfg, seed=81)
+    names = list(synth.layer_tensor_shapes(cfg))
+    mcfg = _lib.model_cfg(cfg)
+    slot, lay = _slot(gpu, mcfg, 0, [W[n] for n in names])
+    saved_bytes = _lib.size_query("mt_layer_saved_bytes", mcfg, B, S)
+    ws_bytes = _lib.size_query("mt_layer_workspace_bytes", mcfg, B, S)
+    cs = np.empty((S, cfg.head_dim // 2), dtype=np.float32)
+    sn = np.empty_like(cs)
+    call("mt_rope_tables", ctypes.byref(mcfg), S, cs.ctypes.data_as(ctypes.c_void_p),
+         sn.ctypes.data_as(ctypes.c_void_p))
+    d_cs, d_sn = torch.from_numpy(cs).to(gpu), torch.from_numpy(sn).to(gpu)
+    d_x = torch.from_numpy(x.view(np.int16)).to(gpu)
+    d_dyb = torch.from_numpy(dy.view(np.int16)).to(gpu)
+    d_dy = d_dyb.view(torch.bfloat16).float()
+    outs = []
+    for with_saved in (True, False):
+        gslot = torch.zeros_like(slot)
+        v = MtLayerView()
+        call("mt_bind", ctypes.byref(mcfg), 0, ptr(slot), ptr(gslot), ctypes.byref(v))
+        nws = ws_bytes if with_saved else ws_bytes + saved_bytes
+        ws = torch.empty(nws, dtype=torch.uint8, device=gpu)
+        saved = torch.empty(saved_bytes, dtype=torch.uint8, device=gpu) if with_saved else None
+        d_y = torch.empty_like(d_x)
+        d_dx = torch.empty((T, h), dtype=torch.float32, device=gpu)
+        d_dxb = torch.empty((T, h), dtype=torch.int16, device=gpu)
+        a = MtAct()
+        a.batch, a.seq = B, S
+        a.x_in, a.x_out = d_x.data_ptr(), d_y.data_ptr()
+        a.dy, a.dy_bf16, a.dx, a.dx_bf16 = d_dy.data_ptr(), d_dyb.data_ptr(), d_dx.data_ptr(), d_dxb.data_ptr()
+        a.rope_cos, a.rope_sin = d_cs.data_ptr(), d_sn.data_ptr()
+        a.saved, a.saved_bytes = (saved.data_ptr(), saved_bytes) if with_saved else (None, 0)
+        a.workspace, a.workspace_bytes = ws.data_ptr(), nws
+        if with_saved:
+            call("mt_layer_fwd", ctypes.byref(v), ctypes.byref(mcfg), ctypes.byref(a), stream())
+        else:
+            # one byte short of the required workspace is rejected
+            a.workspace_bytes = nws - 1
+            with pytest.raises(_lib.MtError):
+                call("mt_layer_recompute_bwd", ctypes.byref(v), ctypes.byref(mcfg), ctypes.byref(a), stream())
+            a.workspace_bytes = nws
+        call("mt_layer_recompute_bwd", ctypes.byref(v), ctypes.byref(mcfg), ctypes.byref(a), stream())
+        torch.cuda.synchronize()
+        outs.append((d_dx.cpu().numpy(), d_dxb.cpu().numpy(), gslot.cpu().numpy()))
+        del ws, saved
+    for u, w_ in zip(outs[0], outs[1]):
+        assert np.array_equal(u.view(np.uint8), w_.view(np.uint8))
+
+
 @pytest.mark.parametrize("name", ["7b", "14b"])
 def test_head_full_shape_vs_oracle(gpu, name):
     import torch
