@@ -1,17 +1,17 @@
 // Causal attention on gfx950 matrix cores: tiled online-softmax forward and a
-// two-kernel backward (dK/dV over key tiles, dQ over query tiles), so no
-// gradient is ever accumulated with atomics.
+// backward in three kernels (dV and dK over key tiles, dQ over query tiles),
+// so no gradient is ever accumulated with atomics.
 //
 // Scores are computed transposed where that keeps each query's softmax state
 // inside one lane: with S^T = K Q^T on v_mfma_f32_32x32x16_bf16 a lane owns
 // one query column and 16 key rows of each 32x32 tile, so the row max / row
 // sum need one cross-half shuffle, the running rescale of O^T = V^T P^T is a
 // per-lane multiply, and the probabilities are already laid out as the B
-// operand of the next MFMA.  The dK/dV kernel uses the untransposed S = Q K^T
-// so that each lane owns one key column.
+// operand of the next MFMA.  The dK and dV kernels use the untransposed
+// S = Q K^T so that each lane owns one key column.
 //
 // Streamed operands (K and V in the forward and dQ kernels, Q and dO in the
-// dK/dV kernel) are 64-row tiles copied straight from global memory into LDS
+// dK and dV kernels) are 64-row tiles copied straight from global memory into LDS
 // (global_load_lds_dwordx4, double buffered, one barrier per tile) in their
 // natural [row][feature] layout.  Each tile is read two ways: along the
 // feature index as an ordinary MFMA fragment (Q K^T, dO V^T), and along the
@@ -274,8 +274,9 @@ __global__ __launch_bounds__(256) void attn_bwd_pre_kernel(const uint16_t* __res
 // ---------------------------------------------------------------------------
 // backward: dQ, one workgroup per 128 queries, loop over key tiles
 // ---------------------------------------------------------------------------
+// Two workgroups per CU (the LDS allows it; 256 registers per lane suffice).
 template <int HD>
-__global__ __launch_bounds__(ATT_THREADS) void attn_bwd_dq_kernel(const uint16_t* __restrict__ qkv,
+__global__ __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bwd_dq_kernel(const uint16_t* __restrict__ qkv,
                                                                   const float* __restrict__ lse,
                                                                   const uint16_t* __restrict__ dout,
                                                                   const float* __restrict__ dvec,
@@ -386,10 +387,14 @@ __global__ __launch_bounds__(ATT_THREADS) void attn_bwd_dq_kernel(const uint16_t
 }
 
 // ---------------------------------------------------------------------------
-// backward: dK and dV, one workgroup per 128 keys, loop over query tiles
+// backward: dV (GRAD_K = false) or dK (GRAD_K = true), one workgroup per 128
+// keys, loop over query tiles.  The two gradients are separate launches: one
+// kernel holding K, V, dK and dV for its keys needs about 300 registers per
+// lane (one wave per SIMD); apart, each runs two workgroups per CU, which more
+// than pays for recomputing Q K^T once more.
 // ---------------------------------------------------------------------------
-template <int HD>
-__global__ __launch_bounds__(ATT_THREADS) void attn_bwd_dkdv_kernel(
+template <int HD, bool GRAD_K>
+__global__ __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bwd_kv_kernel(
     const uint16_t* __restrict__ qkv, const float* __restrict__ lse, const uint16_t* __restrict__ dout,
     const float* __restrict__ dvec, uint16_t* __restrict__ dqkv, int S, int heads, float sl2, float scale) {
     using TL = ATile<HD>;
@@ -409,22 +414,19 @@ __global__ __launch_bounds__(ATT_THREADS) void attn_bwd_dkdv_kernel(
     const int k0 = kw0 + wave * 32;   // first key of this wave
     const int kj = k0 + (lane & 31);  // key owned by this lane
 
-    uint4 kf[HD / 16], vf[HD / 16];
+    uint4 kf[HD / 16], vf[GRAD_K ? HD / 16 : 1];
 #pragma unroll
     for (int ds = 0; ds < HD / 16; ++ds) {
         kf[ds] = make_uint4(0, 0, 0, 0);
-        vf[ds] = make_uint4(0, 0, 0, 0);
-        if (kj < S) {
-            kf[ds] = *(const uint4*)(Kg + (int64_t)kj * ld + ds * 16 + 8 * half);
-            vf[ds] = *(const uint4*)(Vg + (int64_t)kj * ld + ds * 16 + 8 * half);
+        if (kj < S) kf[ds] = *(const uint4*)(Kg + (int64_t)kj * ld + ds * 16 + 8 * half);
+        if constexpr (GRAD_K) {
+            vf[ds] = make_uint4(0, 0, 0, 0);
+            if (kj < S) vf[ds] = *(const uint4*)(Vg + (int64_t)kj * ld + ds * 16 + 8 * half);
         }
     }
-    f32x16 dk[HD / 32], dv[HD / 32];
+    f32x16 acc[HD / 32];  // dK or dV of this lane's key
 #pragma unroll
-    for (int dt = 0; dt < HD / 32; ++dt) {
-        zero(dk[dt]);
-        zero(dv[dt]);
-    }
+    for (int dt = 0; dt < HD / 32; ++dt) zero(acc[dt]);
 
     const int qstart = (kw0 / ATT_T) * ATT_T;
     const int nqt = (S - qstart + ATT_T - 1) / ATT_T;
@@ -451,20 +453,22 @@ __global__ __launch_bounds__(ATT_THREADS) void attn_bwd_dkdv_kernel(
         const uint16_t* dOs = cur + TL::ELEMS;
 #pragma unroll
         for (int qt = 0; qt < ATT_T / 32; ++qt) {
+            const int row = qt * 32 + (lane & 31);
             f32x16 s, dp;
             zero(s);
-            zero(dp);
 #pragma unroll
-            for (int ds = 0; ds < HD / 16; ++ds) {
-                const int row = qt * 32 + (lane & 31);
+            for (int ds = 0; ds < HD / 16; ++ds)
                 s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(TL::frag_row(Qs, row, ds, half), as_bf16x8(kf[ds]), s, 0,
                                                             0, 0);
-                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(TL::frag_row(dOs, row, ds, half), as_bf16x8(vf[ds]), dp,
-                                                             0, 0, 0);
+            if constexpr (GRAD_K) {
+                zero(dp);
+#pragma unroll
+                for (int ds = 0; ds < HD / 16; ++ds)
+                    dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(TL::frag_row(dOs, row, ds, half), as_bf16x8(vf[ds]),
+                                                                 dp, 0, 0, 0);
             }
             // mask only where this 32-query sub-tile reaches below this wave's keys or past the end
             const bool edge = q0 + qt * 32 < k0 + 31 || q0 + qt * 32 + 32 > S || k0 + 32 > S;
-            f32x16 p;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int ql = qt * 32 + acc_row(r, half);
@@ -474,20 +478,18 @@ __global__ __launch_bounds__(ATT_THREADS) void attn_bwd_dkdv_kernel(
                     if (kj > q || q >= S || kj >= S) sv = -INFINITY;
                 }
                 const float pv = __builtin_amdgcn_exp2f(fmaf(sv, sl2, -ls[ql]));
-                p[r] = pv;
-                s[r] = pv * (dp[r] - dd[ql]);  // dS
+                if constexpr (GRAD_K)
+                    s[r] = pv * (dp[r] - dd[ql]);  // dS
+                else
+                    s[r] = pv;  // P
             }
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
-                const bf16x8 pb = frag_acc(p, ks * 8);
                 const bf16x8 sb = frag_acc(s, ks * 8);
 #pragma unroll
-                for (int dt = 0; dt < HD / 32; ++dt) {
-                    dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(TL::frag_tr(dOs, dt * 32, qt * 2 + ks, lane), pb,
-                                                                     dv[dt], 0, 0, 0);
-                    dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(TL::frag_tr(Qs, dt * 32, qt * 2 + ks, lane), sb,
-                                                                     dk[dt], 0, 0, 0);
-                }
+                for (int dt = 0; dt < HD / 32; ++dt)
+                    acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        TL::frag_tr(GRAD_K ? Qs : dOs, dt * 32, qt * 2 + ks, lane), sb, acc[dt], 0, 0, 0);
             }
         }
     };
@@ -512,17 +514,15 @@ __global__ __launch_bounds__(ATT_THREADS) void attn_bwd_dkdv_kernel(
         __syncthreads();
     }
     if (kj < S) {
-        uint16_t* krow = dqkv + ((int64_t)b * S + kj) * ld + H + (int64_t)head * HD;
-        uint16_t* vrow = krow + H;
+        uint16_t* orow = dqkv + ((int64_t)b * S + kj) * ld + (GRAD_K ? H : 2 * H) + (int64_t)head * HD;
+        const float sc = GRAD_K ? scale : 1.0f;
 #pragma unroll
         for (int dt = 0; dt < HD / 32; ++dt)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int d = dt * 32 + 8 * g + 4 * half;
-                *(uint2*)(krow + d) = make_uint2(pack_bf2(dk[dt][4 * g] * scale, dk[dt][4 * g + 1] * scale),
-                                                 pack_bf2(dk[dt][4 * g + 2] * scale, dk[dt][4 * g + 3] * scale));
-                *(uint2*)(vrow + d) = make_uint2(pack_bf2(dv[dt][4 * g], dv[dt][4 * g + 1]),
-                                                 pack_bf2(dv[dt][4 * g + 2], dv[dt][4 * g + 3]));
+                *(uint2*)(orow + d) = make_uint2(pack_bf2(acc[dt][4 * g] * sc, acc[dt][4 * g + 1] * sc),
+                                                 pack_bf2(acc[dt][4 * g + 2] * sc, acc[dt][4 * g + 3] * sc));
             }
     }
 }
@@ -564,20 +564,25 @@ void attention_bwd(const uint16_t* qkv, const uint16_t* o, const float* lse, con
     const int64_t T = (int64_t)B * S;
     const int64_t n = T * heads;
     const dim3 gq((S + ATT_BQ - 1) / ATT_BQ, B * heads), gk((S + ATT_BK - 1) / ATT_BK, B * heads);
-    // causal entries x (QK^T recompute, dP, dV, dK, dQ) at 2*hd flops each
+    // causal entries x (QK^T recompute, dP, dV, dK, dQ) at 2*hd flops each (the
+    // kernels execute 16*hd: Q K^T three times and dO V^T twice)
     ProfScope prof(PROF_ATTN_BWD, 10.0 * hd * (double)B * heads * ((double)S * (S + 1) / 2), s);
     if (hd == 128) {
         hipLaunchKernelGGL(attn_bwd_pre_kernel<128>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, o, dout, dvec,
                            T, S, heads);
-        hipLaunchKernelGGL(attn_bwd_dkdv_kernel<128>, gk, dim3(ATT_THREADS), 0, s, qkv, lse, dout, dvec, dqkv, S, heads,
-                           sl2, scale);
+        hipLaunchKernelGGL((attn_bwd_kv_kernel<128, false>), gk, dim3(ATT_THREADS), 0, s, qkv, lse, dout, dvec, dqkv, S,
+                           heads, sl2, scale);
+        hipLaunchKernelGGL((attn_bwd_kv_kernel<128, true>), gk, dim3(ATT_THREADS), 0, s, qkv, lse, dout, dvec, dqkv, S,
+                           heads, sl2, scale);
         hipLaunchKernelGGL(attn_bwd_dq_kernel<128>, gq, dim3(ATT_THREADS), 0, s, qkv, lse, dout, dvec, dqkv, S, heads,
                            sl2, scale);
     } else {
         hipLaunchKernelGGL(attn_bwd_pre_kernel<64>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, o, dout, dvec, T,
                            S, heads);
-        hipLaunchKernelGGL(attn_bwd_dkdv_kernel<64>, gk, dim3(ATT_THREADS), 0, s, qkv, lse, dout, dvec, dqkv, S, heads,
-                           sl2, scale);
+        hipLaunchKernelGGL((attn_bwd_kv_kernel<64, false>), gk, dim3(ATT_THREADS), 0, s, qkv, lse, dout, dvec, dqkv, S,
+                           heads, sl2, scale);
+        hipLaunchKernelGGL((attn_bwd_kv_kernel<64, true>), gk, dim3(ATT_THREADS), 0, s, qkv, lse, dout, dvec, dqkv, S,
+                           heads, sl2, scale);
         hipLaunchKernelGGL(attn_bwd_dq_kernel<64>, gq, dim3(ATT_THREADS), 0, s, qkv, lse, dout, dvec, dqkv, S, heads,
                            sl2, scale);
     }
