@@ -124,12 +124,17 @@ __device__ __forceinline__ void zero(f32x16& a) {
 // ---------------------------------------------------------------------------
 // forward
 // ---------------------------------------------------------------------------
+// Software-pipelined over key tiles: while the softmax of tile j runs on the
+// vector ALUs, the MFMAs of tile j+1's scores are already in flight.  K and V
+// have separate double buffers with staggered loads: during step j the LDS
+// holds K_{j+1} and V_j (read) while K_{j+2} and V_{j+1} arrive.
 template <int HD>
-__global__ __launch_bounds__(ATT_THREADS) void attn_fwd_kernel(const uint16_t* __restrict__ qkv,
+__global__ __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_kernel(const uint16_t* __restrict__ qkv,
                                                                uint16_t* __restrict__ o, float* __restrict__ lse, int S,
                                                                int heads, float sl2) {
     using TL = ATile<HD>;
-    __shared__ __attribute__((aligned(1024))) uint16_t smem[2][2 * TL::ELEMS];  // [buffer][K | V]
+    __shared__ __attribute__((aligned(1024))) uint16_t kbuf[2][TL::ELEMS];
+    __shared__ __attribute__((aligned(1024))) uint16_t vbuf[2][TL::ELEMS];
     const int nqb = (S + ATT_BQ - 1) / ATT_BQ;
     const int qb = nqb - 1 - (int)blockIdx.x;  // most work first
     const int bh = blockIdx.y;
@@ -155,19 +160,10 @@ __global__ __launch_bounds__(ATT_THREADS) void attn_fwd_kernel(const uint16_t* _
 
     const int kv_end = min(S, qb * ATT_BQ + ATT_BQ);
     const int nkv = (kv_end + ATT_T - 1) / ATT_T;
-    auto load = [&](int t, uint16_t* __restrict__ buf) {
-        TL::load(Kg, ld, t * ATT_T, S, buf, wave, lane);
-        TL::load(Vg, ld, t * ATT_T, S, buf + TL::ELEMS, wave, lane);
-    };
-    // One key tile: start the loads of the next tile into the other buffer
-    // (restrict: the compiler need not wait for them before reading this one)
-    auto step = [&](const uint16_t* __restrict__ cur, uint16_t* __restrict__ nxt, int kb) {
-        if (kb + 1 < nkv) load(kb + 1, nxt);
-        const int k0 = kb * ATT_T;
-        if (k0 > q0 + 31) return;  // every key of this tile is in this wave's future
-        const uint16_t* Ks = cur;
-        const uint16_t* Vs = cur + TL::ELEMS;
-        f32x16 st[2];
+    // key tiles this wave needs: k0 <= q0 + 31
+    const int nk_wave = min(nkv, (q0 + 31) / ATT_T + 1);
+
+    auto scores = [&](const uint16_t* Ks, f32x16* st) {
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) {
             zero(st[kt]);
@@ -176,6 +172,8 @@ __global__ __launch_bounds__(ATT_THREADS) void attn_fwd_kernel(const uint16_t* _
                 st[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(TL::frag_row(Ks, kt * 32 + (lane & 31), ds, half),
                                                                  as_bf16x8(qf[ds]), st[kt], 0, 0, 0);
         }
+    };
+    auto softmax_pv = [&](f32x16* st, const uint16_t* Vs, int k0) {
         // masking only where the tile crosses this wave's diagonal or the end
         if (k0 + ATT_T - 1 > q0 || k0 + ATT_T > S) {
 #pragma unroll
@@ -205,11 +203,15 @@ __global__ __launch_bounds__(ATT_THREADS) void attn_fwd_kernel(const uint16_t* _
             }
         ps += __shfl_xor(ps, 32);
         l_run = l_run * alpha + ps;
+        // once the running maxima settle, most tiles leave every one of them
+        // unchanged (alpha == 1 exactly): skip the rescale then
+        if (__any(m_new != m_run)) {
+#pragma unroll
+            for (int dt = 0; dt < HD / 32; ++dt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+        }
         m_run = m_new;
-#pragma unroll
-        for (int dt = 0; dt < HD / 32; ++dt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -222,12 +224,30 @@ __global__ __launch_bounds__(ATT_THREADS) void attn_fwd_kernel(const uint16_t* _
             }
     };
 
-    load(0, smem[0]);
+    f32x16 st_cur[2], st_nxt[2];
+    // Step j: loads into the buffers not read in this step (restrict: the
+    // compiler need not wait for them before the reads), the scores of tile
+    // j+1, then the softmax and PV of tile j.
+    auto step = [&](const uint16_t* __restrict__ kread, const uint16_t* __restrict__ vread,
+                    uint16_t* __restrict__ kwrite, uint16_t* __restrict__ vwrite, int j) {
+        if (j + 2 < nkv) TL::load(Kg, ld, (j + 2) * ATT_T, S, kwrite, wave, lane);
+        if (j + 1 < nkv) TL::load(Vg, ld, (j + 1) * ATT_T, S, vwrite, wave, lane);
+        if (j + 1 < nk_wave) scores(kread, st_nxt);
+        if (j < nk_wave) softmax_pv(st_cur, vread, j * ATT_T);
+    };
+
+    TL::load(Kg, ld, 0, S, kbuf[0], wave, lane);
+    TL::load(Vg, ld, 0, S, vbuf[0], wave, lane);
+    if (nkv > 1) TL::load(Kg, ld, ATT_T, S, kbuf[1], wave, lane);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    for (int kb = 0; kb < nkv; ++kb) {
-        const int cur = kb & 1;
-        step(smem[cur], smem[cur ^ 1], kb);
+    scores(kbuf[0], st_cur);
+    __syncthreads();  // every wave has read K_0 before step 0 loads K_2 over it
+    for (int j = 0; j < nkv; ++j) {
+        const int c = j & 1;
+        step(kbuf[c ^ 1], vbuf[c], kbuf[c], vbuf[c ^ 1], j);
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) st_cur[kt] = st_nxt[kt];
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     }
