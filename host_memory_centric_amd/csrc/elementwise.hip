@@ -186,16 +186,29 @@ void rmsnorm_bwd(const float* dy, const uint16_t* x, const float* rstd, const ui
     launch_check("rmsnorm_bwd", s);
 }
 
-__global__ void colsum_kernel(const float* __restrict__ part, int64_t nblk, int h, uint16_t* __restrict__ out) {
-    const int j = blockIdx.x * blockDim.x + threadIdx.x;
-    if (j >= h) return;
+// Column sums of the gain partials in a fixed order: 16 row groups per column
+// (group g sums rows g, g+16, ... in ascending order), then the 16 group sums
+// in ascending group order.
+__global__ __launch_bounds__(1024) void colsum_kernel(const float* __restrict__ part, int64_t nblk, int h,
+                                                      uint16_t* __restrict__ out) {
+    __shared__ float red[16][64];
+    const int c = threadIdx.x & 63, rg = threadIdx.x >> 6;
+    const int j = blockIdx.x * 64 + c;
     float v = 0.f;
-    for (int64_t b = 0; b < nblk; ++b) v += part[b * h + j];
-    out[j] = f2bf(v);
+    if (j < h)
+        for (int64_t b = rg; b < nblk; b += 16) v += part[b * h + j];
+    red[rg][c] = v;
+    __syncthreads();
+    if (rg == 0 && j < h) {
+        float t = 0.f;
+#pragma unroll
+        for (int g = 0; g < 16; ++g) t += red[g][c];
+        out[j] = f2bf(t);
+    }
 }
 
 void colsum_to_bf16(const float* part, int64_t nblk, int h, uint16_t* out, hipStream_t s) {
-    hipLaunchKernelGGL(colsum_kernel, dim3((h + 255) / 256), dim3(256), 0, s, part, nblk, h, out);
+    hipLaunchKernelGGL(colsum_kernel, dim3((h + 63) / 64), dim3(1024), 0, s, part, nblk, h, out);
     launch_check("colsum", s);
 }
 
