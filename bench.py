@@ -59,7 +59,7 @@ def measured_traffic(kernel, workload):
         return None
     data = json.loads(m.group(1))
     csrc = os.path.join(ROOT, "host_memory_centric_amd", "csrc")
-    src = open(os.path.join(csrc, "gemm.hip")).read() + open(os.path.join(csrc, "gemm_kernel.h")).read()
+    src = "".join(open(os.path.join(csrc, f)).read() for f in ("gemm.hip", "gemm_kernel.h", "gemm_pipe.h"))
     if hashlib.sha256(src.encode()).hexdigest()[:16] != data.get("source_sha256_16"):
         return None
     k = data.get("kernels", {}).get(kernel)

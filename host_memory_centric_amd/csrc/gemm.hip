@@ -5,20 +5,29 @@
 //   forward      Y[T, out]  = X[T, in] * W[out, in]^T   A K-major, B K-major
 //   input grad   dX[T, in]  = dY[T, out] * W[out, in]   A K-major, B N-major
 //   weight grad  dW[out,in] = dY[T, out]^T * X[T, in]   A M-major, B N-major
-// 256x256 output tiles, 8 waves each computing 128x64 with 32x32x16 MFMAs;
-// operand tiles go straight from global memory into a double-buffered LDS
-// ring (global_load_lds_dwordx4), one barrier per K step of 64; the loads of
-// the next tile overlap the MFMAs of the current one (see the restrict note in
-// gemm_kernel.h).  An operand
-// whose contraction index is strided (the N-major weight in dX, both
-// operands of dW) is copied into LDS as it lies and read with the
-// transposing ds_read_b64_tr_b16, so no orientation needs register staging
-// (the tile layouts and swizzles are described in gemm_kernel.h).  The
+//
+// Large operands (M, N >= 256, K in whole steps of 32) run gemm_pipe_kernel
+// (gemm_pipe.h): 256x256 output tiles, one workgroup of 4 waves per CU, each
+// wave 128x128 (its 256 fp32 accumulators live in the accumulation
+// registers); K advances in sub-steps of 32 through a four-slot LDS ring that
+// direct global->LDS buffer loads keep three sub-steps ahead (the depth the
+// memory latency needs at full MFMA rate; a two-slot ring of 64-wide steps
+// left the MFMAs waiting for loads), with one wait + barrier per sub-step.
+// The output tile is written through LDS as whole 512-byte rows (per-lane
+// scattered stores cost a fifth of the kernel).  Smaller operands use
+// gemm_kernel (gemm_kernel.h): 256x256 or 128x128 tiles of 8 or 4 waves and a
+// two-slot ring of 64-wide K steps, with zero-filled partial K steps.
+//
+// Either way an operand whose contraction index is strided (the N-major
+// weight in dX, both operands of dW) is copied into LDS as it lies and read
+// with the transposing ds_read_b64_tr_b16, so no orientation needs register
+// staging.  Every output element accumulates its products in the same K order
+// in both kernels, so results do not depend on which kernel runs.  The
 // weight-gradient GEMMs reduce over all tokens; when their tile grid is too
 // small to fill 256 CUs they split K into fixed slices whose fp32 partials
 // are summed in slice order by a second kernel: results never depend on
 // scheduling (no atomics).
-#include "gemm_kernel.h"
+#include "gemm_pipe.h"
 
 namespace mt {
 
@@ -38,8 +47,7 @@ __global__ void splitk_reduce_kernel(const float* part, int splits, int64_t M, i
     if (Cb) Cb[o] = f2bf(v);
 }
 
-template <int BM, int BN, int WM, int WN>
-static void launch_tiles(const GemmDesc& d, hipStream_t s, float* part, int splits, int64_t kps) {
+static GemmArgs make_args(const GemmDesc& d, float* part, int splits, int64_t kps, int bm, int bn) {
     GemmArgs p;
     p.M = d.M;
     p.N = d.N;
@@ -48,8 +56,8 @@ static void launch_tiles(const GemmDesc& d, hipStream_t s, float* part, int spli
     p.lda = d.lda;
     p.B = (const uint16_t*)d.B;
     p.ldb = d.ldb;
-    p.tiles_m = (int)((d.M + BM - 1) / BM);
-    p.tiles_n = (int)((d.N + BN - 1) / BN);
+    p.tiles_m = (int)((d.M + bm - 1) / bm);
+    p.tiles_n = (int)((d.N + bn - 1) / bn);
     p.k_per_split = kps;
     if (splits > 1) {
         p.Cf = part;
@@ -66,6 +74,12 @@ static void launch_tiles(const GemmDesc& d, hipStream_t s, float* part, int spli
         p.accumulate = d.accumulate;
         p.split_stride = 0;
     }
+    return p;
+}
+
+template <int BM, int BN, int WM, int WN>
+static void launch_tiles(const GemmDesc& d, hipStream_t s, float* part, int splits, int64_t kps) {
+    const GemmArgs p = make_args(d, part, splits, kps, BM, BN);
     dim3 grid(p.tiles_m * p.tiles_n, splits);
     dim3 block(WM * WN * 64);
     if (d.a_kmajor && d.b_kmajor)
@@ -76,6 +90,28 @@ static void launch_tiles(const GemmDesc& d, hipStream_t s, float* part, int spli
         hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, false, false>), grid, block, 0, s, p);
     else
         hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, false, true>), grid, block, 0, s, p);
+}
+
+static void launch_pipe(const GemmDesc& d, hipStream_t s, float* part, int splits, int64_t kps) {
+    const GemmArgs p = make_args(d, part, splits, kps, 256, 256);
+    dim3 grid(p.tiles_m * p.tiles_n, splits);
+    dim3 block(256);
+    if (d.a_kmajor && d.b_kmajor)
+        hipLaunchKernelGGL((gemm_pipe_kernel<true, true>), grid, block, 0, s, p);
+    else if (d.a_kmajor && !d.b_kmajor)
+        hipLaunchKernelGGL((gemm_pipe_kernel<true, false>), grid, block, 0, s, p);
+    else if (!d.a_kmajor && !d.b_kmajor)
+        hipLaunchKernelGGL((gemm_pipe_kernel<false, false>), grid, block, 0, s, p);
+    else
+        hipLaunchKernelGGL((gemm_pipe_kernel<false, true>), grid, block, 0, s, p);
+}
+
+// The pipelined kernel needs whole 256x256 tiles inside the operands (the
+// last tile is moved back to the edge), K slices of whole 32-wide sub-steps,
+// and per-lane byte offsets below 2^31 (256 rows or 64 k-rows of an operand).
+static bool pipe_ok(const GemmDesc& d, int64_t kps) {
+    return d.M >= 256 && d.N >= 256 && d.K % PBK == 0 && kps % PBK == 0 && d.lda < (1 << 22) &&
+           d.ldb < (1 << 22);
 }
 
 size_t gemm_splitk_bytes(int64_t M, int64_t N, int64_t K) {
@@ -118,7 +154,9 @@ void gemm(const GemmDesc& d, hipStream_t s) {
     float* part = splits > 1 ? (float*)d.ws : nullptr;
     const ProfClass pc = d.a_kmajor ? (d.b_kmajor ? PROF_GEMM_NT : PROF_GEMM_NN) : PROF_GEMM_TN;
     ProfScope prof(pc, 2.0 * (double)d.M * (double)d.N * (double)d.K, s);
-    if (use_big(d.M, d.N))
+    if (pipe_ok(d, kps))
+        launch_pipe(d, s, part, splits, kps);
+    else if (use_big(d.M, d.N))
         launch_tiles<256, 256, 2, 4>(d, s, part, splits, kps);
     else
         launch_tiles<128, 128, 2, 2>(d, s, part, splits, kps);

@@ -53,7 +53,7 @@ def _run_gemm(gpu, M, N, K, ak, bk, epi, seed, ws_mb=64):
     dR = _dev(R.view(np.int16), gpu)
     ws = torch.empty(ws_mb << 20, dtype=torch.uint8, device=gpu)
     use_f, use_b, use_r, acc = {"f32": (1, 0, 0, 0), "bf16": (0, 1, 0, 0), "resid": (1, 1, 1, 0),
-                                "accum": (1, 0, 0, 1)}[epi]
+                                "bresid": (0, 1, 1, 0), "accum": (1, 0, 0, 1)}[epi]
     call("mt_op_gemm", M, N, K, _p(dA), K if ak else M, int(ak), _p(dB), K if bk else N, int(bk),
          _p(cf) if use_f else None, _p(cb) if use_b else None, _p(dR) if use_r else None, N, acc, _p(ws),
          ws.numel(), _stream())
@@ -70,15 +70,21 @@ def _run_gemm(gpu, M, N, K, ak, bk, epi, seed, ws_mb=64):
 
 
 @pytest.mark.parametrize("ak,bk", [(True, True), (True, False), (False, False), (False, True)])
-@pytest.mark.parametrize("M,N,K", [(136, 264, 200), (8, 8, 8), (1032, 1288, 520)])
+# (1032, 1288, 520): K not in whole 32-steps (8-wave kernel, zero-filled tail
+# step); (1032, 1288, 512), (264, 520, 96), (264, 520, 32): the pipelined
+# kernel with ragged M/N tiles and with fewer K sub-steps than its ring depth.
+@pytest.mark.parametrize("M,N,K", [(136, 264, 200), (8, 8, 8), (1032, 1288, 520), (1032, 1288, 512),
+                                   (264, 520, 96), (264, 520, 32)])
 def test_gemm_integer_exact(gpu, ak, bk, M, N, K):
     _run_gemm(gpu, M, N, K, ak, bk, "f32", seed=M + N + K)
 
 
-@pytest.mark.parametrize("epi", ["bf16", "resid", "accum"])
+@pytest.mark.parametrize("epi", ["bf16", "resid", "bresid", "accum"])
 def test_gemm_epilogues(gpu, epi):
     _run_gemm(gpu, 264, 136, 128, True, True, epi, seed=3)
     _run_gemm(gpu, 1040, 1024, 64, True, False, epi, seed=4)
+    _run_gemm(gpu, 1288, 1032, 256, True, True, epi, seed=7)
+    _run_gemm(gpu, 520, 776, 160, False, False, epi, seed=8)
 
 
 @pytest.mark.parametrize("ak,bk", [(False, False), (True, False)])
