@@ -113,6 +113,33 @@ def overlap_report(tl):
             "gpu_idle_ms": round(span - _total(comp), 2)}
 
 
+def host_probe(tr, reps=3):
+    """Host DRAM rates of the two host-side passes, measured on layer 0 after
+    the timed steps with the GPU idle: the packer (W region -> pinned slab,
+    read + non-temporal write, 4 bytes per parameter) and the Adam step
+    (slab read, G written, W/m/v read and written, 24 bytes per parameter).
+    The Adam calls advance layer 0's optimizer state; nothing runs after."""
+    import ctypes
+
+    from host_memory_centric_amd._lib import call
+    lay = tr.lay
+    params = lay.w_bytes // 2
+    slab = tr.gslab[0]
+    tr.finish()
+    t = time.perf_counter()
+    for _ in range(reps):
+        call("mt_pack_layer", tr.store.ptr, 0, tr.wslab[0].ptr, tr.slot_bytes)
+    pack_s = (time.perf_counter() - t) / reps
+    step_t = tr.t + 1
+    t = time.perf_counter()
+    for i in range(reps):
+        call("mt_step", tr.store.ptr, 0, slab.ptr, ctypes.byref(tr.madam), step_t + i, None)
+    adam_s = (time.perf_counter() - t) / reps
+    return {"threads": len(os.sched_getaffinity(0)), "pack_ms_per_layer": round(1e3 * pack_s, 2),
+            "pack_GBps": round(4 * params / pack_s / 1e9, 1), "adam_ms_per_layer": round(1e3 * adam_s, 2),
+            "adam_GBps": round(24 * params / adam_s / 1e9, 1)}
+
+
 def link_probe(tr, nbytes=1 << 30, reps=3):
     """Pinned host <-> device copy rates on this machine: each direction alone and
     both at once (the trainer's weight and gradient streams)."""
@@ -212,6 +239,7 @@ def main():
     ap.add_argument("--mode", default="streamed", choices=["streamed", "resident"])
     ap.add_argument("--slots", type=int, default=2)
     ap.add_argument("--grad-slabs", type=int, default=16)
+    ap.add_argument("--ckpt-every", type=int, default=None, help="override the workload's checkpoint interval")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--timeline-out", default=None, help="write the event timeline of one step as JSON")
     args = ap.parse_args()
@@ -227,6 +255,9 @@ def main():
     from host_memory_centric_amd.engine import Trainer
 
     cfg = synth.preset(args.workload)
+    if args.ckpt_every is not None:
+        import dataclasses
+        cfg = dataclasses.replace(cfg, ckpt_every=args.ckpt_every)
     adam = synth.AdamCfg()
     t_init = time.perf_counter()
     tr = Trainer(cfg, adam, mode=args.mode, n_slots=args.slots, n_grad_slabs=args.grad_slabs, device="cuda:0")
@@ -262,6 +293,7 @@ def main():
         with open(args.timeline_out, "w") as fh:
             json.dump(tl, fh)
     link = link_probe(tr)
+    host = host_probe(tr)
 
     T = cfg.tokens
     ms_step = 1e3 * dt / args.steps
@@ -304,6 +336,16 @@ def main():
                      h2d_link_frac=round(h2d / (ms_step * 1e-3) / (link["h2d_GBps"] * 1e9), 4),
                      h2d_active_GBps=round(h2d / 1e9 / (overlap["h2d_busy_frac"] * overlap["step_ms"] * 1e-3), 2)),
     }
+    # host DRAM bytes of one step: every weight load is packed once (4 B per
+    # parameter), every parameter gets one Adam update (24 B), and the DMA
+    # engines read the H2D bytes from and write the D2H bytes to host memory;
+    # the floor divides them by the faster of the two measured host rates
+    n_params = sum(tr.store.layout_of(u).w_bytes // 2 for u in tr.store.units)
+    host_bytes = 4 * (lay.w_bytes // 2) * (n_loads - 1) + 4 * (lay_h.w_bytes // 2) + 24 * n_params + h2d + d2h
+    host["bytes_per_step"] = int(host_bytes)
+    host["floor_ms"] = round(1e3 * host_bytes / (max(host["pack_GBps"], host["adam_GBps"]) * 1e9), 1)
+    host["floor_frac_of_step"] = round(host["floor_ms"] / ms_step, 3)
+    out["host"] = host
     tr.close()
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg)

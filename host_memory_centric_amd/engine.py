@@ -192,7 +192,9 @@ class Trainer:
 
     cfg: model shape + batch/seq (``synth.ModelCfg``-like); adam: optimizer
     settings; mode: 'streamed' or 'resident'; n_slots: device weight slots
-    (2 = the pages' double buffering); n_grad_slabs: pinned gradient slabs;
+    (2 = the pages' double buffering; 1 = none, each load waits for the op
+    before it; more = a recomputed block stays resident for its backward);
+    n_grad_slabs: pinned gradient slabs;
     weights: None (seeded fill by the library) or bf16 bit arrays;
     capture_w32: keep each unit's updated fp32 weights before their bf16
     rounding (``self.w32[unit]``, W-region indexing) for parity checks."""
@@ -206,7 +208,7 @@ class Trainer:
         self.dev = torch.device(device)
         self.L = cfg.layers
         self.K = self.L if mode == "resident" else (ckpt_every or cfg.ckpt_every)
-        self.n_slots = self.L + 1 if mode == "resident" else max(2, n_slots)
+        self.n_slots = self.L + 1 if mode == "resident" else max(1, n_slots)
         self.B, self.S = cfg.batch, cfg.seq
         self.T = self.B * self.S
         h = cfg.hidden

@@ -281,6 +281,15 @@ def test_plan_orders_ops_as_the_method():
                           ("bwd", 3), ("bwd", 2), ("bwd", 1), ("bwd", 0)]
 
 
+@pytest.mark.parametrize("L,K", [(32, 4), (4, 1), (2, 1)])
+def test_one_slot_loads_every_change(L, K):
+    # one slot (no double buffering): every use of another unit than the op
+    # before it is a load into the same slot
+    _, units, slot_of, load = _loads(L, K, 1)
+    assert set(slot_of) == {0}
+    assert load == [i == 0 or units[i] != units[i - 1] for i in range(len(units))]
+
+
 @pytest.mark.parametrize("L,K", [(32, 4), (48, 4), (180, 4), (24, 4), (4, 1), (2, 1)])
 def test_two_slot_load_count(L, K):
     _, units, slot_of, load = _loads(L, K, 2)
