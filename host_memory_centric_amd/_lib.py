@@ -15,6 +15,8 @@ LIB_PATH = os.path.join(HERE, "libmt.so")
 
 MT_UNIT_EMBED = -1
 MT_UNIT_HEAD = -2
+MT_STORE_MASTER_FP32 = 1
+MT_STORE_GRAD_ACCUM = 2
 ERRORS = {-1: "MT_E_ARG", -2: "MT_E_SHAPE", -3: "MT_E_ALIGN", -4: "MT_E_NOMEM", -5: "MT_E_HIP", -6: "MT_E_STATE"}
 
 
@@ -31,8 +33,8 @@ class MtModelCfg(ctypes.Structure):
 
 class MtUnitLayout(ctypes.Structure):
     _fields_ = [("n_tensors", c_int32), ("pad_", c_int32), ("tensor_off", c_uint64 * 6),
-                ("tensor_numel", c_uint64 * 6), ("w_bytes", c_uint64), ("region_off", c_uint64 * 4),
-                ("region_bytes", c_uint64 * 4), ("block_bytes", c_uint64), ("params", c_uint64)]
+                ("tensor_numel", c_uint64 * 6), ("w_bytes", c_uint64), ("region_off", c_uint64 * 6),
+                ("region_bytes", c_uint64 * 6), ("block_bytes", c_uint64), ("params", c_uint64)]
 
 
 class MtAdamCfg(ctypes.Structure):
@@ -63,7 +65,11 @@ class MtProfEntry(ctypes.Structure):
 # name -> (argtypes)
 _SIGS = {
     "mt_unit_layout_get": [POINTER(MtModelCfg), c_int, POINTER(MtUnitLayout)],
+    "mt_unit_layout_get_ex": [POINTER(MtModelCfg), c_uint32, c_int, POINTER(MtUnitLayout)],
     "mt_store_create": [POINTER(MtModelCfg), POINTER(c_void_p)],
+    "mt_store_create_ex": [POINTER(MtModelCfg), c_uint32, POINTER(c_void_p)],
+    "mt_store_sync_master": [c_void_p],
+    "mt_grad_accumulate": [c_void_p, c_int, c_void_p],
     "mt_store_block": [c_void_p, c_int, POINTER(c_void_p)],
     "mt_store_bytes": [c_void_p, POINTER(c_uint64)],
     "mt_store_fill_normal": [c_void_p, c_uint32, c_double],
@@ -141,9 +147,9 @@ def adam_cfg(a):
     return MtAdamCfg(a.lr, a.beta1, a.beta2, a.eps, a.weight_decay)
 
 
-def unit_layout(mcfg, unit):
+def unit_layout(mcfg, unit, flags=0):
     out = MtUnitLayout()
-    call("mt_unit_layout_get", ctypes.byref(mcfg), unit, ctypes.byref(out))
+    call("mt_unit_layout_get_ex", ctypes.byref(mcfg), flags, unit, ctypes.byref(out))
     return out
 
 

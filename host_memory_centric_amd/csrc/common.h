@@ -52,7 +52,7 @@ int guard(F&& f) {
 inline uint64_t round_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
 
 // Validated layout of a unit (throws on bad config).
-mt_unit_layout layout_of(const mt_model_cfg* cfg, int unit);
+mt_unit_layout layout_of(const mt_model_cfg* cfg, int unit, uint32_t flags = 0);
 void check_cfg(const mt_model_cfg* cfg);
 
 }  // namespace mt

@@ -57,8 +57,10 @@ void check_cfg(const mt_model_cfg* cfg) {
     if (!(cfg->eps > 0.f) || !(cfg->rope_base > 1.f)) MT_FAIL(MT_E_ARG, "bad eps or rope_base");
 }
 
-mt_unit_layout layout_of(const mt_model_cfg* cfg, int unit) {
+mt_unit_layout layout_of(const mt_model_cfg* cfg, int unit, uint32_t flags) {
     check_cfg(cfg);
+    MT_CHECK_ARG((flags & ~(uint32_t)(MT_STORE_MASTER_FP32 | MT_STORE_GRAD_ACCUM)) == 0, "unknown store flags %u",
+                 flags);
     mt_unit_layout L;
     memset(&L, 0, sizeof(L));
     const uint64_t h = cfg->hidden, f = cfg->ffn, V = cfg->vocab;
@@ -91,9 +93,11 @@ mt_unit_layout layout_of(const mt_model_cfg* cfg, int unit) {
     }
     L.w_bytes = off;
     const uint64_t elems = L.w_bytes / 2;
-    const uint64_t rb[4] = {L.w_bytes, L.w_bytes, 4 * elems, 4 * elems};
+    const uint64_t rb[6] = {L.w_bytes, L.w_bytes, 4 * elems, 4 * elems,
+                            (flags & MT_STORE_MASTER_FP32) ? 4 * elems : 0,
+                            (flags & MT_STORE_GRAD_ACCUM) ? 4 * elems : 0};
     uint64_t pos = 0;
-    for (int r = 0; r < 4; ++r) {
+    for (int r = 0; r < 6; ++r) {
         L.region_off[r] = pos;
         L.region_bytes[r] = round_up(rb[r], MT_BLOCK_ALIGN);
         pos += L.region_bytes[r];
@@ -185,9 +189,11 @@ static void par_memcpy(void* dst, const void* src, uint64_t bytes) {
 
 struct mt_store {
     mt_model_cfg cfg;
+    uint32_t flags = 0;                  // MT_STORE_* regions present
     std::vector<void*> blocks;           // index: unit + 2 (embed, head, layers...)
     std::vector<uint64_t> mapped_bytes;  // mmap lengths
     std::vector<mt_unit_layout> layouts;
+    std::vector<int64_t> n_accum;        // micro-batch gradients in A since the unit's last step
 };
 
 namespace mt {
@@ -334,12 +340,120 @@ __attribute__((target("avx512f,avx512bw"))) static void adam_avx512(uint16_t* W,
     if (src && g_aligned) _mm_sfence();
     if (i < e) adam_scalar(W, G, M, Vv, src, wout, i, e, k);
 }
+// Adam with the optional regions (same operation order as adam_scalar): P,
+// the fp32 master weights, replaces W as the weight read and receives w';
+// with A (k >= 1 accumulated micro-batches) the gradient landed in G is
+// bf16((A + bf16 src) / nf), nf = k + 1, src = the last micro-batch's
+// gradient (the slab, or G itself).
+static void adam_ex_scalar(uint16_t* W, uint16_t* G, float* M, float* Vv, float* P, const float* A, float nf,
+                           const uint16_t* src, float* wout, uint64_t b, uint64_t e, const AdamK& k) {
+    for (uint64_t i = b; i < e; ++i) {
+        if (A) {
+            const float s = A[i] + bf16_to_f32(src ? src[i] : G[i]);
+            G[i] = f32_to_bf16(s / nf);
+        } else if (src) {
+            G[i] = src[i];
+        }
+        float w = P ? P[i] : bf16_to_f32(W[i]);
+        if (k.wd) w = w * k.decay;
+        const float g = bf16_to_f32(G[i]);
+        const float m = k.b1 * M[i] + k.omb1 * g;
+        const float v = k.b2 * Vv[i] + k.omb2 * (g * g);
+        M[i] = m;
+        Vv[i] = v;
+        const float denom = std::sqrt(v) + k.eps_hat;
+        const float step = k.alpha * m;
+        const float wn = w - step / denom;
+        if (wout) wout[i] = wn;
+        if (P) P[i] = wn;
+        W[i] = f32_to_bf16(wn);
+    }
+}
+
+__attribute__((target("avx512f,avx512bw"))) static inline __m512 bf16x16_to_f32(__m256i b) {
+    return _mm512_castsi512_ps(_mm512_slli_epi32(_mm512_cvtepu16_epi32(b), 16));
+}
+// round to nearest even (finite values)
+__attribute__((target("avx512f,avx512bw"))) static inline __m256i f32x16_to_bf16(__m512 x) {
+    __m512i u = _mm512_castps_si512(x);
+    u = _mm512_add_epi32(u, _mm512_add_epi32(_mm512_set1_epi32(0x7fff),
+                                              _mm512_and_si512(_mm512_srli_epi32(u, 16), _mm512_set1_epi32(1))));
+    return _mm512_cvtepi32_epi16(_mm512_srli_epi32(u, 16));
+}
+
+__attribute__((target("avx512f,avx512bw"))) static void adam_ex_avx512(uint16_t* W, uint16_t* G, float* M,
+                                                                         float* Vv, float* P, const float* A,
+                                                                         float nf, const uint16_t* src,
+                                                                         float* wout, uint64_t b, uint64_t e,
+                                                                         const AdamK& k) {
+    const __m512 b1 = _mm512_set1_ps(k.b1), b2 = _mm512_set1_ps(k.b2), omb1 = _mm512_set1_ps(k.omb1),
+                 omb2 = _mm512_set1_ps(k.omb2), alpha = _mm512_set1_ps(k.alpha), eps = _mm512_set1_ps(k.eps_hat),
+                 dec = _mm512_set1_ps(k.decay), nfv = _mm512_set1_ps(nf);
+    uint64_t i = b;
+    for (; i + 16 <= e; i += 16) {
+        __m256i gb;
+        if (A) {
+            const __m256i lb = _mm256_loadu_si256((const __m256i*)((src ? src : G) + i));
+            const __m512 s = _mm512_add_ps(_mm512_loadu_ps(A + i), bf16x16_to_f32(lb));
+            gb = f32x16_to_bf16(_mm512_div_ps(s, nfv));
+            _mm256_storeu_si256((__m256i*)(G + i), gb);
+        } else if (src) {
+            gb = _mm256_loadu_si256((const __m256i*)(src + i));
+            _mm256_storeu_si256((__m256i*)(G + i), gb);
+        } else {
+            gb = _mm256_loadu_si256((const __m256i*)(G + i));
+        }
+        __m512 w = P ? _mm512_loadu_ps(P + i) : bf16x16_to_f32(_mm256_loadu_si256((const __m256i*)(W + i)));
+        if (k.wd) w = _mm512_mul_ps(w, dec);
+        const __m512 g = bf16x16_to_f32(gb);
+        const __m512 m = _mm512_add_ps(_mm512_mul_ps(b1, _mm512_loadu_ps(M + i)), _mm512_mul_ps(omb1, g));
+        const __m512 v = _mm512_add_ps(_mm512_mul_ps(b2, _mm512_loadu_ps(Vv + i)),
+                                       _mm512_mul_ps(omb2, _mm512_mul_ps(g, g)));
+        _mm512_storeu_ps(M + i, m);
+        _mm512_storeu_ps(Vv + i, v);
+        const __m512 denom = _mm512_add_ps(_mm512_sqrt_ps(v), eps);
+        const __m512 step = _mm512_mul_ps(alpha, m);
+        const __m512 wn = _mm512_sub_ps(w, _mm512_div_ps(step, denom));
+        if (wout) _mm512_storeu_ps(wout + i, wn);
+        if (P) _mm512_storeu_ps(P + i, wn);
+        _mm256_storeu_si256((__m256i*)(W + i), f32x16_to_bf16(wn));
+    }
+    if (i < e) adam_ex_scalar(W, G, M, Vv, P, A, nf, src, wout, i, e, k);
+}
+
+// A = bf16 src (first micro-batch after a step) or A + bf16 src
+static void accum_scalar(float* A, const uint16_t* src, bool first, uint64_t b, uint64_t e) {
+    for (uint64_t i = b; i < e; ++i) A[i] = first ? bf16_to_f32(src[i]) : A[i] + bf16_to_f32(src[i]);
+}
+
+__attribute__((target("avx512f,avx512bw"))) static void accum_avx512(float* A, const uint16_t* src, bool first,
+                                                                       uint64_t b, uint64_t e) {
+    uint64_t i = b;
+    for (; i + 16 <= e; i += 16) {
+        const __m512 g = bf16x16_to_f32(_mm256_loadu_si256((const __m256i*)(src + i)));
+        _mm512_storeu_ps(A + i, first ? g : _mm512_add_ps(_mm512_loadu_ps(A + i), g));
+    }
+    if (i < e) accum_scalar(A, src, first, i, e);
+}
 #pragma clang fp contract(on)
 
 static bool have_avx512() {
     static const bool ok = __builtin_cpu_supports("avx512f") && __builtin_cpu_supports("avx512bw") &&
                            getenv("MT_NO_AVX512") == nullptr;
     return ok;
+}
+
+// P = fp32(W) for every unit of a master-weight store
+static void sync_master(mt_store* st) {
+    for (size_t idx = 0; idx < st->blocks.size(); ++idx) {
+        const mt_unit_layout& L = st->layouts[idx];
+        const char* blk = (const char*)st->blocks[idx];
+        const uint16_t* W = (const uint16_t*)(blk + L.region_off[0]);
+        float* P = (float*)((char*)st->blocks[idx] + L.region_off[4]);
+        parallel_for(L.w_bytes / 2, 1 << 20, [&](uint64_t b, uint64_t e) {
+            for (uint64_t i = b; i < e; ++i) P[i] = bf16_to_f32(W[i]);
+        });
+    }
 }
 
 }  // namespace mt
@@ -361,25 +475,34 @@ int mt_set_threads(int n) {
 }
 
 int mt_unit_layout_get(const mt_model_cfg* cfg, int unit, mt_unit_layout* out) {
+    return mt_unit_layout_get_ex(cfg, 0, unit, out);
+}
+
+int mt_unit_layout_get_ex(const mt_model_cfg* cfg, uint32_t flags, int unit, mt_unit_layout* out) {
     return guard([&] {
         MT_CHECK_ARG(out != nullptr, "out is NULL");
-        *out = layout_of(cfg, unit);
+        *out = layout_of(cfg, unit, flags);
     });
 }
 
-int mt_store_create(const mt_model_cfg* cfg, mt_store** out) {
+int mt_store_create(const mt_model_cfg* cfg, mt_store** out) { return mt_store_create_ex(cfg, 0, out); }
+
+int mt_store_create_ex(const mt_model_cfg* cfg, uint32_t flags, mt_store** out) {
     return guard([&] {
         MT_CHECK_ARG(out != nullptr, "out is NULL");
         check_cfg(cfg);
+        layout_of(cfg, 0, flags);  // validates the flags
         auto* st = new mt_store();
         st->cfg = *cfg;
+        st->flags = flags;
         try {
             for (int u = MT_UNIT_HEAD; u < cfg->layers; ++u) {
-                mt_unit_layout L = layout_of(cfg, u);
+                mt_unit_layout L = layout_of(cfg, u, flags);
                 const uint64_t len = round_up(L.block_bytes, 2ull << 20);
                 st->layouts.push_back(L);
                 st->blocks.push_back(map_block(len));
                 st->mapped_bytes.push_back(len);
+                st->n_accum.push_back(0);
             }
         } catch (...) {
             mt_store_destroy(st);
@@ -435,6 +558,35 @@ int mt_store_fill_normal(mt_store* st, uint32_t seed, double std_) {
                 }
             }
         }
+        if (st->flags & MT_STORE_MASTER_FP32) sync_master(st);
+    });
+}
+
+int mt_store_sync_master(mt_store* st) {
+    return guard([&] {
+        MT_CHECK_ARG(st != nullptr, "store is NULL");
+        if (!(st->flags & MT_STORE_MASTER_FP32)) MT_FAIL(MT_E_STATE, "the store has no master weights");
+        sync_master(st);
+    });
+}
+
+int mt_grad_accumulate(mt_store* st, int unit, const void* grad_src) {
+    return guard([&] {
+        const int idx = unit_index(st, unit);
+        if (!(st->flags & MT_STORE_GRAD_ACCUM)) MT_FAIL(MT_E_STATE, "the store has no gradient accumulator");
+        const mt_unit_layout& L = st->layouts[idx];
+        char* blk = (char*)st->blocks[idx];
+        float* A = (float*)(blk + L.region_off[5]);
+        const uint16_t* src = grad_src ? (const uint16_t*)grad_src : (const uint16_t*)(blk + L.region_off[1]);
+        const bool first = st->n_accum[idx] == 0;
+        const bool simd = have_avx512();
+        parallel_for(L.w_bytes / 2, 1 << 18, [&](uint64_t b, uint64_t e) {
+            if (simd)
+                accum_avx512(A, src, first, b, e);
+            else
+                accum_scalar(A, src, first, b, e);
+        });
+        ++st->n_accum[idx];
     });
 }
 
@@ -496,12 +648,26 @@ int mt_step(mt_store* st, int unit, const void* grad_src, const mt_adam_cfg* ada
         const uint64_t n = L.w_bytes / 2;
         const uint16_t* src = (const uint16_t*)grad_src;
         const bool simd = have_avx512();
-        parallel_for(n, 1 << 18, [&](uint64_t b, uint64_t e) {
-            if (simd)
-                adam_avx512(W, G, M, Vv, src, w_fp32_out, b, e, k);
-            else
-                adam_scalar(W, G, M, Vv, src, w_fp32_out, b, e, k);
-        });
+        float* P = (st->flags & MT_STORE_MASTER_FP32) ? (float*)(blk + L.region_off[4]) : nullptr;
+        const int64_t k_acc = st->n_accum[idx];
+        const float* A = k_acc > 0 ? (const float*)(blk + L.region_off[5]) : nullptr;
+        if (!P && !A) {
+            parallel_for(n, 1 << 18, [&](uint64_t b, uint64_t e) {
+                if (simd)
+                    adam_avx512(W, G, M, Vv, src, w_fp32_out, b, e, k);
+                else
+                    adam_scalar(W, G, M, Vv, src, w_fp32_out, b, e, k);
+            });
+        } else {
+            const float nf = (float)(k_acc + 1);
+            parallel_for(n, 1 << 18, [&](uint64_t b, uint64_t e) {
+                if (simd)
+                    adam_ex_avx512(W, G, M, Vv, P, A, nf, src, w_fp32_out, b, e, k);
+                else
+                    adam_ex_scalar(W, G, M, Vv, P, A, nf, src, w_fp32_out, b, e, k);
+            });
+        }
+        st->n_accum[idx] = 0;
     });
 }
 

@@ -197,10 +197,13 @@ class Trainer:
     n_grad_slabs: pinned gradient slabs;
     weights: None (seeded fill by the library) or bf16 bit arrays;
     capture_w32: keep each unit's updated fp32 weights before their bf16
-    rounding (``self.w32[unit]``, W-region indexing) for parity checks."""
+    rounding (``self.w32[unit]``, W-region indexing) for parity checks;
+    micro_batches: micro-batches of [batch, seq] tokens per step, whose
+    gradients the host accumulates (``mt_grad_accumulate``) before one Adam
+    step on their mean; master: keep fp32 master weights in the host store."""
 
     def __init__(self, cfg, adam, mode="streamed", n_slots=2, n_grad_slabs=16, ckpt_every=None, weights=None,
-                 device="cuda:0", capture_w32=False, timeline=False):
+                 device="cuda:0", capture_w32=False, timeline=False, micro_batches=1, master=False):
         if mode not in ("streamed", "resident"):
             raise ValueError("mode must be 'streamed' or 'resident'")
         _lib.load()
@@ -215,8 +218,9 @@ class Trainer:
         self.mcfg = _lib.model_cfg(cfg)
         self.madam = _lib.adam_cfg(adam)
         self.t = 0
+        self.n_micro = max(1, int(micro_batches))
 
-        self.store = HostStore(cfg)
+        self.store = HostStore(cfg, master=master, accum=self.n_micro > 1)
         if weights is None:
             self.store.fill_normal()
         else:
@@ -273,6 +277,7 @@ class Trainer:
         for k in range(len(self.gslab)):
             self.slab_free.put(k)
         self.pending = {}              # unit -> future of its host update still running
+        self.accum_jobs = {}           # unit -> future of its last micro-batch accumulation
         self.gslot_d2h = [None, None]  # last copy out of each device gradient slot
         self.head_d2h = None           # last copy out of the head's gradient buffer
         self.record_timeline = timeline
@@ -289,12 +294,19 @@ class Trainer:
 
     # ------------------------------------------------------------------
     def finish(self):
-        """Wait for every host update of the previous steps."""
+        """Wait for every host update (and accumulation) of the previous steps."""
+        for u in list(self.accum_jobs):
+            self._wait_acc(u)
         for u in list(self.pending):
             self._wait_unit(u)
 
     def _wait_unit(self, unit):
         f = self.pending.pop(unit, None)
+        if f is not None:
+            f.result()
+
+    def _wait_acc(self, unit):
+        f = self.accum_jobs.pop(unit, None)
         if f is not None:
             f.result()
 
@@ -344,22 +356,39 @@ class Trainer:
 
     # ------------------------------------------------------------------
     def step(self, tokens):
-        """One training step on int32 tokens [B, S].  Returns the loss."""
+        """One training step on int32 tokens [micro_batches * B, S]: each
+        micro-batch of B rows runs forward, head and backward; the host
+        accumulates their gradients and runs Adam once, on their mean, after
+        the last.  Returns the loss (mean over the micro-batches)."""
         tokens = np.ascontiguousarray(tokens, dtype=np.int32)
-        if tokens.shape != (self.B, self.S):
-            raise ValueError(f"tokens must have shape {(self.B, self.S)}")
+        if tokens.shape != (self.n_micro * self.B, self.S):
+            raise ValueError(f"tokens must have shape {(self.n_micro * self.B, self.S)}")
         self.t += 1
-        t = self.t
+        t0 = time.perf_counter()
+        tl = self._timeline_begin(self.s_comp) if self.record_timeline else None
+        losses = []
+        n_loads = 0
+        for i in range(self.n_micro):
+            loss, n = self._pass(tokens[i * self.B:(i + 1) * self.B], self.t, i == self.n_micro - 1, tl)
+            losses.append(loss)
+            n_loads += n
+        self.stats = {"step_s": time.perf_counter() - t0, "weight_loads": n_loads, "losses": losses}
+        if tl is not None:
+            self._tl = tl
+        return float(np.mean(np.asarray(losses, dtype=np.float64)))
+
+    def _pass(self, tokens, t, final, tl):
+        """Forward, head and backward of one micro-batch; its gradients go to
+        Adam (``final``) or to the host accumulator.  Returns (loss, loads)."""
         h = self.cfg.hidden
         cs, hs, ds = self.s_comp, self.s_h2d, self.s_d2h
         sc, sh, sd = (ctypes.c_void_p(s.cuda_stream) for s in (cs, hs, ds))
-        t0 = time.perf_counter()
-
-        tl = self._timeline_begin(cs) if self.record_timeline else None
 
         # embedding gather + tokens (host) -> device, after the embedding's
-        # update of the previous step (which also still reads the token buffer)
+        # update of the previous step (which also still reads the token
+        # buffer), or its accumulation of the previous micro-batch
         self._wait_unit(MT_UNIT_EMBED)
+        self._wait_acc(MT_UNIT_EMBED)
         tok_host = self.tok_pin.view(np.int32)
         tok_host[:] = tokens.reshape(-1)
         call("mt_embed_gather", self.store.ptr, self.tok_pin.ptr, self.T, self.x0_pin.ptr)
@@ -431,7 +460,10 @@ class Trainer:
 
         def adam_layer(ev, unit, slab):
             ev.synchronize()
-            call("mt_step", self.store.ptr, unit, slab.ptr, ctypes.byref(self.madam), t, self._w32_ptr(unit))
+            if final:
+                call("mt_step", self.store.ptr, unit, slab.ptr, ctypes.byref(self.madam), t, self._w32_ptr(unit))
+            else:
+                call("mt_grad_accumulate", self.store.ptr, unit, slab.ptr)
 
         def adam_layer_slab(ev, unit, k):
             try:
@@ -442,8 +474,13 @@ class Trainer:
         def adam_embed(ev):
             ev.synchronize()
             call("mt_embed_grad", self.store.ptr, self.tok_pin.ptr, self.T, self.dx0_pin.ptr)
-            call("mt_step", self.store.ptr, MT_UNIT_EMBED, None, ctypes.byref(self.madam), t,
-                 self._w32_ptr(MT_UNIT_EMBED))
+            if final:
+                call("mt_step", self.store.ptr, MT_UNIT_EMBED, None, ctypes.byref(self.madam), t,
+                     self._w32_ptr(MT_UNIT_EMBED))
+            else:
+                call("mt_grad_accumulate", self.store.ptr, MT_UNIT_EMBED, None)
+
+        jobs = self.pending if final else self.accum_jobs
 
         issue_ready_loads(-1)
         for i, (kind, l, si) in enumerate(self.ops):
@@ -497,6 +534,7 @@ class Trainer:
                     tl["ops"][-1][2] = ev
             if kind == "head":
                 self._wait_unit(MT_UNIT_HEAD)  # the previous update still reads the head's slab
+                self._wait_acc(MT_UNIT_HEAD)   # (or the previous micro-batch's accumulation)
                 d2h = torch.cuda.Event(enable_timing=self.record_timeline)
                 with torch.cuda.stream(ds):
                     ds.wait_event(ev)
@@ -505,8 +543,8 @@ class Trainer:
                     call("mt_copy_d2h", self.head_gslab.ptr, _ptr(self.head_g), self.lay_head.w_bytes, sd)
                     d2h.record(ds)
                 self.head_d2h = d2h
-                self.pending[MT_UNIT_HEAD] = self.optimizer.submit(self._urgency(MT_UNIT_HEAD), d2h, adam_layer, d2h,
-                                                                   MT_UNIT_HEAD, self.head_gslab)
+                jobs[MT_UNIT_HEAD] = self.optimizer.submit(self._urgency(MT_UNIT_HEAD), d2h, adam_layer, d2h,
+                                                           MT_UNIT_HEAD, self.head_gslab)
             elif kind == "bwd":
                 g = n_bwd % 2
                 n_bwd += 1
@@ -526,20 +564,15 @@ class Trainer:
                         call("mt_copy_d2h", self.dx0_pin.ptr, _ptr(self.dgrad[cur]), self.T * h * 4, sd)
                         d2h_x.record(ds)
                 gslot_d2h[g] = d2h
-                self.pending[l] = self.optimizer.submit(self._urgency(l), d2h, adam_layer_slab, d2h, l, k)
+                jobs[l] = self.optimizer.submit(self._urgency(l), d2h, adam_layer_slab, d2h, l, k)
                 if l == 0:
-                    self.pending[MT_UNIT_EMBED] = self.optimizer.submit(self._urgency(MT_UNIT_EMBED), d2h_x,
-                                                                        adam_embed, d2h_x)
+                    jobs[MT_UNIT_EMBED] = self.optimizer.submit(self._urgency(MT_UNIT_EMBED), d2h_x, adam_embed, d2h_x)
             issue_ready_loads(i)
 
         for f in list(pack_fut.values()):
             f.result()
         cs.synchronize()
-        loss = float(self.loss_dev.item())
-        self.stats = {"step_s": time.perf_counter() - t0, "weight_loads": len(loads)}
-        if tl is not None:
-            self._tl = tl
-        return loss
+        return float(self.loss_dev.item()), len(loads)
 
     def _urgency(self, unit):
         """Order in which the next step needs a unit's updated weights."""

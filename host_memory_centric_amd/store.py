@@ -8,9 +8,10 @@ import ctypes
 
 import numpy as np
 
-from ._lib import MT_UNIT_EMBED, MT_UNIT_HEAD, call, load, model_cfg, unit_layout
+from ._lib import (MT_STORE_GRAD_ACCUM, MT_STORE_MASTER_FP32, MT_UNIT_EMBED, MT_UNIT_HEAD, call, load, model_cfg,
+                   unit_layout)
 
-REGION_W, REGION_G, REGION_M, REGION_V = 0, 1, 2, 3
+REGION_W, REGION_G, REGION_M, REGION_V, REGION_P, REGION_A = 0, 1, 2, 3, 4, 5
 LAYER_TENSORS = ("g_attn", "wqkv", "wo", "g_mlp", "wgu", "wd")
 
 
@@ -25,15 +26,19 @@ def tensor_shapes(cfg, unit):
 
 
 class HostStore:
-    def __init__(self, cfg):
+    """master: keep fp32 master weights (region P); accum: keep an fp32
+    gradient accumulator for micro-batches (region A)."""
+
+    def __init__(self, cfg, master=False, accum=False):
         load()
         self.cfg = cfg
         self.mcfg = model_cfg(cfg)
+        self.flags = (MT_STORE_MASTER_FP32 if master else 0) | (MT_STORE_GRAD_ACCUM if accum else 0)
         p = ctypes.c_void_p()
-        call("mt_store_create", ctypes.byref(self.mcfg), ctypes.byref(p))
+        call("mt_store_create_ex", ctypes.byref(self.mcfg), self.flags, ctypes.byref(p))
         self.ptr = p
         self.units = [MT_UNIT_HEAD, MT_UNIT_EMBED] + list(range(cfg.layers))
-        self.layout = {u: unit_layout(self.mcfg, u) for u in (MT_UNIT_HEAD, MT_UNIT_EMBED, 0)}
+        self.layout = {u: unit_layout(self.mcfg, u, self.flags) for u in (MT_UNIT_HEAD, MT_UNIT_EMBED, 0)}
 
     def layout_of(self, unit):
         return self.layout[unit if unit < 0 else 0]
@@ -60,8 +65,10 @@ class HostStore:
         return p.value
 
     def region(self, unit, r):
-        """numpy view of a region over the W indexing (uint16 for W/G, float32 for M/V)."""
+        """numpy view of a region over the W indexing (uint16 for W/G, float32 for M/V/P/A)."""
         L = self.layout_of(unit)
+        if L.region_bytes[r] == 0:
+            raise ValueError(f"the store has no region {r}")
         n = L.w_bytes // 2
         dt = np.uint16 if r in (REGION_W, REGION_G) else np.float32
         addr = self.block_addr(unit) + L.region_off[r]
@@ -81,9 +88,10 @@ class HostStore:
         call("mt_store_fill_normal", self.ptr, self.cfg.seed if seed is None else seed, std)
 
     def load_bits(self, bits):
-        """Copy weights given as bf16 bit arrays (the synth layout) into the W regions; zero G, M, V."""
+        """Copy weights given as bf16 bit arrays (the synth layout) into the W regions; zero G, M, V
+        (and A); the master weights P, if any, become the exact fp32 values of W."""
         for u in self.units:
-            for r in (REGION_G, REGION_M, REGION_V):
+            for r in (REGION_G, REGION_M, REGION_V) + ((REGION_A,) if self.flags & MT_STORE_GRAD_ACCUM else ()):
                 self.region(u, r)[:] = 0
         self.tensor(MT_UNIT_EMBED, "embed")[:] = bits["embed"]
         self.tensor(MT_UNIT_HEAD, "g_final")[:] = bits["g_final"]
@@ -91,6 +99,8 @@ class HostStore:
         for l, lw in enumerate(bits["layers"]):
             for name in LAYER_TENSORS:
                 self.tensor(l, name)[:] = lw[name]
+        if self.flags & MT_STORE_MASTER_FP32:
+            call("mt_store_sync_master", self.ptr)
 
     def read_bits(self):
         """Copy of all weights as bf16 bit arrays (the synth layout)."""

@@ -65,22 +65,37 @@ typedef struct mt_model_cfg {
  * regions M and V, each starting on a 4 KB boundary.  Tensors sit in W (and
  * at the same offsets in G and in the device staging slot) at 256-byte
  * aligned offsets; M and V use the same element indexing as W (4 bytes per
- * element).  Padding elements are zero and stay zero under Adam. */
+ * element).  Padding elements are zero and stay zero under Adam.
+ * Two optional fp32 regions follow, with the same indexing, when the store
+ * is created with the matching flag (0 bytes otherwise): P, a master copy of
+ * the weights (MT_STORE_MASTER_FP32), and A, the gradient accumulator of
+ * micro-batches (MT_STORE_GRAD_ACCUM). */
 typedef struct mt_unit_layout {
     int32_t n_tensors;        /* 6 per layer; 1 for the embedding; 2 for the head */
     int32_t pad_;
     uint64_t tensor_off[6];   /* byte offset of tensor j inside W */
     uint64_t tensor_numel[6]; /* element count of tensor j */
     uint64_t w_bytes;         /* bytes of W incl. inter-tensor padding (== G's) */
-    uint64_t region_off[4];   /* W, G, M, V byte offsets inside the block */
-    uint64_t region_bytes[4]; /* their 4 KB-padded sizes */
+    uint64_t region_off[6];   /* W, G, M, V, P, A byte offsets inside the block */
+    uint64_t region_bytes[6]; /* their 4 KB-padded sizes (P, A: 0 unless enabled) */
     uint64_t block_bytes;     /* total block size */
     uint64_t params;          /* real parameter count of the unit */
 } mt_unit_layout;
 
-/* Pure function: the layout of `unit`.  MT_E_SHAPE if hidden != heads *
- * head_dim, or a dimension is not a positive multiple of 8. */
+/* Optional store regions (flags of mt_store_create_ex / mt_unit_layout_get_ex). */
+/* (paper page, section 2: persistent state needs at least 12 bytes per
+ * parameter -- bf16 weights and gradients, fp32 moments; the master copy
+ * makes it 16 and keeps updates smaller than half a bf16 ulp of a weight.) */
+enum {
+    MT_STORE_MASTER_FP32 = 1, /* fp32 master weights P: Adam updates P, W = bf16(P) */
+    MT_STORE_GRAD_ACCUM = 2   /* fp32 accumulator A for gradient accumulation over micro-batches */
+};
+
+/* Pure function: the layout of `unit` in a store with the given flags
+ * (mt_unit_layout_get: flags 0).  MT_E_SHAPE if hidden != heads * head_dim,
+ * or a dimension is not a positive multiple of 8; MT_E_ARG for unknown flags. */
 int mt_unit_layout_get(const mt_model_cfg* cfg, int unit, mt_unit_layout* out);
+int mt_unit_layout_get_ex(const mt_model_cfg* cfg, uint32_t flags, int unit, mt_unit_layout* out);
 
 /* ------------------------------------------------------------------------ */
 /* Host store (the authoritative copy of all training state).               */
@@ -89,8 +104,10 @@ typedef struct mt_store mt_store;
 
 /* Allocates one page-aligned, zero-filled block per unit (pageable memory;
  * 2 MB huge pages are requested).  Owned by the library; free with
- * mt_store_destroy. */
+ * mt_store_destroy.  mt_store_create_ex adds the optional regions of `flags`
+ * (MT_STORE_*; mt_store_create: none). */
 int mt_store_create(const mt_model_cfg* cfg, mt_store** out);
+int mt_store_create_ex(const mt_model_cfg* cfg, uint32_t flags, mt_store** out);
 void mt_store_destroy(mt_store* st);
 /* Base address of a unit's block (layout as mt_unit_layout_get). */
 int mt_store_block(mt_store* st, int unit, void** block);
@@ -101,6 +118,10 @@ int mt_store_bytes(const mt_store* st, uint64_t* out);
  * embedding 1, final gain 2, LM head 3, layer l tensor j 16 + 8 l + j.
  * Multithreaded.  Zeroes G, M and V. */
 int mt_store_fill_normal(mt_store* st, uint32_t seed, double std);
+/* Master-weight stores: P = fp32(W) for every unit (exact), e.g. after the
+ * caller wrote W through mt_store_block (mt_store_fill_normal does this
+ * itself).  MT_E_STATE without MT_STORE_MASTER_FP32. */
+int mt_store_sync_master(mt_store* st);
 
 /* Number of host worker threads used by pack, Adam, fill and embedding
  * (default: the process's CPU affinity count). */
@@ -151,10 +172,28 @@ typedef struct mt_adam_cfg {
  * the corrections folded into two scalars (one division, one square root
  * per element).  Scalar constants are computed in fp64 and rounded once to
  * fp32.  t >= 1.
+ * Master-weight stores read w from P instead of W and write P = w' (W is
+ * still bf16(w')).  When k >= 1 micro-batch gradients were accumulated
+ * (mt_grad_accumulate) since the unit's last step, the gradient landed is
+ * the mean over the k + 1 micro-batches: G = bf16((A + bf16 src) / (k + 1))
+ * (one fp32 addition, one fp32 division; src = grad_src, or G itself when
+ * grad_src is NULL), and the unit's count restarts at 0.
  * If w_fp32_out is non-NULL it receives w' (w_bytes/2 floats, W indexing)
  * before rounding.  Multithreaded, deterministic. */
 int mt_step(mt_store* st, int unit, const void* grad_src, const mt_adam_cfg* adam, int64_t t,
             float* w_fp32_out);
+
+/* Gradient accumulation over micro-batches (paper page, section 3,
+ * execution workflow: accumulated gradients live in host memory; appendix
+ * A.3: a background CPU thread accumulates the offloaded gradients; the
+ * author blog: larger batches amortise the per-step weight traffic):
+ * adds one micro-batch's bf16 gradient (grad_src in W-region layout, or the
+ * unit's G region when NULL) into the fp32 accumulator A, in call order:
+ * A = bf16 src for the first micro-batch after a step, A = A + bf16 src
+ * after that.  The unit's mt_step after the last micro-batch takes the mean.
+ * MT_E_STATE without MT_STORE_GRAD_ACCUM.  Must not overlap mt_step or
+ * mt_pack_layer on the same unit. */
+int mt_grad_accumulate(mt_store* st, int unit, const void* grad_src);
 
 /* Embedding on the host: dst[t, :] = E[tok[t], :] (bf16, [T, h]). */
 int mt_embed_gather(mt_store* st, const int32_t* tok, int64_t T, void* dst);

@@ -11,5 +11,5 @@ Parity status: every function here is pinned by ``tests/test_oracle_pins.py``
 """
 from .model import (bf16_round, to_float, rmsnorm_fwd, rmsnorm_bwd, rope_tables, rope_fwd, rope_bwd,
                     attention_fwd, attention_bwd, attention_suffix, silu, swiglu_fwd, swiglu_bwd, layer_fwd, layer_bwd,
-                    head_fwd_bwd, adam_update, adam_consts, embed_fwd, embed_bwd, forward_backward,
+                    head_fwd_bwd, adam_update, adam_consts, accumulate_micro, accumulated_mean, embed_fwd, embed_bwd, forward_backward,
                     HostState, train_step, labels_of)

@@ -310,7 +310,7 @@ def adam_consts(adam, t):
                 decay=f(1.0 - adam.lr * adam.weight_decay))
 
 
-def adam_update(w_bits, g_fp32, m, v, adam, t):
+def adam_update(w_bits, g_fp32, m, v, adam, t, master=None):
     """One Adam step on one tensor, all in fp32, one IEEE rounding per operation.
 
     w_bits: bf16 weights (uint16); g_fp32: gradient as computed; m, v: fp32
@@ -318,9 +318,11 @@ def adam_update(w_bits, g_fp32, m, v, adam, t):
     method keeps bf16 gradients on the host.  Operation order:
     m = b1*m + (1-b1)*g;  v = b2*v + (1-b2)*(g*g);
     w' = w - (alpha*m) / (sqrt(v) + eps_hat)   (constants of adam_consts).
+    With ``master`` (fp32 master weights, updated in place) w is read from
+    the master copy instead of the bf16 weights and receives w'.
     Returns (new bf16 bits, the fp32 weight before its bf16 rounding)."""
     k = adam_consts(adam, t)
-    w = bf16_bits_to_f32(w_bits)
+    w = bf16_bits_to_f32(w_bits) if master is None else master.astype(np.float32)
     if adam.weight_decay != 0.0:
         w = w * k["decay"]
     gh = bf16_round(g_fp32)
@@ -329,7 +331,27 @@ def adam_update(w_bits, g_fp32, m, v, adam, t):
     denom = np.sqrt(v) + k["eps_hat"]
     step = k["alpha"] * m
     w_new = (w - step / denom).astype(np.float32)
+    if master is not None:
+        master[...] = w_new
     return f32_to_bf16_bits(w_new), w_new
+
+
+def accumulate_micro(acc, g_fp32, first):
+    """Gradient accumulation over micro-batches (paper page, section 3,
+    execution workflow: accumulated gradients live in host memory; appendix
+    A.3: a CPU thread accumulates the offloaded gradients).  Each
+    micro-batch's gradient is stored as bf16, as the device produces it, and
+    added in fp32 in micro-batch order.  Returns the new accumulator."""
+    gh = bf16_round(np.asarray(g_fp32, dtype=np.float32))
+    return gh.copy() if first else (acc + gh).astype(np.float32)
+
+
+def accumulated_mean(acc, g_last_fp32, n):
+    """The gradient Adam receives after n micro-batches: the mean
+    (acc + bf16 g_last) / n, one fp32 addition and one fp32 division (acc
+    holds the first n - 1)."""
+    gh = bf16_round(np.asarray(g_last_fp32, dtype=np.float32))
+    return ((acc + gh).astype(np.float32) / np.float32(n)).astype(np.float32)
 
 
 # ----------------------------------------------------------------------------
@@ -393,9 +415,10 @@ def forward_backward(Wf, tok, cfg, mode="resident", ckpt_every=None, on_layer_gr
 
 
 class HostState:
-    """Host-resident training state of the oracle: bf16 weights + fp32 moments."""
+    """Host-resident training state of the oracle: bf16 weights + fp32 moments
+    (+ fp32 master weights with ``master``)."""
 
-    def __init__(self, bits):
+    def __init__(self, bits, master=False):
         self.bits = {"embed": bits["embed"].copy(), "g_final": bits["g_final"].copy(),
                      "head": bits["head"].copy(),
                      "layers": [{k: v.copy() for k, v in lw.items()} for lw in bits["layers"]]}
@@ -404,35 +427,82 @@ class HostState:
         self.v = {k: z(self.bits[k]) for k in ("embed", "g_final", "head")}
         self.m["layers"] = [{k: z(a) for k, a in lw.items()} for lw in self.bits["layers"]]
         self.v["layers"] = [{k: z(a) for k, a in lw.items()} for lw in self.bits["layers"]]
+        self.master = None
+        if master:
+            f = bf16_bits_to_f32
+            self.master = {k: f(self.bits[k]).astype(np.float32) for k in ("embed", "g_final", "head")}
+            self.master["layers"] = [{k: f(a).astype(np.float32) for k, a in lw.items()}
+                                     for lw in self.bits["layers"]]
         self.t = 0
 
 
 def train_step(state, tok, cfg, adam, mode="resident", dt=np.float32, ckpt_every=None):
     """One training step on ``state`` (updated in place).
 
-    Returns dict(loss, grads (float, as computed), w_fp32 (pre-rounding fp32
-    weights after Adam, same tree as the weights))."""
+    ``tok``: int tokens [B, S], or a list of n such micro-batches whose
+    gradients are accumulated (``accumulate_micro``) before one Adam step on
+    their mean (``accumulated_mean``); one micro-batch is the plain step.
+    Returns dict(loss (mean over micro-batches), losses, grads (float, as
+    computed; with several micro-batches their accumulated fp32 mean),
+    w_fp32 (pre-rounding fp32 weights after Adam, same tree as the
+    weights))."""
+    micro = list(tok) if isinstance(tok, (list, tuple)) else [tok]
+    n = len(micro)
     state.t += 1
     t = state.t
     Wf = to_float(state.bits, dt)
     w_fp32 = {"layers": [dict() for _ in range(cfg.layers)]}
+    master = state.master
+
+    def upd(bits_parent, key, g, m, v, ms):
+        nb, wf = adam_update(bits_parent[key], g, m, v, adam, t, master=ms)
+        bits_parent[key] = nb
+        return wf
 
     def upd_layer(l, dW):
         for name in layer_tensor_shapes(cfg):
-            nb, wf = adam_update(state.bits["layers"][l][name], dW[name].astype(np.float32),
-                                 state.m["layers"][l][name], state.v["layers"][l][name], adam, t)
-            state.bits["layers"][l][name] = nb
-            w_fp32["layers"][l][name] = wf
+            ms = master["layers"][l][name] if master is not None else None
+            w_fp32["layers"][l][name] = upd(state.bits["layers"][l], name, dW[name].astype(np.float32),
+                                            state.m["layers"][l][name], state.v["layers"][l][name], ms)
 
-    loss, per_pos, grads, _ = forward_backward(
-        Wf, tok, cfg, mode=mode, ckpt_every=ckpt_every,
-        on_layer_grad=upd_layer if mode == "streamed" else None)
-    if mode == "resident":
-        for l in range(cfg.layers):
-            upd_layer(l, grads["layers"][l])
-    for name in ("head", "g_final", "embed"):
-        nb, wf = adam_update(state.bits[name], grads[name].astype(np.float32),
-                             state.m[name], state.v[name], adam, t)
-        state.bits[name] = nb
-        w_fp32[name] = wf
-    return dict(loss=loss, per_pos=per_pos, grads=grads, w_fp32=w_fp32)
+    acc = None
+    losses = []
+    for i, tk in enumerate(micro):
+        last = i == n - 1
+        if not last:
+            loss, per_pos, grads, _ = forward_backward(Wf, tk, cfg, mode=mode, ckpt_every=ckpt_every)
+            first = acc is None
+            if first:
+                acc = {"layers": [dict() for _ in range(cfg.layers)]}
+            for l in range(cfg.layers):
+                for name in layer_tensor_shapes(cfg):
+                    acc["layers"][l][name] = accumulate_micro(acc["layers"][l].get(name), grads["layers"][l][name],
+                                                              first)
+            for name in ("head", "g_final", "embed"):
+                acc[name] = accumulate_micro(acc.get(name), grads[name], first)
+            losses.append(loss)
+            continue
+
+        def mean_of(g, a):
+            return g.astype(np.float32) if a is None else accumulated_mean(a, g, n)
+
+        gmean = {"layers": [None] * cfg.layers}
+
+        def hook(l, dW):
+            gmean["layers"][l] = {name: mean_of(dW[name], acc["layers"][l][name] if acc else None) for name in dW}
+            upd_layer(l, gmean["layers"][l])
+
+        loss, per_pos, grads, _ = forward_backward(Wf, tk, cfg, mode=mode, ckpt_every=ckpt_every,
+                                                   on_layer_grad=hook if mode == "streamed" else None)
+        losses.append(loss)
+        if mode == "resident":
+            for l in range(cfg.layers):
+                hook(l, grads["layers"][l])
+        for name in ("head", "g_final", "embed"):
+            ms = master[name] if master is not None else None
+            gmean[name] = mean_of(grads[name], acc[name] if acc else None)
+            w_fp32[name] = upd(state.bits, name, gmean[name], state.m[name], state.v[name], ms)
+    # grads: as computed for one micro-batch; with several, the fp32 mean
+    # that Adam receives (before its bf16 storage rounding)
+    return dict(loss=float(np.mean(np.asarray(losses, dtype=np.float64))), losses=losses, per_pos=per_pos,
+                grads=grads if n == 1 else gmean, w_fp32=w_fp32)

@@ -92,3 +92,9 @@ def sync_from_oracle(trainer, state, cfg):
             st.tensor(unit, name, REGION_W)[...] = src[0]
             st.tensor(unit, name, REGION_M)[...] = src[1]
             st.tensor(unit, name, REGION_V)[...] = src[2]
+            if state.master is not None:
+                from host_memory_centric_amd.store import REGION_P
+                ms = state.master
+                p = (ms["embed"] if unit == MT_UNIT_EMBED else ms[name] if unit == MT_UNIT_HEAD
+                     else ms["layers"][unit][name])
+                st.tensor(unit, name, REGION_P)[...] = p

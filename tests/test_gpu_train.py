@@ -20,8 +20,8 @@ def _trainer(cfg, bits, **kw):
 
 def _store_regions(tr):
     tr.finish()
-    return {(u, r): tr.store.region(u, r).copy() for u in tr.store.units
-            for r in (REGION_W, REGION_G, REGION_M, REGION_V)}
+    regions = (REGION_W, REGION_G, REGION_M, REGION_V) + ((4,) if tr.store.flags & 1 else ())
+    return {(u, r): tr.store.region(u, r).copy() for u in tr.store.units for r in regions}
 
 
 @pytest.mark.parametrize("mode", ["streamed", "resident"])
@@ -77,3 +77,61 @@ def test_run_twice_deterministic(gpu):
         finally:
             tr.close()
     assert out[0][0] == out[1][0] and np.array_equal(out[0][1], out[1][1])
+
+
+@pytest.mark.parametrize("mode", ["streamed", "resident"])
+def test_micro_batches_with_master_match_oracle(gpu, mode):
+    """Two micro-batches per step, gradients accumulated on the host, one
+    Adam step on their mean over fp32 master weights, against the oracle."""
+    cfg = synth.preset("tiny")
+    bits = synth.make_weights(cfg)
+    adam = synth.AdamCfg()
+    st = oracle.HostState(bits, master=True)
+    tr = _trainer(cfg, bits, mode=mode, micro_batches=2, master=True)
+    try:
+        for step in range(2):
+            mb = [synth.make_tokens(cfg, 2 * step), synth.make_tokens(cfg, 2 * step + 1)]
+            loss = tr.step(np.concatenate(mb, axis=0))
+            res = oracle.train_step(st, mb, cfg, adam)
+            check_step(tr, loss, res, cfg)
+            for got, ref in zip(tr.stats["losses"], res["losses"]):
+                assert abs(got - float(ref)) <= 1e-3 * abs(float(ref))
+            sync_from_oracle(tr, st, cfg)
+    finally:
+        tr.close()
+
+
+def test_micro_batches_streamed_equals_resident_and_repeats_equal_one(gpu):
+    """With micro-batches and master weights the schedule still changes no
+    bit (resident, K = 1 and K = 2, one slot); two identical micro-batches
+    give exactly the one-micro-batch step (the mean of two equal bf16
+    gradients is exact)."""
+    cfg = synth.preset("tiny")
+    bits = synth.make_weights(cfg)
+    runs = {}
+    for name, kw in {"resident": dict(mode="resident"), "k1_2slot": dict(ckpt_every=1, n_slots=2),
+                     "k2_1slot": dict(ckpt_every=2, n_slots=1)}.items():
+        tr = _trainer(cfg, bits, micro_batches=2, master=True, **kw)
+        try:
+            losses = [tr.step(np.concatenate([synth.make_tokens(cfg, 2 * s), synth.make_tokens(cfg, 2 * s + 1)]))
+                      for s in range(2)]
+            runs[name] = (losses, _store_regions(tr))
+        finally:
+            tr.close()
+    ref_losses, ref_regions = runs["resident"]
+    for name, (losses, regions) in runs.items():
+        assert losses == ref_losses, name
+        for key, a in ref_regions.items():
+            assert np.array_equal(regions[key], a), (name, key)
+    out = []
+    for n in (1, 2):
+        tr = _trainer(cfg, bits, micro_batches=n)
+        try:
+            for s in range(2):
+                tk = synth.make_tokens(cfg, s)
+                tr.step(np.concatenate([tk] * n))
+            out.append(_store_regions(tr))
+        finally:
+            tr.close()
+    for key, a in out[0].items():
+        assert np.array_equal(out[1][key], a), key

@@ -20,7 +20,8 @@ import synth
 from host_memory_centric_amd import _lib
 from host_memory_centric_amd._lib import MT_UNIT_EMBED, MT_UNIT_HEAD, MtError, call
 from host_memory_centric_amd.engine import plan_slots, plan_step
-from host_memory_centric_amd.store import REGION_G, REGION_M, REGION_V, REGION_W, HostStore, tensor_shapes
+from host_memory_centric_amd.store import (REGION_G, REGION_M, REGION_P, REGION_V, REGION_W, HostStore,
+                                          tensor_shapes)
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
@@ -193,6 +194,97 @@ def test_host_adam_bitwise_equals_oracle(lib, wd):
         st.close()
 
 
+@pytest.mark.parametrize("master,n_micro", [(False, 2), (True, 1), (True, 3)])
+def test_host_accumulate_and_master_bitwise_equal_oracle(lib, master, n_micro):
+    """mt_grad_accumulate + mt_step on a store with fp32 master weights and
+    a gradient accumulator against the oracle's accumulate_micro /
+    accumulated_mean / adam_update(master=...), over three steps."""
+    cfg = synth.preset("tiny")
+    adam = synth.AdamCfg()
+    st = HostStore(cfg, master=master, accum=n_micro > 1)
+    try:
+        bits = synth.make_weights(cfg)
+        st.load_bits(bits)
+        rng = np.random.default_rng(3)
+        L = st.layout_of(0)
+        n = L.w_bytes // 2
+        shapes = tensor_shapes(cfg, 1)
+        ref = {k: dict(w=a.copy(), m=np.zeros(a.shape, np.float32), v=np.zeros(a.shape, np.float32),
+                       p=synth.bf16_bits_to_f32(a).astype(np.float32) if master else None)
+               for k, a in bits["layers"][1].items()}
+
+        def slab_of(g32):
+            slab = np.zeros(n, dtype=np.uint16)
+            for j, (name, shp) in enumerate(shapes):
+                off = L.tensor_off[j] // 2
+                slab[off:off + int(np.prod(shp))] = synth.f32_to_bf16_bits(g32[name]).reshape(-1)
+            return slab
+
+        for t in (1, 2, 3):
+            gs = [{k: (rng.standard_normal(a.shape) * 10 ** rng.uniform(-7, -2)).astype(np.float32)
+                   for k, a in bits["layers"][1].items()} for _ in range(n_micro)]
+            for i in range(n_micro - 1):
+                slab = slab_of(gs[i])
+                call("mt_grad_accumulate", st.ptr, 1, slab.ctypes.data_as(ctypes.c_void_p))
+            slab = slab_of(gs[-1])
+            wout = np.zeros(n, dtype=np.float32)
+            call("mt_step", st.ptr, 1, slab.ctypes.data_as(ctypes.c_void_p), ctypes.byref(_lib.adam_cfg(adam)), t,
+                 wout.ctypes.data_as(ctypes.c_void_p))
+            for j, (name, shp) in enumerate(shapes):
+                off = L.tensor_off[j] // 2
+                cnt = int(np.prod(shp))
+                r = ref[name]
+                if n_micro > 1:
+                    acc = None
+                    for i in range(n_micro - 1):
+                        acc = oracle.accumulate_micro(acc, gs[i][name], i == 0)
+                    g = oracle.accumulated_mean(acc, gs[-1][name], n_micro)
+                else:
+                    g = gs[-1][name]
+                nb, wf = oracle.adam_update(r["w"], g, r["m"], r["v"], adam, t, master=r["p"])
+                r["w"] = nb
+                assert np.array_equal(wout[off:off + cnt].view(np.uint32), wf.reshape(-1).view(np.uint32)), name
+                assert np.array_equal(st.tensor(1, name), nb), name
+                assert np.array_equal(st.tensor(1, name, REGION_M), r["m"]), name
+                assert np.array_equal(st.tensor(1, name, REGION_G), synth.f32_to_bf16_bits(g)), name
+                if master:
+                    assert np.array_equal(st.tensor(1, name, REGION_P).view(np.uint32), r["p"].view(np.uint32)), name
+    finally:
+        st.close()
+
+
+def test_store_regions_and_flags(lib):
+    cfg = synth.preset("tiny")
+    mcfg = _lib.model_cfg(cfg)
+    plain = _lib.unit_layout(mcfg, 0)
+    both = _lib.unit_layout(mcfg, 0, _lib.MT_STORE_MASTER_FP32 | _lib.MT_STORE_GRAD_ACCUM)
+    assert plain.region_bytes[4] == 0 and plain.region_bytes[5] == 0
+    for r in range(4):
+        assert both.region_off[r] == plain.region_off[r] and both.region_bytes[r] == plain.region_bytes[r]
+    assert both.region_bytes[4] == both.region_bytes[5] == plain.region_bytes[2]
+    assert both.region_off[4] == plain.block_bytes and both.region_off[5] % 4096 == 0
+    assert both.block_bytes == plain.block_bytes + 2 * plain.region_bytes[2]
+    with pytest.raises(MtError):
+        _lib.unit_layout(mcfg, 0, 4)
+    st = HostStore(cfg)
+    try:  # no accumulator, no master copy
+        g = np.zeros(st.layout_of(0).w_bytes // 2, np.uint16)
+        with pytest.raises(MtError) as e:
+            call("mt_grad_accumulate", st.ptr, 0, g.ctypes.data_as(ctypes.c_void_p))
+        assert e.value.code == -6
+        with pytest.raises(MtError):
+            call("mt_store_sync_master", st.ptr)
+    finally:
+        st.close()
+    st = HostStore(cfg, master=True)
+    try:  # the seeded fill leaves P = fp32(W)
+        st.fill_normal()
+        for u in (MT_UNIT_EMBED, MT_UNIT_HEAD, 0):
+            assert np.array_equal(st.region(u, REGION_P), synth.bf16_bits_to_f32(st.region(u, REGION_W)))
+    finally:
+        st.close()
+
+
 def test_host_adam_scalar_path_equals_simd(lib, monkeypatch):
     """The AVX-512 and scalar paths give identical bits (checked in a subprocess)."""
     import subprocess
@@ -208,7 +300,15 @@ g = synth.f32_to_bf16_bits((np.random.default_rng(1).standard_normal(n) * 1e-3).
 out = np.zeros(n, np.float32)
 _lib.call("mt_step", st.ptr, 0, g.ctypes.data_as(ctypes.c_void_p), ctypes.byref(_lib.adam_cfg(synth.AdamCfg())), 1,
           out.ctypes.data_as(ctypes.c_void_p))
+# the extended path: master weights and three accumulated micro-batches
+st2 = HostStore(cfg, master=True, accum=True); st2.fill_normal()
+rng = np.random.default_rng(2)
+for i in range(3):
+    gi = synth.f32_to_bf16_bits((rng.standard_normal(n) * 1e-3).astype(np.float32))
+    _lib.call("mt_grad_accumulate" if i < 2 else "mt_step", st2.ptr, 0, gi.ctypes.data_as(ctypes.c_void_p),
+              *((ctypes.byref(_lib.adam_cfg(synth.AdamCfg())), 1, None) if i == 2 else ()))
 import sys; sys.stdout.write(out.view(np.uint32).tobytes().hex()[:200000])
+sys.stdout.write(st2.region(0, 4).view(np.uint32).tobytes().hex()[:200000])
 '''
     env = dict(os.environ, PYTHONPATH=ROOT)
     a = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=env, cwd=ROOT)

@@ -411,6 +411,102 @@ def test_adam_matches_torch_optim_adam():
     np.testing.assert_allclose(wf, p.detach().numpy(), rtol=0, atol=2e-7 * 4)
 
 
+def test_master_adam_tracks_fp64_recurrence_where_bf16_stagnates():
+    """With fp32 master weights the update is the plain Adam recurrence on w
+    (no bf16 rounding of w between steps): five steps at lr 1e-4 on N(0, 0.02)
+    weights follow the fp64 recurrence, while without the master copy most of
+    these weights do not move at all (half a bf16 ulp exceeds the step)."""
+    adam = synth.AdamCfg()
+    rng = np.random.default_rng(11)
+    n = 4096
+    w0 = synth.f32_to_bf16_bits(rng.standard_normal(n).astype(np.float32) * 0.02)
+    master = synth.bf16_bits_to_f32(w0).astype(np.float32)
+    w_bits, w_plain = w0.copy(), w0.copy()
+    m, v, m2, v2 = (np.zeros(n, np.float32) for _ in range(4))
+    m64, v64 = np.zeros(n), np.zeros(n)
+    w64 = synth.bf16_bits_to_f32(w0).astype(np.float64)
+    for t in range(1, 6):
+        g = rng.standard_normal(n).astype(np.float32) * 1e-3
+        w_bits, wf = oracle.adam_update(w_bits, g, m, v, adam, t, master=master)
+        w_plain, _ = oracle.adam_update(w_plain, g, m2, v2, adam, t)
+        gh = oracle.bf16_round(g).astype(np.float64)
+        m64 = adam.beta1 * m64 + (1 - adam.beta1) * gh
+        v64 = adam.beta2 * v64 + (1 - adam.beta2) * gh * gh
+        w64 = w64 - adam.lr * (m64 / (1 - adam.beta1 ** t)) / (np.sqrt(v64 / (1 - adam.beta2 ** t)) + adam.eps)
+        assert np.array_equal(master, wf)
+        assert np.array_equal(w_bits, synth.f32_to_bf16_bits(master))
+        np.testing.assert_allclose(master, w64, rtol=0, atol=2e-6 * np.abs(w64).max())
+    w0f = synth.bf16_bits_to_f32(w0)
+    moved = np.abs(master - w0f) > 0
+    assert moved.mean() > 0.99
+    # without the master copy, weights with |w| >= 2^-5 (half a bf16 ulp
+    # >= 1.2e-4 > lr) stay where they are
+    big = np.abs(w0f) >= 2.0 ** -5
+    assert big.sum() > 100 and (w_plain[big] == w0[big]).mean() > 0.9 and moved[big].all()
+
+
+@pytest.mark.parametrize("n", [2, 3, 4])
+def test_identical_micro_batches_equal_one_batch(n):
+    """n micro-batches with the same tokens: the accumulated mean is exactly
+    the single micro-batch's bf16 gradient (n * g is exact in fp32, its
+    division by n correctly rounded), so the step is bit-identical."""
+    cfg = synth.preset("tiny")
+    bits = synth.make_weights(cfg)
+    adam = synth.AdamCfg()
+    for master in (False, True):
+        a = oracle.HostState(bits, master=master)
+        b = oracle.HostState(bits, master=master)
+        for step in range(2):
+            tk = synth.make_tokens(cfg, step)
+            ra = oracle.train_step(a, [tk] * n, cfg, adam)
+            rb = oracle.train_step(b, tk, cfg, adam)
+            assert ra["loss"] == rb["loss"]
+        for l in range(cfg.layers):
+            for k in a.bits["layers"][l]:
+                assert np.array_equal(a.bits["layers"][l][k], b.bits["layers"][l][k])
+                assert np.array_equal(a.m["layers"][l][k], b.m["layers"][l][k])
+                assert np.array_equal(a.v["layers"][l][k], b.v["layers"][l][k])
+        for k in ("embed", "head", "g_final"):
+            assert np.array_equal(a.bits[k], b.bits[k]) and np.array_equal(a.v[k], b.v[k])
+
+
+def test_micro_batch_mean_is_the_full_batch_gradient():
+    """In fp64 without the bf16 storage roundings, the mean of the
+    micro-batches' gradients is the gradient of the loss over all of their
+    rows as one batch (every micro-batch has the same number of labelled
+    positions), and the mean of their losses is that loss."""
+    import dataclasses
+    cfg = synth.preset("tiny")
+    rng = np.random.default_rng(12)
+    Wf = _rand_weights(cfg, rng)
+    micro = [synth.make_tokens(cfg, s) for s in range(3)]
+    full_cfg = dataclasses.replace(cfg, batch=3 * cfg.batch)
+    loss_f, _, g_full, _ = oracle.forward_backward(Wf, np.concatenate(micro, axis=0), full_cfg)
+    outs = [oracle.forward_backward(Wf, tk, cfg) for tk in micro]
+    assert abs(np.mean([o[0] for o in outs]) - loss_f) <= 1e-13 * abs(loss_f)
+    for name, layer, _ in _flat_items(Wf):
+        mean = sum(_grad_of(o[2], name, layer) for o in outs) / 3
+        ref = _grad_of(g_full, name, layer)
+        assert np.abs(mean - ref).max() <= 1e-12 * np.abs(ref).max(), (name, layer)
+
+
+def test_streamed_equals_resident_with_micro_batches_and_master():
+    cfg = synth.preset("tiny")
+    bits = synth.make_weights(cfg)
+    adam = synth.AdamCfg()
+    a = oracle.HostState(bits, master=True)
+    b = oracle.HostState(bits, master=True)
+    for step in range(2):
+        mb = [synth.make_tokens(cfg, 2 * step), synth.make_tokens(cfg, 2 * step + 1)]
+        ra = oracle.train_step(a, mb, cfg, adam, mode="resident")
+        rb = oracle.train_step(b, mb, cfg, adam, mode="streamed", ckpt_every=1)
+        assert ra["loss"] == rb["loss"]
+    for l in range(cfg.layers):
+        for k in a.bits["layers"][l]:
+            assert np.array_equal(a.master["layers"][l][k], b.master["layers"][l][k])
+            assert np.array_equal(a.m["layers"][l][k], b.m["layers"][l][k])
+
+
 # ----------------------------------------------------------------------------
 # invariants of the method
 # ----------------------------------------------------------------------------
