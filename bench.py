@@ -15,6 +15,8 @@ import os
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
@@ -113,7 +115,7 @@ def overlap_report(tl):
             "gpu_idle_ms": round(span - _total(comp), 2)}
 
 
-def host_probe(tr, reps=3):
+def host_probe(tr, reps=3, master=False):
     """Host DRAM rates of the two host-side passes, measured on layer 0 after
     the timed steps with the GPU idle: the packer (W region -> pinned slab,
     read + non-temporal write, 4 bytes per parameter) and the Adam step
@@ -135,9 +137,10 @@ def host_probe(tr, reps=3):
     for i in range(reps):
         call("mt_step", tr.store.ptr, 0, slab.ptr, ctypes.byref(tr.madam), step_t + i, None)
     adam_s = (time.perf_counter() - t) / reps
+    adam_b = 24 + (6 if master else 0)  # a master copy: fp32 weight read instead of bf16, fp32 write
     return {"threads": len(os.sched_getaffinity(0)), "pack_ms_per_layer": round(1e3 * pack_s, 2),
             "pack_GBps": round(4 * params / pack_s / 1e9, 1), "adam_ms_per_layer": round(1e3 * adam_s, 2),
-            "adam_GBps": round(24 * params / adam_s / 1e9, 1)}
+            "adam_GBps": round(adam_b * params / adam_s / 1e9, 1)}
 
 
 def link_probe(tr, nbytes=1 << 30, reps=3):
@@ -240,6 +243,10 @@ def main():
     ap.add_argument("--slots", type=int, default=2)
     ap.add_argument("--grad-slabs", type=int, default=16)
     ap.add_argument("--ckpt-every", type=int, default=None, help="override the workload's checkpoint interval")
+    ap.add_argument("--micro-batches", type=int, default=1,
+                    help="micro-batches per optimizer step (gradients accumulated on the host)")
+    ap.add_argument("--master", action="store_true", help="keep fp32 master weights in the host store")
+    ap.add_argument("--batch", type=int, default=None, help="override the workload's batch (sequences per pass)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--timeline-out", default=None, help="write the event timeline of one step as JSON")
     args = ap.parse_args()
@@ -255,17 +262,22 @@ def main():
     from host_memory_centric_amd.engine import Trainer
 
     cfg = synth.preset(args.workload)
-    if args.ckpt_every is not None:
+    if args.ckpt_every is not None or args.batch is not None:
         import dataclasses
-        cfg = dataclasses.replace(cfg, ckpt_every=args.ckpt_every)
+        cfg = dataclasses.replace(cfg, ckpt_every=args.ckpt_every or cfg.ckpt_every, batch=args.batch or cfg.batch)
     adam = synth.AdamCfg()
     t_init = time.perf_counter()
-    tr = Trainer(cfg, adam, mode=args.mode, n_slots=args.slots, n_grad_slabs=args.grad_slabs, device="cuda:0")
+    nmb = max(1, args.micro_batches)
+    tr = Trainer(cfg, adam, mode=args.mode, n_slots=args.slots, n_grad_slabs=args.grad_slabs, device="cuda:0",
+                 micro_batches=nmb, master=args.master)
+
+    def tokens(step):
+        return np.concatenate([synth.make_tokens(cfg, step * nmb + i) for i in range(nmb)], axis=0)
     t_init = time.perf_counter() - t_init
     print(f"[bench] init {t_init:.1f} s, weight loads/step {tr.n_weight_loads()}", file=sys.stderr, flush=True)
     step = 0
     for _ in range(args.warmup):
-        loss = tr.step(synth.make_tokens(cfg, step))
+        loss = tr.step(tokens(step))
         step += 1
         print(f"[bench] warmup step {step}: loss {loss:.4f} {tr.stats['step_s']:.3f} s", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
@@ -273,7 +285,7 @@ def main():
     _lib.call("mt_prof_enable", 1)
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        loss = tr.step(synth.make_tokens(cfg, step))
+        loss = tr.step(tokens(step))
         step += 1
         print(f"[bench] step {step}: loss {loss:.4f} {tr.stats['step_s']:.3f} s", file=sys.stderr, flush=True)
     tr.finish()  # the last step's host updates belong to the timed work
@@ -284,7 +296,7 @@ def main():
 
     # one more (untimed) step with an event timeline: copy/compute overlap
     tr.record_timeline = True
-    tr.step(synth.make_tokens(cfg, step))
+    tr.step(tokens(step))
     tr.finish()
     tl = tr.timeline()
     tr.record_timeline = False
@@ -293,17 +305,17 @@ def main():
         with open(args.timeline_out, "w") as fh:
             json.dump(tl, fh)
     link = link_probe(tr)
-    host = host_probe(tr)
+    host = host_probe(tr, master=args.master)
 
-    T = cfg.tokens
+    T = cfg.tokens * nmb  # tokens per optimizer step
     ms_step = 1e3 * dt / args.steps
-    f_exec, f_model = flops_per_step(cfg, tr.ops)
+    f_exec, f_model = (nmb * f for f in flops_per_step(cfg, tr.ops))
     tflops_exec = f_exec / (dt / args.steps) / 1e12
     tflops_model = f_model / (dt / args.steps) / 1e12
     lay, lay_h = tr.lay, tr.lay_head
-    n_loads = tr.n_weight_loads()
-    h2d = (n_loads - 1) * lay.w_bytes + lay_h.w_bytes + T * cfg.hidden * 2 + T * 4
-    d2h = cfg.layers * lay.w_bytes + lay_h.w_bytes + T * cfg.hidden * 4
+    n_loads = tr.n_weight_loads()  # per micro-batch pass
+    h2d = nmb * ((n_loads - 1) * lay.w_bytes + lay_h.w_bytes) + T * cfg.hidden * 2 + T * 4
+    d2h = nmb * (cfg.layers * lay.w_bytes + lay_h.w_bytes) + T * cfg.hidden * 4
     dom = max(prof.items(), key=lambda kv: kv[1][1]) if prof else None
     roof = None
     if dom:
@@ -319,16 +331,19 @@ def main():
         "metric": METRIC, "value": round(T * args.steps / dt, 2), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 2), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": workload_text(cfg, tr.n_slots) if args.mode == "streamed" else
-                   workload_text(cfg, tr.n_slots).replace(f"{tr.n_slots} device staging slots",
-                                                          "all layers resident on the device"), "name": cfg.name, "global_batch": cfg.batch,
-                   "seq_len": cfg.seq, "mode": args.mode, "slots": tr.n_slots, "ckpt_every": tr.K,
+        "config": {"workload": (workload_text(cfg, tr.n_slots) if args.mode == "streamed" else
+                                workload_text(cfg, tr.n_slots).replace(f"{tr.n_slots} device staging slots",
+                                                                       "all layers resident on the device")) +
+                   (f", {nmb} micro-batches per optimizer step" if nmb > 1 else "") +
+                   (", fp32 master weights" if args.master else ""), "name": cfg.name, "global_batch": cfg.batch * nmb,
+                   "seq_len": cfg.seq, "micro_batches": nmb, "master_fp32": bool(args.master),
+                   "mode": args.mode, "slots": tr.n_slots, "ckpt_every": tr.K,
                    "parallelism": "none (1 GPU)"},
         "tflops_exec": round(tflops_exec, 1), "tflops_model": round(tflops_model, 1),
         "pct_peak_exec": round(100 * tflops_exec / PEAK_BF16_TFLOPS, 2),
         "pct_peak_model": round(100 * tflops_model / PEAK_BF16_TFLOPS, 2),
         "h2d_GBps": round(h2d * args.steps / dt / 1e9, 2), "d2h_GBps": round(d2h * args.steps / dt / 1e9, 2),
-        "weight_loads_per_step": n_loads, "dev_peak_bytes": int(torch.cuda.max_memory_allocated()),
+        "weight_loads_per_step": n_loads * nmb, "dev_peak_bytes": int(torch.cuda.max_memory_allocated()),
         "host_store_bytes": int(tr.store.total_bytes()), "loss": round(loss, 5), "kernels": kernels,
         "roofline": roof,
         "overlap": overlap,
@@ -341,7 +356,12 @@ def main():
     # engines read the H2D bytes from and write the D2H bytes to host memory;
     # the floor divides them by the faster of the two measured host rates
     n_params = sum(tr.store.layout_of(u).w_bytes // 2 for u in tr.store.units)
-    host_bytes = 4 * (lay.w_bytes // 2) * (n_loads - 1) + 4 * (lay_h.w_bytes // 2) + 24 * n_params + h2d + d2h
+    # (micro-batches: each accumulation reads the slab and the accumulator and
+    # writes the accumulator, 10 B per parameter, and the final step also
+    # reads the accumulator; a master copy adds 6 B: fp32 read instead of bf16, fp32 write)
+    adam_b = 24 + (4 if nmb > 1 else 0) + (6 if args.master else 0)
+    host_bytes = (nmb * (4 * (lay.w_bytes // 2) * (n_loads - 1) + 4 * (lay_h.w_bytes // 2)) + adam_b * n_params +
+                  10 * (nmb - 1) * n_params + h2d + d2h)
     host["bytes_per_step"] = int(host_bytes)
     host["floor_ms"] = round(1e3 * host_bytes / (max(host["pack_GBps"], host["adam_GBps"]) * 1e9), 1)
     host["floor_frac_of_step"] = round(host["floor_ms"] / ms_step, 3)
