@@ -247,6 +247,8 @@ def main():
                     help="micro-batches per optimizer step (gradients accumulated on the host)")
     ap.add_argument("--master", action="store_true", help="keep fp32 master weights in the host store")
     ap.add_argument("--batch", type=int, default=None, help="override the workload's batch (sequences per pass)")
+    ap.add_argument("--seq", type=int, default=None, help="override the workload's sequence length")
+    ap.add_argument("--layers", type=int, default=None, help="override the workload's layer count")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--timeline-out", default=None, help="write the event timeline of one step as JSON")
     args = ap.parse_args()
@@ -262,9 +264,10 @@ def main():
     from host_memory_centric_amd.engine import Trainer
 
     cfg = synth.preset(args.workload)
-    if args.ckpt_every is not None or args.batch is not None:
+    if any(v is not None for v in (args.ckpt_every, args.batch, args.seq, args.layers)):
         import dataclasses
-        cfg = dataclasses.replace(cfg, ckpt_every=args.ckpt_every or cfg.ckpt_every, batch=args.batch or cfg.batch)
+        cfg = dataclasses.replace(cfg, ckpt_every=args.ckpt_every or cfg.ckpt_every, batch=args.batch or cfg.batch,
+                                  seq=args.seq or cfg.seq, layers=args.layers or cfg.layers)
     adam = synth.AdamCfg()
     t_init = time.perf_counter()
     nmb = max(1, args.micro_batches)
