@@ -70,6 +70,8 @@ _SIGS = {
     "mt_store_create_ex": [POINTER(MtModelCfg), c_uint32, POINTER(c_void_p)],
     "mt_store_sync_master": [c_void_p],
     "mt_grad_accumulate": [c_void_p, c_int, c_void_p],
+    "mt_store_save": [c_void_p, ctypes.c_char_p, c_int64],
+    "mt_store_load": [c_void_p, ctypes.c_char_p, POINTER(c_int64)],
     "mt_store_block": [c_void_p, c_int, POINTER(c_void_p)],
     "mt_store_bytes": [c_void_p, POINTER(c_uint64)],
     "mt_store_fill_normal": [c_void_p, c_uint32, c_double],

@@ -10,11 +10,14 @@
 // depth.
 #include <hip/hip_runtime_api.h>
 #include <immintrin.h>
+#include <fcntl.h>
 #include <sys/mman.h>
+#include <unistd.h>
 
 #include <algorithm>
 #include <atomic>
 #include <cmath>
+#include <cerrno>
 #include <cstdarg>
 #include <cstring>
 #include <mutex>
@@ -456,6 +459,63 @@ static void sync_master(mt_store* st) {
     }
 }
 
+// ---- checkpoint / resume ---------------------------------------------------
+struct CkptHeader {
+    char magic[8];  // "MTSTORE1"
+    uint32_t version, flags;
+    mt_model_cfg cfg;
+    int64_t t;
+    uint64_t n_units, total_bytes;
+};
+constexpr uint64_t kIoChunk = 64ull << 20;
+
+struct Fd {
+    int fd;
+    ~Fd() {
+        if (fd >= 0) close(fd);
+    }
+};
+
+static void io_fail(const char* what, const char* path) { MT_FAIL(MT_E_IO, "%s %s: %s", what, path, strerror(errno)); }
+
+// pread/pwrite of [off, off + n) in full, retrying short transfers
+template <bool WRITE>
+void io_all(int fd, char* buf, uint64_t n, uint64_t off, const char* path) {
+    while (n > 0) {
+        const ssize_t r = WRITE ? pwrite(fd, buf, n, (off_t)off) : pread(fd, buf, n, (off_t)off);
+        if (r < 0 && errno == EINTR) continue;
+        if (r <= 0) {
+            if (r == 0) errno = EIO;
+            io_fail(WRITE ? "write" : "read", path);
+        }
+        buf += r;
+        off += (uint64_t)r;
+        n -= (uint64_t)r;
+    }
+}
+
+// Transfers every block to/from the file after the header, in 64 MB chunks
+// spread over the worker threads.
+template <bool WRITE>
+void io_blocks(mt_store* st, int fd, const char* path) {
+    std::vector<std::pair<uint64_t, uint64_t>> jobs;  // (block index, offset in block)
+    for (size_t i = 0; i < st->blocks.size(); ++i)
+        for (uint64_t o = 0; o < st->layouts[i].block_bytes; o += kIoChunk) jobs.emplace_back(i, o);
+    std::vector<uint64_t> base(st->blocks.size());
+    uint64_t pos = sizeof(CkptHeader);
+    for (size_t i = 0; i < st->blocks.size(); ++i) {
+        base[i] = pos;
+        pos += st->layouts[i].block_bytes;
+    }
+    parallel_for(jobs.size(), 1, [&](uint64_t b, uint64_t e) {
+        for (uint64_t j = b; j < e; ++j) {
+            const auto [i, o] = jobs[j];
+            const uint64_t n = std::min(kIoChunk, st->layouts[i].block_bytes - o);
+            io_all<WRITE>(fd, (char*)st->blocks[i] + o, n, base[i] + o, path);
+        }
+    });
+}
+
 }  // namespace mt
 
 using namespace mt;
@@ -587,6 +647,49 @@ int mt_grad_accumulate(mt_store* st, int unit, const void* grad_src) {
                 accum_scalar(A, src, first, b, e);
         });
         ++st->n_accum[idx];
+    });
+}
+
+
+int mt_store_save(const mt_store* cst, const char* path, int64_t t) {
+    return guard([&] {
+        MT_CHECK_ARG(cst != nullptr && path != nullptr, "NULL argument");
+        mt_store* st = const_cast<mt_store*>(cst);
+        Fd f{open(path, O_WRONLY | O_CREAT | O_TRUNC, 0644)};
+        if (f.fd < 0) io_fail("open", path);
+        CkptHeader h;
+        memset(&h, 0, sizeof(h));
+        memcpy(h.magic, "MTSTORE1", 8);
+        h.version = 1;
+        h.flags = st->flags;
+        h.cfg = st->cfg;
+        h.t = t;
+        h.n_units = st->blocks.size();
+        for (auto& L : st->layouts) h.total_bytes += L.block_bytes;
+        io_all<true>(f.fd, (char*)&h, sizeof(h), 0, path);
+        io_blocks<true>(st, f.fd, path);
+        io_all<true>(f.fd, (char*)st->n_accum.data(), 8 * st->n_accum.size(), sizeof(h) + h.total_bytes, path);
+        if (fsync(f.fd) != 0) io_fail("fsync", path);
+    });
+}
+
+int mt_store_load(mt_store* st, const char* path, int64_t* t_out) {
+    return guard([&] {
+        MT_CHECK_ARG(st != nullptr && path != nullptr && t_out != nullptr, "NULL argument");
+        Fd f{open(path, O_RDONLY)};
+        if (f.fd < 0) io_fail("open", path);
+        CkptHeader h;
+        io_all<false>(f.fd, (char*)&h, sizeof(h), 0, path);
+        uint64_t total = 0;
+        for (auto& L : st->layouts) total += L.block_bytes;
+        if (memcmp(h.magic, "MTSTORE1", 8) != 0 || h.version != 1)
+            MT_FAIL(MT_E_ARG, "%s is not a store checkpoint", path);
+        if (memcmp(&h.cfg, &st->cfg, sizeof(mt_model_cfg)) != 0 || h.flags != st->flags ||
+            h.n_units != st->blocks.size() || h.total_bytes != total)
+            MT_FAIL(MT_E_ARG, "%s was written for another model config or store flags", path);
+        io_blocks<false>(st, f.fd, path);
+        io_all<false>(f.fd, (char*)st->n_accum.data(), 8 * st->n_accum.size(), sizeof(h) + total, path);
+        *t_out = h.t;
     });
 }
 

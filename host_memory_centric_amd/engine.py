@@ -300,6 +300,19 @@ class Trainer:
         for u in list(self.pending):
             self._wait_unit(u)
 
+    def save(self, path):
+        """Checkpoint the training state (host store and step counter) after
+        every pending update; a trainer that loads it continues bit-identically
+        (the device holds no state across steps)."""
+        self.finish()
+        self.store.save(path, self.t)
+
+    def load(self, path):
+        """Resume from a checkpoint written by save() for the same model,
+        store options and batch shape."""
+        self.finish()
+        self.t = self.store.load(path)
+
     def _wait_unit(self, unit):
         f = self.pending.pop(unit, None)
         if f is not None:

@@ -84,6 +84,16 @@ class HostStore:
                 return reg[off:off + int(np.prod(shape))].reshape(shape)
         raise KeyError(name)
 
+    def save(self, path, t):
+        """Checkpoint every block (and the step counter t) to a file."""
+        call("mt_store_save", self.ptr, str(path).encode(), int(t))
+
+    def load(self, path):
+        """Restore a checkpoint written by save() for this config and flags; returns t."""
+        t = ctypes.c_int64()
+        call("mt_store_load", self.ptr, str(path).encode(), ctypes.byref(t))
+        return t.value
+
     def fill_normal(self, seed=None, std=0.02):
         call("mt_store_fill_normal", self.ptr, self.cfg.seed if seed is None else seed, std)
 

@@ -40,7 +40,8 @@ enum {
     MT_E_ALIGN = -3,  /* pointer not aligned as documented */
     MT_E_NOMEM = -4,  /* host allocation failed */
     MT_E_HIP = -5,    /* a HIP runtime call failed (message holds its error) */
-    MT_E_STATE = -6   /* call out of order */
+    MT_E_STATE = -6,  /* call out of order */
+    MT_E_IO = -7      /* file I/O failed (message holds the system error) */
 };
 
 /* Units of the host store: layers are 0..layers-1. */
@@ -122,6 +123,20 @@ int mt_store_fill_normal(mt_store* st, uint32_t seed, double std);
  * caller wrote W through mt_store_block (mt_store_fill_normal does this
  * itself).  MT_E_STATE without MT_STORE_MASTER_FP32. */
 int mt_store_sync_master(mt_store* st);
+
+/* Checkpoint and resume of the host store (the store is the authoritative
+ * copy of all training state -- paper page, section 3, execution workflow --
+ * so a step counter and the blocks are a complete checkpoint; the pages list
+ * an SSD tier below host memory as future work, section 6).  mt_store_save
+ * writes a header (format tag, model config, store flags, t, block sizes),
+ * every unit's whole block (embedding, head, layers 0..L-1: W, G, M, V and
+ * the optional regions) and the per-unit micro-batch accumulation counts,
+ * in parallel, then syncs the file.  mt_store_load reads such a file into a
+ * store created with the same config and flags (MT_E_ARG otherwise) and
+ * returns t; a run resumed from it continues bit-identically.  MT_E_IO on
+ * I/O errors.  Neither may overlap any other call on the store. */
+int mt_store_save(const mt_store* st, const char* path, int64_t t);
+int mt_store_load(mt_store* st, const char* path, int64_t* t_out);
 
 /* Number of host worker threads used by pack, Adam, fill and embedding
  * (default: the process's CPU affinity count). */

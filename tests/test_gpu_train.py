@@ -135,3 +135,42 @@ def test_micro_batches_streamed_equals_resident_and_repeats_equal_one(gpu):
             tr.close()
     for key, a in out[0].items():
         assert np.array_equal(out[1][key], a), key
+
+
+def test_resume_from_checkpoint_is_bit_identical(gpu, tmp_path):
+    """Three steps in one run equal one step, a checkpoint of the host store,
+    a new trainer (whose own state is first moved by a step of its own) that
+    loads it, and two more steps: losses and every store region bit for bit
+    (two micro-batches and master weights, so every region is exercised)."""
+    cfg = synth.preset("tiny")
+    bits = synth.make_weights(cfg)
+
+    def toks(s):
+        return np.concatenate([synth.make_tokens(cfg, 2 * s), synth.make_tokens(cfg, 2 * s + 1)])
+
+    kw = dict(micro_batches=2, master=True)
+    a = _trainer(cfg, bits, **kw)
+    try:
+        la = [a.step(toks(s)) for s in range(3)]
+        ra = _store_regions(a)
+    finally:
+        a.close()
+    path = tmp_path / "run.ckpt"
+    b = _trainer(cfg, bits, **kw)
+    try:
+        lb = [b.step(toks(0))]
+        b.save(path)
+    finally:
+        b.close()
+    c = _trainer(cfg, bits, **kw)
+    try:
+        c.step(toks(9))
+        c.load(path)
+        assert c.t == 1
+        lb += [c.step(toks(s)) for s in (1, 2)]
+        rc = _store_regions(c)
+    finally:
+        c.close()
+    assert la == lb
+    for key, x in ra.items():
+        assert np.array_equal(rc[key], x), key

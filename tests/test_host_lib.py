@@ -285,6 +285,50 @@ def test_store_regions_and_flags(lib):
         st.close()
 
 
+def test_store_checkpoint_round_trip(lib, tmp_path):
+    """save/load restore every region (incl. the optional ones and the
+    accumulation counts) and t; a file for another config or other flags is
+    refused; a missing file is an I/O error."""
+    cfg = synth.preset("tiny")
+    st = HostStore(cfg, master=True, accum=True)
+    st2 = HostStore(cfg, master=True, accum=True)
+    try:
+        st.fill_normal()
+        rng = np.random.default_rng(5)
+        n = st.layout_of(1).w_bytes // 2
+        g = synth.f32_to_bf16_bits((rng.standard_normal(n) * 1e-3).astype(np.float32))
+        call("mt_step", st.ptr, 1, g.ctypes.data_as(ctypes.c_void_p), ctypes.byref(_lib.adam_cfg(synth.AdamCfg())), 1,
+             None)
+        call("mt_grad_accumulate", st.ptr, 0, g.ctypes.data_as(ctypes.c_void_p))  # a pending accumulation
+        path = tmp_path / "store.ckpt"
+        st.save(path, 7)
+        assert st2.load(path) == 7
+        for u in st.units:
+            for r in range(6):
+                assert np.array_equal(st.region(u, r), st2.region(u, r)), (u, r)
+        # the restored accumulation count: the next step on unit 0 averages 2 micro-batches in both
+        outs = []
+        for s_ in (st, st2):
+            w = np.zeros(n, np.float32)
+            call("mt_step", s_.ptr, 0, g.ctypes.data_as(ctypes.c_void_p), ctypes.byref(_lib.adam_cfg(synth.AdamCfg())),
+                 2, w.ctypes.data_as(ctypes.c_void_p))
+            outs.append(w)
+        assert np.array_equal(outs[0], outs[1])
+        other = HostStore(cfg)
+        try:
+            with pytest.raises(MtError) as e:
+                other.load(path)
+            assert e.value.code == -1
+        finally:
+            other.close()
+        with pytest.raises(MtError) as e:
+            st2.load(tmp_path / "missing.ckpt")
+        assert e.value.code == -7
+    finally:
+        st.close()
+        st2.close()
+
+
 def test_host_adam_scalar_path_equals_simd(lib, monkeypatch):
     """The AVX-512 and scalar paths give identical bits (checked in a subprocess)."""
     import subprocess
