@@ -315,7 +315,7 @@ def main():
     f_exec, f_model = (nmb * f for f in flops_per_step(cfg, tr.ops))
     tflops_exec = f_exec / (dt / args.steps) / 1e12
     tflops_model = f_model / (dt / args.steps) / 1e12
-    lay, lay_h = tr.lay, tr.lay_head
+    lay, lay_h = tr.lay, tr.lay_head_dev
     n_loads = tr.n_weight_loads()  # per micro-batch pass
     h2d = nmb * ((n_loads - 1) * lay.w_bytes + lay_h.w_bytes) + T * cfg.hidden * 2 + T * 4
     d2h = nmb * (cfg.layers * lay.w_bytes + lay_h.w_bytes) + T * cfg.hidden * 4

@@ -28,7 +28,7 @@ class MtError(RuntimeError):
 
 class MtModelCfg(ctypes.Structure):
     _fields_ = [("layers", c_int32), ("hidden", c_int32), ("heads", c_int32), ("head_dim", c_int32),
-                ("ffn", c_int32), ("vocab", c_int32), ("eps", c_float), ("rope_base", c_float)]
+                ("ffn", c_int32), ("vocab", c_int32), ("eps", c_float), ("rope_base", c_float), ("tied", c_int32)]
 
 
 class MtUnitLayout(ctypes.Structure):
@@ -84,6 +84,8 @@ _SIGS = {
     "mt_step": [c_void_p, c_int, c_void_p, POINTER(MtAdamCfg), c_int64, c_void_p],
     "mt_embed_gather": [c_void_p, c_void_p, c_int64, c_void_p],
     "mt_embed_grad": [c_void_p, c_void_p, c_int64, c_void_p],
+    "mt_embed_grad_tied": [c_void_p, c_void_p, c_int64, c_void_p, c_void_p],
+    "mt_pack_head_tied": [c_void_p, c_void_p, c_size_t],
     "mt_rope_tables": [POINTER(MtModelCfg), c_int32, c_void_p, c_void_p],
     "mt_bind": [POINTER(MtModelCfg), c_int, c_void_p, c_void_p, POINTER(MtLayerView)],
     "mt_layer_saved_bytes": [POINTER(MtModelCfg), c_int32, c_int32, POINTER(c_size_t)],
@@ -142,7 +144,8 @@ def call(name, *args):
 
 def model_cfg(cfg):
     """MtModelCfg from any object with the model-shape attributes."""
-    return MtModelCfg(cfg.layers, cfg.hidden, cfg.heads, cfg.head_dim, cfg.ffn, cfg.vocab, cfg.eps, cfg.rope_base)
+    return MtModelCfg(cfg.layers, cfg.hidden, cfg.heads, cfg.head_dim, cfg.ffn, cfg.vocab, cfg.eps, cfg.rope_base,
+                      int(bool(getattr(cfg, "tied", False))))
 
 
 def adam_cfg(a):

@@ -58,6 +58,7 @@ void check_cfg(const mt_model_cfg* cfg) {
     if (cfg->hidden % 8 || cfg->ffn % 8 || cfg->vocab % 8 || cfg->head_dim % 8)
         MT_FAIL(MT_E_SHAPE, "hidden, ffn, vocab and head_dim must be multiples of 8");
     if (!(cfg->eps > 0.f) || !(cfg->rope_base > 1.f)) MT_FAIL(MT_E_ARG, "bad eps or rope_base");
+    if (cfg->tied != 0 && cfg->tied != 1) MT_FAIL(MT_E_ARG, "tied must be 0 or 1");
 }
 
 mt_unit_layout layout_of(const mt_model_cfg* cfg, int unit, uint32_t flags) {
@@ -81,9 +82,9 @@ mt_unit_layout layout_of(const mt_model_cfg* cfg, int unit, uint32_t flags) {
         L.n_tensors = 1;
         numel[0] = V * h;
     } else if (unit == MT_UNIT_HEAD) {
-        L.n_tensors = 2;
-        numel[0] = h;      // final RMSNorm gain
-        numel[1] = V * h;  // LM head
+        L.n_tensors = cfg->tied ? 1 : 2;
+        numel[0] = h;                    // final RMSNorm gain
+        numel[1] = cfg->tied ? 0 : V * h;  // LM head (the embedding when tied)
     } else {
         MT_FAIL(MT_E_ARG, "unknown unit %d", unit);
     }
@@ -704,6 +705,24 @@ int mt_pack_layer(mt_store* st, int unit, void* dst, size_t dst_bytes) {
     });
 }
 
+int mt_pack_head_tied(mt_store* st, void* dst, size_t dst_bytes) {
+    return guard([&] {
+        MT_CHECK_ARG(st != nullptr && dst != nullptr, "NULL argument");
+        MT_CHECK_ARG(st->cfg.tied, "the model does not tie its embedding and head");
+        mt_model_cfg untied = st->cfg;
+        untied.tied = 0;
+        const mt_unit_layout D = layout_of(&untied, MT_UNIT_HEAD);
+        MT_CHECK_ARG(dst_bytes >= D.w_bytes, "dst holds %zu bytes, the head slot needs %llu", dst_bytes,
+                     (unsigned long long)D.w_bytes);
+        const int hi = unit_index(st, MT_UNIT_HEAD), ei = unit_index(st, MT_UNIT_EMBED);
+        const char* hw = (const char*)st->blocks[hi] + st->layouts[hi].region_off[0];
+        const char* ew = (const char*)st->blocks[ei] + st->layouts[ei].region_off[0];
+        memset(dst, 0, D.tensor_off[1]);                                   // gain and its padding
+        memcpy((char*)dst, hw, 2 * D.tensor_numel[0]);                     // final gain
+        par_memcpy((char*)dst + D.tensor_off[1], ew, 2 * D.tensor_numel[1]);  // E as the LM head
+    });
+}
+
 int mt_pinned_alloc(size_t bytes, void** out) {
     return guard([&] {
         MT_CHECK_ARG(out != nullptr && bytes > 0, "bad arguments");
@@ -789,42 +808,55 @@ int mt_embed_gather(mt_store* st, const int32_t* tok, int64_t T, void* dst) {
     });
 }
 
-int mt_embed_grad(mt_store* st, const int32_t* tok, int64_t T, const float* dx0) {
-    return guard([&] {
-        const int idx = unit_index(st, MT_UNIT_EMBED);
-        MT_CHECK_ARG(tok && dx0 && T >= 0, "bad arguments");
-        const uint64_t h = st->cfg.hidden, V = st->cfg.vocab;
-        for (int64_t t = 0; t < T; ++t)
-            MT_CHECK_ARG(tok[t] >= 0 && tok[t] < st->cfg.vocab, "token out of range");
-        uint16_t* G = (uint16_t*)((char*)st->blocks[idx] + st->layouts[idx].region_off[1]);
-        // Positions grouped by token id, ascending position inside a group
-        // (a stable counting sort): row v of the gradient is the sum of the
-        // rows dx0[t] with tok[t] = v taken in ascending t, accumulated in
-        // fp32 and rounded once to bf16; rows of absent tokens are zero.
-        std::vector<int64_t> start(V + 1, 0), pos(T);
-        for (int64_t t = 0; t < T; ++t) ++start[tok[t] + 1];
-        for (uint64_t v = 0; v < V; ++v) start[v + 1] += start[v];
-        {
-            std::vector<int64_t> fill(start.begin(), start.end() - 1);
-            for (int64_t t = 0; t < T; ++t) pos[fill[tok[t]]++] = t;
-        }
-        parallel_for(V, 64, [&](uint64_t v0, uint64_t v1) {
-            std::vector<float> acc(h);
-            for (uint64_t v = v0; v < v1; ++v) {
-                uint16_t* g = G + v * h;
-                const int64_t b = start[v], e = start[v + 1];
-                if (b == e) {
+// Embedding gradient into G: row v = bf16 of (init[v], or 0) + the rows
+// dx0[t] with tok[t] = v taken in ascending t, accumulated in fp32.
+static void embed_grad_rows(mt_store* st, const int32_t* tok, int64_t T, const float* dx0, const uint16_t* init) {
+    const int idx = unit_index(st, MT_UNIT_EMBED);
+    MT_CHECK_ARG(tok && dx0 && T >= 0, "bad arguments");
+    const uint64_t h = st->cfg.hidden, V = st->cfg.vocab;
+    for (int64_t t = 0; t < T; ++t)
+        MT_CHECK_ARG(tok[t] >= 0 && tok[t] < st->cfg.vocab, "token out of range");
+    uint16_t* G = (uint16_t*)((char*)st->blocks[idx] + st->layouts[idx].region_off[1]);
+    // Positions grouped by token id, ascending position inside a group (a
+    // stable counting sort), then one fp32 row sum per token.
+    std::vector<int64_t> start(V + 1, 0), pos(T);
+    for (int64_t t = 0; t < T; ++t) ++start[tok[t] + 1];
+    for (uint64_t v = 0; v < V; ++v) start[v + 1] += start[v];
+    {
+        std::vector<int64_t> fill(start.begin(), start.end() - 1);
+        for (int64_t t = 0; t < T; ++t) pos[fill[tok[t]]++] = t;
+    }
+    parallel_for(V, 64, [&](uint64_t v0, uint64_t v1) {
+        std::vector<float> acc(h);
+        for (uint64_t v = v0; v < v1; ++v) {
+            uint16_t* g = G + v * h;
+            const int64_t b = start[v], e = start[v + 1];
+            if (b == e) {
+                if (init)
+                    memcpy(g, init + v * h, 2 * h);
+                else
                     memset(g, 0, 2 * h);
-                    continue;
-                }
-                std::fill(acc.begin(), acc.end(), 0.f);
-                for (int64_t i = b; i < e; ++i) {
-                    const float* src = dx0 + (uint64_t)pos[i] * h;
-                    for (uint64_t c = 0; c < h; ++c) acc[c] += src[c];
-                }
-                for (uint64_t c = 0; c < h; ++c) g[c] = f32_to_bf16(acc[c]);
+                continue;
             }
-        });
+            for (uint64_t c = 0; c < h; ++c) acc[c] = init ? bf16_to_f32(init[v * h + c]) : 0.f;
+            for (int64_t i = b; i < e; ++i) {
+                const float* src = dx0 + (uint64_t)pos[i] * h;
+                for (uint64_t c = 0; c < h; ++c) acc[c] += src[c];
+            }
+            for (uint64_t c = 0; c < h; ++c) g[c] = f32_to_bf16(acc[c]);
+        }
+    });
+}
+
+int mt_embed_grad(mt_store* st, const int32_t* tok, int64_t T, const float* dx0) {
+    return guard([&] { embed_grad_rows(st, tok, T, dx0, nullptr); });
+}
+
+int mt_embed_grad_tied(mt_store* st, const int32_t* tok, int64_t T, const float* dx0, const void* head_grad) {
+    return guard([&] {
+        MT_CHECK_ARG(st != nullptr && head_grad != nullptr, "NULL argument");
+        MT_CHECK_ARG(st->cfg.tied, "the model does not tie its embedding and head");
+        embed_grad_rows(st, tok, T, dx0, (const uint16_t*)head_grad);
     });
 }
 

@@ -294,7 +294,10 @@ int mt_bind(const mt_model_cfg* cfg, int unit, const void* dev_w_slot, void* dev
         MT_CHECK_ARG(out != nullptr && dev_w_slot != nullptr, "NULL argument");
         if (((uintptr_t)dev_w_slot | (uintptr_t)dev_g_slot) & 255)
             MT_FAIL(MT_E_ALIGN, "device slots must be 256-byte aligned");
-        const mt_unit_layout L = layout_of(cfg, unit);
+        // the head's device slot has the untied layout even for tied weights
+        mt_model_cfg c = *cfg;
+        if (unit == MT_UNIT_HEAD) c.tied = 0;
+        const mt_unit_layout L = layout_of(&c, unit);
         memset(out, 0, sizeof(*out));
         for (int j = 0; j < L.n_tensors; ++j) {
             out->w[j] = (const char*)dev_w_slot + L.tensor_off[j];

@@ -40,6 +40,7 @@ PyTorch provides device memory, streams and events only; every step of the
 computation runs in libmt.so.
 """
 import ctypes
+import dataclasses
 import queue
 import threading
 import time
@@ -227,7 +228,13 @@ class Trainer:
             self.store.load_bits(weights)
         self.lay = self.store.layout_of(0)
         self.lay_head = self.store.layout_of(MT_UNIT_HEAD)
-        self.slot_bytes = max(self.lay.w_bytes, self.lay_head.w_bytes)
+        # the head's device slot, gradient buffer and slab use the untied head
+        # layout (final gain, LM head); with tied weights the LM head part is
+        # the embedding matrix, packed from the embedding unit
+        self.tied = bool(getattr(cfg, "tied", False))
+        self.lay_head_dev = _lib.unit_layout(_lib.model_cfg(dataclasses.replace(cfg, tied=False))
+                                             if self.tied else self.mcfg, MT_UNIT_HEAD)
+        self.slot_bytes = max(self.lay.w_bytes, self.lay_head_dev.w_bytes)
 
         self.ops = plan_step(self.L, self.K, mode == "resident")
         units = [MT_UNIT_HEAD if k == "head" else l for (k, l, _) in self.ops]
@@ -238,7 +245,7 @@ class Trainer:
         bf, f32 = torch.bfloat16, torch.float32
         self.slots = [torch.empty(self.slot_bytes, dtype=torch.uint8, device=d) for _ in range(self.n_slots)]
         self.gslots = [torch.empty(self.lay.w_bytes, dtype=torch.uint8, device=d) for _ in range(2)]
-        self.head_g = torch.empty(self.lay_head.w_bytes, dtype=torch.uint8, device=d)
+        self.head_g = torch.empty(self.lay_head_dev.w_bytes, dtype=torch.uint8, device=d)
         nblk = (self.L + self.K - 1) // self.K
         self.ckpt = [torch.empty((T, h), dtype=bf, device=d) for _ in range(nblk)]
         self.blockx = [None] + [torch.empty((T, h), dtype=bf, device=d) for _ in range(1, self.K)]
@@ -263,7 +270,7 @@ class Trainer:
 
         self.wslab = [PinnedBuffer(self.slot_bytes) for _ in range(2)]
         self.gslab = [PinnedBuffer(self.lay.w_bytes) for _ in range(max(1, n_grad_slabs))]
-        self.head_gslab = PinnedBuffer(self.lay_head.w_bytes)
+        self.head_gslab = PinnedBuffer(self.lay_head_dev.w_bytes)
         self.x0_pin = PinnedBuffer(T * h * 2)
         self.dx0_pin = PinnedBuffer(T * h * 4)
         self.tok_pin = PinnedBuffer(T * 4)
@@ -433,7 +440,10 @@ class Trainer:
             f = pending.get(unit)
             if f is not None:
                 f.result()  # the unit's update of the previous step has landed
-            call("mt_pack_layer", self.store.ptr, unit, self.wslab[j % 2].ptr, self.slot_bytes)
+            if unit == MT_UNIT_HEAD and self.tied:
+                call("mt_pack_head_tied", self.store.ptr, self.wslab[j % 2].ptr, self.slot_bytes)
+            else:
+                call("mt_pack_layer", self.store.ptr, unit, self.wslab[j % 2].ptr, self.slot_bytes)
 
         pack_fut = {j: self.packer.submit(pack, j) for j in range(min(2, len(loads)))}
         next_load = [0]
@@ -442,7 +452,7 @@ class Trainer:
             i = loads[j]
             pack_fut.pop(j).result()
             unit = self.op_unit[i]
-            nbytes = (self.lay_head if unit == MT_UNIT_HEAD else self.lay).w_bytes
+            nbytes = (self.lay_head_dev if unit == MT_UNIT_HEAD else self.lay).w_bytes
             with torch.cuda.stream(hs):
                 if slot_prev[i] is not None:
                     hs.wait_event(op_done[slot_prev[i]])  # buffer-free
@@ -486,7 +496,11 @@ class Trainer:
 
         def adam_embed(ev):
             ev.synchronize()
-            call("mt_embed_grad", self.store.ptr, self.tok_pin.ptr, self.T, self.dx0_pin.ptr)
+            if self.tied:  # the shared matrix: the head's gradient (in the head slab) plus the embedding's
+                head_grad = ctypes.c_void_p(self.head_gslab.ptr.value + self.lay_head_dev.tensor_off[1])
+                call("mt_embed_grad_tied", self.store.ptr, self.tok_pin.ptr, self.T, self.dx0_pin.ptr, head_grad)
+            else:
+                call("mt_embed_grad", self.store.ptr, self.tok_pin.ptr, self.T, self.dx0_pin.ptr)
             if final:
                 call("mt_step", self.store.ptr, MT_UNIT_EMBED, None, ctypes.byref(self.madam), t,
                      self._w32_ptr(MT_UNIT_EMBED))
@@ -553,7 +567,7 @@ class Trainer:
                     ds.wait_event(ev)
                     if tl is not None:
                         tl["d2h"].append([self._ev(ds), d2h])
-                    call("mt_copy_d2h", self.head_gslab.ptr, _ptr(self.head_g), self.lay_head.w_bytes, sd)
+                    call("mt_copy_d2h", self.head_gslab.ptr, _ptr(self.head_g), self.lay_head_dev.w_bytes, sd)
                     d2h.record(ds)
                 self.head_d2h = d2h
                 jobs[MT_UNIT_HEAD] = self.optimizer.submit(self._urgency(MT_UNIT_HEAD), d2h, adam_layer, d2h,

@@ -19,8 +19,8 @@ def tensor_shapes(cfg, unit):
     h, f, V = cfg.hidden, cfg.ffn, cfg.vocab
     if unit == MT_UNIT_EMBED:
         return [("embed", (V, h))]
-    if unit == MT_UNIT_HEAD:
-        return [("g_final", (h,)), ("head", (V, h))]
+    if unit == MT_UNIT_HEAD:  # with tied weights the LM head is the embedding
+        return [("g_final", (h,))] if getattr(cfg, "tied", False) else [("g_final", (h,)), ("head", (V, h))]
     return [("g_attn", (h,)), ("wqkv", (3 * h, h)), ("wo", (h, h)), ("g_mlp", (h,)), ("wgu", (2 * f, h)),
             ("wd", (h, f))]
 
@@ -105,7 +105,8 @@ class HostStore:
                 self.region(u, r)[:] = 0
         self.tensor(MT_UNIT_EMBED, "embed")[:] = bits["embed"]
         self.tensor(MT_UNIT_HEAD, "g_final")[:] = bits["g_final"]
-        self.tensor(MT_UNIT_HEAD, "head")[:] = bits["head"]
+        if bits.get("head") is not None:
+            self.tensor(MT_UNIT_HEAD, "head")[:] = bits["head"]
         for l, lw in enumerate(bits["layers"]):
             for name in LAYER_TENSORS:
                 self.tensor(l, name)[:] = lw[name]
@@ -116,7 +117,8 @@ class HostStore:
         """Copy of all weights as bf16 bit arrays (the synth layout)."""
         out = {"embed": self.tensor(MT_UNIT_EMBED, "embed").copy(),
                "g_final": self.tensor(MT_UNIT_HEAD, "g_final").copy(),
-               "head": self.tensor(MT_UNIT_HEAD, "head").copy(), "layers": []}
+               "head": None if getattr(self.cfg, "tied", False) else self.tensor(MT_UNIT_HEAD, "head").copy(),
+               "layers": []}
         for l in range(self.cfg.layers):
             out["layers"].append({n: self.tensor(l, n).copy() for n in LAYER_TENSORS})
         return out

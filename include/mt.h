@@ -52,12 +52,15 @@ enum { MT_UNIT_EMBED = -1, MT_UNIT_HEAD = -2 };
 
 /* Model shape.  Llama-style decoder: per layer RMSNorm gain [h], fused QKV
  * weight [3h, h], output projection [h, h], RMSNorm gain [h], fused gate/up
- * weight [2f, h] (gate rows first), down projection [h, f]; untied embedding
- * [V, h]; final RMSNorm gain [h] and LM head [V, h].  Weights are [out, in]. */
+ * weight [2f, h] (gate rows first), down projection [h, f]; embedding [V, h];
+ * final RMSNorm gain [h] and LM head [V, h], which with `tied` is the
+ * embedding matrix itself (paper page, appendix A.1: tied embedding and
+ * head share one physical store).  Weights are [out, in]. */
 typedef struct mt_model_cfg {
     int32_t layers, hidden, heads, head_dim, ffn, vocab;
     float eps;       /* RMSNorm epsilon (inside the square root) */
     float rope_base; /* RoPE base (rotate-half pairs (i, i + hd/2)) */
+    int32_t tied;    /* 1: the LM head is the embedding matrix (weight tying), 0: untied */
 } mt_model_cfg;
 
 /* Layout of one unit's block.  Layer-contiguous tiling (paper page, appendix
@@ -72,7 +75,7 @@ typedef struct mt_model_cfg {
  * the weights (MT_STORE_MASTER_FP32), and A, the gradient accumulator of
  * micro-batches (MT_STORE_GRAD_ACCUM). */
 typedef struct mt_unit_layout {
-    int32_t n_tensors;        /* 6 per layer; 1 for the embedding; 2 for the head */
+    int32_t n_tensors;        /* 6 per layer; 1 for the embedding; 2 for the head (1 when tied) */
     int32_t pad_;
     uint64_t tensor_off[6];   /* byte offset of tensor j inside W */
     uint64_t tensor_numel[6]; /* element count of tensor j */
@@ -153,6 +156,13 @@ int mt_set_threads(int n);
  * distinct units concurrently; must not overlap mt_step on the same unit. */
 int mt_pack_layer(mt_store* st, int unit, void* dst, size_t dst_bytes);
 
+/* Tied weights (paper page, appendix A.1: structural aliasing of the
+ * embedding and the LM head, one transfer of the shared matrix): packs the
+ * head's device slot from the two units -- the head's final gain and the
+ * embedding matrix E as the LM head -- in the untied head layout (dst holds
+ * at least that layout's w_bytes).  MT_E_ARG unless cfg.tied. */
+int mt_pack_head_tied(mt_store* st, void* dst, size_t dst_bytes);
+
 /* Pinned (page-locked) host memory, hipHostMalloc-backed, owned by the
  * library.  Used for the two weight staging buffers and the gradient slabs
  * (paper page, appendix A.3: two pinned staging buffers sized to the largest
@@ -216,6 +226,12 @@ int mt_embed_gather(mt_store* st, const int32_t* tok, int64_t T, void* dst);
  * (fp32, accumulated in ascending t), rounded once to bf16 into the
  * embedding unit's G region.  dx0: fp32 [T, h] on the host. */
 int mt_embed_grad(mt_store* st, const int32_t* tok, int64_t T, const float* dx0);
+/* Tied weights: the shared matrix's gradient is the LM head's plus the
+ * embedding's.  head_grad: the head's bf16 gradient [V, h] (its slab, at the
+ * LM head's offset); row v of the landed gradient is bf16 of the fp32 sum
+ * head_grad[v] + dx0[t] over t with tok[t] == v, in ascending t (rows of
+ * absent tokens: head_grad[v]).  MT_E_ARG unless cfg.tied. */
+int mt_embed_grad_tied(mt_store* st, const int32_t* tok, int64_t T, const float* dx0, const void* head_grad);
 
 /* RoPE tables computed on the host in fp64 (angle s * base^(-2i/hd)) and
  * rounded to fp32: cos_out, sin_out are [seq, head_dim/2]. */
@@ -234,7 +250,9 @@ typedef struct mt_layer_view {
 
 /* Bind (paper page, appendix A.4; hyper.ai summary, method: a Bind primitive
  * maps views of the streaming buffer onto the template's input slots).  Pure
- * pointer arithmetic over the unit layout: no copy, no launch.  dev_g_slot may
+ * pointer arithmetic over the unit layout: no copy, no launch.  The head's
+ * device slot always has the untied head layout (final gain, then the LM
+ * head [V, h]); with tied weights mt_pack_head_tied fills it.  dev_g_slot may
  * be NULL (forward only).  MT_E_ALIGN unless both slots are 256-byte
  * aligned. */
 int mt_bind(const mt_model_cfg* cfg, int unit, const void* dev_w_slot, void* dev_g_slot,

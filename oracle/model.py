@@ -46,9 +46,14 @@ def bf16_round(x):
 
 
 def to_float(bits_tree, dt):
-    """Convert a (nested) dict/list of bf16 bit arrays into float arrays of dtype dt."""
+    """Convert a (nested) dict/list of bf16 bit arrays into float arrays of
+    dtype dt.  A model whose "head" is None ties its LM head to the
+    embedding: the float tree's "head" is then the embedding array itself."""
     if isinstance(bits_tree, dict):
-        return {k: to_float(v, dt) for k, v in bits_tree.items()}
+        out = {k: to_float(v, dt) for k, v in bits_tree.items() if v is not None}
+        if "embed" in bits_tree and "head" in bits_tree and bits_tree["head"] is None:
+            out["head"] = out["embed"]
+        return out
     if isinstance(bits_tree, list):
         return [to_float(v, dt) for v in bits_tree]
     return bf16_bits_to_f32(bits_tree).astype(dt)
@@ -362,9 +367,13 @@ def embed_fwd(embed, tok):
     return embed[tok.reshape(-1)]
 
 
-def embed_bwd(dx0, tok, V):
-    """dE[v] = sum over positions t with tok_t == v of dx0[t], accumulated in ascending t."""
-    dE = np.zeros((V, dx0.shape[1]), dtype=dx0.dtype)
+def embed_bwd(dx0, tok, V, init=None):
+    """dE[v] = init[v] (or 0) + sum over positions t with tok_t == v of
+    dx0[t], accumulated in ascending t.  With a tied LM head ``init`` is the
+    head's gradient as the device stores it (bf16): the shared matrix's
+    gradient is the sum of both uses (paper page, appendix A.1: tied
+    embedding and head share one physical store)."""
+    dE = np.zeros((V, dx0.shape[1]), dtype=dx0.dtype) if init is None else np.array(init, dtype=dx0.dtype)
     np.add.at(dE, tok.reshape(-1), dx0)
     return dE
 
@@ -419,18 +428,20 @@ class HostState:
     (+ fp32 master weights with ``master``)."""
 
     def __init__(self, bits, master=False):
+        self.tied = bits.get("head") is None
         self.bits = {"embed": bits["embed"].copy(), "g_final": bits["g_final"].copy(),
-                     "head": bits["head"].copy(),
+                     "head": None if self.tied else bits["head"].copy(),
                      "layers": [{k: v.copy() for k, v in lw.items()} for lw in bits["layers"]]}
         z = lambda a: np.zeros(a.shape, dtype=np.float32)
-        self.m = {k: z(self.bits[k]) for k in ("embed", "g_final", "head")}
-        self.v = {k: z(self.bits[k]) for k in ("embed", "g_final", "head")}
+        top = ("embed", "g_final") if self.tied else ("embed", "g_final", "head")
+        self.m = {k: z(self.bits[k]) for k in top}
+        self.v = {k: z(self.bits[k]) for k in top}
         self.m["layers"] = [{k: z(a) for k, a in lw.items()} for lw in self.bits["layers"]]
         self.v["layers"] = [{k: z(a) for k, a in lw.items()} for lw in self.bits["layers"]]
         self.master = None
         if master:
             f = bf16_bits_to_f32
-            self.master = {k: f(self.bits[k]).astype(np.float32) for k in ("embed", "g_final", "head")}
+            self.master = {k: f(self.bits[k]).astype(np.float32) for k in top}
             self.master["layers"] = [{k: f(a).astype(np.float32) for k, a in lw.items()}
                                      for lw in self.bits["layers"]]
         self.t = 0
@@ -465,12 +476,24 @@ def train_step(state, tok, cfg, adam, mode="resident", dt=np.float32, ckpt_every
             w_fp32["layers"][l][name] = upd(state.bits["layers"][l], name, dW[name].astype(np.float32),
                                             state.m["layers"][l][name], state.v["layers"][l][name], ms)
 
+    tied = state.tied
+    top = ("g_final", "embed") if tied else ("head", "g_final", "embed")
+
+    def top_grads(grads, dx0, tk):
+        """Gradients of the non-layer units; tied: the embedding's is the sum
+        of its two uses, the head's (stored bf16 by the device) first."""
+        out = {k: grads[k] for k in ("head", "g_final", "embed")}
+        if tied:
+            out["embed"] = embed_bwd(dx0, tk, cfg.vocab, init=bf16_round(grads["head"].astype(np.float32)))
+        return out
+
     acc = None
     losses = []
     for i, tk in enumerate(micro):
         last = i == n - 1
         if not last:
-            loss, per_pos, grads, _ = forward_backward(Wf, tk, cfg, mode=mode, ckpt_every=ckpt_every)
+            loss, per_pos, grads, dx0 = forward_backward(Wf, tk, cfg, mode=mode, ckpt_every=ckpt_every)
+            tg = top_grads(grads, dx0, tk)
             first = acc is None
             if first:
                 acc = {"layers": [dict() for _ in range(cfg.layers)]}
@@ -478,8 +501,8 @@ def train_step(state, tok, cfg, adam, mode="resident", dt=np.float32, ckpt_every
                 for name in layer_tensor_shapes(cfg):
                     acc["layers"][l][name] = accumulate_micro(acc["layers"][l].get(name), grads["layers"][l][name],
                                                               first)
-            for name in ("head", "g_final", "embed"):
-                acc[name] = accumulate_micro(acc.get(name), grads[name], first)
+            for name in top:
+                acc[name] = accumulate_micro(acc.get(name), tg[name], first)
             losses.append(loss)
             continue
 
@@ -492,17 +515,20 @@ def train_step(state, tok, cfg, adam, mode="resident", dt=np.float32, ckpt_every
             gmean["layers"][l] = {name: mean_of(dW[name], acc["layers"][l][name] if acc else None) for name in dW}
             upd_layer(l, gmean["layers"][l])
 
-        loss, per_pos, grads, _ = forward_backward(Wf, tk, cfg, mode=mode, ckpt_every=ckpt_every,
-                                                   on_layer_grad=hook if mode == "streamed" else None)
+        loss, per_pos, grads, dx0 = forward_backward(Wf, tk, cfg, mode=mode, ckpt_every=ckpt_every,
+                                                     on_layer_grad=hook if mode == "streamed" else None)
         losses.append(loss)
         if mode == "resident":
             for l in range(cfg.layers):
                 hook(l, grads["layers"][l])
-        for name in ("head", "g_final", "embed"):
+        tg = top_grads(grads, dx0, tk)
+        for name in top:
             ms = master[name] if master is not None else None
-            gmean[name] = mean_of(grads[name], acc[name] if acc else None)
+            gmean[name] = mean_of(tg[name], acc[name] if acc else None)
             w_fp32[name] = upd(state.bits, name, gmean[name], state.m[name], state.v[name], ms)
     # grads: as computed for one micro-batch; with several, the fp32 mean
     # that Adam receives (before its bf16 storage rounding)
+    if n == 1:
+        gmean = dict(grads, embed=tg["embed"])
     return dict(loss=float(np.mean(np.asarray(losses, dtype=np.float64))), losses=losses, per_pos=per_pos,
-                grads=grads if n == 1 else gmean, w_fp32=w_fp32)
+                grads=gmean, w_fp32=w_fp32)

@@ -40,6 +40,7 @@ class ModelCfg:
     eps: float = 1e-5
     rope_base: float = 10000.0
     seed: int = 0
+    tied: bool = False  # LM head = embedding matrix
 
     @property
     def tokens(self):
@@ -102,12 +103,13 @@ def make_layer_weights(cfg, layer, std=0.02):
 
 
 def make_weights(cfg, std=0.02):
-    """All weights of the model as bf16 bit arrays."""
+    """All weights of the model as bf16 bit arrays (no separate LM head when
+    the embedding is tied to it)."""
     h, V = cfg.hidden, cfg.vocab
     return {
         "embed": normal_bf16_bits(cfg.seed, STREAM_EMBED, V * h, std).reshape(V, h),
         "g_final": np.full((h,), BF16_ONE, dtype=np.uint16),
-        "head": normal_bf16_bits(cfg.seed, STREAM_HEAD, V * h, std).reshape(V, h),
+        "head": None if getattr(cfg, "tied", False) else normal_bf16_bits(cfg.seed, STREAM_HEAD, V * h, std).reshape(V, h),
         "layers": [make_layer_weights(cfg, l, std) for l in range(cfg.layers)],
     }
 

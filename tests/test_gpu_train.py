@@ -174,3 +174,37 @@ def test_resume_from_checkpoint_is_bit_identical(gpu, tmp_path):
     assert la == lb
     for key, x in ra.items():
         assert np.array_equal(rc[key], x), key
+
+
+def test_tied_embeddings_match_oracle_and_schedules_agree(gpu):
+    """Weight tying on the tiny model: the head's slot carries the embedding
+    matrix, its gradient is summed with the embedding's on the host, one
+    Adam updates the shared matrix; against the oracle over two steps, and
+    streamed (K = 1, 2 slots) == resident bit for bit."""
+    import dataclasses
+    cfg = dataclasses.replace(synth.preset("tiny"), tied=True)
+    bits = synth.make_weights(cfg)
+    assert bits["head"] is None
+    adam = synth.AdamCfg()
+    st = oracle.HostState(bits)
+    tr = _trainer(cfg, bits)
+    try:
+        for step in range(2):
+            tok = synth.make_tokens(cfg, step)
+            loss = tr.step(tok)
+            res = oracle.train_step(st, tok, cfg, adam)
+            check_step(tr, loss, res, cfg)
+            sync_from_oracle(tr, st, cfg)
+    finally:
+        tr.close()
+    runs = {}
+    for name, kw in {"resident": dict(mode="resident"), "k1_2slot": dict(ckpt_every=1, n_slots=2)}.items():
+        tr = _trainer(cfg, bits, **kw)
+        try:
+            losses = [tr.step(synth.make_tokens(cfg, s)) for s in range(3)]
+            runs[name] = (losses, _store_regions(tr))
+        finally:
+            tr.close()
+    assert runs["resident"][0] == runs["k1_2slot"][0]
+    for key, a in runs["resident"][1].items():
+        assert np.array_equal(runs["k1_2slot"][1][key], a), key

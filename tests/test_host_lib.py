@@ -329,6 +329,43 @@ def test_store_checkpoint_round_trip(lib, tmp_path):
         st2.close()
 
 
+def test_tied_head_pack_and_summed_embedding_gradient(lib):
+    """Tied weights: the head's device slot is packed as [final gain | E] in
+    the untied head layout, and the embedding's landed gradient is bf16 of
+    the head's bf16 gradient plus the token rows, as the oracle sums them."""
+    import dataclasses
+    cfg = dataclasses.replace(synth.preset("tiny"), tied=True)
+    st = HostStore(cfg)
+    try:
+        st.fill_normal()
+        assert [n for n, _ in tensor_shapes(cfg, MT_UNIT_HEAD)] == ["g_final"]
+        dev = _lib.unit_layout(_lib.model_cfg(dataclasses.replace(cfg, tied=False)), MT_UNIT_HEAD)
+        slab = np.full(dev.w_bytes // 2, 0x7777, dtype=np.uint16)
+        call("mt_pack_head_tied", st.ptr, slab.ctypes.data_as(ctypes.c_void_p), slab.nbytes)
+        h, V = cfg.hidden, cfg.vocab
+        assert np.array_equal(slab[:h], st.tensor(MT_UNIT_HEAD, "g_final"))
+        assert not slab[h:dev.tensor_off[1] // 2].any()
+        off = dev.tensor_off[1] // 2
+        assert np.array_equal(slab[off:off + V * h].reshape(V, h), st.tensor(MT_UNIT_EMBED, "embed"))
+        rng = np.random.default_rng(4)
+        T = 300
+        tok = rng.integers(0, V // 3, T).astype(np.int32)  # most rows absent
+        dx0 = (rng.standard_normal((T, h)) * 1e-2).astype(np.float32)
+        hg = synth.f32_to_bf16_bits((rng.standard_normal((V, h)) * 1e-3).astype(np.float32))
+        call("mt_embed_grad_tied", st.ptr, tok.ctypes.data_as(ctypes.c_void_p), T, dx0.ctypes.data_as(ctypes.c_void_p),
+             hg.ctypes.data_as(ctypes.c_void_p))
+        ref = oracle.embed_bwd(dx0, tok, V, init=synth.bf16_bits_to_f32(hg))
+        assert np.array_equal(st.tensor(MT_UNIT_EMBED, "embed", REGION_G), synth.f32_to_bf16_bits(ref))
+        untied = HostStore(synth.preset("tiny"))
+        try:
+            with pytest.raises(MtError):
+                call("mt_pack_head_tied", untied.ptr, slab.ctypes.data_as(ctypes.c_void_p), slab.nbytes)
+        finally:
+            untied.close()
+    finally:
+        st.close()
+
+
 def test_host_adam_scalar_path_equals_simd(lib, monkeypatch):
     """The AVX-512 and scalar paths give identical bits (checked in a subprocess)."""
     import subprocess

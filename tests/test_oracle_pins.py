@@ -95,6 +95,38 @@ def test_fd_coordinates_every_tensor():
     assert worst < 1e-5
 
 
+def test_fd_tied_embedding_gradient_is_the_sum_of_both_uses():
+    """Weight tying: the LM head is the embedding array itself.  Central
+    differences of the loss w.r.t. entries of the shared matrix (rows of
+    tokens that occur and rows that do not) equal the head's gradient plus
+    the embedding's, the sum the tied update uses."""
+    cfg = synth.preset("micro")
+    rng = np.random.default_rng(13)
+    W = _rand_weights(cfg, rng)
+    W["head"] = W["embed"]  # one array, both uses
+    tok = synth.make_tokens(cfg)
+    _, _, grads, dx0 = oracle.forward_backward(W, tok, cfg)
+    tied = oracle.embed_bwd(dx0, tok, cfg.vocab, init=grads["head"])
+    assert np.array_equal(tied, grads["head"] + grads["embed"]) or np.abs(
+        tied - (grads["head"] + grads["embed"])).max() <= 1e-15 * np.abs(tied).max()
+    E = W["embed"]
+    present = np.unique(tok)
+    absent = np.setdiff1d(np.arange(cfg.vocab), present)
+    rows = list(present[:5]) + list(absent[:3])
+    eps = 1e-5
+    for r in rows:
+        for c in rng.integers(0, E.shape[1], 4):
+            old = E[r, c]
+            E[r, c] = old + eps
+            lp = _loss(W, tok, cfg)
+            E[r, c] = old - eps
+            lm = _loss(W, tok, cfg)
+            E[r, c] = old
+            fd = (lp - lm) / (2 * eps)
+            an = tied[r, c]
+            assert abs(fd - an) <= 1e-6 * (abs(fd) + abs(an)) + 2e-10, (r, c, fd, an)
+
+
 def test_fd_directional_tiny_init():
     """Directional derivatives on the tiny training shape with its own init."""
     cfg = synth.preset("tiny")
