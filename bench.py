@@ -247,6 +247,7 @@ def main():
                     help="micro-batches per optimizer step (gradients accumulated on the host)")
     ap.add_argument("--master", action="store_true", help="keep fp32 master weights in the host store")
     ap.add_argument("--batch", type=int, default=None, help="override the workload's batch (sequences per pass)")
+    ap.add_argument("--adam-threads", type=int, default=0, help="host threads of the optimizer calls (0: all)")
     ap.add_argument("--seq", type=int, default=None, help="override the workload's sequence length")
     ap.add_argument("--layers", type=int, default=None, help="override the workload's layer count")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -271,6 +272,8 @@ def main():
     adam = synth.AdamCfg()
     t_init = time.perf_counter()
     nmb = max(1, args.micro_batches)
+    _lib.load()
+    _lib.call("mt_set_optimizer_threads", args.adam_threads)
     tr = Trainer(cfg, adam, mode=args.mode, n_slots=args.slots, n_grad_slabs=args.grad_slabs, device="cuda:0",
                  micro_batches=nmb, master=args.master)
 

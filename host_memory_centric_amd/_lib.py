@@ -76,6 +76,7 @@ _SIGS = {
     "mt_store_bytes": [c_void_p, POINTER(c_uint64)],
     "mt_store_fill_normal": [c_void_p, c_uint32, c_double],
     "mt_set_threads": [c_int],
+    "mt_set_optimizer_threads": [c_int],
     "mt_pack_layer": [c_void_p, c_int, c_void_p, c_size_t],
     "mt_pinned_alloc": [c_size_t, POINTER(c_void_p)],
     "mt_pinned_free": [c_void_p],

@@ -124,11 +124,14 @@ static int n_threads() {
     return std::max(1, t);
 }
 
+// Threads of the optimizer calls (mt_step, mt_grad_accumulate); 0: n_threads().
+static std::atomic<int> g_opt_threads{0};
+
 template <class F>
-static void parallel_for(uint64_t n, uint64_t grain, F&& fn) {
+static void parallel_for(uint64_t n, uint64_t grain, F&& fn, int max_threads = 0) {
     if (n == 0) return;
     const uint64_t chunks = (n + grain - 1) / grain;
-    const int nt = (int)std::min<uint64_t>(chunks, (uint64_t)n_threads());
+    const int nt = (int)std::min<uint64_t>(chunks, (uint64_t)(max_threads > 0 ? max_threads : n_threads()));
     if (nt <= 1) {
         fn(0, n);
         return;
@@ -535,6 +538,13 @@ int mt_set_threads(int n) {
     });
 }
 
+int mt_set_optimizer_threads(int n) {
+    return guard([&] {
+        MT_CHECK_ARG(n >= 0 && n <= 4096, "bad thread count %d", n);
+        g_opt_threads.store(n);
+    });
+}
+
 int mt_unit_layout_get(const mt_model_cfg* cfg, int unit, mt_unit_layout* out) {
     return mt_unit_layout_get_ex(cfg, 0, unit, out);
 }
@@ -646,7 +656,7 @@ int mt_grad_accumulate(mt_store* st, int unit, const void* grad_src) {
                 accum_avx512(A, src, first, b, e);
             else
                 accum_scalar(A, src, first, b, e);
-        });
+        }, g_opt_threads.load());
         ++st->n_accum[idx];
     });
 }
@@ -779,7 +789,7 @@ int mt_step(mt_store* st, int unit, const void* grad_src, const mt_adam_cfg* ada
                     adam_avx512(W, G, M, Vv, src, w_fp32_out, b, e, k);
                 else
                     adam_scalar(W, G, M, Vv, src, w_fp32_out, b, e, k);
-            });
+            }, g_opt_threads.load());
         } else {
             const float nf = (float)(k_acc + 1);
             parallel_for(n, 1 << 18, [&](uint64_t b, uint64_t e) {
@@ -787,7 +797,7 @@ int mt_step(mt_store* st, int unit, const void* grad_src, const mt_adam_cfg* ada
                     adam_ex_avx512(W, G, M, Vv, P, A, nf, src, w_fp32_out, b, e, k);
                 else
                     adam_ex_scalar(W, G, M, Vv, P, A, nf, src, w_fp32_out, b, e, k);
-            });
+            }, g_opt_threads.load());
         }
         st->n_accum[idx] = 0;
     });

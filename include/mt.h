@@ -144,6 +144,11 @@ int mt_store_load(mt_store* st, const char* path, int64_t* t_out);
 /* Number of host worker threads used by pack, Adam, fill and embedding
  * (default: the process's CPU affinity count). */
 int mt_set_threads(int n);
+/* Threads of the optimizer calls alone (mt_step, mt_grad_accumulate); 0
+ * (default) = as mt_set_threads.  Results do not depend on it.  Fewer
+ * threads leave host memory bandwidth to the packer and the DMA engines
+ * while an update overlaps them. */
+int mt_set_optimizer_threads(int n);
 
 /* ------------------------------------------------------------------------ */
 /* Transfer engine                                                          */
