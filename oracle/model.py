@@ -23,13 +23,15 @@ only to check that the schedule leaves the result unchanged.
 Every function is generic over numpy float32 / float64 (``dt``); arithmetic is
 done in that precision on weights that are exact bf16 values.
 
-Readings taken where the pages are silent (each listed in the design doc):
+Readings taken where the pages are silent:
 Llama-style pre-norm RMSNorm with eps inside the square root and the gain after
 normalising; fused QKV; rotate-half RoPE with cos/sin tables computed in fp64
 and rounded to fp32; causal softmax attention with scale 1/sqrt(hd); SwiGLU
-silu(gate) * up; untied LM head behind a final RMSNorm; mean next-token cross
+silu(gate) * up; an LM head behind a final RMSNorm, untied unless the tied
+form (head = embedding matrix) is asked for; mean next-token cross
 entropy over the B*(S-1) labelled positions; PyTorch-form Adam with bias
-correction, no master fp32 weights.
+correction, on the bf16 weights themselves unless an fp32 master copy is
+kept; micro-batch gradients are rounded to bf16 each and averaged in fp32.
 """
 import numpy as np
 
