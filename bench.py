@@ -118,29 +118,34 @@ def overlap_report(tl):
 def host_probe(tr, reps=3, master=False):
     """Host DRAM rates of the two host-side passes, measured on layer 0 after
     the timed steps with the GPU idle: the packer (W region -> pinned slab,
-    read + non-temporal write, 4 bytes per parameter) and the Adam step
-    (slab read, G written, W/m/v read and written, 24 bytes per parameter).
-    The Adam calls advance layer 0's optimizer state; nothing runs after."""
+    read + non-temporal write, 4 bytes per parameter; not run with a pinned
+    store, which has no packer copy) and the Adam step (slab read, G written,
+    W/m/v read and written, 24 bytes per parameter; with a pinned store the
+    gradient is already in G: G read, 22 bytes per parameter).  The Adam
+    calls advance layer 0's optimizer state; nothing runs after."""
     import ctypes
 
     from host_memory_centric_amd._lib import call
     lay = tr.lay
     params = lay.w_bytes // 2
-    slab = tr.gslab[0]
     tr.finish()
-    t = time.perf_counter()
-    for _ in range(reps):
-        call("mt_pack_layer", tr.store.ptr, 0, tr.wslab[0].ptr, tr.slot_bytes)
-    pack_s = (time.perf_counter() - t) / reps
+    out = {"threads": len(os.sched_getaffinity(0)), "pack_ms_per_layer": None, "pack_GBps": None}
+    if not tr.direct:
+        t = time.perf_counter()
+        for _ in range(reps):
+            call("mt_pack_layer", tr.store.ptr, 0, tr.wslab[0].ptr, tr.slot_bytes)
+        pack_s = (time.perf_counter() - t) / reps
+        out.update(pack_ms_per_layer=round(1e3 * pack_s, 2), pack_GBps=round(4 * params / pack_s / 1e9, 1))
+    src = None if tr.direct else tr.gslab[0].ptr
     step_t = tr.t + 1
     t = time.perf_counter()
     for i in range(reps):
-        call("mt_step", tr.store.ptr, 0, slab.ptr, ctypes.byref(tr.madam), step_t + i, None)
+        call("mt_step", tr.store.ptr, 0, src, ctypes.byref(tr.madam), step_t + i, None)
     adam_s = (time.perf_counter() - t) / reps
-    adam_b = 24 + (6 if master else 0)  # a master copy: fp32 weight read instead of bf16, fp32 write
-    return {"threads": len(os.sched_getaffinity(0)), "pack_ms_per_layer": round(1e3 * pack_s, 2),
-            "pack_GBps": round(4 * params / pack_s / 1e9, 1), "adam_ms_per_layer": round(1e3 * adam_s, 2),
-            "adam_GBps": round(adam_b * params / adam_s / 1e9, 1)}
+    # a master copy: fp32 weight read instead of bf16, fp32 write
+    adam_b = (22 if tr.direct else 24) + (6 if master else 0)
+    out.update(adam_ms_per_layer=round(1e3 * adam_s, 2), adam_GBps=round(adam_b * params / adam_s / 1e9, 1))
+    return out
 
 
 def link_probe(tr, nbytes=1 << 30, reps=3):
@@ -242,6 +247,9 @@ def main():
     ap.add_argument("--mode", default="streamed", choices=["streamed", "resident"])
     ap.add_argument("--slots", type=int, default=2)
     ap.add_argument("--grad-slabs", type=int, default=16)
+    ap.add_argument("--pinned-store", action="store_true",
+                    help="page-lock the store's W and G regions and copy weights and gradients directly (no packer "
+                         "copy, no gradient slabs); default: the pageable store with the packer and slabs")
     ap.add_argument("--ckpt-every", type=int, default=None, help="override the workload's checkpoint interval")
     ap.add_argument("--micro-batches", type=int, default=1,
                     help="micro-batches per optimizer step (gradients accumulated on the host)")
@@ -275,7 +283,7 @@ def main():
     _lib.load()
     _lib.call("mt_set_optimizer_threads", args.adam_threads)
     tr = Trainer(cfg, adam, mode=args.mode, n_slots=args.slots, n_grad_slabs=args.grad_slabs, device="cuda:0",
-                 micro_batches=nmb, master=args.master)
+                 micro_batches=nmb, master=args.master, pinned_store=args.pinned_store)
 
     def tokens(step):
         return np.concatenate([synth.make_tokens(cfg, step * nmb + i) for i in range(nmb)], axis=0)
@@ -341,9 +349,12 @@ def main():
                                 workload_text(cfg, tr.n_slots).replace(f"{tr.n_slots} device staging slots",
                                                                        "all layers resident on the device")) +
                    (f", {nmb} micro-batches per optimizer step" if nmb > 1 else "") +
-                   (", fp32 master weights" if args.master else ""), "name": cfg.name, "global_batch": cfg.batch * nmb,
+                   (", fp32 master weights" if args.master else "") +
+                   (", host store W/G page-locked (direct copies, no packer)" if args.pinned_store else ""),
+                   "name": cfg.name, "global_batch": cfg.batch * nmb,
                    "seq_len": cfg.seq, "micro_batches": nmb, "master_fp32": bool(args.master),
                    "mode": args.mode, "slots": tr.n_slots, "ckpt_every": tr.K,
+                   "host_store": "pinned_dma" if args.pinned_store else "pageable",
                    "parallelism": "none (1 GPU)"},
         "tflops_exec": round(tflops_exec, 1), "tflops_model": round(tflops_model, 1),
         "pct_peak_exec": round(100 * tflops_exec / PEAK_BF16_TFLOPS, 2),
@@ -357,19 +368,21 @@ def main():
                      h2d_link_frac=round(h2d / (ms_step * 1e-3) / (link["h2d_GBps"] * 1e9), 4),
                      h2d_active_GBps=round(h2d / 1e9 / (overlap["h2d_busy_frac"] * overlap["step_ms"] * 1e-3), 2)),
     }
-    # host DRAM bytes of one step: every weight load is packed once (4 B per
-    # parameter), every parameter gets one Adam update (24 B), and the DMA
-    # engines read the H2D bytes from and write the D2H bytes to host memory;
-    # the floor divides them by the faster of the two measured host rates
+    # host DRAM bytes of one step: with a pageable store every weight load is
+    # packed once (4 B per parameter) and every parameter gets one Adam update
+    # that lands its gradient from a slab (24 B); with a pinned store there is
+    # no packing and Adam reads the gradient from G (22 B).  The DMA engines
+    # read the H2D bytes from and write the D2H bytes to host memory; the
+    # floor divides the sum by the faster of the measured host rates
     n_params = sum(tr.store.layout_of(u).w_bytes // 2 for u in tr.store.units)
-    # (micro-batches: each accumulation reads the slab and the accumulator and
+    # (micro-batches: each accumulation reads the gradient and the accumulator and
     # writes the accumulator, 10 B per parameter, and the final step also
     # reads the accumulator; a master copy adds 6 B: fp32 read instead of bf16, fp32 write)
-    adam_b = 24 + (4 if nmb > 1 else 0) + (6 if args.master else 0)
-    host_bytes = (nmb * (4 * (lay.w_bytes // 2) * (n_loads - 1) + 4 * (lay_h.w_bytes // 2)) + adam_b * n_params +
-                  10 * (nmb - 1) * n_params + h2d + d2h)
+    adam_b = (22 if tr.direct else 24) + (4 if nmb > 1 else 0) + (6 if args.master else 0)
+    pack_b = 0 if tr.direct else nmb * (4 * (lay.w_bytes // 2) * (n_loads - 1) + 4 * (lay_h.w_bytes // 2))
+    host_bytes = pack_b + adam_b * n_params + 10 * (nmb - 1) * n_params + h2d + d2h
     host["bytes_per_step"] = int(host_bytes)
-    host["floor_ms"] = round(1e3 * host_bytes / (max(host["pack_GBps"], host["adam_GBps"]) * 1e9), 1)
+    host["floor_ms"] = round(1e3 * host_bytes / (max(host["pack_GBps"] or 0, host["adam_GBps"]) * 1e9), 1)
     host["floor_frac_of_step"] = round(host["floor_ms"] / ms_step, 3)
     out["host"] = host
     tr.close()

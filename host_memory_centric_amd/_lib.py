@@ -17,6 +17,7 @@ MT_UNIT_EMBED = -1
 MT_UNIT_HEAD = -2
 MT_STORE_MASTER_FP32 = 1
 MT_STORE_GRAD_ACCUM = 2
+MT_STORE_PINNED_DMA = 4
 ERRORS = {-1: "MT_E_ARG", -2: "MT_E_SHAPE", -3: "MT_E_ALIGN", -4: "MT_E_NOMEM", -5: "MT_E_HIP", -6: "MT_E_STATE"}
 
 
@@ -73,6 +74,7 @@ _SIGS = {
     "mt_store_save": [c_void_p, ctypes.c_char_p, c_int64],
     "mt_store_load": [c_void_p, ctypes.c_char_p, POINTER(c_int64)],
     "mt_store_block": [c_void_p, c_int, POINTER(c_void_p)],
+    "mt_store_region": [c_void_p, c_int, c_int, POINTER(c_void_p)],
     "mt_store_bytes": [c_void_p, POINTER(c_uint64)],
     "mt_store_fill_normal": [c_void_p, c_uint32, c_double],
     "mt_set_threads": [c_int],

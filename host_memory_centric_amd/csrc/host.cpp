@@ -63,8 +63,8 @@ void check_cfg(const mt_model_cfg* cfg) {
 
 mt_unit_layout layout_of(const mt_model_cfg* cfg, int unit, uint32_t flags) {
     check_cfg(cfg);
-    MT_CHECK_ARG((flags & ~(uint32_t)(MT_STORE_MASTER_FP32 | MT_STORE_GRAD_ACCUM)) == 0, "unknown store flags %u",
-                 flags);
+    MT_CHECK_ARG((flags & ~(uint32_t)(MT_STORE_MASTER_FP32 | MT_STORE_GRAD_ACCUM | MT_STORE_PINNED_DMA)) == 0,
+                 "unknown store flags %u", flags);
     mt_unit_layout L;
     memset(&L, 0, sizeof(L));
     const uint64_t h = cfg->hidden, f = cfg->ffn, V = cfg->vocab;
@@ -194,11 +194,16 @@ static void par_memcpy(void* dst, const void* src, uint64_t bytes) {
 // ---------------------------------------------------------------------------
 }  // namespace mt
 
+// Each unit's block is held as two segments: [W | G], the part the DMA
+// engines read and write, and [M | V | P | A], the optimizer's part.  In a
+// pageable store both lie in one mapping (seg1 = seg0 + region_off[2]); with
+// MT_STORE_PINNED_DMA the first is page-locked (hipHostMalloc) and the second
+// a separate pageable mapping.  Index: unit + 2 (embed, head, layers...).
 struct mt_store {
     mt_model_cfg cfg;
-    uint32_t flags = 0;                  // MT_STORE_* regions present
-    std::vector<void*> blocks;           // index: unit + 2 (embed, head, layers...)
-    std::vector<uint64_t> mapped_bytes;  // mmap lengths
+    uint32_t flags = 0;                  // MT_STORE_* flags
+    std::vector<char*> seg0, seg1;
+    std::vector<uint64_t> mapped_bytes;  // mmap length of each unit's pageable mapping
     std::vector<mt_unit_layout> layouts;
     std::vector<int64_t> n_accum;        // micro-batch gradients in A since the unit's last step
 };
@@ -209,6 +214,12 @@ static int unit_index(const mt_store* st, int unit) {
     MT_CHECK_ARG(st != nullptr, "store is NULL");
     MT_CHECK_ARG(unit >= MT_UNIT_HEAD && unit < st->cfg.layers, "unit %d out of range", unit);
     return unit + 2;
+}
+
+// Address of region r (0..5: W, G, M, V, P, A) of the unit at index idx.
+static char* region_ptr(const mt_store* st, size_t idx, int r) {
+    const mt_unit_layout& L = st->layouts[idx];
+    return r < 2 ? st->seg0[idx] + L.region_off[r] : st->seg1[idx] + (L.region_off[r] - L.region_off[2]);
 }
 
 static void* map_block(uint64_t bytes) {
@@ -452,11 +463,10 @@ static bool have_avx512() {
 
 // P = fp32(W) for every unit of a master-weight store
 static void sync_master(mt_store* st) {
-    for (size_t idx = 0; idx < st->blocks.size(); ++idx) {
+    for (size_t idx = 0; idx < st->layouts.size(); ++idx) {
         const mt_unit_layout& L = st->layouts[idx];
-        const char* blk = (const char*)st->blocks[idx];
-        const uint16_t* W = (const uint16_t*)(blk + L.region_off[0]);
-        float* P = (float*)((char*)st->blocks[idx] + L.region_off[4]);
+        const uint16_t* W = (const uint16_t*)region_ptr(st, idx, 0);
+        float* P = (float*)region_ptr(st, idx, 4);
         parallel_for(L.w_bytes / 2, 1 << 20, [&](uint64_t b, uint64_t e) {
             for (uint64_t i = b; i < e; ++i) P[i] = bf16_to_f32(W[i]);
         });
@@ -498,25 +508,28 @@ void io_all(int fd, char* buf, uint64_t n, uint64_t off, const char* path) {
     }
 }
 
-// Transfers every block to/from the file after the header, in 64 MB chunks
-// spread over the worker threads.
+// Transfers every block to/from the file after the header (blocks in unit
+// order, each in its layout's byte order whatever the store's segments), in
+// chunks of at most 64 MB spread over the worker threads.
 template <bool WRITE>
 void io_blocks(mt_store* st, int fd, const char* path) {
-    std::vector<std::pair<uint64_t, uint64_t>> jobs;  // (block index, offset in block)
-    for (size_t i = 0; i < st->blocks.size(); ++i)
-        for (uint64_t o = 0; o < st->layouts[i].block_bytes; o += kIoChunk) jobs.emplace_back(i, o);
-    std::vector<uint64_t> base(st->blocks.size());
+    struct Job {
+        char* mem;
+        uint64_t n, file_off;
+    };
+    std::vector<Job> jobs;
     uint64_t pos = sizeof(CkptHeader);
-    for (size_t i = 0; i < st->blocks.size(); ++i) {
-        base[i] = pos;
-        pos += st->layouts[i].block_bytes;
+    for (size_t i = 0; i < st->layouts.size(); ++i) {
+        const mt_unit_layout& L = st->layouts[i];
+        const uint64_t seg_lo[2] = {0, L.region_off[2]}, seg_hi[2] = {L.region_off[2], L.block_bytes};
+        char* seg[2] = {st->seg0[i], st->seg1[i]};
+        for (int k = 0; k < 2; ++k)
+            for (uint64_t o = seg_lo[k]; o < seg_hi[k]; o += kIoChunk)
+                jobs.push_back({seg[k] + (o - seg_lo[k]), std::min(kIoChunk, seg_hi[k] - o), pos + o});
+        pos += L.block_bytes;
     }
     parallel_for(jobs.size(), 1, [&](uint64_t b, uint64_t e) {
-        for (uint64_t j = b; j < e; ++j) {
-            const auto [i, o] = jobs[j];
-            const uint64_t n = std::min(kIoChunk, st->layouts[i].block_bytes - o);
-            io_all<WRITE>(fd, (char*)st->blocks[i] + o, n, base[i] + o, path);
-        }
+        for (uint64_t j = b; j < e; ++j) io_all<WRITE>(fd, jobs[j].mem, jobs[j].n, jobs[j].file_off, path);
     });
 }
 
@@ -566,14 +579,33 @@ int mt_store_create_ex(const mt_model_cfg* cfg, uint32_t flags, mt_store** out) 
         auto* st = new mt_store();
         st->cfg = *cfg;
         st->flags = flags;
+        const bool pinned = flags & MT_STORE_PINNED_DMA;
         try {
             for (int u = MT_UNIT_HEAD; u < cfg->layers; ++u) {
                 mt_unit_layout L = layout_of(cfg, u, flags);
-                const uint64_t len = round_up(L.block_bytes, 2ull << 20);
+                const uint64_t dma = L.region_off[2];  // [W | G]
+                const uint64_t len = round_up(pinned ? L.block_bytes - dma : L.block_bytes, 2ull << 20);
                 st->layouts.push_back(L);
-                st->blocks.push_back(map_block(len));
-                st->mapped_bytes.push_back(len);
+                st->seg0.push_back(nullptr);
+                st->seg1.push_back(nullptr);
+                st->mapped_bytes.push_back(0);
                 st->n_accum.push_back(0);
+                char* m = (char*)map_block(len);
+                st->mapped_bytes.back() = len;
+                if (pinned) {
+                    st->seg1.back() = m;
+                    void* p = nullptr;
+                    const hipError_t e = hipHostMalloc(&p, dma, hipHostMallocDefault);
+                    if (e != hipSuccess)
+                        MT_FAIL(e == hipErrorOutOfMemory ? MT_E_NOMEM : MT_E_HIP,
+                                "page-locking the W and G regions of unit %d (%llu bytes): %s", u,
+                                (unsigned long long)dma, hipGetErrorString(e));
+                    st->seg0.back() = (char*)p;
+                    parallel_for(dma, 8ull << 20, [&](uint64_t b, uint64_t e2) { memset((char*)p + b, 0, e2 - b); });
+                } else {
+                    st->seg0.back() = m;
+                    st->seg1.back() = m + dma;
+                }
             }
         } catch (...) {
             mt_store_destroy(st);
@@ -585,15 +617,36 @@ int mt_store_create_ex(const mt_model_cfg* cfg, uint32_t flags, mt_store** out) 
 
 void mt_store_destroy(mt_store* st) {
     if (!st) return;
-    for (size_t i = 0; i < st->blocks.size(); ++i)
-        if (st->blocks[i]) munmap(st->blocks[i], st->mapped_bytes[i]);
+    const bool pinned = st->flags & MT_STORE_PINNED_DMA;
+    for (size_t i = 0; i < st->layouts.size(); ++i) {
+        if (pinned) {
+            if (st->seg0[i]) (void)hipHostFree(st->seg0[i]);
+            if (st->seg1[i]) munmap(st->seg1[i], st->mapped_bytes[i]);
+        } else if (st->seg0[i]) {
+            munmap(st->seg0[i], st->mapped_bytes[i]);
+        }
+    }
     delete st;
 }
 
 int mt_store_block(mt_store* st, int unit, void** block) {
     return guard([&] {
         MT_CHECK_ARG(block != nullptr, "block is NULL");
-        *block = st->blocks[unit_index(st, unit)];
+        const int idx = unit_index(st, unit);
+        if (st->flags & MT_STORE_PINNED_DMA)
+            MT_FAIL(MT_E_STATE, "a pinned-DMA store has no contiguous block; address regions with mt_store_region");
+        *block = st->seg0[idx];
+    });
+}
+
+int mt_store_region(mt_store* st, int unit, int region, void** ptr) {
+    return guard([&] {
+        MT_CHECK_ARG(ptr != nullptr, "ptr is NULL");
+        const int idx = unit_index(st, unit);
+        MT_CHECK_ARG(region >= 0 && region < 6, "region %d out of range", region);
+        if (st->layouts[idx].region_bytes[region] == 0)
+            MT_FAIL(MT_E_STATE, "region %d is not present in this store", region);
+        *ptr = region_ptr(st, idx, region);
     });
 }
 
@@ -613,11 +666,14 @@ int mt_store_fill_normal(mt_store* st, uint32_t seed, double std_) {
         for (int u = MT_UNIT_HEAD; u < st->cfg.layers; ++u) {
             const int idx = unit_index(st, u);
             const mt_unit_layout& L = st->layouts[idx];
-            char* blk = (char*)st->blocks[idx];
             // zero every region first (first touch happens here, in parallel)
-            parallel_for(L.block_bytes, 8ull << 20, [&](uint64_t b, uint64_t e) { memset(blk + b, 0, e - b); });
+            const uint64_t dma = L.region_off[2];
+            parallel_for(dma, 8ull << 20, [&](uint64_t b, uint64_t e) { memset(st->seg0[idx] + b, 0, e - b); });
+            parallel_for(L.block_bytes - dma, 8ull << 20,
+                         [&](uint64_t b, uint64_t e) { memset(st->seg1[idx] + b, 0, e - b); });
+            char* w = region_ptr(st, idx, 0);
             for (int j = 0; j < L.n_tensors; ++j) {
-                uint16_t* t = (uint16_t*)(blk + L.tensor_off[j]);
+                uint16_t* t = (uint16_t*)(w + L.tensor_off[j]);
                 const uint64_t n = L.tensor_numel[j];
                 const bool gain = (u >= 0 && (j == 0 || j == 3)) || (u == MT_UNIT_HEAD && j == 0);
                 if (gain) {
@@ -646,9 +702,8 @@ int mt_grad_accumulate(mt_store* st, int unit, const void* grad_src) {
         const int idx = unit_index(st, unit);
         if (!(st->flags & MT_STORE_GRAD_ACCUM)) MT_FAIL(MT_E_STATE, "the store has no gradient accumulator");
         const mt_unit_layout& L = st->layouts[idx];
-        char* blk = (char*)st->blocks[idx];
-        float* A = (float*)(blk + L.region_off[5]);
-        const uint16_t* src = grad_src ? (const uint16_t*)grad_src : (const uint16_t*)(blk + L.region_off[1]);
+        float* A = (float*)region_ptr(st, idx, 5);
+        const uint16_t* src = grad_src ? (const uint16_t*)grad_src : (const uint16_t*)region_ptr(st, idx, 1);
         const bool first = st->n_accum[idx] == 0;
         const bool simd = have_avx512();
         parallel_for(L.w_bytes / 2, 1 << 18, [&](uint64_t b, uint64_t e) {
@@ -672,10 +727,10 @@ int mt_store_save(const mt_store* cst, const char* path, int64_t t) {
         memset(&h, 0, sizeof(h));
         memcpy(h.magic, "MTSTORE1", 8);
         h.version = 1;
-        h.flags = st->flags;
+        h.flags = st->flags & ~(uint32_t)MT_STORE_PINNED_DMA;  // placement is not part of the format
         h.cfg = st->cfg;
         h.t = t;
-        h.n_units = st->blocks.size();
+        h.n_units = st->layouts.size();
         for (auto& L : st->layouts) h.total_bytes += L.block_bytes;
         io_all<true>(f.fd, (char*)&h, sizeof(h), 0, path);
         io_blocks<true>(st, f.fd, path);
@@ -695,8 +750,8 @@ int mt_store_load(mt_store* st, const char* path, int64_t* t_out) {
         for (auto& L : st->layouts) total += L.block_bytes;
         if (memcmp(h.magic, "MTSTORE1", 8) != 0 || h.version != 1)
             MT_FAIL(MT_E_ARG, "%s is not a store checkpoint", path);
-        if (memcmp(&h.cfg, &st->cfg, sizeof(mt_model_cfg)) != 0 || h.flags != st->flags ||
-            h.n_units != st->blocks.size() || h.total_bytes != total)
+        if (memcmp(&h.cfg, &st->cfg, sizeof(mt_model_cfg)) != 0 || h.flags != (st->flags & ~(uint32_t)MT_STORE_PINNED_DMA) ||
+            h.n_units != st->layouts.size() || h.total_bytes != total)
             MT_FAIL(MT_E_ARG, "%s was written for another model config or store flags", path);
         io_blocks<false>(st, f.fd, path);
         io_all<false>(f.fd, (char*)st->n_accum.data(), 8 * st->n_accum.size(), sizeof(h) + total, path);
@@ -711,7 +766,7 @@ int mt_pack_layer(mt_store* st, int unit, void* dst, size_t dst_bytes) {
         MT_CHECK_ARG(dst != nullptr, "dst is NULL");
         MT_CHECK_ARG(dst_bytes >= L.w_bytes, "dst holds %zu bytes, unit needs %llu", dst_bytes,
                      (unsigned long long)L.w_bytes);
-        par_memcpy(dst, (const char*)st->blocks[idx] + L.region_off[0], L.w_bytes);
+        par_memcpy(dst, region_ptr(st, idx, 0), L.w_bytes);
     });
 }
 
@@ -725,8 +780,8 @@ int mt_pack_head_tied(mt_store* st, void* dst, size_t dst_bytes) {
         MT_CHECK_ARG(dst_bytes >= D.w_bytes, "dst holds %zu bytes, the head slot needs %llu", dst_bytes,
                      (unsigned long long)D.w_bytes);
         const int hi = unit_index(st, MT_UNIT_HEAD), ei = unit_index(st, MT_UNIT_EMBED);
-        const char* hw = (const char*)st->blocks[hi] + st->layouts[hi].region_off[0];
-        const char* ew = (const char*)st->blocks[ei] + st->layouts[ei].region_off[0];
+        const char* hw = region_ptr(st, hi, 0);
+        const char* ew = region_ptr(st, ei, 0);
         memset(dst, 0, D.tensor_off[1]);                                   // gain and its padding
         memcpy((char*)dst, hw, 2 * D.tensor_numel[0]);                     // final gain
         par_memcpy((char*)dst + D.tensor_off[1], ew, 2 * D.tensor_numel[1]);  // E as the LM head
@@ -771,18 +826,17 @@ int mt_step(mt_store* st, int unit, const void* grad_src, const mt_adam_cfg* ada
         MT_CHECK_ARG(adam != nullptr, "adam is NULL");
         MT_CHECK_ARG(t >= 1, "step counter must be >= 1");
         const mt_unit_layout& L = st->layouts[idx];
-        char* blk = (char*)st->blocks[idx];
-        uint16_t* W = (uint16_t*)(blk + L.region_off[0]);
-        uint16_t* G = (uint16_t*)(blk + L.region_off[1]);
-        float* M = (float*)(blk + L.region_off[2]);
-        float* Vv = (float*)(blk + L.region_off[3]);
+        uint16_t* W = (uint16_t*)region_ptr(st, idx, 0);
+        uint16_t* G = (uint16_t*)region_ptr(st, idx, 1);
+        float* M = (float*)region_ptr(st, idx, 2);
+        float* Vv = (float*)region_ptr(st, idx, 3);
         const AdamK k = adam_consts(adam, t);
         const uint64_t n = L.w_bytes / 2;
         const uint16_t* src = (const uint16_t*)grad_src;
         const bool simd = have_avx512();
-        float* P = (st->flags & MT_STORE_MASTER_FP32) ? (float*)(blk + L.region_off[4]) : nullptr;
+        float* P = (st->flags & MT_STORE_MASTER_FP32) ? (float*)region_ptr(st, idx, 4) : nullptr;
         const int64_t k_acc = st->n_accum[idx];
-        const float* A = k_acc > 0 ? (const float*)(blk + L.region_off[5]) : nullptr;
+        const float* A = k_acc > 0 ? (const float*)region_ptr(st, idx, 5) : nullptr;
         if (!P && !A) {
             parallel_for(n, 1 << 18, [&](uint64_t b, uint64_t e) {
                 if (simd)
@@ -808,7 +862,7 @@ int mt_embed_gather(mt_store* st, const int32_t* tok, int64_t T, void* dst) {
         const int idx = unit_index(st, MT_UNIT_EMBED);
         MT_CHECK_ARG(tok && dst && T >= 0, "bad arguments");
         const uint64_t h = st->cfg.hidden;
-        const uint16_t* E = (const uint16_t*)((const char*)st->blocks[idx] + st->layouts[idx].region_off[0]);
+        const uint16_t* E = (const uint16_t*)region_ptr(st, idx, 0);
         for (int64_t t = 0; t < T; ++t)
             MT_CHECK_ARG(tok[t] >= 0 && tok[t] < st->cfg.vocab, "token %d at %lld out of range", tok[t],
                          (long long)t);
@@ -826,7 +880,7 @@ static void embed_grad_rows(mt_store* st, const int32_t* tok, int64_t T, const f
     const uint64_t h = st->cfg.hidden, V = st->cfg.vocab;
     for (int64_t t = 0; t < T; ++t)
         MT_CHECK_ARG(tok[t] >= 0 && tok[t] < st->cfg.vocab, "token out of range");
-    uint16_t* G = (uint16_t*)((char*)st->blocks[idx] + st->layouts[idx].region_off[1]);
+    uint16_t* G = (uint16_t*)region_ptr(st, idx, 1);
     // Positions grouped by token id, ascending position inside a group (a
     // stable counting sort), then one fp32 row sum per token.
     std::vector<int64_t> start(V + 1, 0), pos(T);

@@ -201,10 +201,16 @@ class Trainer:
     rounding (``self.w32[unit]``, W-region indexing) for parity checks;
     micro_batches: micro-batches of [batch, seq] tokens per step, whose
     gradients the host accumulates (``mt_grad_accumulate``) before one Adam
-    step on their mean; master: keep fp32 master weights in the host store."""
+    step on their mean; master: keep fp32 master weights in the host store;
+    pinned_store: page-lock the store's W and G regions and copy weights to
+    the device straight from W and gradients straight into G (no packer
+    copy, no gradient slabs; the packer thread only waits for each unit's
+    pending update), which removes 4 bytes per parameter of host memory
+    traffic per weight load and 2 per update."""
 
     def __init__(self, cfg, adam, mode="streamed", n_slots=2, n_grad_slabs=16, ckpt_every=None, weights=None,
-                 device="cuda:0", capture_w32=False, timeline=False, micro_batches=1, master=False):
+                 device="cuda:0", capture_w32=False, timeline=False, micro_batches=1, master=False,
+                 pinned_store=False):
         if mode not in ("streamed", "resident"):
             raise ValueError("mode must be 'streamed' or 'resident'")
         _lib.load()
@@ -221,7 +227,8 @@ class Trainer:
         self.t = 0
         self.n_micro = max(1, int(micro_batches))
 
-        self.store = HostStore(cfg, master=master, accum=self.n_micro > 1)
+        self.direct = bool(pinned_store)
+        self.store = HostStore(cfg, master=master, accum=self.n_micro > 1, pinned=self.direct)
         if weights is None:
             self.store.fill_normal()
         else:
@@ -268,9 +275,20 @@ class Trainer:
         self.tok_dev = torch.empty((self.B, self.S), dtype=torch.int32, device=d)
         self.loss_dev = torch.zeros(1, dtype=f32, device=d)
 
-        self.wslab = [PinnedBuffer(self.slot_bytes) for _ in range(2)]
-        self.gslab = [PinnedBuffer(self.lay.w_bytes) for _ in range(max(1, n_grad_slabs))]
-        self.head_gslab = PinnedBuffer(self.lay_head_dev.w_bytes)
+        # staging: packed weights and landed gradients pass through pinned
+        # slabs, unless the store's own W and G regions are pinned (the tied
+        # head's gradient still goes through its slab: it updates two units)
+        n_wslab, n_gslab = (0, 0) if self.direct else (2, max(1, n_grad_slabs))
+        self.wslab = [PinnedBuffer(self.slot_bytes) for _ in range(n_wslab)]
+        self.gslab = [PinnedBuffer(self.lay.w_bytes) for _ in range(n_gslab)]
+        self.head_gslab = PinnedBuffer(self.lay_head_dev.w_bytes) if (self.tied or not self.direct) else None
+        if self.direct and self.tied:  # the head slot is filled from two W regions
+            off = self.lay_head_dev.tensor_off[1]
+            if (self.store.layout_of(MT_UNIT_HEAD).w_bytes != off or
+                    self.store.layout_of(MT_UNIT_EMBED).w_bytes != self.lay_head_dev.w_bytes - off):
+                raise RuntimeError("tied head slot does not match the gain and embedding W regions")
+        self.w_addr = {u: ctypes.c_void_p(self.store.region_addr(u, 0)) for u in self.store.units}
+        self.g_addr = {u: ctypes.c_void_p(self.store.region_addr(u, 1)) for u in self.store.units}
         self.x0_pin = PinnedBuffer(T * h * 2)
         self.dx0_pin = PinnedBuffer(T * h * 4)
         self.tok_pin = PinnedBuffer(T * 4)
@@ -338,7 +356,8 @@ class Trainer:
             self.packer.shutdown(wait=True)
             self.optimizer.shutdown()
         for b in self.wslab + self.gslab + [self.head_gslab, self.x0_pin, self.dx0_pin, self.tok_pin]:
-            b.free()
+            if b is not None:
+                b.free()
         self.store.close()
 
     def n_weight_loads(self):
@@ -434,9 +453,14 @@ class Trainer:
         pending = dict(self.pending)  # updates of the previous step still running
 
         def pack(j):
+            unit = self.op_unit[loads[j]]
+            if self.direct:  # the copy reads the store itself: only wait for the update
+                f = pending.get(unit)
+                if f is not None:
+                    f.result()
+                return
             if j >= 2:
                 ready_ev[j - 2].synchronize()  # the copy that read this staging buffer is done
-            unit = self.op_unit[loads[j]]
             f = pending.get(unit)
             if f is not None:
                 f.result()  # the unit's update of the previous step has landed
@@ -458,7 +482,17 @@ class Trainer:
                     hs.wait_event(op_done[slot_prev[i]])  # buffer-free
                 if tl is not None:
                     tl["h2d"].append([self._ev(hs), ready_ev[j]])
-                call("mt_copy_h2d", _ptr(self.slots[self.op_slot[i]]), self.wslab[j % 2].ptr, nbytes, sh)
+                dst = _ptr(self.slots[self.op_slot[i]])
+                if not self.direct:
+                    call("mt_copy_h2d", dst, self.wslab[j % 2].ptr, nbytes, sh)
+                elif unit == MT_UNIT_HEAD and self.tied:  # [final gain | embedding matrix as the LM head]
+                    lh = self.store.layout_of(MT_UNIT_HEAD)
+                    off = self.lay_head_dev.tensor_off[1]
+                    call("mt_copy_h2d", dst, self.w_addr[MT_UNIT_HEAD], lh.w_bytes, sh)
+                    call("mt_copy_h2d", ctypes.c_void_p(dst.value + off), self.w_addr[MT_UNIT_EMBED],
+                         nbytes - off, sh)
+                else:
+                    call("mt_copy_h2d", dst, self.w_addr[unit], nbytes, sh)
                 ready_ev[j].record(hs)  # weights-ready
             if j + 2 < len(loads):
                 pack_fut[j + 2] = self.packer.submit(pack, j + 2)
@@ -481,16 +515,17 @@ class Trainer:
         cur = 0
         n_bwd = 0
 
-        def adam_layer(ev, unit, slab):
+        def adam_layer(ev, unit, src):
+            # src: the pinned slab holding the gradient, or None: already in G
             ev.synchronize()
             if final:
-                call("mt_step", self.store.ptr, unit, slab.ptr, ctypes.byref(self.madam), t, self._w32_ptr(unit))
+                call("mt_step", self.store.ptr, unit, src, ctypes.byref(self.madam), t, self._w32_ptr(unit))
             else:
-                call("mt_grad_accumulate", self.store.ptr, unit, slab.ptr)
+                call("mt_grad_accumulate", self.store.ptr, unit, src)
 
         def adam_layer_slab(ev, unit, k):
             try:
-                adam_layer(ev, unit, self.gslab[k])
+                adam_layer(ev, unit, self.gslab[k].ptr)
             finally:
                 slab_free.put(k)
 
@@ -563,26 +598,35 @@ class Trainer:
                 self._wait_unit(MT_UNIT_HEAD)  # the previous update still reads the head's slab
                 self._wait_acc(MT_UNIT_HEAD)   # (or the previous micro-batch's accumulation)
                 d2h = torch.cuda.Event(enable_timing=self.record_timeline)
+                head_dst = self.head_gslab.ptr if self.head_gslab is not None else self.g_addr[MT_UNIT_HEAD]
                 with torch.cuda.stream(ds):
                     ds.wait_event(ev)
                     if tl is not None:
                         tl["d2h"].append([self._ev(ds), d2h])
-                    call("mt_copy_d2h", self.head_gslab.ptr, _ptr(self.head_g), self.lay_head_dev.w_bytes, sd)
+                    call("mt_copy_d2h", head_dst, _ptr(self.head_g), self.lay_head_dev.w_bytes, sd)
                     d2h.record(ds)
                 self.head_d2h = d2h
-                jobs[MT_UNIT_HEAD] = self.optimizer.submit(self._urgency(MT_UNIT_HEAD), d2h, adam_layer, d2h,
-                                                           MT_UNIT_HEAD, self.head_gslab)
+                jobs[MT_UNIT_HEAD] = self.optimizer.submit(
+                    self._urgency(MT_UNIT_HEAD), d2h, adam_layer, d2h, MT_UNIT_HEAD,
+                    self.head_gslab.ptr if self.head_gslab is not None else None)
             elif kind == "bwd":
                 g = n_bwd % 2
                 n_bwd += 1
-                k = slab_free.get()
                 self._wait_unit(l)  # (finished long ago: the previous step's update of this layer)
+                if self.direct:
+                    # G is the copy's destination: the previous micro-batch's
+                    # accumulation (long finished) must have read it
+                    self._wait_acc(l)
+                    k, g_dst = None, self.g_addr[l]
+                else:
+                    k = slab_free.get()
+                    g_dst = self.gslab[k].ptr
                 d2h = torch.cuda.Event(enable_timing=self.record_timeline)
                 with torch.cuda.stream(ds):
                     ds.wait_event(ev)
                     if tl is not None:
                         tl["d2h"].append([self._ev(ds), d2h])
-                    call("mt_copy_d2h", self.gslab[k].ptr, _ptr(self.gslots[g]), self.lay.w_bytes, sd)
+                    call("mt_copy_d2h", g_dst, _ptr(self.gslots[g]), self.lay.w_bytes, sd)
                     d2h.record(ds)
                     if l == 0:
                         d2h_x = torch.cuda.Event(enable_timing=self.record_timeline)
@@ -591,7 +635,10 @@ class Trainer:
                         call("mt_copy_d2h", self.dx0_pin.ptr, _ptr(self.dgrad[cur]), self.T * h * 4, sd)
                         d2h_x.record(ds)
                 gslot_d2h[g] = d2h
-                jobs[l] = self.optimizer.submit(self._urgency(l), d2h, adam_layer_slab, d2h, l, k)
+                if k is None:
+                    jobs[l] = self.optimizer.submit(self._urgency(l), d2h, adam_layer, d2h, l, None)
+                else:
+                    jobs[l] = self.optimizer.submit(self._urgency(l), d2h, adam_layer_slab, d2h, l, k)
                 if l == 0:
                     jobs[MT_UNIT_EMBED] = self.optimizer.submit(self._urgency(MT_UNIT_EMBED), d2h_x, adam_embed, d2h_x)
             issue_ready_loads(i)

@@ -8,8 +8,8 @@ import ctypes
 
 import numpy as np
 
-from ._lib import (MT_STORE_GRAD_ACCUM, MT_STORE_MASTER_FP32, MT_UNIT_EMBED, MT_UNIT_HEAD, call, load, model_cfg,
-                   unit_layout)
+from ._lib import (MT_STORE_GRAD_ACCUM, MT_STORE_MASTER_FP32, MT_STORE_PINNED_DMA, MT_UNIT_EMBED, MT_UNIT_HEAD, call,
+                   load, model_cfg, unit_layout)
 
 REGION_W, REGION_G, REGION_M, REGION_V, REGION_P, REGION_A = 0, 1, 2, 3, 4, 5
 LAYER_TENSORS = ("g_attn", "wqkv", "wo", "g_mlp", "wgu", "wd")
@@ -27,13 +27,17 @@ def tensor_shapes(cfg, unit):
 
 class HostStore:
     """master: keep fp32 master weights (region P); accum: keep an fp32
-    gradient accumulator for micro-batches (region A)."""
+    gradient accumulator for micro-batches (region A); pinned: page-lock the
+    W and G regions so that the DMA engines read weights from and write
+    gradients to the store itself (needs a HIP device)."""
 
-    def __init__(self, cfg, master=False, accum=False):
+    def __init__(self, cfg, master=False, accum=False, pinned=False):
         load()
         self.cfg = cfg
         self.mcfg = model_cfg(cfg)
-        self.flags = (MT_STORE_MASTER_FP32 if master else 0) | (MT_STORE_GRAD_ACCUM if accum else 0)
+        self.flags = ((MT_STORE_MASTER_FP32 if master else 0) | (MT_STORE_GRAD_ACCUM if accum else 0)
+                      | (MT_STORE_PINNED_DMA if pinned else 0))
+        self.pinned = bool(pinned)
         p = ctypes.c_void_p()
         call("mt_store_create_ex", ctypes.byref(self.mcfg), self.flags, ctypes.byref(p))
         self.ptr = p
@@ -60,8 +64,14 @@ class HostStore:
         return out.value
 
     def block_addr(self, unit):
+        """Base address of a unit's block (pageable stores only)."""
         p = ctypes.c_void_p()
         call("mt_store_block", self.ptr, unit, ctypes.byref(p))
+        return p.value
+
+    def region_addr(self, unit, r):
+        p = ctypes.c_void_p()
+        call("mt_store_region", self.ptr, unit, r, ctypes.byref(p))
         return p.value
 
     def region(self, unit, r):
@@ -71,7 +81,7 @@ class HostStore:
             raise ValueError(f"the store has no region {r}")
         n = L.w_bytes // 2
         dt = np.uint16 if r in (REGION_W, REGION_G) else np.float32
-        addr = self.block_addr(unit) + L.region_off[r]
+        addr = self.region_addr(unit, r)
         buf = (ctypes.c_char * (n * np.dtype(dt).itemsize)).from_address(addr)
         return np.frombuffer(buf, dtype=dt, count=n)
 

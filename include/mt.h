@@ -92,7 +92,16 @@ typedef struct mt_unit_layout {
  * makes it 16 and keeps updates smaller than half a bf16 ulp of a weight.) */
 enum {
     MT_STORE_MASTER_FP32 = 1, /* fp32 master weights P: Adam updates P, W = bf16(P) */
-    MT_STORE_GRAD_ACCUM = 2   /* fp32 accumulator A for gradient accumulation over micro-batches */
+    MT_STORE_GRAD_ACCUM = 2,  /* fp32 accumulator A for gradient accumulation over micro-batches */
+    /* Placement only (the layout is unchanged): each unit's W and G regions
+     * are page-locked (hipHostMalloc), so weight loads can be copied to the
+     * device straight from W and gradients straight into G, with no staging
+     * copy through host memory; M, V, P and A stay pageable.  Needs a HIP
+     * device; page-locked memory is a limited resource (MT_E_NOMEM when the
+     * system refuses).  A layer of the method's format moves through host
+     * DRAM once per transfer instead of three times (paper page, appendix
+     * A.1 stages every load through pinned buffers). */
+    MT_STORE_PINNED_DMA = 4
 };
 
 /* Pure function: the layout of `unit` in a store with the given flags
@@ -109,12 +118,18 @@ typedef struct mt_store mt_store;
 /* Allocates one page-aligned, zero-filled block per unit (pageable memory;
  * 2 MB huge pages are requested).  Owned by the library; free with
  * mt_store_destroy.  mt_store_create_ex adds the optional regions of `flags`
- * (MT_STORE_*; mt_store_create: none). */
+ * (MT_STORE_*; mt_store_create: none); with MT_STORE_PINNED_DMA each block
+ * is held as two allocations, [W | G] page-locked and [M | V | P | A]
+ * pageable, and regions are addressed with mt_store_region. */
 int mt_store_create(const mt_model_cfg* cfg, mt_store** out);
 int mt_store_create_ex(const mt_model_cfg* cfg, uint32_t flags, mt_store** out);
 void mt_store_destroy(mt_store* st);
-/* Base address of a unit's block (layout as mt_unit_layout_get). */
+/* Base address of a unit's block (layout as mt_unit_layout_get); MT_E_STATE
+ * for a MT_STORE_PINNED_DMA store, whose blocks are not contiguous. */
 int mt_store_block(mt_store* st, int unit, void** block);
+/* Address of region `region` (0..5: W, G, M, V, P, A) of a unit, for every
+ * kind of store; MT_E_STATE if the store does not hold that region. */
+int mt_store_region(mt_store* st, int unit, int region, void** ptr);
 /* Total bytes of all blocks. */
 int mt_store_bytes(const mt_store* st, uint64_t* out);
 /* Fills every W region from the seeded SplitMix64 generator: matrices
@@ -123,7 +138,7 @@ int mt_store_bytes(const mt_store* st, uint64_t* out);
  * Multithreaded.  Zeroes G, M and V. */
 int mt_store_fill_normal(mt_store* st, uint32_t seed, double std);
 /* Master-weight stores: P = fp32(W) for every unit (exact), e.g. after the
- * caller wrote W through mt_store_block (mt_store_fill_normal does this
+ * caller wrote W through mt_store_region (mt_store_fill_normal does this
  * itself).  MT_E_STATE without MT_STORE_MASTER_FP32. */
 int mt_store_sync_master(mt_store* st);
 
@@ -135,7 +150,8 @@ int mt_store_sync_master(mt_store* st);
  * every unit's whole block (embedding, head, layers 0..L-1: W, G, M, V and
  * the optional regions) and the per-unit micro-batch accumulation counts,
  * in parallel, then syncs the file.  mt_store_load reads such a file into a
- * store created with the same config and flags (MT_E_ARG otherwise) and
+ * store created with the same config and region flags (MT_E_ARG otherwise;
+ * MT_STORE_PINNED_DMA is placement, not format, and may differ) and
  * returns t; a run resumed from it continues bit-identically.  MT_E_IO on
  * I/O errors.  Neither may overlap any other call on the store. */
 int mt_store_save(const mt_store* st, const char* path, int64_t t);

@@ -435,17 +435,22 @@ def test_streamed_step_7b_shape_equals_resident(gpu):
     from host_memory_centric_amd.engine import Trainer
     cfg = synth.preset("7b", layers=8)
     runs = {}
-    for mode in ("streamed", "resident"):
-        _log(f"step 7b-shape 8 layers {mode}")
-        tr = Trainer(cfg, synth.AdamCfg(), mode=mode)
+    # the streamed run as the benchmark launches it (pageable store, packer,
+    # gradient slabs), the same with W and G page-locked and copied directly,
+    # and the resident run
+    for name, kw in (("streamed", dict(mode="streamed")), ("streamed_pinned", dict(mode="streamed", pinned_store=True)),
+                     ("resident", dict(mode="resident"))):
+        _log(f"step 7b-shape 8 layers {name}")
+        tr = Trainer(cfg, synth.AdamCfg(), **kw)
         try:
             losses = [tr.step(synth.make_tokens(cfg, s)) for s in range(2)]
-            runs[mode] = (losses, _digest(tr), tr.n_weight_loads())
+            runs[name] = (losses, _digest(tr), tr.n_weight_loads())
         finally:
             tr.close()
     (ls, ds, ns), (lr, dr, nr) = runs["streamed"], runs["resident"]
     assert ls == lr, (ls, lr)
     assert ds == dr
+    assert runs["streamed_pinned"][:2] == (ls, ds)
     assert ns > nr  # the streamed run re-loaded weights for the recompute
     # initial loss in the band of a random model: ln V plus the logits' variance
     lnV = np.log(cfg.vocab)

@@ -24,13 +24,13 @@ def _store_regions(tr):
     return {(u, r): tr.store.region(u, r).copy() for u in tr.store.units for r in regions}
 
 
-@pytest.mark.parametrize("mode", ["streamed", "resident"])
-def test_tiny_steps_match_oracle(gpu, mode):
+@pytest.mark.parametrize("mode,pinned", [("streamed", False), ("resident", False), ("streamed", True)])
+def test_tiny_steps_match_oracle(gpu, mode, pinned):
     cfg = synth.preset("tiny")
     bits = synth.make_weights(cfg)
     adam = synth.AdamCfg()
     st = oracle.HostState(bits)
-    tr = _trainer(cfg, bits, mode=mode)
+    tr = _trainer(cfg, bits, mode=mode, pinned_store=pinned)
     try:
         for step in range(2):
             tok = synth.make_tokens(cfg, step)
@@ -208,3 +208,57 @@ def test_tied_embeddings_match_oracle_and_schedules_agree(gpu):
     assert runs["resident"][0] == runs["k1_2slot"][0]
     for key, a in runs["resident"][1].items():
         assert np.array_equal(runs["k1_2slot"][1][key], a), key
+
+
+@pytest.mark.parametrize("variant", ["k1_2slot", "k2_1slot_micro_master", "tied_k1_2slot", "resident"])
+def test_pinned_store_equals_pageable_bitwise(gpu, variant, tmp_path):
+    """Copying weights straight from the page-locked W regions and gradients
+    straight into G (no packer, no slabs) changes no bit: losses and every
+    store region over three steps equal the pageable store's.  The
+    checkpoint format is the same for both placements: a pinned run saved
+    after one step and resumed in a pageable store continues identically."""
+    import dataclasses
+    cfg = synth.preset("tiny")
+    kw = {"k1_2slot": dict(ckpt_every=1, n_slots=2),
+          "k2_1slot_micro_master": dict(ckpt_every=2, n_slots=1, micro_batches=2, master=True),
+          "tied_k1_2slot": dict(ckpt_every=1, n_slots=2),
+          "resident": dict(mode="resident")}[variant]
+    if variant.startswith("tied"):
+        cfg = dataclasses.replace(cfg, tied=True)
+    bits = synth.make_weights(cfg)
+    n = kw.get("micro_batches", 1)
+
+    def toks(s):
+        return np.concatenate([synth.make_tokens(cfg, n * s + i) for i in range(n)])
+
+    runs = {}
+    for pinned in (False, True):
+        tr = _trainer(cfg, bits, pinned_store=pinned, **kw)
+        try:
+            assert tr.direct == pinned and (not pinned or not tr.wslab and not tr.gslab)
+            losses = [tr.step(toks(s)) for s in range(3)]
+            runs[pinned] = (losses, _store_regions(tr))
+        finally:
+            tr.close()
+    assert runs[True][0] == runs[False][0]
+    for key, a in runs[False][1].items():
+        assert np.array_equal(runs[True][1][key], a), key
+    if variant != "k1_2slot":
+        return
+    path = tmp_path / "pinned.ckpt"
+    b = _trainer(cfg, bits, pinned_store=True, **kw)
+    try:
+        lb = [b.step(toks(0))]
+        b.save(path)
+    finally:
+        b.close()
+    c = _trainer(cfg, bits, pinned_store=False, **kw)
+    try:
+        c.load(path)
+        lb += [c.step(toks(s)) for s in (1, 2)]
+        rc = _store_regions(c)
+    finally:
+        c.close()
+    assert lb == runs[False][0]
+    for key, a in runs[False][1].items():
+        assert np.array_equal(rc[key], a), key

@@ -265,9 +265,23 @@ def test_store_regions_and_flags(lib):
     assert both.region_off[4] == plain.block_bytes and both.region_off[5] % 4096 == 0
     assert both.block_bytes == plain.block_bytes + 2 * plain.region_bytes[2]
     with pytest.raises(MtError):
-        _lib.unit_layout(mcfg, 0, 4)
+        _lib.unit_layout(mcfg, 0, 8)
+    # the page-locking flag is placement only: the layout does not change
+    pinned = _lib.unit_layout(mcfg, 0, _lib.MT_STORE_PINNED_DMA | _lib.MT_STORE_MASTER_FP32 | _lib.MT_STORE_GRAD_ACCUM)
+    for r in range(6):
+        assert pinned.region_off[r] == both.region_off[r] and pinned.region_bytes[r] == both.region_bytes[r]
+    assert pinned.block_bytes == both.block_bytes
     st = HostStore(cfg)
     try:  # no accumulator, no master copy
+        for u in (MT_UNIT_EMBED, MT_UNIT_HEAD, 0, cfg.layers - 1):
+            L = st.layout_of(u)
+            for r in range(4):  # a pageable block is contiguous
+                assert st.region_addr(u, r) == st.block_addr(u) + L.region_off[r]
+            with pytest.raises(MtError) as e:
+                st.region_addr(u, 4)
+            assert e.value.code == -6
+        with pytest.raises(MtError):
+            st.region_addr(0, 6)
         g = np.zeros(st.layout_of(0).w_bytes // 2, np.uint16)
         with pytest.raises(MtError) as e:
             call("mt_grad_accumulate", st.ptr, 0, g.ctypes.data_as(ctypes.c_void_p))
