@@ -247,6 +247,8 @@ def main():
     ap.add_argument("--mode", default="streamed", choices=["streamed", "resident"])
     ap.add_argument("--slots", type=int, default=2)
     ap.add_argument("--grad-slabs", type=int, default=16)
+    ap.add_argument("--update-order", default="arrival", choices=["arrival", "urgent"],
+                    help="order of the host updates: as gradients arrive, or most urgent for the next step first")
     ap.add_argument("--pinned-store", action="store_true",
                     help="page-lock the store's W and G regions and copy weights and gradients directly (no packer "
                          "copy, no gradient slabs); default: the pageable store with the packer and slabs")
@@ -283,7 +285,8 @@ def main():
     _lib.load()
     _lib.call("mt_set_optimizer_threads", args.adam_threads)
     tr = Trainer(cfg, adam, mode=args.mode, n_slots=args.slots, n_grad_slabs=args.grad_slabs, device="cuda:0",
-                 micro_batches=nmb, master=args.master, pinned_store=args.pinned_store)
+                 micro_batches=nmb, master=args.master, pinned_store=args.pinned_store,
+                 update_order=args.update_order)
 
     def tokens(step):
         return np.concatenate([synth.make_tokens(cfg, step * nmb + i) for i in range(nmb)], axis=0)
@@ -355,6 +358,7 @@ def main():
                    "seq_len": cfg.seq, "micro_batches": nmb, "master_fp32": bool(args.master),
                    "mode": args.mode, "slots": tr.n_slots, "ckpt_every": tr.K,
                    "host_store": "pinned_dma" if args.pinned_store else "pageable",
+                   "update_order": args.update_order,
                    "parallelism": "none (1 GPU)"},
         "tflops_exec": round(tflops_exec, 1), "tflops_model": round(tflops_model, 1),
         "pct_peak_exec": round(100 * tflops_exec / PEAK_BF16_TFLOPS, 2),

@@ -50,7 +50,8 @@ def test_streamed_equals_resident_bitwise(gpu):
     runs = {}
     for name, kw in {"resident": dict(mode="resident"), "k1_2slot": dict(ckpt_every=1, n_slots=2),
                      "k2_2slot": dict(ckpt_every=2, n_slots=2), "k1_3slot": dict(ckpt_every=1, n_slots=3),
-                     "k1_1slab": dict(ckpt_every=1, n_grad_slabs=1), "k1_1slot": dict(ckpt_every=1, n_slots=1)}.items():
+                     "k1_1slab": dict(ckpt_every=1, n_grad_slabs=1), "k1_1slot": dict(ckpt_every=1, n_slots=1),
+                     "k2_2slot_urgent": dict(ckpt_every=2, n_slots=2, update_order="urgent")}.items():
         tr = _trainer(cfg, bits, **kw)
         try:
             losses = [tr.step(synth.make_tokens(cfg, s)) for s in range(3)]
