@@ -6,28 +6,34 @@
 //   input grad   dX[T, in]  = dY[T, out] * W[out, in]   A K-major, B N-major
 //   weight grad  dW[out,in] = dY[T, out]^T * X[T, in]   A M-major, B N-major
 //
-// Large operands (M, N >= 256, K in whole steps of 32) run gemm_pipe_kernel
-// (gemm_pipe.h): 256x256 output tiles, one workgroup of 4 waves per CU, each
-// wave 128x128 (its 256 fp32 accumulators live in the accumulation
-// registers); K advances in sub-steps of 32 through a four-slot LDS ring that
-// direct global->LDS buffer loads keep three sub-steps ahead (the depth the
-// memory latency needs at full MFMA rate; a two-slot ring of 64-wide steps
-// left the MFMAs waiting for loads), with one wait + barrier per sub-step.
-// The output tile is written through LDS as whole 512-byte rows (per-lane
-// scattered stores cost a fifth of the kernel).  Smaller operands use
-// gemm_kernel (gemm_kernel.h): 256x256 or 128x128 tiles of 8 or 4 waves and a
-// two-slot ring of 64-wide K steps, with zero-filled partial K steps.
+// Large operands (M, N >= 256, K in whole steps of 32) run gemm_pp_kernel
+// (gemm_pp.h): 256x256 output tiles, one workgroup of 8 waves per CU, each
+// wave 128x64, two waves per SIMD that take turns: one reads its fragments
+// from LDS and issues the direct global->LDS loads of a later K sub-step
+// while the other runs its MFMAs, with one workgroup barrier per phase.  K
+// advances in sub-steps of 32 through a four-slot LDS ring that the loads
+// keep three sub-steps ahead.  The output tile is written through LDS as
+// whole 512-byte rows (per-lane scattered stores cost a fifth of the kernel).
+// gemm_pipe_kernel (gemm_pipe.h; MT_GEMM_IMPL=pipe) is the earlier design of
+// the same tiles with one wave per SIMD (4 waves of 128x128) interleaving its
+// own loads, reads and MFMAs; it is 12-20 % slower on the 7B layer shapes.
+// Smaller operands use gemm_kernel (gemm_kernel.h): 256x256 or 128x128
+// tiles of 8 or 4 waves and a two-slot ring of 64-wide K steps, with
+// zero-filled partial K steps.
 //
 // Either way an operand whose contraction index is strided (the N-major
 // weight in dX, both operands of dW) is copied into LDS as it lies and read
 // with the transposing ds_read_b64_tr_b16, so no orientation needs register
 // staging.  Every output element accumulates its products in the same K order
-// in both kernels, so results do not depend on which kernel runs.  The
+// in every kernel, so results do not depend on which kernel runs.  The
 // weight-gradient GEMMs reduce over all tokens; when their tile grid is too
 // small to fill 256 CUs they split K into fixed slices whose fp32 partials
 // are summed in slice order by a second kernel: results never depend on
 // scheduling (no atomics).
-#include "gemm_pipe.h"
+#include <cstdlib>
+#include <cstring>
+
+#include "gemm_pp.h"
 
 namespace mt {
 
@@ -106,7 +112,31 @@ static void launch_pipe(const GemmDesc& d, hipStream_t s, float* part, int split
         hipLaunchKernelGGL((gemm_pipe_kernel<false, true>), grid, block, 0, s, p);
 }
 
-// The pipelined kernel needs whole 256x256 tiles inside the operands (the
+static void launch_pp(const GemmDesc& d, hipStream_t s, float* part, int splits, int64_t kps) {
+    const GemmArgs p = make_args(d, part, splits, kps, 256, 256);
+    dim3 grid(p.tiles_m * p.tiles_n, splits);
+    dim3 block(512);
+    if (d.a_kmajor && d.b_kmajor)
+        hipLaunchKernelGGL((gemm_pp_kernel<true, true>), grid, block, 0, s, p);
+    else if (d.a_kmajor && !d.b_kmajor)
+        hipLaunchKernelGGL((gemm_pp_kernel<true, false>), grid, block, 0, s, p);
+    else if (!d.a_kmajor && !d.b_kmajor)
+        hipLaunchKernelGGL((gemm_pp_kernel<false, false>), grid, block, 0, s, p);
+    else
+        hipLaunchKernelGGL((gemm_pp_kernel<false, true>), grid, block, 0, s, p);
+}
+
+// Kernel for large operands: MT_GEMM_IMPL=pipe selects the 4-wave pipelined
+// kernel, anything else the 8-wave ping-pong kernel (read once per process).
+static bool use_pp() {
+    static const bool v = [] {
+        const char* e = getenv("MT_GEMM_IMPL");
+        return !(e && strcmp(e, "pipe") == 0);
+    }();
+    return v;
+}
+
+// The large-operand kernels need whole 256x256 tiles inside the operands (the
 // last tile is moved back to the edge), K slices of whole 32-wide sub-steps,
 // and per-lane byte offsets below 2^31 (256 rows or 64 k-rows of an operand).
 static bool pipe_ok(const GemmDesc& d, int64_t kps) {
@@ -154,8 +184,10 @@ void gemm(const GemmDesc& d, hipStream_t s) {
     float* part = splits > 1 ? (float*)d.ws : nullptr;
     const ProfClass pc = d.a_kmajor ? (d.b_kmajor ? PROF_GEMM_NT : PROF_GEMM_NN) : PROF_GEMM_TN;
     ProfScope prof(pc, 2.0 * (double)d.M * (double)d.N * (double)d.K, s);
-    if (pipe_ok(d, kps))
-        launch_pipe(d, s, part, splits, kps);
+    if (pipe_ok(d, kps)) {
+        if (use_pp()) launch_pp(d, s, part, splits, kps);
+        else launch_pipe(d, s, part, splits, kps);
+    }
     else if (use_big(d.M, d.N))
         launch_tiles<256, 256, 2, 4>(d, s, part, splits, kps);
     else

@@ -130,8 +130,9 @@ struct Tile {
 // Tile order: blocks are dispatched round-robin over the 8 XCDs; give each
 // XCD a contiguous run of tiles, and walk tiles in groups of GROUP_M tile rows
 // so that concurrently running tiles share A rows and B columns in L2.
+template <int GROUP_M = 8>
 __device__ __forceinline__ void tile_coords(int bid, int nblk, int tm, int tn, int& pm, int& pn) {
-    constexpr int XCD = 8, GROUP_M = 8;
+    constexpr int XCD = 8;
     if (nblk % XCD == 0) bid = (bid % XCD) * (nblk / XCD) + bid / XCD;
     const int in_group = GROUP_M * tn;
     const int g = bid / in_group;

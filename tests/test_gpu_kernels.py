@@ -96,6 +96,55 @@ def test_gemm_split_k_exact(gpu, ak, bk):
     _run_gemm(gpu, 256, 256, 16384, ak, bk, "resid", seed=6)
 
 
+def test_gemm_large_kernels_bit_identical(gpu):
+    """The 8-wave ping-pong kernel (default) and the 4-wave pipelined kernel
+    (MT_GEMM_IMPL=pipe) accumulate every output in the same K order, so on
+    real-valued operands they give the same bits in every orientation and
+    epilogue (each run in its own process: the choice is read once)."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    code = r'''
+import ctypes, hashlib, sys
+import numpy as np, torch, synth
+from host_memory_centric_amd import _lib
+from host_memory_centric_amd._lib import call
+dev = torch.device("cuda:0")
+ws = torch.empty(64 << 20, dtype=torch.uint8, device=dev)
+st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+P = lambda t: ctypes.c_void_p(t.data_ptr()) if t is not None else None
+h = hashlib.sha256()
+# ragged tiles (moved-back edge tiles), fewer sub-steps than the ring,
+# split-K (4 tiles over K = 16384), residual and accumulate epilogues
+for i, (M, N, K, ak, bk) in enumerate([(1032, 1288, 512, 1, 1), (1288, 1032, 544, 1, 0), (776, 520, 256, 0, 0),
+                                       (520, 776, 64, 0, 1), (256, 256, 16384, 0, 0), (2048, 2304, 1024, 1, 1)]):
+    mk = lambda shape, s: torch.from_numpy(synth.f32_to_bf16_bits(
+        np.random.default_rng(s).standard_normal(shape).astype(np.float32)).view(np.int16)).to(dev)
+    A = mk((M, K) if ak else (K, M), 10 + i)
+    B = mk((N, K) if bk else (K, N), 20 + i)
+    R = mk((M, N), 30 + i)
+    cf = torch.from_numpy(np.random.default_rng(40 + i).standard_normal((M, N)).astype(np.float32)).to(dev)
+    cb = torch.zeros((M, N), dtype=torch.int16, device=dev)
+    call("mt_op_gemm", M, N, K, P(A), K if ak else M, ak, P(B), K if bk else N, bk, None, P(cb), P(R), N, 0,
+         P(ws), ws.numel(), st)
+    call("mt_op_gemm", M, N, K, P(A), K if ak else M, ak, P(B), K if bk else N, bk, P(cf), None, None, N, 1,
+         P(ws), ws.numel(), st)
+    torch.cuda.synchronize()
+    h.update(cb.cpu().numpy().tobytes())
+    h.update(cf.cpu().numpy().tobytes())
+sys.stdout.write(h.hexdigest())
+'''
+    outs = []
+    for impl in ("pp", "pipe"):
+        env = dict(os.environ, PYTHONPATH=root, MT_GEMM_IMPL=impl)
+        r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=env, cwd=root,
+                           timeout=120)
+        assert r.returncode == 0, r.stderr[-2000:]
+        outs.append(r.stdout)
+    assert len(outs[0]) == 64 and outs[0] == outs[1]
+
+
 def test_gemm_rejects_bad_shapes(gpu):
     import torch
     t = torch.zeros(64, dtype=torch.int16, device=gpu)
