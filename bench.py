@@ -61,7 +61,7 @@ def measured_traffic(kernel, workload):
         return None
     data = json.loads(m.group(1))
     csrc = os.path.join(ROOT, "host_memory_centric_amd", "csrc")
-    src = "".join(open(os.path.join(csrc, f)).read() for f in ("gemm.hip", "gemm_kernel.h", "gemm_pipe.h"))
+    src = "".join(open(os.path.join(csrc, f)).read() for f in ("gemm.hip", "gemm_kernel.h", "gemm_pipe.h", "gemm_pp.h"))
     if hashlib.sha256(src.encode()).hexdigest()[:16] != data.get("source_sha256_16"):
         return None
     k = data.get("kernels", {}).get(kernel)
