@@ -1,6 +1,9 @@
 // Causal attention on gfx950 matrix cores: tiled online-softmax forward and a
 // backward in three kernels (dV and dK over key tiles, dQ over query tiles),
-// so no gradient is ever accumulated with atomics.
+// so no gradient is ever accumulated with atomics.  The forward runs the
+// 8-wave ping-pong kernel (attn_fwd_pp_kernel: the two waves of a SIMD take
+// turns at the MFMAs and the softmax); the 4-wave software-pipelined kernel
+// (attn_fwd_kernel, MT_ATTN_FWD=pipe) gives the same bits 7-9 % slower.
 //
 // Scores are computed transposed where that keeps each query's softmax state
 // inside one lane: with S^T = K Q^T on v_mfma_f32_32x32x16_bf16 a lane owns
@@ -29,6 +32,10 @@
 // Layout: qkv is the fused projection output [B*S, 3*H] (q | k | v, head h at
 // columns h*hd .. h*hd + hd - 1 of each third), o is [B*S, H], lse is
 // [B, heads, S] natural-log row logsumexp of the scaled scores.
+#include <cstdlib>
+#include <cstring>
+#include <type_traits>
+
 #include "common.h"
 #include "device.h"
 #include "kernels.h"
@@ -122,7 +129,7 @@ __device__ __forceinline__ void zero(f32x16& a) {
 }
 
 // ---------------------------------------------------------------------------
-// forward
+// forward, 4 waves (128 queries) per workgroup
 // ---------------------------------------------------------------------------
 // Software-pipelined over key tiles: while the softmax of tile j runs on the
 // vector ALUs, the MFMAs of tile j+1's scores are already in flight.  K and V
@@ -251,6 +258,214 @@ __global__ __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(2, 
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     }
+    if (qi < S) {
+        const float inv_l = 1.0f / l_run;
+        uint16_t* orow = o + ((int64_t)b * S + qi) * H + (int64_t)head * HD;
+#pragma unroll
+        for (int dt = 0; dt < HD / 32; ++dt)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int d = dt * 32 + 8 * g + 4 * half;
+                *(uint2*)(orow + d) = make_uint2(pack_bf2(oacc[dt][4 * g] * inv_l, oacc[dt][4 * g + 1] * inv_l),
+                                                 pack_bf2(oacc[dt][4 * g + 2] * inv_l, oacc[dt][4 * g + 3] * inv_l));
+            }
+        if (half == 0) lse[(int64_t)bh * S + qi] = (m_run + log2f(l_run)) * LN2;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// forward, ping-pong: 8 waves (256 queries) per workgroup, two per SIMD.
+// ---------------------------------------------------------------------------
+// Each wave alternates an MFMA cluster M(j) (the scores of key tile j+1 and
+// O += V_j^T P_j^T) with a vector cluster V(j+1) (the softmax of tile j+1: max,
+// exp2, sum, the running rescale of O, P to bf16).  Group 1 (waves 4-7) runs
+// one phase behind group 0, with one workgroup barrier between phases, so in
+// every phase one wave of each SIMD feeds the matrix core while the other runs
+// the softmax.  Wave (g, w) owns queries 64w + 32g .. +31 of the block, so
+// both groups need about the same key tiles.
+//
+// LDS: two slots, slot t % 2 holding K_t and V_{t-1} (the operands of M(t-1)).
+// M(t-1) runs in phases 2t (group 0) and 2t+1 (group 1); the loads of slot
+// t+2 are issued by all waves at phase 2t+2 (after both groups read slot t)
+// and waited for at the end of phase 2t+3, before the first read at 2t+4.
+// Every wave runs the same loop of 2*NT+2 phases with one barrier each, so
+// the barrier sequence is the same for all waves whatever their work.
+constexpr int ATT_PP_WAVES = 8;
+constexpr int ATT_PP_THREADS = ATT_PP_WAVES * 64;
+constexpr int ATT_PP_BQ = ATT_PP_WAVES * 32;
+
+template <int HD>
+__global__ __launch_bounds__(ATT_PP_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_pp_kernel(
+    const uint16_t* __restrict__ qkv, uint16_t* __restrict__ o, float* __restrict__ lse, int S, int heads, float sl2) {
+    using TL = ATile<HD>;
+    __shared__ __attribute__((aligned(1024))) uint16_t kbuf[2][TL::ELEMS];
+    __shared__ __attribute__((aligned(1024))) uint16_t vbuf[2][TL::ELEMS];
+    const int nqb = (S + ATT_PP_BQ - 1) / ATT_PP_BQ;
+    const int qb = nqb - 1 - (int)blockIdx.x;  // most work first
+    const int bh = blockIdx.y;
+    const int b = bh / heads, head = bh % heads;
+    const int lane = threadIdx.x & 63, half = lane >> 5;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int grp = wave >> 2, w4 = wave & 3;
+    const int64_t H = (int64_t)heads * HD, ld = 3 * H;
+    const uint16_t* Qg = qkv + (int64_t)b * S * ld + (int64_t)head * HD;
+    const uint16_t* Kg = Qg + H;
+    const uint16_t* Vg = Qg + 2 * H;
+    const int q0 = qb * ATT_PP_BQ + w4 * 64 + grp * 32;
+    const int qi = q0 + (lane & 31);
+
+    uint4 qf[HD / 16];
+#pragma unroll
+    for (int ds = 0; ds < HD / 16; ++ds) {
+        qf[ds] = make_uint4(0, 0, 0, 0);
+        if (qi < S) qf[ds] = *(const uint4*)(Qg + (int64_t)qi * ld + ds * 16 + 8 * half);
+    }
+    f32x16 oacc[HD / 32];
+#pragma unroll
+    for (int dt = 0; dt < HD / 32; ++dt) zero(oacc[dt]);
+    float m_run = -INFINITY, l_run = 0.f;
+
+    const int kv_end = min(S, qb * ATT_PP_BQ + ATT_PP_BQ);
+    const int NT = (kv_end + ATT_T - 1) / ATT_T;  // key tiles of the workgroup
+    const int nk_wave = min(NT, (q0 + 31) / ATT_T + 1);  // key tiles this wave needs
+
+    // Loads of one 64-row tile (K or V) by all 8 waves: 2 (hd 128) or 1 (hd
+    // 64) direct 1 KB instructions per wave, or the register path for the
+    // last, partial tile.
+    auto load_tile = [&](const uint16_t* G, int r0, uint16_t* __restrict__ T) __attribute__((always_inline)) {
+        if (r0 + ATT_T <= S) {
+#pragma unroll
+            for (int jj = 0; jj < TL::INSTR / ATT_PP_WAVES; ++jj) {
+                const int j = wave + jj * ATT_PP_WAVES;
+                const int row = j * TL::RPI + lane / TL::CPR, pc = lane % TL::CPR;
+                const uint16_t* g = G + (int64_t)(r0 + row) * ld + 8 * (pc ^ TL::fz(row));
+                __builtin_amdgcn_global_load_lds((const void*)g, (att_lds_void*)(T + j * 512), 16, 0, 0);
+            }
+        } else {
+            for (int u = threadIdx.x; u < ATT_T * TL::CPR; u += ATT_PP_THREADS) {
+                const int row = u / TL::CPR, c = u % TL::CPR;
+                uint4 v = make_uint4(0, 0, 0, 0);
+                if (r0 + row < S) v = *(const uint4*)(G + (int64_t)(r0 + row) * ld + 8 * c);
+                *(uint4*)(T + row * HD + 8 * TL::phys(row, c)) = v;
+            }
+        }
+    };
+    // slot t: K_t (t < NT) and V_{t-1} (t >= 1)
+    auto load_slot = [&](int t, uint16_t* __restrict__ kdst, uint16_t* __restrict__ vdst) __attribute__((always_inline)) {
+        if (t < NT) load_tile(Kg, t * ATT_T, kdst);
+        if (t >= 1) load_tile(Vg, (t - 1) * ATT_T, vdst);
+    };
+
+    f32x16 st[2];   // scores of the next tile (written in M, read in V)
+    bf16x8 pb[4];   // probabilities of the current tile as MFMA operands
+    // M(j): O += V_j^T P_j^T (j < nk_wave), then the scores of tile j+1
+    // (j+1 < nk_wave); in this order the probabilities are dead before the
+    // scores are written (registers)
+    auto mcluster = [&](const uint16_t* __restrict__ Ks, const uint16_t* __restrict__ Vs, int j) __attribute__((always_inline)) {
+        if (j >= 0 && j < nk_wave) {
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                    for (int dt = 0; dt < HD / 32; ++dt)
+                        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                            TL::frag_tr(Vs, dt * 32, kt * 2 + ks, lane), pb[kt * 2 + ks], oacc[dt], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (j + 1 < nk_wave) {
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt) {
+                zero(st[kt]);
+#pragma unroll
+                for (int ds = 0; ds < HD / 16; ++ds)
+                    st[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        TL::frag_row(Ks, kt * 32 + (lane & 31), ds, half), as_bf16x8(qf[ds]), st[kt], 0, 0, 0);
+            }
+        }
+    };
+    // V(j): softmax of tile j (j < nk_wave), the same arithmetic as attn_fwd_kernel
+    auto vcluster = [&](int j) __attribute__((always_inline)) {
+        if (j >= nk_wave) return;
+        const int k0 = j * ATT_T;
+        if (k0 + ATT_T - 1 > q0 || k0 + ATT_T > S) {
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = k0 + kt * 32 + acc_row(r, half);
+                    if (key > qi || key >= S) st[kt][r] = -INFINITY;
+                }
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[kt][r]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_new = fmaxf(m_run, mx * sl2);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        float ps = 0.f;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float p = __builtin_amdgcn_exp2f(fmaf(st[kt][r], sl2, -m_new));
+                st[kt][r] = p;
+                ps += p;
+            }
+        ps += __shfl_xor(ps, 32);
+        l_run = l_run * alpha + ps;
+        if (__any(m_new != m_run)) {
+#pragma unroll
+            for (int dt = 0; dt < HD / 32; ++dt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+        }
+        m_run = m_new;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) pb[kt * 2 + ks] = frag_acc(st[kt], ks * 8);
+    };
+
+    load_slot(0, kbuf[0], vbuf[0]);
+    if (NT >= 1) load_slot(1, kbuf[1], vbuf[1]);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    // Group 0 runs M(j) in phase 2j+2 and V(j) in phase 2j+1, group 1 one
+    // phase later (its extra barrier comes first, group 0's last).  The loads
+    // of slot j+2 go out in phase 2j+2 (group 0 at the start of M(j), group 1
+    // at the start of V(j)) and are waited for at the end of phase 2j+3.
+    auto fence = [&](bool wait) __attribute__((always_inline)) {
+        if (wait) __builtin_amdgcn_s_waitcnt(0);
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    auto vstep = [&](int j) __attribute__((always_inline)) {
+        if (grp == 1 && j + 2 <= NT) load_slot(j + 2, kbuf[j & 1], vbuf[j & 1]);  // slot j+2 has j's parity
+        vcluster(j);
+        fence(grp == 0);
+    };
+    auto mstep = [&](const uint16_t* __restrict__ Ks, const uint16_t* __restrict__ Vs, uint16_t* __restrict__ kl,
+                     uint16_t* __restrict__ vl, int j) __attribute__((always_inline)) {
+        if (grp == 0 && j + 2 <= NT) load_slot(j + 2, kl, vl);
+        mcluster(Ks, Vs, j);
+        fence(grp == 1);
+    };
+    if (grp == 1) fence(false);
+    mcluster(kbuf[0], vbuf[0], -1);
+    fence(false);
+    for (int j = 0; j < NT; j += 2) {
+        vstep(j);
+        mstep(kbuf[1], vbuf[1], kbuf[0], vbuf[0], j);  // M(j) reads slot j+1 (odd), loads slot j+2 (even)
+        if (j + 1 < NT) {
+            vstep(j + 1);
+            mstep(kbuf[0], vbuf[0], kbuf[1], vbuf[1], j + 1);
+        }
+    }
+    if (grp == 0) fence(false);
     if (qi < S) {
         const float inv_l = 1.0f / l_run;
         uint16_t* orow = o + ((int64_t)b * S + qi) * H + (int64_t)head * HD;
@@ -564,13 +779,27 @@ void attention_fwd(const uint16_t* qkv, uint16_t* o, float* lse, int B, int S, i
                    hipStream_t s) {
     check_attn(B, S, heads, hd);
     const float sl2 = LOG2E / sqrtf((float)hd);
-    const dim3 grid((S + ATT_BQ - 1) / ATT_BQ, B * heads);
     // causal: S(S+1)/2 score entries, each 2*hd flops for QK^T and 2*hd for PV
     ProfScope prof(PROF_ATTN_FWD, 4.0 * hd * (double)B * heads * ((double)S * (S + 1) / 2), s);
-    if (hd == 128)
-        hipLaunchKernelGGL(attn_fwd_kernel<128>, grid, dim3(ATT_THREADS), 0, s, qkv, o, lse, S, heads, sl2);
-    else
-        hipLaunchKernelGGL(attn_fwd_kernel<64>, grid, dim3(ATT_THREADS), 0, s, qkv, o, lse, S, heads, sl2);
+    // MT_ATTN_FWD=pipe: the 4-wave software-pipelined kernel; otherwise the
+    // 8-wave ping-pong kernel (same arithmetic, bit-identical results)
+    static const bool pipe = [] {
+        const char* e = getenv("MT_ATTN_FWD");
+        return e && strcmp(e, "pipe") == 0;
+    }();
+    if (pipe) {
+        const dim3 grid((S + ATT_BQ - 1) / ATT_BQ, B * heads);
+        if (hd == 128)
+            hipLaunchKernelGGL(attn_fwd_kernel<128>, grid, dim3(ATT_THREADS), 0, s, qkv, o, lse, S, heads, sl2);
+        else
+            hipLaunchKernelGGL(attn_fwd_kernel<64>, grid, dim3(ATT_THREADS), 0, s, qkv, o, lse, S, heads, sl2);
+    } else {
+        const dim3 grid((S + ATT_PP_BQ - 1) / ATT_PP_BQ, B * heads);
+        if (hd == 128)
+            hipLaunchKernelGGL(attn_fwd_pp_kernel<128>, grid, dim3(ATT_PP_THREADS), 0, s, qkv, o, lse, S, heads, sl2);
+        else
+            hipLaunchKernelGGL(attn_fwd_pp_kernel<64>, grid, dim3(ATT_PP_THREADS), 0, s, qkv, o, lse, S, heads, sl2);
+    }
     launch_check("attention_fwd", s);
 }
 

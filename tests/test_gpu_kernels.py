@@ -218,6 +218,51 @@ def test_attention_fwd_bwd_vs_oracle(gpu, hd, B, S, nh):
         assert mar < 3e-2 and cos > 0.9995, (name, mar, cos)
 
 
+def test_attention_fwd_kernels_bit_identical(gpu):
+    """The 8-wave ping-pong forward (default) and the 4-wave pipelined forward
+    (MT_ATTN_FWD=pipe) run the same per-query arithmetic in the same order,
+    so outputs and log-sum-exps are the same bits (each kernel in its own
+    process: the choice is read once).  Shapes cover partial last tiles,
+    a single key, both head sizes and more than one 256-query block."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    code = r'''
+import ctypes, hashlib, sys
+import numpy as np, torch, synth
+from host_memory_centric_amd import _lib
+from host_memory_centric_amd._lib import call
+dev = torch.device("cuda:0")
+st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+P = lambda t: ctypes.c_void_p(t.data_ptr())
+h = hashlib.sha256()
+for i, (B, S, nh, hd) in enumerate([(2, 200, 3, 128), (1, 1, 2, 64), (1, 37, 1, 128), (1, 1000, 2, 64),
+                                    (1, 777, 2, 128), (2, 512, 1, 128)]):
+    H = nh * hd
+    x = np.random.default_rng(50 + i).standard_normal((B * S, 3 * H)).astype(np.float32)
+    qkv = torch.from_numpy(synth.f32_to_bf16_bits(x).view(np.int16)).to(dev)
+    o = torch.zeros((B * S, H), dtype=torch.int16, device=dev)
+    lse = torch.zeros((B, nh, S), dtype=torch.float32, device=dev)
+    n = ctypes.c_size_t()
+    call("mt_op_attention_ws_bytes", B, S, nh, hd, ctypes.byref(n))
+    ws = torch.empty(max(n.value, 256), dtype=torch.uint8, device=dev)
+    call("mt_op_attention_fwd", B, S, nh, hd, P(qkv), P(o), P(lse), P(ws), ws.numel(), st)
+    torch.cuda.synchronize()
+    h.update(o.cpu().numpy().tobytes())
+    h.update(lse.cpu().numpy().tobytes())
+sys.stdout.write(h.hexdigest())
+'''
+    outs = []
+    for impl in ("pp", "pipe"):
+        env = dict(os.environ, PYTHONPATH=root, MT_ATTN_FWD=impl)
+        r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=env, cwd=root,
+                           timeout=120)
+        assert r.returncode == 0, r.stderr[-2000:]
+        outs.append(r.stdout)
+    assert len(outs[0]) == 64 and outs[0] == outs[1]
+
+
 def test_attention_rejects_head_dim(gpu):
     import torch
     t = torch.zeros(1 << 16, dtype=torch.int16, device=gpu)
