@@ -65,6 +65,38 @@ def test_streamed_equals_resident_bitwise(gpu):
             assert np.array_equal(regions[key], a), (name, key)
 
 
+def test_ragged_blocks_and_sequence(gpu):
+    """Five layers (blocks of 2, 2, 1 and of 3, 2) at a sequence of 100
+    (partial attention and GEMM tiles): every schedule gives the resident
+    step's bits, and the streamed step matches the oracle."""
+    cfg = synth.preset("tiny", layers=5, ckpt_every=2, seq=100)
+    bits = synth.make_weights(cfg)
+    adam = synth.AdamCfg()
+    runs = {}
+    for name, kw in {"resident": dict(mode="resident"), "k2_2slot": dict(n_slots=2), "k2_3slot": dict(n_slots=3),
+                     "k3_1slot": dict(ckpt_every=3, n_slots=1), "k3_4slot": dict(ckpt_every=3, n_slots=4)}.items():
+        tr = _trainer(cfg, bits, **kw)
+        try:
+            losses = [tr.step(synth.make_tokens(cfg, s)) for s in range(2)]
+            runs[name] = (losses, _store_regions(tr))
+        finally:
+            tr.close()
+    ref_losses, ref_regions = runs["resident"]
+    for name, (losses, regions) in runs.items():
+        assert losses == ref_losses, name
+        for key, a in ref_regions.items():
+            assert np.array_equal(regions[key], a), (name, key)
+    st = oracle.HostState(bits)
+    tok = synth.make_tokens(cfg, 0)
+    tr = _trainer(cfg, bits, n_slots=2)
+    try:
+        loss = tr.step(tok)
+        res = oracle.train_step(st, tok, cfg, adam, mode="resident")
+        check_step(tr, loss, res, cfg)
+    finally:
+        tr.close()
+
+
 def test_run_twice_deterministic(gpu):
     cfg = synth.preset("tiny")
     bits = synth.make_weights(cfg)

@@ -515,3 +515,48 @@ def test_resident_loads_each_unit_once():
     ops, units, slot_of, load = _loads(6, 6, 7, resident=True)
     assert sum(load) == 7
     assert not any(k == "refwd" for k, _, _ in ops)
+
+
+@pytest.mark.parametrize("L", [1, 2, 3, 5, 7, 9])
+@pytest.mark.parametrize("K", [1, 2, 3, 4])
+def test_plan_invariants_any_depth(L, K):
+    """For any depth and checkpoint interval (the last block may be short):
+    one forward and one backward per layer, the head between them, backward
+    top-down, every block but the last recomputed (bottom-up, before its
+    backward) from its checkpoint, saved-buffer indices within the block;
+    and for any slot count the slot plan keeps every used unit resident,
+    loads exactly when it is not, and never reuses the slot of the op just
+    before."""
+    for resident in (False, True):
+        Kr = L if resident else K
+        ops = plan_step(L, K, resident)
+        kinds = [(k, l) for k, l, _ in ops]
+        assert [l for k, l in kinds if k == "fwd"] == list(range(L))
+        assert [l for k, l in kinds if k == "bwd"] == list(reversed(range(L)))
+        h = kinds.index(("head", None))
+        assert all(k == "fwd" for k, _ in kinds[:h]) and all(k != "fwd" for k, _ in kinds[h + 1:])
+        nblk = (L + Kr - 1) // Kr
+        for b in range(nblk):
+            lo, hi = b * Kr, min(L, (b + 1) * Kr)
+            re = [i for i, (k, l) in enumerate(kinds) if k == "refwd" and lo <= l < hi]
+            if b == nblk - 1:
+                assert not re
+            else:
+                assert [kinds[i][1] for i in re] == list(range(lo, hi))
+                assert max(re) < kinds.index(("bwd", hi - 1)) and min(re) > kinds.index(("bwd", hi))
+        for k, l, si in ops:
+            if k in ("refwd", "bwd"):
+                assert si == l - (l // Kr) * Kr
+            elif k == "fwd":
+                last0 = (nblk - 1) * Kr
+                assert si == (l - last0 if l >= last0 else None)
+        units = [-2 if k == "head" else l for k, l, _ in ops]
+        for slots in sorted({1, 2, 3, Kr + 1}):
+            slot_of, load = plan_slots(units, slots)
+            content = [None] * slots
+            for i, u in enumerate(units):
+                assert load[i] == (u not in content)
+                if load[i] and slots > 1 and i > 0:
+                    assert slot_of[i] != slot_of[i - 1]
+                content[slot_of[i]] = u
+                assert content[slot_of[i]] == u and content.count(u) == 1
