@@ -22,6 +22,15 @@
  *    mt_pinned_alloc and the host worker threads belong to the library;
  *  - all bf16 data is stored as raw 16-bit patterns (uint16), row-major;
  *    floating-point roundings to bf16 are round-to-nearest-even.
+ *
+ * Environment switches (read once per process; results never depend on them):
+ *  - MT_SYNC_CHECK=1: synchronise the stream after every device call;
+ *  - MT_GEMM_IMPL=pipe: large GEMMs on the 4-wave pipelined kernel instead of
+ *    the 8-wave ping-pong kernel (same bits);
+ *  - MT_ATTN_FWD=pipe: attention forward on the 4-wave pipelined kernel
+ *    instead of the 8-wave ping-pong kernel (same bits);
+ *  - MT_NO_AVX512=1: the host Adam and accumulation on their scalar path
+ *    (same bits).
  */
 #ifndef MT_H
 #define MT_H
