@@ -560,3 +560,63 @@ def test_plan_invariants_any_depth(L, K):
                     assert slot_of[i] != slot_of[i - 1]
                 content[slot_of[i]] = u
                 assert content[slot_of[i]] == u and content.count(u) == 1
+
+
+def test_device_entries_reject_bad_arguments_before_any_launch(lib):
+    """The layer, head and bind entry points check shapes, pointers, alignment
+    and buffer sizes on the host and return the documented code (with a
+    message) before anything is enqueued: the fake, aligned device addresses
+    below are never touched."""
+    from host_memory_centric_amd._lib import MtAct, MtHeadIO, MtLayerView
+    cfg = synth.preset("tiny")
+    mc = _lib.model_cfg(cfg)
+    base = 1 << 28  # a fake device address, 256-byte aligned
+    ws = ctypes.c_size_t()
+    _lib.call("mt_layer_workspace_bytes", ctypes.byref(mc), 2, 128, ctypes.byref(ws))
+    view = MtLayerView()
+    for j in range(6):
+        view.w[j] = base + j * 4096
+        view.g[j] = base + (1 << 20) + j * 4096
+
+    def act(**kw):
+        a = MtAct()
+        a.batch, a.seq = 2, 128
+        for f in ("x_in", "x_out", "dy", "dy_bf16", "dx", "dx_bf16", "rope_cos", "rope_sin", "workspace"):
+            setattr(a, f, base)
+        a.workspace_bytes = 1 << 40
+        for k, v in kw.items():
+            setattr(a, k, v)
+        return a
+
+    def code(name, *args):
+        with pytest.raises(MtError) as e:
+            _lib.call(name, *args)
+        assert str(e.value).split(": ", 1)[1].strip()  # a message, not only the code
+        return e.value.code
+
+    def fwd(a, m=mc):
+        return code("mt_layer_fwd", ctypes.byref(view), ctypes.byref(m), ctypes.byref(a), None)
+
+    assert fwd(act(batch=0)) == -2                       # empty batch
+    assert fwd(act(batch=2, seq=3)) == -2                # batch*seq not a multiple of 8
+    assert fwd(act(x_in=None)) == -1                     # missing input
+    assert fwd(act(x_out=base + 8)) == -3                # misaligned output
+    assert fwd(act(workspace_bytes=ws.value - 256)) == -1  # workspace too small (no saved buffer)
+    assert fwd(act(saved=base, saved_bytes=16, workspace_bytes=ws.value)) == -1  # saved buffer too small
+    assert fwd(act(), _lib.model_cfg(cfg.with_(hidden=288, heads=3, head_dim=96))) == -2  # head_dim not 64 or 128
+    assert code("mt_layer_recompute_bwd", ctypes.byref(view), ctypes.byref(mc), ctypes.byref(act(dy=None)),
+                None) == -1
+    hv = MtLayerView()
+    for j in range(2):
+        hv.w[j] = base + j * 4096
+        hv.g[j] = base + (1 << 20) + j * 4096
+    hio = MtHeadIO()
+    hio.batch, hio.seq = 8, 1                            # no next token to predict
+    hio.x = hio.tokens = hio.dx = hio.dx_bf16 = hio.loss = hio.workspace = base
+    hio.workspace_bytes = 1 << 40
+    assert code("mt_head_fwd_bwd", ctypes.byref(hv), ctypes.byref(mc), ctypes.byref(hio), None) == -2
+    hio.batch, hio.seq, hio.workspace_bytes = 2, 128, 256
+    assert code("mt_head_fwd_bwd", ctypes.byref(hv), ctypes.byref(mc), ctypes.byref(hio), None) == -1
+    out = MtLayerView()
+    assert code("mt_bind", ctypes.byref(mc), 0, ctypes.c_void_p(base + 128), None, ctypes.byref(out)) == -3
+    assert code("mt_bind", ctypes.byref(mc), 0, None, None, ctypes.byref(out)) == -1
