@@ -169,6 +169,22 @@ def host_probe(tr, reps=3, master=False):
     return out
 
 
+def probe_mfma(tr, iters=100000):
+    """Sustained bf16 MFMA rate of this GPU (mt_probe_mfma: independent MFMA
+    chains on every SIMD, no memory traffic, ~50 ms after a warm-up): the peak
+    the chip holds under MFMA load, beside the published 2.4 GHz figure."""
+    import ctypes
+
+    import torch
+
+    from host_memory_centric_amd import _lib
+    sink = torch.empty(2048, dtype=torch.float32, device=tr.dev)
+    out = ctypes.c_double()
+    _lib.call("mt_probe_mfma", iters, ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(tr.s_comp.cuda_stream),
+              ctypes.byref(out))
+    return round(out.value, 1)
+
+
 def link_probe(tr, nbytes=1 << 30, reps=3):
     """Pinned host <-> device copy rates on this machine: each direction alone and
     both at once (the trainer's weight and gradient streams)."""
@@ -332,6 +348,8 @@ def main():
     _lib.call("mt_prof_enable", 0)
     prof = _lib.prof_collect(reset=True)
 
+    # the trainer's device footprint: taken before the probes allocate their buffers
+    dev_peak = int(torch.cuda.max_memory_allocated())
     # one more (untimed) step with an event timeline: copy/compute overlap
     tr.record_timeline = True
     tr.step(tokens(step))
@@ -343,6 +361,7 @@ def main():
         with open(args.timeline_out, "w") as fh:
             json.dump(tl, fh)
     link = link_probe(tr)
+    mfma_probe = probe_mfma(tr)
     host = host_probe(tr, master=args.master)
 
     T = cfg.tokens * nmb  # tokens per optimizer step
@@ -365,7 +384,9 @@ def main():
                 "avg_launch_ms": round(ms / n, 4), "launches": n,
                 # cycles the MFMA units are busy (rocprofv3 PMC, committed profile): the rest of the
                 # gap to the published peak is the clock, which falls well below 2.4 GHz under this load
-                "mfma_busy_frac_pmc": measured_mfma_busy(name, args.workload)}
+                "mfma_busy_frac_pmc": measured_mfma_busy(name, args.workload),
+                # the same rate against the MFMA rate this GPU sustains (probe, same run)
+                "frac_of_probed_peak": round(ach / mfma_probe, 4)}
     kernels = {k: {"launches": n, "avg_ms": round(ms / n, 4), "tflops": round(fl / (ms * 1e-3) / 1e12, 1),
                    "share_of_step": round(ms / (1e3 * dt), 3)} for k, (n, ms, fl) in prof.items()}
     out = {
@@ -387,8 +408,10 @@ def main():
         "tflops_exec": round(tflops_exec, 1), "tflops_model": round(tflops_model, 1),
         "pct_peak_exec": round(100 * tflops_exec / PEAK_BF16_TFLOPS, 2),
         "pct_peak_model": round(100 * tflops_model / PEAK_BF16_TFLOPS, 2),
+        "mfma_probe_tflops": mfma_probe,
+        "pct_probe_exec": round(100 * tflops_exec / mfma_probe, 2),
         "h2d_GBps": round(h2d * args.steps / dt / 1e9, 2), "d2h_GBps": round(d2h * args.steps / dt / 1e9, 2),
-        "weight_loads_per_step": n_loads * nmb, "dev_peak_bytes": int(torch.cuda.max_memory_allocated()),
+        "weight_loads_per_step": n_loads * nmb, "dev_peak_bytes": dev_peak,
         "host_store_bytes": int(tr.store.total_bytes()), "loss": round(loss, 5), "kernels": kernels,
         "roofline": roof,
         "overlap": overlap,

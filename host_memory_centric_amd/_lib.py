@@ -99,6 +99,7 @@ _SIGS = {
     "mt_head_fwd_bwd": [POINTER(MtLayerView), POINTER(MtModelCfg), POINTER(MtHeadIO), c_void_p],
     "mt_op_gemm": [c_int64, c_int64, c_int64, c_void_p, c_int64, c_int, c_void_p, c_int64, c_int, c_void_p, c_void_p,
                    c_void_p, c_int64, c_int, c_void_p, c_size_t, c_void_p],
+    "mt_probe_mfma": [c_int32, c_void_p, c_void_p, POINTER(c_double)],
     "mt_prof_enable": [c_int],
     "mt_prof_collect": [POINTER(MtProfEntry), c_int, POINTER(c_int), c_int],
     "mt_op_attention_fwd": [c_int32, c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,

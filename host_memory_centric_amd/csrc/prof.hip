@@ -1,12 +1,14 @@
 // Live kernel timing: HIP events recorded around the launches of the timed
 // kernel classes, on the launch's own stream, so that the average duration of
 // a kernel can be measured while the training step runs.
+#include <algorithm>
 #include <atomic>
 #include <cstring>
 #include <mutex>
 #include <vector>
 
 #include "common.h"
+#include "device.h"
 #include "kernels.h"
 
 namespace mt {
@@ -54,11 +56,68 @@ ProfScope::~ProfScope() {
     (void)hipEventRecord(g_recs[idx].b, s);
 }
 
+// MFMA probe: every wave runs four independent accumulator chains of
+// v_mfma_f32_32x32x16_bf16 on register operands (no memory traffic), so the
+// rate it reaches is what the matrix cores sustain at the clock the chip holds
+// under that load.  The sink is written only if the sum of the accumulators
+// equals a value it cannot take (the chains stay live).
+constexpr int PROBE_WGS = 2048;  // 8 workgroups of 4 waves per CU on 256 CUs
+constexpr int PROBE_CHAINS = 4;
+
+__global__ __launch_bounds__(256) void mfma_probe_kernel(float* sink, int iters) {
+    const int lane = threadIdx.x & 63;
+    bf16x8 a, b;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        a[e] = (__bf16)(0.125f * (float)((lane + e) & 7));
+        b[e] = (__bf16)(0.0625f * (float)((lane * 3 + e) & 7));
+    }
+    f32x16 acc[PROBE_CHAINS];
+#pragma unroll
+    for (int k = 0; k < PROBE_CHAINS; ++k)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[k][r] = 0.f;
+    for (int i = 0; i < iters; ++i) {
+#pragma unroll
+        for (int k = 0; k < PROBE_CHAINS; ++k) acc[k] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[k], 0, 0, 0);
+    }
+    float sum = 0.f;
+#pragma unroll
+    for (int k = 0; k < PROBE_CHAINS; ++k)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sum += acc[k][r];
+    if (sum == -1.0f) sink[blockIdx.x] = sum;  // the products are non-negative
+}
+
 }  // namespace mt
 
 using namespace mt;
 
 extern "C" {
+
+int mt_probe_mfma(int32_t iters, float* sink, void* stream, double* tflops) {
+    return guard([&] {
+        MT_CHECK_ARG(iters > 0 && sink != nullptr && tflops != nullptr, "bad arguments");
+        const hipStream_t s = (hipStream_t)stream;
+        hipEvent_t a, b;
+        if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess)
+            MT_FAIL(MT_E_HIP, "hipEventCreate failed");
+        // a warm-up fifth of the work, then the timed run
+        hipLaunchKernelGGL(mfma_probe_kernel, dim3(PROBE_WGS), dim3(256), 0, s, sink, std::max(1, iters / 5));
+        hipError_t e = hipEventRecord(a, s);
+        hipLaunchKernelGGL(mfma_probe_kernel, dim3(PROBE_WGS), dim3(256), 0, s, sink, iters);
+        if (e == hipSuccess) e = hipGetLastError();
+        if (e == hipSuccess) e = hipEventRecord(b, s);
+        if (e == hipSuccess) e = hipEventSynchronize(b);
+        float ms = 0.f;
+        if (e == hipSuccess) e = hipEventElapsedTime(&ms, a, b);
+        (void)hipEventDestroy(a);
+        (void)hipEventDestroy(b);
+        if (e != hipSuccess) MT_FAIL(MT_E_HIP, "mfma probe: %s", hipGetErrorString(e));
+        const double flops = (double)PROBE_WGS * 4 * PROBE_CHAINS * (double)iters * 2.0 * 32 * 32 * 16;
+        *tflops = flops / (ms * 1e-3) / 1e12;
+    });
+}
 
 int mt_prof_enable(int on) {
     return guard([&] { g_on.store(on != 0); });

@@ -400,6 +400,16 @@ typedef struct mt_prof_entry {
     double flops;
 } mt_prof_entry;
 
+/* Attainable bf16 MFMA rate of this GPU under sustained load (the denominator
+ * of an MFMA utilisation that the clock under load cannot distort): launches,
+ * on `stream`, a kernel of independent v_mfma_f32_32x32x16_bf16 chains on
+ * register operands on every SIMD (no memory traffic) for iters / 5
+ * iterations, then times one with `iters` iterations (1e5 takes about 50 ms)
+ * and returns its rate in TFLOP/s in *tflops; synchronises the stream.
+ * sink: device buffer of at least 2048 floats (written only by a result the
+ * kernel cannot produce).  Not part of the training path. */
+int mt_probe_mfma(int32_t iters, float* sink, void* stream, double* tflops);
+
 /* on != 0: from now on every launch of a timed class is bracketed by two HIP
  * events recorded on the launch's own stream; on == 0 stops recording. */
 int mt_prof_enable(int on);

@@ -263,6 +263,19 @@ sys.stdout.write(h.hexdigest())
     assert len(outs[0]) == 64 and outs[0] == outs[1]
 
 
+def test_mfma_probe_is_plausible(gpu):
+    """The sustained-MFMA probe returns a rate below the published bf16 peak
+    (2.5 PFLOP/s at 2.4 GHz) and far above what any memory-bound path gives."""
+    import torch
+    sink = torch.zeros(2048, dtype=torch.float32, device=gpu)
+    out = ctypes.c_double()
+    call("mt_probe_mfma", 20000, _p(sink), _stream(), ctypes.byref(out))
+    assert 300.0 < out.value < 2600.0, out.value
+    assert float(sink.abs().sum().cpu()) == 0.0  # the sink is never written
+    with pytest.raises(MtError):
+        call("mt_probe_mfma", 0, _p(sink), _stream(), ctypes.byref(out))
+
+
 def test_attention_rejects_head_dim(gpu):
     import torch
     t = torch.zeros(1 << 16, dtype=torch.int16, device=gpu)
