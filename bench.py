@@ -47,11 +47,26 @@ def flops_per_step(cfg, ops):
     return exec_, model
 
 
+def gemm_source_hash():
+    """Hash of the GEMM kernel sources with comments and blank lines removed,
+    so that the committed counter figures stay valid across comment edits and
+    are dropped (null) once any code changes."""
+    import hashlib
+    import re
+    csrc = os.path.join(ROOT, "host_memory_centric_amd", "csrc")
+    code = []
+    for f in ("gemm.hip", "gemm_kernel.h", "gemm_pipe.h", "gemm_pp.h"):
+        for line in open(os.path.join(csrc, f)):
+            line = re.sub(r"//.*", "", line).rstrip()
+            if line:
+                code.append(line)
+    return hashlib.sha256("\n".join(code).encode()).hexdigest()[:16]
+
+
 def measured_traffic(kernel, workload):
     """HBM bytes per launch of a GEMM class from the committed rocprofv3 PMC
     summary (profiles/gemm_7b_traffic.md), or None if that summary is for
     another workload or the GEMM sources changed since it was taken."""
-    import hashlib
     import re
     path = os.path.join(ROOT, "profiles", "gemm_7b_traffic.md")
     if workload != "7b" or not os.path.exists(path):
@@ -60,9 +75,7 @@ def measured_traffic(kernel, workload):
     if not m:
         return None
     data = json.loads(m.group(1))
-    csrc = os.path.join(ROOT, "host_memory_centric_amd", "csrc")
-    src = "".join(open(os.path.join(csrc, f)).read() for f in ("gemm.hip", "gemm_kernel.h", "gemm_pipe.h", "gemm_pp.h"))
-    if hashlib.sha256(src.encode()).hexdigest()[:16] != data.get("source_sha256_16"):
+    if gemm_source_hash() != data.get("source_sha256_16"):
         return None
     k = data.get("kernels", {}).get(kernel)
     return k["hbm_bytes"] if k else None
@@ -72,7 +85,6 @@ def measured_mfma_busy(kernel, workload):
     """Fraction of cycles the MFMA units are busy in a GEMM class, from the
     committed rocprofv3 PMC summary (profiles/mfma_util_7b_gemm_attention.md),
     or None for another workload or once the GEMM sources changed."""
-    import hashlib
     import re
     path = os.path.join(ROOT, "profiles", "mfma_util_7b_gemm_attention.md")
     if workload != "7b" or not os.path.exists(path):
@@ -81,9 +93,7 @@ def measured_mfma_busy(kernel, workload):
     if not m:
         return None
     data = json.loads(m.group(1))
-    csrc = os.path.join(ROOT, "host_memory_centric_amd", "csrc")
-    src = "".join(open(os.path.join(csrc, f)).read() for f in ("gemm.hip", "gemm_kernel.h", "gemm_pipe.h", "gemm_pp.h"))
-    if hashlib.sha256(src.encode()).hexdigest()[:16] != data.get("source_sha256_16"):
+    if gemm_source_hash() != data.get("source_sha256_16"):
         return None
     k = data.get("kernels", {}).get(kernel)
     return k["mfma_busy_frac"] if k else None

@@ -5,9 +5,9 @@
 // global->LDS loads three sub-steps ahead) and a compute phase (16 MFMAs on
 // those fragments), one phase apart, with one workgroup barrier between
 // phases: while one wave of the SIMD reads and loads, the other keeps the
-// matrix core busy.  The LDS tile layouts and the ring
-// are those of gemm_pipe.h; the per-output K order is the same, so the
-// results are bit-identical to the other kernels.
+// matrix core busy.  The LDS tile layouts and the ring are those of
+// gemm_pipe.h; the per-output K order is the same, so the results are
+// bit-identical to the other kernels.
 #pragma once
 #include "gemm_pipe.h"
 
@@ -22,8 +22,10 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmArgs p) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    // Waves w and w + 4 share a SIMD; group 0 (waves 0-3) runs half a phase
-    // ahead of group 1.  Wave tile: rows wm*128 .. +127, columns wn*64 .. +63.
+    // Waves w and w + 4 share a SIMD (wave i of a workgroup is placed on SIMD
+    // i mod 4; correctness does not depend on it); group 0 (waves 0-3) runs
+    // one phase ahead of group 1.  Wave tile: rows wm*128 .. +127, columns
+    // wn*64 .. +63.
     const int grp = wave >> 2, w4 = wave & 3;
     const int wm = w4 & 1, wn = 2 * grp + (w4 >> 1);
     int pm, pn;
