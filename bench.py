@@ -309,6 +309,12 @@ def main():
     ap.add_argument("--layers", type=int, default=None, help="override the workload's layer count")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--timeline-out", default=None, help="write the event timeline of one step as JSON")
+    ap.add_argument("--no-timeline", action="store_true",
+                    help="skip the extra untimed step that records the copy/compute timeline (long steps)")
+    ap.add_argument("--progress", action="store_true",
+                    help="print each op as it is enqueued (the enqueue runs a few ops ahead of the GPU)")
+    ap.add_argument("--offload-ckpt", type=int, default=0,
+                    help="hold the checkpoints of the first N blocks in host memory (long contexts)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU sharding or collectives; "
@@ -333,7 +339,15 @@ def main():
     _lib.call("mt_set_optimizer_threads", args.adam_threads)
     tr = Trainer(cfg, adam, mode=args.mode, n_slots=args.slots, n_grad_slabs=args.grad_slabs, device="cuda:0",
                  micro_batches=nmb, master=args.master, pinned_store=args.pinned_store,
-                 update_order=args.update_order)
+                 update_order=args.update_order, offload_ckpt=args.offload_ckpt)
+
+    if args.progress:
+        t_prog = time.perf_counter()
+
+        def progress(kind, layer):
+            print(f"[bench] {time.perf_counter() - t_prog:8.1f} s  {kind} {'' if layer is None else layer}",
+                  file=sys.stderr, flush=True)
+        tr.progress = progress
 
     def tokens(step):
         return np.concatenate([synth.make_tokens(cfg, step * nmb + i) for i in range(nmb)], axis=0)
@@ -361,13 +375,15 @@ def main():
     # the trainer's device footprint: taken before the probes allocate their buffers
     dev_peak = int(torch.cuda.max_memory_allocated())
     # one more (untimed) step with an event timeline: copy/compute overlap
-    tr.record_timeline = True
-    tr.step(tokens(step))
-    tr.finish()
-    tl = tr.timeline()
-    tr.record_timeline = False
-    overlap = overlap_report(tl)
-    if args.timeline_out:
+    overlap = None
+    if not args.no_timeline:
+        tr.record_timeline = True
+        tr.step(tokens(step))
+        tr.finish()
+        tl = tr.timeline()
+        tr.record_timeline = False
+        overlap = overlap_report(tl)
+    if args.timeline_out and overlap is not None:
         with open(args.timeline_out, "w") as fh:
             json.dump(tl, fh)
     link = link_probe(tr)
@@ -381,8 +397,10 @@ def main():
     tflops_model = f_model / (dt / args.steps) / 1e12
     lay, lay_h = tr.lay, tr.lay_head_dev
     n_loads = tr.n_weight_loads()  # per micro-batch pass
-    h2d = nmb * ((n_loads - 1) * lay.w_bytes + lay_h.w_bytes) + T * cfg.hidden * 2 + T * 4
-    d2h = nmb * (cfg.layers * lay.w_bytes + lay_h.w_bytes) + T * cfg.hidden * 4
+    # (block checkpoints held in host memory go out and come back once per pass)
+    ck = nmb * tr.n_host * tr.ckpt_bytes
+    h2d = nmb * ((n_loads - 1) * lay.w_bytes + lay_h.w_bytes) + T * cfg.hidden * 2 + T * 4 + ck
+    d2h = nmb * (cfg.layers * lay.w_bytes + lay_h.w_bytes) + T * cfg.hidden * 4 + ck
     dom = max(prof.items(), key=lambda kv: kv[1][1]) if prof else None
     roof = None
     if dom:
@@ -408,12 +426,13 @@ def main():
                                                                        "all layers resident on the device")) +
                    (f", {nmb} micro-batches per optimizer step" if nmb > 1 else "") +
                    (", fp32 master weights" if args.master else "") +
-                   (", host store W/G page-locked (direct copies, no packer)" if args.pinned_store else ""),
+                   (", host store W/G page-locked (direct copies, no packer)" if args.pinned_store else "") +
+                   (f", checkpoints of the first {tr.n_host} blocks in host memory" if tr.n_host else ""),
                    "name": cfg.name, "global_batch": cfg.batch * nmb,
                    "seq_len": cfg.seq, "micro_batches": nmb, "master_fp32": bool(args.master),
                    "mode": args.mode, "slots": tr.n_slots, "ckpt_every": tr.K,
                    "host_store": "pinned_dma" if args.pinned_store else "pageable",
-                   "update_order": args.update_order,
+                   "update_order": args.update_order, "ckpt_host_blocks": tr.n_host,
                    "parallelism": "none (1 GPU)"},
         "tflops_exec": round(tflops_exec, 1), "tflops_model": round(tflops_model, 1),
         "pct_peak_exec": round(100 * tflops_exec / PEAK_BF16_TFLOPS, 2),
@@ -427,7 +446,8 @@ def main():
         "overlap": overlap,
         "link": dict(link, h2d_bytes_per_step=int(h2d), d2h_bytes_per_step=int(d2h),
                      h2d_link_frac=round(h2d / (ms_step * 1e-3) / (link["h2d_GBps"] * 1e9), 4),
-                     h2d_active_GBps=round(h2d / 1e9 / (overlap["h2d_busy_frac"] * overlap["step_ms"] * 1e-3), 2)),
+                     h2d_active_GBps=(round(h2d / 1e9 / (overlap["h2d_busy_frac"] * overlap["step_ms"] * 1e-3), 2)
+                                      if overlap else None)),
     }
     # host DRAM bytes of one step: with a pageable store every weight load is
     # packed once (4 B per parameter) and every parameter gets one Adam update
@@ -441,7 +461,10 @@ def main():
     # reads the accumulator; a master copy adds 6 B: fp32 read instead of bf16, fp32 write)
     adam_b = (22 if tr.direct else 24) + (4 if nmb > 1 else 0) + (6 if args.master else 0)
     pack_b = 0 if tr.direct else nmb * (4 * (lay.w_bytes // 2) * (n_loads - 1) + 4 * (lay_h.w_bytes // 2))
-    host_bytes = pack_b + adam_b * n_params + 10 * (nmb - 1) * n_params + h2d + d2h
+    # (checkpoints in host memory: a host copy out of the slab each, and one back into it
+    # for all but the two that are still in their slabs, each read plus write)
+    ck_copy = 2 * nmb * (tr.n_host + max(0, tr.n_host - 2)) * tr.ckpt_bytes
+    host_bytes = pack_b + adam_b * n_params + 10 * (nmb - 1) * n_params + h2d + d2h + ck_copy
     host["bytes_per_step"] = int(host_bytes)
     host["floor_ms"] = round(1e3 * host_bytes / (max(host["pack_GBps"] or 0, host["adam_GBps"]) * 1e9), 1)
     host["floor_frac_of_step"] = round(host["floor_ms"] / ms_step, 3)

@@ -82,6 +82,7 @@ _SIGS = {
     "mt_pack_layer": [c_void_p, c_int, c_void_p, c_size_t],
     "mt_pinned_alloc": [c_size_t, POINTER(c_void_p)],
     "mt_pinned_free": [c_void_p],
+    "mt_host_copy": [c_void_p, c_void_p, c_size_t],
     "mt_copy_h2d": [c_void_p, c_void_p, c_size_t, c_void_p],
     "mt_copy_d2h": [c_void_p, c_void_p, c_size_t, c_void_p],
     "mt_step": [c_void_p, c_int, c_void_p, POINTER(MtAdamCfg), c_int64, c_void_p],

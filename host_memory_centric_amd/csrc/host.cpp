@@ -803,6 +803,15 @@ int mt_pinned_free(void* p) {
     });
 }
 
+int mt_host_copy(void* dst, const void* src, size_t bytes) {
+    return guard([&] {
+        MT_CHECK_ARG(dst && src, "NULL pointer");
+        MT_CHECK_ARG((char*)dst + bytes <= (const char*)src || (const char*)src + bytes <= (char*)dst,
+                     "the buffers overlap");
+        if (bytes) par_memcpy(dst, src, bytes);
+    });
+}
+
 int mt_copy_h2d(void* dst_dev, const void* src_host, size_t bytes, void* stream) {
     return guard([&] {
         MT_CHECK_ARG(dst_dev && src_host, "NULL pointer");

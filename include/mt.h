@@ -200,6 +200,12 @@ int mt_pack_head_tied(mt_store* st, void* dst, size_t dst_bytes);
 int mt_pinned_alloc(size_t bytes, void** out);
 int mt_pinned_free(void* p);
 
+/* Host memory copy with the library's threads and non-temporal stores (the
+ * packer's copy), for staging between pageable buffers and pinned slabs, e.g.
+ * block checkpoints kept in host memory.  dst and src must not overlap
+ * (MT_E_ARG).  Synchronous. */
+int mt_host_copy(void* dst, const void* src, size_t bytes);
+
 /* Asynchronous copies on a caller stream (hipStream_t passed as void*):
  * host->device weight stream and device->host gradient evacuation (paper
  * page, appendix A.2: weight and gradient streams beside the compute stream).

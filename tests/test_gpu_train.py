@@ -97,6 +97,53 @@ def test_ragged_blocks_and_sequence(gpu):
         tr.close()
 
 
+def test_offloaded_checkpoints_bit_identical(gpu):
+    """Block checkpoints held in host memory (the ring of two device buffers,
+    copies out in the forward and back in the backward) give the bits of the
+    step that keeps them all on the device: one layer per block with one, two
+    and the most host blocks, blocks of two, micro-batches, and with the event
+    timeline recorded."""
+    cfg = synth.preset("tiny", layers=6, ckpt_every=1, seq=100)
+    bits = synth.make_weights(cfg)
+    runs = {}
+    cases = {"k1": dict(), "k1_h1": dict(offload_ckpt=1), "k1_h2": dict(offload_ckpt=2, n_slots=3),
+             "k1_h4": dict(offload_ckpt=4), "k1_h3_tl": dict(offload_ckpt=3, timeline=True),
+             "k4": dict(ckpt_every=4), "k2_h1": dict(ckpt_every=2, offload_ckpt=1)}
+    for name, kw in cases.items():
+        tr = _trainer(cfg, bits, **kw)
+        try:
+            assert tr.n_host == kw.get("offload_ckpt", 0)
+            losses = [tr.step(synth.make_tokens(cfg, s)) for s in range(3)]
+            if "timeline" in kw:
+                tl = tr.timeline()
+                assert len(tl["d2h"]) >= cfg.layers + tr.n_host and len(tl["h2d"]) >= tr.n_host
+            runs[name] = (losses, _store_regions(tr))
+        finally:
+            tr.close()
+    ref_losses, ref_regions = runs["k1"]
+    for name, (losses, regions) in runs.items():
+        assert losses == ref_losses, name
+        for key, a in ref_regions.items():
+            assert np.array_equal(regions[key], a), (name, key)
+    # micro-batches: two passes per step, each with its own copies out and back
+    mb = {}
+    for name, kw in {"mb": dict(), "mb_h3": dict(offload_ckpt=3)}.items():
+        tr = _trainer(cfg, bits, micro_batches=2, **kw)
+        try:
+            losses = [tr.step(np.concatenate([synth.make_tokens(cfg, 2 * s + i) for i in range(2)]))
+                      for s in range(2)]
+            mb[name] = (losses, _store_regions(tr))
+        finally:
+            tr.close()
+    assert mb["mb"][0] == mb["mb_h3"][0]
+    for key, a in mb["mb"][1].items():
+        assert np.array_equal(mb["mb_h3"][1][key], a), key
+    from host_memory_centric_amd.engine import Trainer
+    for kw in (dict(offload_ckpt=5), dict(offload_ckpt=1, mode="resident")):
+        with pytest.raises(ValueError):
+            Trainer(cfg, synth.AdamCfg(), weights=bits, **kw)
+
+
 def test_run_twice_deterministic(gpu):
     cfg = synth.preset("tiny")
     bits = synth.make_weights(cfg)

@@ -149,6 +149,28 @@ def test_pack_copies_w_region(lib):
         st.close()
 
 
+def test_host_copy(lib):
+    """The library's multi-threaded host copy (used for block checkpoints held in
+    host memory): every byte, aligned or not, across several 4 MB chunks, and
+    overlapping buffers rejected."""
+    rng = np.random.default_rng(5)
+    src = rng.integers(0, 256, size=(9 << 20) + 77, dtype=np.uint8)
+    for off, n in [(0, 0), (0, 1), (0, 255), (0, 257), (64, 9 << 20), (3, (9 << 20) + 13), (0, src.nbytes)]:
+        dst = np.zeros(src.nbytes + 64, dtype=np.uint8)
+        pd = ctypes.c_void_p(dst.ctypes.data + off)
+        call("mt_host_copy", pd, src.ctypes.data_as(ctypes.c_void_p), n)
+        assert np.array_equal(dst[off:off + n], src[:n]), (off, n)
+        assert not dst[:off].any() and not dst[off + n:].any(), (off, n)
+    buf = src.copy()
+    for d in (0, 1000):
+        with pytest.raises(MtError) as e:
+            call("mt_host_copy", ctypes.c_void_p(buf.ctypes.data + d), ctypes.c_void_p(buf.ctypes.data + 500), 4096)
+        assert e.value.code == -1
+    with pytest.raises(MtError):
+        call("mt_host_copy", None, buf.ctypes.data_as(ctypes.c_void_p), 16)
+    assert np.array_equal(buf, src)
+
+
 @pytest.mark.parametrize("wd", [0.0, 0.1])
 def test_host_adam_bitwise_equals_oracle(lib, wd):
     cfg = synth.preset("tiny")
