@@ -108,6 +108,7 @@ def test_offloaded_checkpoints_bit_identical(gpu):
     runs = {}
     cases = {"k1": dict(), "k1_h1": dict(offload_ckpt=1), "k1_h2": dict(offload_ckpt=2, n_slots=3),
              "k1_h4": dict(offload_ckpt=4), "k1_h3_tl": dict(offload_ckpt=3, timeline=True),
+             "k1_h2_pinned": dict(offload_ckpt=2, pinned_store=True),
              "k4": dict(ckpt_every=4), "k2_h1": dict(ckpt_every=2, offload_ckpt=1)}
     for name, kw in cases.items():
         tr = _trainer(cfg, bits, **kw)
