@@ -242,6 +242,11 @@ class Trainer:
         self.L = cfg.layers
         self.K = self.L if mode == "resident" else (ckpt_every or cfg.ckpt_every)
         self.n_slots = self.L + 1 if mode == "resident" else max(1, n_slots)
+        self.n_host = int(offload_ckpt)
+        nblk = (self.L + self.K - 1) // self.K
+        if self.n_host and (mode == "resident" or not 0 < self.n_host <= nblk - 2):
+            raise ValueError(f"offload_ckpt must be 0, or in a streamed step between 1 and the block count "
+                             f"less two ({nblk - 2})")
         self.B, self.S = cfg.batch, cfg.seq
         self.T = self.B * self.S
         h = cfg.hidden
@@ -276,11 +281,6 @@ class Trainer:
         self.slots = [torch.empty(self.slot_bytes, dtype=torch.uint8, device=d) for _ in range(self.n_slots)]
         self.gslots = [torch.empty(self.lay.w_bytes, dtype=torch.uint8, device=d) for _ in range(2)]
         self.head_g = torch.empty(self.lay_head_dev.w_bytes, dtype=torch.uint8, device=d)
-        nblk = (self.L + self.K - 1) // self.K
-        self.n_host = int(offload_ckpt)
-        if self.n_host and (mode == "resident" or not 0 < self.n_host <= nblk - 2):
-            raise ValueError(f"offload_ckpt must be 0, or in a streamed step between 1 and the block count "
-                             f"less two ({nblk - 2})")
         n_ring = self.n_host + 2 if self.n_host else 0  # blocks below n_ring use the two ring buffers
         self.n_ring = n_ring
         self.ckpt_ring = [torch.empty((T, h), dtype=bf, device=d) for _ in range(2 if n_ring else 0)]

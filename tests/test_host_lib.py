@@ -584,6 +584,17 @@ def test_plan_invariants_any_depth(L, K):
                 assert content[slot_of[i]] == u and content.count(u) == 1
 
 
+@pytest.mark.parametrize("kw", [dict(offload_ckpt=5), dict(offload_ckpt=-1), dict(offload_ckpt=1, mode="resident"),
+                                dict(offload_ckpt=3, ckpt_every=2)])
+def test_offload_ckpt_argument_checked_before_any_allocation(lib, kw):
+    """Host-held block checkpoints need a streamed step and leave at least the
+    two top blocks on the device (6 layers: 6 blocks of 1, or 3 of 2)."""
+    from host_memory_centric_amd.engine import Trainer
+    cfg = synth.preset("tiny", layers=6, ckpt_every=1)
+    with pytest.raises(ValueError, match="offload_ckpt"):
+        Trainer(cfg, synth.AdamCfg(), **kw)
+
+
 def test_device_entries_reject_bad_arguments_before_any_launch(lib):
     """The layer, head and bind entry points check shapes, pointers, alignment
     and buffer sizes on the host and return the documented code (with a
