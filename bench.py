@@ -317,7 +317,7 @@ def main():
                     help="hold the checkpoints of the first N blocks in host memory (long contexts)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU sharding or collectives; "
+        print("bench.py measures one GPU only: the library has no multi-GPU sharding or collectives; "
               "run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
