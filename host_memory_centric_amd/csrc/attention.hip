@@ -435,8 +435,8 @@ __global__ __launch_bounds__(ATT_PP_THREADS) __attribute__((amdgpu_waves_per_eu(
     __syncthreads();
     // Group 0 runs M(j) in phase 2j+2 and V(j) in phase 2j+1, group 1 one
     // phase later (its extra barrier comes first, group 0's last).  The loads
-    // of slot j+2 go out in phase 2j+2 (group 0 at the start of M(j), group 1
-    // at the start of V(j)) and are waited for at the end of phase 2j+3.
+    // of slot j+2 go out in phase 2j+2 (group 0 after its M(j) cluster, group
+    // 1 at the start of V(j)) and are waited for at the end of phase 2j+3.
     auto fence = [&](bool wait) __attribute__((always_inline)) {
         if (wait) __builtin_amdgcn_s_waitcnt(0);
         __builtin_amdgcn_sched_barrier(0);
@@ -450,8 +450,11 @@ __global__ __launch_bounds__(ATT_PP_THREADS) __attribute__((amdgpu_waves_per_eu(
     };
     auto mstep = [&](const uint16_t* __restrict__ Ks, const uint16_t* __restrict__ Vs, uint16_t* __restrict__ kl,
                      uint16_t* __restrict__ vl, int j) __attribute__((always_inline)) {
-        if (grp == 0 && j + 2 <= NT) load_slot(j + 2, kl, vl);
         mcluster(Ks, Vs, j);
+        // after the cluster: the compiler makes every LDS read wait for the
+        // wave's outstanding direct loads, so loads issued before the reads
+        // would be waited for at once
+        if (grp == 0 && j + 2 <= NT) load_slot(j + 2, kl, vl);
         fence(grp == 1);
     };
     if (grp == 1) fence(false);
