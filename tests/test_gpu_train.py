@@ -126,6 +126,19 @@ def test_offloaded_checkpoints_bit_identical(gpu):
         assert losses == ref_losses, name
         for key, a in ref_regions.items():
             assert np.array_equal(regions[key], a), (name, key)
+    # ragged blocks (7 layers in blocks of 2, 2, 2, 1), two of them in host memory
+    cfg7 = synth.preset("tiny", layers=7, ckpt_every=2, seq=100)
+    bits7 = synth.make_weights(cfg7)
+    r7 = {}
+    for name, kw in {"k2": dict(), "k2_h2": dict(offload_ckpt=2)}.items():
+        tr = _trainer(cfg7, bits7, **kw)
+        try:
+            r7[name] = ([tr.step(synth.make_tokens(cfg7, s)) for s in range(2)], _store_regions(tr))
+        finally:
+            tr.close()
+    assert r7["k2"][0] == r7["k2_h2"][0]
+    for key, a in r7["k2"][1].items():
+        assert np.array_equal(r7["k2_h2"][1][key], a), key
     # micro-batches: two passes per step, each with its own copies out and back
     mb = {}
     for name, kw in {"mb": dict(), "mb_h3": dict(offload_ckpt=3)}.items():
