@@ -201,9 +201,13 @@ int mt_pinned_alloc(size_t bytes, void** out);
 int mt_pinned_free(void* p);
 
 /* Host memory copy with the library's threads and non-temporal stores (the
- * packer's copy), for staging between pageable buffers and pinned slabs, e.g.
- * block checkpoints kept in host memory.  dst and src must not overlap
- * (MT_E_ARG).  Synchronous. */
+ * packer's copy), for staging between pageable buffers and pinned slabs.  Its
+ * user is an extension of the pages' design: block checkpoints held in host
+ * memory for long contexts at full depth (the pages keep activations on the
+ * GPU and bound them per block: paper page, section 3 execution workflow;
+ * 512K-token runs: section 4, long-context training).  dst and src must not
+ * overlap (MT_E_ARG); NULL pointers are MT_E_ARG; 0 bytes is a no-op.
+ * Synchronous. */
 int mt_host_copy(void* dst, const void* src, size_t bytes);
 
 /* Asynchronous copies on a caller stream (hipStream_t passed as void*):
