@@ -146,7 +146,9 @@ __global__ __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(2, 
     const int qb = nqb - 1 - (int)blockIdx.x;  // most work first
     const int bh = blockIdx.y;
     const int b = bh / heads, head = bh % heads;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, half = lane >> 5;
+    const int lane = threadIdx.x & 63, half = lane >> 5;
+    // the wave index is uniform: conditions on it become scalar branches
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t H = (int64_t)heads * HD, ld = 3 * H;
     const uint16_t* Qg = qkv + (int64_t)b * S * ld + (int64_t)head * HD;
     const uint16_t* Kg = Qg + H;
@@ -305,6 +307,7 @@ __global__ __launch_bounds__(ATT_PP_THREADS) __attribute__((amdgpu_waves_per_eu(
     const int bh = blockIdx.y;
     const int b = bh / heads, head = bh % heads;
     const int lane = threadIdx.x & 63, half = lane >> 5;
+    // the wave index is uniform: conditions on it become scalar branches
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int grp = wave >> 2, w4 = wave & 3;
     const int64_t H = (int64_t)heads * HD, ld = 3 * H;
@@ -526,7 +529,9 @@ __global__ __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(2, 
     const int qb = nqb - 1 - (int)blockIdx.x;
     const int bh = blockIdx.y;
     const int b = bh / heads, head = bh % heads;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, half = lane >> 5;
+    const int lane = threadIdx.x & 63, half = lane >> 5;
+    // the wave index is uniform: conditions on it become scalar branches
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t H = (int64_t)heads * HD, ld = 3 * H;
     const uint16_t* Qg = qkv + (int64_t)b * S * ld + (int64_t)head * HD;
     const uint16_t* Kg = Qg + H;
@@ -641,7 +646,9 @@ __global__ __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(2, 
     const int kbk = (int)blockIdx.x;  // key block; low blocks (most work) first
     const int bh = blockIdx.y;
     const int b = bh / heads, head = bh % heads;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, half = lane >> 5;
+    const int lane = threadIdx.x & 63, half = lane >> 5;
+    // the wave index is uniform: conditions on it become scalar branches
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t H = (int64_t)heads * HD, ld = 3 * H;
     const uint16_t* Qg = qkv + (int64_t)b * S * ld + (int64_t)head * HD;
     const uint16_t* Kg = Qg + H;
@@ -706,16 +713,18 @@ __global__ __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(2, 
                                                                  dp, 0, 0, 0);
             }
             // mask only where this 32-query sub-tile reaches below this wave's keys or past the end
-            const bool edge = q0 + qt * 32 < k0 + 31 || q0 + qt * 32 + 32 > S || k0 + 32 > S;
+            // (a uniform condition: one branch around the whole mask)
+            if (q0 + qt * 32 < k0 + 31 || q0 + qt * 32 + 32 > S || k0 + 32 > S) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int q = q0 + qt * 32 + acc_row(r, half);
+                    if (kj > q || q >= S || kj >= S) s[r] = -INFINITY;
+                }
+            }
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int ql = qt * 32 + acc_row(r, half);
-                float sv = s[r];
-                if (edge) {
-                    const int q = q0 + ql;
-                    if (kj > q || q >= S || kj >= S) sv = -INFINITY;
-                }
-                const float pv = __builtin_amdgcn_exp2f(fmaf(sv, sl2, -ls[ql]));
+                const float pv = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, -ls[ql]));
                 if constexpr (GRAD_K)
                     s[r] = pv * (dp[r] - dd[ql]);  // dS
                 else
