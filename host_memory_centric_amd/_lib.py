@@ -18,7 +18,8 @@ MT_UNIT_HEAD = -2
 MT_STORE_MASTER_FP32 = 1
 MT_STORE_GRAD_ACCUM = 2
 MT_STORE_PINNED_DMA = 4
-ERRORS = {-1: "MT_E_ARG", -2: "MT_E_SHAPE", -3: "MT_E_ALIGN", -4: "MT_E_NOMEM", -5: "MT_E_HIP", -6: "MT_E_STATE"}
+ERRORS = {-1: "MT_E_ARG", -2: "MT_E_SHAPE", -3: "MT_E_ALIGN", -4: "MT_E_NOMEM", -5: "MT_E_HIP", -6: "MT_E_STATE",
+          -7: "MT_E_IO"}
 
 
 class MtError(RuntimeError):

@@ -62,8 +62,8 @@ void rope_apply(uint16_t* qkv, const float* cos, const float* sin, int64_t T, in
 void swiglu_fwd(const uint16_t* gu, uint16_t* a, int64_t T, int f, hipStream_t s);
 void swiglu_bwd(const uint16_t* da, const uint16_t* gu, uint16_t* dgu, int64_t T, int f, hipStream_t s);
 
-// Causal flash attention on a fused qkv buffer (scratch: transposed operand
-// copies, and the backward's row dot products).
+// Causal flash attention on a fused qkv buffer (scratch: the backward's row
+// dot products D = rowsum(dO * O); the forward needs none).
 size_t attention_fwd_ws_bytes(int B, int S, int heads, int hd);
 size_t attention_bwd_ws_bytes(int B, int S, int heads, int hd);
 void attention_fwd(const uint16_t* qkv, uint16_t* o, float* lse, int B, int S, int heads, int hd, void* ws,

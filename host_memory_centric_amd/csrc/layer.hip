@@ -65,7 +65,7 @@ struct BwdWs {
     uint16_t* dxm_b;  // its bf16 copy
     uint16_t* dout;   // gradient of the attention output [T, h]
     uint16_t* dqkv;   // [T, 3h]
-    void* attn;       // attention scratch (transposed operands, row dot products)
+    void* attn;       // attention scratch (the backward's row dot products)
     size_t attn_bytes;
     float* dg_part;   // RMSNorm gain partials [blocks, h]
     void* splitk;     // split-K partials

@@ -453,6 +453,9 @@ class Trainer:
         self.stats = {"step_s": time.perf_counter() - t0, "weight_loads": n_loads, "losses": losses}
         if tl is not None:
             self._tl = tl
+        # reporting only: every micro-batch's loss and gradients come from the
+        # head kernel (mt_head_fwd_bwd); their mean is the value returned to the
+        # caller and takes no part in the update
         return float(np.mean(np.asarray(losses, dtype=np.float64)))
 
     def _pass(self, tokens, t, final, tl):

@@ -384,7 +384,8 @@ int mt_op_gemm(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, int 
  * (q | k | v, head-major inside each), o bf16 [batch*seq, heads*hd],
  * lse fp32 [batch, heads, seq] (natural-log row logsumexp of the scaled
  * scores).  Scale 1/sqrt(hd).  hd in {64, 128}.  ws: device scratch of at
- * least mt_op_attention_ws_bytes (transposed operand copies). */
+ * least mt_op_attention_ws_bytes (the backward's per-row dot products
+ * D = rowsum(dO * O), fp32 [batch, heads, seq]; the forward needs none). */
 int mt_op_attention_fwd(int32_t batch, int32_t seq, int32_t heads, int32_t hd, const void* qkv, void* o,
                         float* lse, void* ws, size_t ws_bytes, void* stream);
 /* Its backward: writes dq | dk | dv into dqkv (same layout as qkv). */
