@@ -262,6 +262,196 @@ def layer_bwd(dy, c, W, cfg, cos, sin):
 
 
 # ----------------------------------------------------------------------------
+# one layer of a long sequence, for an output gradient that is zero outside a
+# few row blocks (the long-context shapes: the plain layer's S x S
+# probabilities and all-rows attention backward do not fit a CPU budget)
+# ----------------------------------------------------------------------------
+
+def _par(fn, items, workers=None):
+    """fn over independent items on a thread pool (numpy and BLAS release the
+    GIL inside array operations); returns the results in item order.  Only
+    evaluation order changes: each item's arithmetic is the same as in a
+    loop, and every sum across items is taken afterwards in item order."""
+    import os
+    from concurrent.futures import ThreadPoolExecutor
+    items = list(items)
+    n = workers or max(1, min(len(items), len(os.sched_getaffinity(0))))
+    if n == 1:
+        return [fn(it) for it in items]
+    with ThreadPoolExecutor(n) as ex:
+        return list(ex.map(fn, items))
+
+
+def _blas_one_thread():
+    """Context in which BLAS calls run single-threaded (used around thread
+    pools whose items each call BLAS, so the pools do not oversubscribe)."""
+    from threadpoolctl import threadpool_limits
+    return threadpool_limits(limits=1, user_api="blas")
+
+
+def _rope_rows(a, cos, sin, nh, hd, inverse=False):
+    """RoPE on token rows [n, nh*hd] whose positions are the rows of cos/sin
+    ([n, hd/2]): the rotation of rope_fwd (rope_bwd when ``inverse``) applied
+    to each head."""
+    n = a.shape[0]
+    ah = a.reshape(n, nh, hd).transpose(1, 0, 2)
+    r = rope_bwd(ah, cos, sin) if inverse else rope_fwd(ah, cos, sin)
+    return np.ascontiguousarray(r.transpose(1, 0, 2)).reshape(n, nh * hd)
+
+
+def layer_rows(x, W, cfg, cos, sin, blocks, dy_blocks, dx_blocks=None, wqkv_rows=None, chunk=16384):
+    """Forward and backward of one layer (layer_fwd / layer_bwd) on ONE
+    sequence x [S, h] (positions 0..S-1) when the output gradient dy is zero
+    outside the disjoint row ranges ``blocks`` = [(r0, r1), ...], with
+    dy[r0:r1] = dy_blocks[i].
+
+    Why this needs only those rows' queries: the layer is per token except
+    for attention, and a query s attends to keys 0..s.  With dy zero outside
+    the blocks, the MLP, the output projection and dO are zero outside them
+    too, so the attention backward has terms only for the blocks' queries:
+    dq lives on the block rows, while dk_j and dv_j collect, for every key
+    j <= s, the terms of those queries.  So the exact result needs the
+    softmax rows of the blocks' queries only (against all their keys), plus
+    per-token work on every row: the attention RMSNorm, the keys and values
+    with RoPE, the RoPE backward of dk, the QKV weight gradient (a reduction
+    over all S tokens), dn1 and the RMSNorm backward.
+
+    Per-token operations run in token chunks of ``chunk`` rows; attention
+    runs exactly (full softmax over keys 0..s, no online rescaling) per
+    (head, query block).  Sums over chunks, blocks and heads are taken in
+    that order.
+
+    dx_blocks: None for dx on all S rows (and the attention gain's
+    gradient, a sum over all rows); or a list of (r0, r1) ranges where dx is
+    wanted (the gain gradient is then not formed: None).  wqkv_rows: None for
+    the whole QKV weight gradient; or output-row indices of Wqkv whose
+    gradient rows are wanted (each still a sum over all S tokens).
+
+    Returns dict(y=[y rows of each block], dx=[S, h] array or [dx rows of each
+    dx block], dW={g_attn, wqkv (rows in wqkv_rows order if given), wo,
+    g_mlp, wgu, wd})."""
+    dt = x.dtype
+    S, h = x.shape
+    nh, hd, f = cfg.heads, cfg.head_dim, cfg.ffn
+    assert nh * hd == h and cos.shape[0] >= S
+    scale = dt.type(1.0 / np.sqrt(hd))
+    chunks = [(a, min(S, a + chunk)) for a in range(0, S, chunk)]
+    cos, sin = cos[:S], sin[:S]
+    wq, wk, wv = W["wqkv"][:h], W["wqkv"][h:2 * h], W["wqkv"][2 * h:]
+
+    # forward on every row: attention RMSNorm, keys (RoPE) and values
+    n1, xh1 = np.empty_like(x), np.empty_like(x)
+    r1 = np.empty((S, 1), dt)
+
+    def norm1(c):
+        a, b = c
+        n1[a:b], xh1[a:b], r1[a:b] = rmsnorm_fwd(x[a:b], W["g_attn"], cfg.eps)
+    _par(norm1, chunks)
+    k = n1 @ wk.T
+    v = n1 @ wv.T
+
+    def rope_k(c):
+        a, b = c
+        k[a:b] = _rope_rows(k[a:b], cos[a:b], sin[a:b], nh, hd)
+    _par(rope_k, chunks)
+
+    dW = {"wo": np.zeros_like(W["wo"]), "wgu": np.zeros_like(W["wgu"]), "wd": np.zeros_like(W["wd"]),
+          "g_mlp": np.zeros_like(W["g_mlp"])}
+    dk, dv = np.zeros_like(k), np.zeros_like(v)
+    ys, dq_blocks, dxm_blocks = [], [], []
+    for (r0, r1_), dy in zip(blocks, dy_blocks):
+        # forward of the block's rows: queries, attention per head, the rest per token
+        q = _rope_rows(n1[r0:r1_] @ wq.T, cos[r0:r1_], sin[r0:r1_], nh, hd)
+        future = np.arange(r1_)[None, :] > np.arange(r0, r1_)[:, None]
+        o = np.empty_like(q)
+        probs = [None] * nh
+
+        def attn(hh):
+            cols = slice(hh * hd, (hh + 1) * hd)
+            A = (q[:, cols] @ k[:r1_, cols].T) * scale
+            A[future] = -np.inf
+            A = A - A.max(axis=-1, keepdims=True)
+            E = np.exp(A)
+            P = E / E.sum(axis=-1, keepdims=True)
+            probs[hh] = P
+            o[:, cols] = P @ v[:r1_, cols]
+        with _blas_one_thread():
+            _par(attn, range(nh))
+        xm = x[r0:r1_] + o @ W["wo"].T
+        n2, xh2, r2 = rmsnorm_fwd(xm, W["g_mlp"], cfg.eps)
+        gu = n2 @ W["wgu"].T
+        gate, up = gu[:, :f], gu[:, f:]
+        a = swiglu_fwd(gate, up)
+        ys.append(xm + a @ W["wd"].T)
+        # backward of the block's rows (layer_bwd restricted to them)
+        dW["wd"] += dy.T @ a
+        dgate, dup = swiglu_bwd(dy @ W["wd"], gate, up)
+        dgu = np.concatenate([dgate, dup], axis=1)
+        dW["wgu"] += dgu.T @ n2
+        dxm_norm, dg = rmsnorm_bwd(dgu @ W["wgu"], xh2, r2, W["g_mlp"])
+        dW["g_mlp"] += dg
+        dxm = dy + dxm_norm
+        dxm_blocks.append(dxm)
+        dW["wo"] += dxm.T @ o
+        do = dxm @ W["wo"]
+        dq = np.empty_like(q)
+
+        def attn_bwd(hh):
+            cols = slice(hh * hd, (hh + 1) * hd)
+            P = probs[hh]
+            dv[:r1_, cols] += P.T @ do[:, cols]
+            dP = do[:, cols] @ v[:r1_, cols].T
+            D = np.sum(do[:, cols] * o[:, cols], axis=-1, keepdims=True)
+            dA = P * (dP - D)
+            dq[:, cols] = (dA @ k[:r1_, cols]) * scale
+            dk[:r1_, cols] += (dA.T @ q[:, cols]) * scale
+        with _blas_one_thread():
+            _par(attn_bwd, range(nh))
+        dq_blocks.append(_rope_rows(dq, cos[r0:r1_], sin[r0:r1_], nh, hd, inverse=True))
+        del probs
+
+    def rope_dk(c):
+        a, b = c
+        dk[a:b] = _rope_rows(dk[a:b], cos[a:b], sin[a:b], nh, hd, inverse=True)
+    _par(rope_dk, chunks)
+
+    def dqkv_rows(a, b):
+        """[b - a, 3h] gradient of the fused QKV output on rows a..b-1."""
+        d = np.concatenate([np.zeros((b - a, h), dt), dk[a:b], dv[a:b]], axis=1)
+        for (r0, r1_), dq in zip(blocks, dq_blocks):
+            lo, hi = max(a, r0), min(b, r1_)
+            if lo < hi:
+                d[lo - a:hi - a, :h] = dq[lo - r0:hi - r0]
+        return d
+
+    # QKV weight gradient: a reduction over all S tokens, chunk by chunk
+    sel = None if wqkv_rows is None else np.asarray(wqkv_rows)
+    dW["wqkv"] = np.zeros((3 * h if sel is None else len(sel), h), dt)
+    for a, b in chunks:
+        d = dqkv_rows(a, b)
+        dW["wqkv"] += (d if sel is None else d[:, sel]).T @ n1[a:b]
+
+    def dx_rows(a, b):
+        dxn, dg = rmsnorm_bwd(dqkv_rows(a, b) @ W["wqkv"], xh1[a:b], r1[a:b], W["g_attn"])
+        for (r0, r1_), dxm in zip(blocks, dxm_blocks):
+            lo, hi = max(a, r0), min(b, r1_)
+            if lo < hi:
+                dxn[lo - a:hi - a] += dxm[lo - r0:hi - r0]
+        return dxn, dg
+
+    if dx_blocks is None:
+        dx = np.empty_like(x)
+        dW["g_attn"] = np.zeros_like(W["g_attn"])
+        for a, b in chunks:
+            dx[a:b], dg = dx_rows(a, b)
+            dW["g_attn"] += dg
+    else:
+        dx = [dx_rows(a, b)[0] for a, b in dx_blocks]
+        dW["g_attn"] = None
+    return dict(y=ys, dx=dx, dW=dW)
+
+
+# ----------------------------------------------------------------------------
 # head: final RMSNorm, LM head, next-token cross entropy
 # ----------------------------------------------------------------------------
 

@@ -616,3 +616,54 @@ def test_tokens_and_normals_properties():
     # element i does not depend on how the tensor is chunked
     part = synth.normal_bf16_bits(0, 17, 1000, start=5000)
     assert np.array_equal(part, synth.normal_bf16_bits(0, 17, 6000)[5000:])
+
+
+# ----------------------------------------------------------------------------
+# the long-context layer mode: layer_rows equals the plain layer
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("chunk", [7, 64])
+def test_layer_rows_equals_plain_layer(chunk):
+    """layer_rows (per-token work in token chunks, attention per head and
+    query block, dy nonzero on a few row blocks only) reaches the plain
+    layer_fwd / layer_bwd result with the same dy, in fp64: y on the
+    blocks, dx on every row and every weight gradient; the sampled form
+    (dx on some row ranges, chosen QKV gradient rows) gives the same
+    entries.  A plausible slip in it (a missed key range, a block's dq on the
+    wrong rows, RoPE of dk skipped or the wrong way, a chunk boundary
+    dropped) changes some of these by far more than rounding."""
+    cfg = synth.preset("micro", batch=1, seq=41, layers=1)
+    rng = np.random.default_rng(5)
+    W = _rand_weights(cfg, rng)["layers"][0]
+    S, h = cfg.seq, cfg.hidden
+    x = rng.standard_normal((S, h))
+    blocks = [(0, 5), (17, 23), (36, 41)]
+    dy = np.zeros((S, h))
+    for a, b in blocks:
+        dy[a:b] = rng.standard_normal((b - a, h))
+    cos, sin = oracle.rope_tables(S, cfg.head_dim, cfg.rope_base)
+    y_ref, cache = oracle.layer_fwd(x, W, cfg, cos, sin)
+    dx_ref, dW_ref = oracle.layer_bwd(dy, cache, W, cfg, cos, sin)
+
+    def close(a, b):
+        assert np.abs(a - b).max() <= 1e-11 * max(1.0, np.abs(b).max())
+
+    r = oracle.layer_rows(x, W, cfg, cos, sin, blocks, [dy[a:b] for a, b in blocks], chunk=chunk)
+    for (a, b), yb in zip(blocks, r["y"]):
+        close(yb, y_ref[a:b])
+    close(r["dx"], dx_ref)
+    for name, g in dW_ref.items():
+        close(r["dW"][name], g)
+    # dk and dv reach rows outside the blocks: dx there is not just the residual
+    assert np.abs(dx_ref[6:17]).max() > 1e-3
+
+    sel = [1, h + 3, 2 * h + 60, 3 * h - 1]
+    dxb = [(2, 9), (30, 41)]
+    r2 = oracle.layer_rows(x, W, cfg, cos, sin, blocks, [dy[a:b] for a, b in blocks], dx_blocks=dxb,
+                           wqkv_rows=sel, chunk=chunk)
+    for (a, b), d in zip(dxb, r2["dx"]):
+        close(d, dx_ref[a:b])
+    close(r2["dW"]["wqkv"], dW_ref["wqkv"][sel])
+    assert r2["dW"]["g_attn"] is None
+    for name in ("wo", "wgu", "wd", "g_mlp"):
+        close(r2["dW"][name], dW_ref[name])
