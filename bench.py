@@ -7,7 +7,7 @@ tokens/s (value), executed and model TFLOPS against the bf16 dense MFMA peak,
 host-link GB/s, the live-measured roofline of the dominant kernel, and the
 CPU oracle timed on a bounded sample of the same workload.
 
-    python bench.py [--steps K] [--warmup W] [--workload 7b] [--mode streamed]
+    python bench.py [--steps K] [--warmup W] [--workload 14b] [--mode streamed]
 """
 import argparse
 import json
@@ -236,53 +236,71 @@ def link_probe(tr, nbytes=1 << 30, reps=3):
             "bidir_d2h_GBps": both["d2h"], "probe_bytes": nbytes}
 
 
-def cpu_baseline(cfg, seconds_hint=""):
-    """Time the oracle (fp32 numpy) on one sequence through one layer
-    (forward + backward), the head, and one layer's Adam; scale to the step."""
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def cpu_baseline(cfg):
+    """The fp32 CPU oracle on this host, timed on a bounded sample of the
+    step: one whole layer forward + backward over the full batch (every
+    token of the step), the head (final norm, LM head, cross entropy and
+    their backward) over the full batch, and one layer's Adam; the step's
+    time is extrapolated from them (layers x (layer + Adam) + head + the
+    embedding's and head's Adam at the layer's rate per parameter)."""
     import numpy as np
     from threadpoolctl import threadpool_info
 
     import oracle
     import synth
 
-    rng = np.random.default_rng(0)
-    S, h, V = cfg.seq, cfg.hidden, cfg.vocab
-    sub = cfg.with_(batch=1)
-    std = 0.02
-    W = {k: (rng.standard_normal(shp, dtype=np.float32) * std if not k.startswith("g_") else np.ones(shp, np.float32))
-         for k, shp in synth.layer_tensor_shapes(cfg).items()}
-    W = {k: oracle.bf16_round(v) for k, v in W.items()}
-    x = oracle.bf16_round(rng.standard_normal((S, h), dtype=np.float32))
-    dy = rng.standard_normal((S, h), dtype=np.float32) * 1e-3
+    B, S, h, V, f = cfg.batch, cfg.seq, cfg.hidden, cfg.vocab, cfg.ffn
+    T = B * S
+    W = {}
+    for j, (k, shp) in enumerate(synth.layer_tensor_shapes(cfg).items()):
+        W[k] = (np.ones(shp, np.float32) if k.startswith("g_") else
+                synth.bf16_bits_to_f32(synth.torch_normal_bf16_bits(500 + j, shp, std=0.02)))
+    x = synth.bf16_bits_to_f32(synth.torch_normal_bf16_bits(510, (T, h), std=1.0))
+    dy = synth.bf16_bits_to_f32(synth.torch_normal_bf16_bits(511, (T, h), std=1e-3))
     cos, sin = oracle.rope_tables(S, cfg.head_dim, cfg.rope_base)
     t0 = time.perf_counter()
-    y, cache = oracle.layer_fwd(x, W, sub, cos, sin)
-    oracle.layer_bwd(dy, cache, W, sub, cos, sin)
+    y, cache = oracle.layer_fwd(x, W, cfg, cos, sin)
+    oracle.layer_bwd(dy, cache, W, cfg, cos, sin)
     t_layer = time.perf_counter() - t0
     del cache
-    head = oracle.bf16_round(rng.standard_normal((V, h), dtype=np.float32) * std)
-    tok = synth.tokens(0, V, 1, S)
+    head = synth.bf16_bits_to_f32(synth.torch_normal_bf16_bits(512, (V, h), std=0.02))
+    tok = synth.tokens(0, V, B, S)
     t0 = time.perf_counter()
-    oracle.head_fwd_bwd(y, np.ones(h, np.float32), head, tok, sub)
+    oracle.head_fwd_bwd(y, np.ones(h, np.float32), head, tok, cfg)
     t_head = time.perf_counter() - t0
+    del head, y
     P_L = sum(v.size for v in W.values())
     t0 = time.perf_counter()
-    for k, v in W.items():
-        oracle.adam_update(synth.f32_to_bf16_bits(v), dy.reshape(-1)[: v.size].reshape(v.shape) if v.size <= dy.size
-                           else np.full(v.shape, 1e-3, np.float32), np.zeros(v.shape, np.float32),
+    for j, (k, v) in enumerate(W.items()):
+        g = synth.bf16_bits_to_f32(synth.torch_normal_bf16_bits(520 + j, v.shape, std=1e-3))
+        oracle.adam_update(synth.f32_to_bf16_bits(v), g, np.zeros(v.shape, np.float32),
                            np.zeros(v.shape, np.float32), synth.AdamCfg(), 1)
     t_adam = time.perf_counter() - t0
+    lin = 2.0 * T * (4 * h * h + 3 * h * f)
+    attn = 2.0 * B * S * (S + 1) * h
+    flops = 3 * lin + 3.5 * attn + 6.0 * T * h * V  # the sample's forward + backward
     sample_s = t_layer + t_head + t_adam
-    scale_b = cfg.batch  # the sample is one of the batch's sequences
-    t_step = cfg.layers * (t_layer * scale_b + t_adam) + t_head * scale_b + t_adam * (2 * V * h + h) / P_L
+    t_step = cfg.layers * (t_layer + t_adam) + t_head + t_adam * (2 * V * h + h) / P_L
     blas = [i.get("num_threads") for i in threadpool_info() if i.get("user_api") == "blas"]
-    cores = max(blas) if blas else 1
-    return {"value": round(cfg.tokens / t_step, 3), "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": (f"fp32 oracle on 1 of {cfg.batch} sequences ({S} tokens): one layer forward+backward "
-                       f"{t_layer:.2f} s, head forward+backward {t_head:.2f} s, one layer's Adam {t_adam:.2f} s "
-                       f"(total {sample_s:.1f} s), scaled to {cfg.layers} layers x {cfg.batch} sequences plus "
-                       f"embedding/head Adam"),
-            "step_s_est": round(t_step, 2)}
+    return {"value": round(T / t_step, 3), "unit": "tokens/s", "cores": len(os.sched_getaffinity(0)),
+            "kind": "oracle",
+            "sample": (f"fp32 numpy oracle on the full batch ({B} x {S} tokens): one layer forward+backward "
+                       f"{t_layer:.2f} s, head forward+backward {t_head:.2f} s, one layer's Adam ({P_L} params) "
+                       f"{t_adam:.2f} s (total {sample_s:.1f} s); the step is {cfg.layers} x (layer + Adam) + head "
+                       f"+ embedding/head Adam"),
+            "step_s_est": round(t_step, 2), "blas_threads": int(max(blas)) if blas else None,
+            "cpu_model": _cpu_model(), "fp32_gflops": round(flops / (t_layer + t_head) / 1e9, 1)}
 
 
 def main():
@@ -290,7 +308,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--workload", default="7b", choices=WORKLOADS)
+    ap.add_argument("--workload", default="14b", choices=WORKLOADS)
     ap.add_argument("--mode", default="streamed", choices=["streamed", "resident"])
     ap.add_argument("--slots", type=int, default=2)
     ap.add_argument("--grad-slabs", type=int, default=16)
@@ -469,6 +487,17 @@ def main():
     host["floor_ms"] = round(1e3 * host_bytes / (max(host["pack_GBps"] or 0, host["adam_GBps"]) * 1e9), 1)
     host["floor_frac_of_step"] = round(host["floor_ms"] / ms_step, 3)
     out["host"] = host
+    # the three floors of a streamed step: the host link (the step's H2D and
+    # D2H bytes at the probed rates), host DRAM (above) and the GPU's own
+    # busy time (compute stream, from the timeline step); the step's time
+    # against the largest of them
+    floors = {"link_ms": round(1e3 * max(h2d / (link["h2d_GBps"] * 1e9), d2h / (link["d2h_GBps"] * 1e9)), 1),
+              "host_dram_ms": host["floor_ms"],
+              "gpu_busy_ms": (round(overlap["compute_busy_frac"] * overlap["step_ms"], 1) if overlap else None)}
+    bind = max((k for k in floors if floors[k] is not None), key=lambda k: floors[k])
+    floors.update(binding=bind, binding_frac_of_step=round(floors[bind] / ms_step, 3),
+                  tflops_exec_at_binding=round(f_exec / (floors[bind] * 1e-3) / 1e12, 1))
+    out["floors"] = floors
     tr.close()
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg)

@@ -8,7 +8,7 @@ import oracle
 import synth
 from host_memory_centric_amd.store import REGION_G, REGION_M, REGION_V, REGION_W
 
-from parity import check_step, sync_from_oracle
+from parity import check_step, snapshot_weights, sync_from_oracle
 
 pytestmark = pytest.mark.gpu
 
@@ -35,8 +35,9 @@ def test_tiny_steps_match_oracle(gpu, mode, pinned):
         for step in range(2):
             tok = synth.make_tokens(cfg, step)
             loss = tr.step(tok)
+            prev = snapshot_weights(st)
             res = oracle.train_step(st, tok, cfg, adam, mode="resident")
-            check_step(tr, loss, res, cfg)
+            check_step(tr, loss, res, cfg, w_prev=prev)
             # continue both from the oracle's state so the second step is
             # checked on identical inputs
             sync_from_oracle(tr, st, cfg)
@@ -91,8 +92,9 @@ def test_ragged_blocks_and_sequence(gpu):
     tr = _trainer(cfg, bits, n_slots=2)
     try:
         loss = tr.step(tok)
+        prev = snapshot_weights(st)
         res = oracle.train_step(st, tok, cfg, adam, mode="resident")
-        check_step(tr, loss, res, cfg)
+        check_step(tr, loss, res, cfg, w_prev=prev)
     finally:
         tr.close()
 
@@ -182,8 +184,9 @@ def test_micro_batches_with_master_match_oracle(gpu, mode):
         for step in range(2):
             mb = [synth.make_tokens(cfg, 2 * step), synth.make_tokens(cfg, 2 * step + 1)]
             loss = tr.step(np.concatenate(mb, axis=0))
+            prev = snapshot_weights(st)
             res = oracle.train_step(st, mb, cfg, adam)
-            check_step(tr, loss, res, cfg)
+            check_step(tr, loss, res, cfg, w_prev=prev)
             for got, ref in zip(tr.stats["losses"], res["losses"]):
                 assert abs(got - float(ref)) <= 1e-3 * abs(float(ref))
             sync_from_oracle(tr, st, cfg)
@@ -266,6 +269,52 @@ def test_resume_from_checkpoint_is_bit_identical(gpu, tmp_path):
         assert np.array_equal(rc[key], x), key
 
 
+@pytest.mark.parametrize("kw", [dict(), dict(micro_batches=2, master=True)], ids=["plain", "micro2_master"])
+def test_resumed_run_matches_oracle(gpu, tmp_path, kw):
+    """A run checkpointed after its first step and resumed in a fresh trainer
+    (whose own state is first moved by a step of its own, so only the loaded
+    checkpoint can give the right state) matches the oracle's three steps:
+    each GPU step starts from the oracle's state and is checked against the
+    oracle's step at the parity bar, including the Adam step counter that
+    the checkpoint carries (its bias corrections enter every update)."""
+    cfg = synth.preset("tiny")
+    bits = synth.make_weights(cfg)
+    adam = synth.AdamCfg()
+    n = kw.get("micro_batches", 1)
+    st = oracle.HostState(bits, master=kw.get("master", False))
+
+    def toks(s):
+        mb = [synth.make_tokens(cfg, n * s + i) for i in range(n)]
+        return np.concatenate(mb, axis=0), (mb if n > 1 else mb[0])
+
+    path = tmp_path / "resume.ckpt"
+    a = _trainer(cfg, bits, **kw)
+    try:
+        tk, otk = toks(0)
+        loss = a.step(tk)
+        prev = snapshot_weights(st)
+        res = oracle.train_step(st, otk, cfg, adam)
+        check_step(a, loss, res, cfg, w_prev=prev)
+        sync_from_oracle(a, st, cfg)
+        a.save(path)
+    finally:
+        a.close()
+    b = _trainer(cfg, bits, **kw)
+    try:
+        b.step(toks(7)[0])  # a state of its own, overwritten by the load
+        b.load(path)
+        assert b.t == 1
+        for s in (1, 2):
+            tk, otk = toks(s)
+            loss = b.step(tk)
+            prev = snapshot_weights(st)
+            res = oracle.train_step(st, otk, cfg, adam)
+            check_step(b, loss, res, cfg, w_prev=prev)
+            sync_from_oracle(b, st, cfg)
+    finally:
+        b.close()
+
+
 def test_tied_embeddings_match_oracle_and_schedules_agree(gpu):
     """Weight tying on the tiny model: the head's slot carries the embedding
     matrix, its gradient is summed with the embedding's on the host, one
@@ -282,8 +331,9 @@ def test_tied_embeddings_match_oracle_and_schedules_agree(gpu):
         for step in range(2):
             tok = synth.make_tokens(cfg, step)
             loss = tr.step(tok)
+            prev = snapshot_weights(st)
             res = oracle.train_step(st, tok, cfg, adam)
-            check_step(tr, loss, res, cfg)
+            check_step(tr, loss, res, cfg, w_prev=prev)
             sync_from_oracle(tr, st, cfg)
     finally:
         tr.close()
