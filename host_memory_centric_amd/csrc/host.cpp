@@ -16,6 +16,8 @@
 
 #include <algorithm>
 #include <atomic>
+#include <condition_variable>
+#include <functional>
 #include <cmath>
 #include <cerrno>
 #include <cstdarg>
@@ -127,8 +129,113 @@ static int n_threads() {
 // Threads of the optimizer calls (mt_step, mt_grad_accumulate); 0: n_threads().
 static std::atomic<int> g_opt_threads{0};
 
+// One persistent pool of host workers shared by every parallel host pass
+// (packer copies, Adam, accumulation, embedding gradient, fill, save/load).
+// A pass is a job split into chunks; the calling thread works on its own
+// job's chunks and the pool's workers help, taking chunks from the active
+// job of highest priority: the packer's copies (priority 1, on the weight
+// stream's critical path) go before optimizer work (priority 0) when both
+// run at once.  No thread is created per call; passes from several host
+// threads run concurrently on the same workers.
+class WorkerPool {
+  public:
+    struct Job {
+        uint64_t n = 0, grain = 1, chunks = 0;
+        const std::function<void(uint64_t, uint64_t)>* fn = nullptr;
+        int prio = 0;
+        int max_helpers = 0;               // workers allowed on the job at once (besides the caller)
+        std::atomic<uint64_t> next{0};
+        std::atomic<uint64_t> done{0};
+        int helpers = 0;                   // workers inside a chunk of this job (pool mutex)
+        std::exception_ptr err;
+        std::mutex err_mu;
+
+        // Runs chunks until none is left; returns the number run.
+        uint64_t work(bool one) {
+            uint64_t ran = 0;
+            for (;;) {
+                const uint64_t c = next.fetch_add(1);
+                if (c >= chunks) break;
+                try {
+                    (*fn)(c * grain, std::min(n, (c + 1) * grain));
+                } catch (...) {
+                    std::lock_guard<std::mutex> lk(err_mu);
+                    if (!err) err = std::current_exception();
+                }
+                done.fetch_add(1);
+                ++ran;
+                if (one) break;
+            }
+            return ran;
+        }
+    };
+
+    static WorkerPool& get() {
+        static WorkerPool* pool = new WorkerPool();  // never destroyed: workers may outlive static destructors
+        return *pool;
+    }
+
+    void run(Job& j) {
+        ensure_workers();
+        {
+            std::lock_guard<std::mutex> lk(mu_);
+            active_.push_back(&j);
+        }
+        cv_work_.notify_all();
+        j.work(false);
+        std::unique_lock<std::mutex> lk(mu_);
+        cv_done_.wait(lk, [&] { return j.done.load() == j.chunks && j.helpers == 0; });
+        active_.erase(std::find(active_.begin(), active_.end(), &j));
+    }
+
+  private:
+    std::mutex mu_;
+    std::condition_variable cv_work_, cv_done_;
+    std::vector<Job*> active_;
+    std::vector<std::thread> workers_;
+
+    // Grows the pool to n_threads() - 1 workers (the caller is the n-th).
+    void ensure_workers() {
+        const int want = n_threads() - 1;
+        std::lock_guard<std::mutex> lk(mu_);
+        while ((int)workers_.size() < want) {
+            workers_.emplace_back([this] { loop(); });
+            workers_.back().detach();
+        }
+    }
+
+    Job* pick() {  // under mu_: the highest-priority job with chunks left and room for a helper
+        Job* best = nullptr;
+        for (Job* j : active_)
+            if (j->next.load() < j->chunks && j->helpers < j->max_helpers && (!best || j->prio > best->prio))
+                best = j;
+        return best;
+    }
+
+    void loop() {
+        for (;;) {
+            Job* j;
+            {
+                std::unique_lock<std::mutex> lk(mu_);
+                cv_work_.wait(lk, [&] { return (j = pick()) != nullptr; });
+                ++j->helpers;
+            }
+            j->work(true);  // one chunk, then look again: a higher-priority job may have arrived
+            bool finished;
+            {
+                std::lock_guard<std::mutex> lk(mu_);
+                --j->helpers;
+                finished = j->done.load() == j->chunks && j->helpers == 0;
+            }
+            if (finished) cv_done_.notify_all();
+        }
+    }
+};
+
+// Blocking parallel-for over [0, n) in chunks of `grain` on the worker pool;
+// at most max_threads threads (0: all) work on it, the caller included.
 template <class F>
-static void parallel_for(uint64_t n, uint64_t grain, F&& fn, int max_threads = 0) {
+static void parallel_for(uint64_t n, uint64_t grain, F&& fn, int max_threads = 0, int prio = 0) {
     if (n == 0) return;
     const uint64_t chunks = (n + grain - 1) / grain;
     const int nt = (int)std::min<uint64_t>(chunks, (uint64_t)(max_threads > 0 ? max_threads : n_threads()));
@@ -136,27 +243,16 @@ static void parallel_for(uint64_t n, uint64_t grain, F&& fn, int max_threads = 0
         fn(0, n);
         return;
     }
-    std::atomic<uint64_t> next{0};
-    std::exception_ptr err;
-    std::mutex err_mu;
-    auto work = [&]() {
-        try {
-            for (;;) {
-                const uint64_t c = next.fetch_add(1);
-                if (c >= chunks) break;
-                fn(c * grain, std::min(n, (c + 1) * grain));
-            }
-        } catch (...) {
-            std::lock_guard<std::mutex> lk(err_mu);
-            if (!err) err = std::current_exception();
-        }
-    };
-    std::vector<std::thread> ts;
-    ts.reserve(nt - 1);
-    for (int i = 0; i < nt - 1; ++i) ts.emplace_back(work);
-    work();
-    for (auto& t : ts) t.join();
-    if (err) std::rethrow_exception(err);
+    const std::function<void(uint64_t, uint64_t)> f = [&](uint64_t b, uint64_t e) { fn(b, e); };
+    WorkerPool::Job j;
+    j.n = n;
+    j.grain = grain;
+    j.chunks = chunks;
+    j.fn = &f;
+    j.prio = prio;
+    j.max_helpers = nt - 1;
+    WorkerPool::get().run(j);
+    if (j.err) std::rethrow_exception(j.err);
 }
 
 static bool have_avx512();
@@ -186,7 +282,7 @@ static void par_memcpy(void* dst, const void* src, uint64_t bytes) {
             stream_copy((char*)dst + b, (const char*)src + b, e - b);
         else
             memcpy((char*)dst + b, (const char*)src + b, e - b);
-    });
+    }, 0, /*prio=*/1);
 }
 
 // ---------------------------------------------------------------------------
