@@ -226,14 +226,25 @@ class Trainer:
     done, while block b + 1's runs.  The last two ring blocks never leave the
     device.  Long contexts at full depth need it: a 7B-shaped block input is
     4.3 GB at 512K tokens.  Results are bit-identical to keeping them all on
-    the device."""
+    the device;
+    poison (debug): fill every buffer with NaN as soon as the event that
+    frees it fires -- a device weight slot after the op that last reads it
+    before a reload, a device gradient slot after the copy that evacuates
+    it, a pinned weight staging buffer after the copy that read it, a pinned
+    gradient slab after the update that consumed it -- so that any read that
+    the event ordering does not cover sees NaN;  delay_seed (debug): random
+    host-side delays (0-3 ms, seeded) before every packer and optimizer job.
+    With correct ordering neither changes a bit of the results."""
 
     def __init__(self, cfg, adam, mode="streamed", n_slots=2, n_grad_slabs=16, ckpt_every=None, weights=None,
                  device="cuda:0", capture_w32=False, timeline=False, micro_batches=1, master=False,
-                 pinned_store=False, update_order="arrival", offload_ckpt=0):
+                 pinned_store=False, update_order="arrival", offload_ckpt=0, poison=False, delay_seed=None):
         if update_order not in ("arrival", "urgent"):
             raise ValueError("update_order must be 'arrival' or 'urgent'")
         self.update_order = update_order
+        self.poison = bool(poison)
+        self._delay_rng = None if delay_seed is None else np.random.default_rng(delay_seed)
+        self._delay_mu = threading.Lock()
         if mode not in ("streamed", "resident"):
             raise ValueError("mode must be 'streamed' or 'resident'")
         _lib.load()
@@ -347,6 +358,27 @@ class Trainer:
         if capture_w32:
             for u in self.store.units:
                 self.w32[u] = np.zeros(self.store.layout_of(u).w_bytes // 2, dtype=np.float32)
+
+    def _debug_delay(self):
+        if self._delay_rng is not None:
+            with self._delay_mu:
+                d = float(self._delay_rng.uniform(0.0, 3e-3))
+            time.sleep(d)
+
+    def _tensor_ranges(self, lay):
+        """(byte offset, bytes) of each tensor of a unit layout (its padding excluded)."""
+        return [(int(lay.tensor_off[j]), 2 * int(lay.tensor_numel[j])) for j in range(lay.n_tensors)]
+
+    def _poison_dev(self, buf, lay):
+        """NaN (all-ones bytes) over the tensors of a device buffer in ``lay``'s
+        layout, on the current stream."""
+        for off, n in self._tensor_ranges(lay):
+            buf[off:off + n].fill_(0xFF)
+
+    def _poison_host(self, pinned, lay):
+        v = pinned.view(np.uint8, lay.w_bytes)
+        for off, n in self._tensor_ranges(lay):
+            v[off:off + n] = 0xFF
 
     def _w32_ptr(self, unit):
         a = self.w32.get(unit)
@@ -567,8 +599,11 @@ class Trainer:
             last[s] = i
 
         pending = dict(self.pending)  # updates of the previous step still running
+        # ops after which their slot is reloaded (the load waits for the op's event)
+        poison_slot_after = {slot_prev[i] for i in loads if slot_prev[i] is not None} if self.poison else set()
 
         def pack(j):
+            self._debug_delay()
             unit = self.op_unit[loads[j]]
             if self.direct:  # the copy reads the store itself: only wait for the update
                 f = pending.get(unit)
@@ -577,6 +612,9 @@ class Trainer:
                 return
             if j >= 2:
                 ready_ev[j - 2].synchronize()  # the copy that read this staging buffer is done
+                if self.poison:
+                    prev = self.op_unit[loads[j - 2]]
+                    self._poison_host(self.wslab[j % 2], self.lay_head_dev if prev == MT_UNIT_HEAD else self.lay)
             f = pending.get(unit)
             if f is not None:
                 f.result()  # the unit's update of the previous step has landed
@@ -633,6 +671,7 @@ class Trainer:
 
         def adam_layer(ev, unit, src):
             # src: the pinned slab holding the gradient, or None: already in G
+            self._debug_delay()
             ev.synchronize()
             if final:
                 call("mt_step", self.store.ptr, unit, src, ctypes.byref(self.madam), t, self._w32_ptr(unit))
@@ -643,9 +682,12 @@ class Trainer:
             try:
                 adam_layer(ev, unit, self.gslab[k].ptr)
             finally:
+                if self.poison:
+                    self._poison_host(self.gslab[k], self.lay)
                 slab_free.put(k)
 
         def adam_embed(ev):
+            self._debug_delay()
             ev.synchronize()
             if self.tied:  # the shared matrix: the head's gradient (in the head slab) plus the embedding's
                 head_grad = ctypes.c_void_p(self.head_gslab.ptr.value + self.lay_head_dev.tensor_off[1])
@@ -719,6 +761,8 @@ class Trainer:
                                   dx=self.dgrad[1 - cur], dxb=self.dgrad_b[1 - cur])
                     call("mt_layer_recompute_bwd", ctypes.byref(v), ctypes.byref(self.mcfg), ctypes.byref(a), sc)
                     cur = 1 - cur
+                if i in poison_slot_after:
+                    self._poison_dev(self.slots[slot], self.lay_head_dev if kind == "head" else self.lay)
                 ev = torch.cuda.Event(enable_timing=self.record_timeline)
                 ev.record(cs)
                 op_done[i] = ev
@@ -736,6 +780,8 @@ class Trainer:
                     if tl is not None:
                         tl["d2h"].append([self._ev(ds), d2h])
                     call("mt_copy_d2h", head_dst, _ptr(self.head_g), self.lay_head_dev.w_bytes, sd)
+                    if self.poison:
+                        self._poison_dev(self.head_g, self.lay_head_dev)
                     d2h.record(ds)
                 self.head_d2h = d2h
                 jobs[MT_UNIT_HEAD] = self.optimizer.submit(
@@ -759,6 +805,8 @@ class Trainer:
                     if tl is not None:
                         tl["d2h"].append([self._ev(ds), d2h])
                     call("mt_copy_d2h", g_dst, _ptr(self.gslots[g]), self.lay.w_bytes, sd)
+                    if self.poison:
+                        self._poison_dev(self.gslots[g], self.lay)
                     d2h.record(ds)
                     if l == 0:
                         d2h_x = torch.cuda.Event(enable_timing=self.record_timeline)

@@ -1,0 +1,103 @@
+"""The schedule's ordering and the device footprint, on the GPU.
+
+* Poison and delays: every buffer is filled with NaN as soon as the event
+  that frees it fires (device weight slots after their last reader,
+  device gradient slots after their evacuation, pinned staging buffers after
+  the copy that read them, pinned gradient slabs after the update that
+  consumed them), and the packer and optimizer threads sleep for random
+  times before each job.  A read or write that the events (weights-ready,
+  buffer-free, backward-done, copy completion) do not order would then see
+  NaN or land late; with correct ordering every loss and every host region
+  equals the clean run's bit for bit.
+* Footprint: at a fixed width the streamed step's device peak does not grow
+  with depth except by the one [T, h] bf16 block checkpoint per block.
+"""
+import numpy as np
+import pytest
+
+import synth
+from host_memory_centric_amd.store import REGION_G, REGION_M, REGION_V, REGION_W
+
+pytestmark = pytest.mark.gpu
+
+
+def _regions(tr):
+    tr.finish()
+    regions = (REGION_W, REGION_G, REGION_M, REGION_V) + ((4,) if tr.store.flags & 1 else ())
+    return {(u, r): tr.store.region(u, r).copy() for u in tr.store.units for r in regions}
+
+
+def _run(cfg, bits, steps, **kw):
+    from host_memory_centric_amd.engine import Trainer
+    n = kw.get("micro_batches", 1)
+    tr = Trainer(cfg, synth.AdamCfg(), weights=bits, **kw)
+    try:
+        losses = [tr.step(np.concatenate([synth.make_tokens(cfg, n * s + i) for i in range(n)])) for s in range(steps)]
+        regions = _regions(tr)
+        if kw.get("poison"):
+            # the poison did run: each device gradient slot was filled after its last
+            # evacuation, and (with slabs) every recycled gradient slab after its update
+            import torch
+            torch.cuda.synchronize()
+            for g in tr.gslots:
+                for off, nb in tr._tensor_ranges(tr.lay):
+                    assert bool((g[off:off + nb] == 0xFF).all())
+            off, nb = tr._tensor_ranges(tr.lay)[1]
+            poisoned = [bool((slab.view(np.uint8, tr.lay.w_bytes)[off:off + nb] == 0xFF).all()) for slab in tr.gslab]
+            assert not tr.gslab or any(poisoned)
+        return losses, regions
+    finally:
+        tr.close()
+
+
+@pytest.mark.parametrize("variant", ["k1_2slot", "k2_1slot", "k2_3slot_1slab", "pinned_k1_2slot",
+                                     "micro_master_k1_2slot", "tied_k2_2slot"])
+def test_poison_and_delays_change_no_bit(gpu, variant):
+    import dataclasses
+    kw = {"k1_2slot": dict(ckpt_every=1, n_slots=2),
+          "k2_1slot": dict(ckpt_every=2, n_slots=1),
+          "k2_3slot_1slab": dict(ckpt_every=2, n_slots=3, n_grad_slabs=1),
+          "pinned_k1_2slot": dict(ckpt_every=1, n_slots=2, pinned_store=True),
+          "micro_master_k1_2slot": dict(ckpt_every=1, n_slots=2, micro_batches=2, master=True),
+          "tied_k2_2slot": dict(ckpt_every=2, n_slots=2)}[variant]
+    cfg = synth.preset("tiny", layers=5, seq=100)
+    if variant.startswith("tied"):
+        cfg = dataclasses.replace(cfg, tied=True)
+    bits = synth.make_weights(cfg)
+    ref_losses, ref = _run(cfg, bits, 3, **kw)
+    assert all(np.isfinite(ref_losses))
+    for seed in (1, 2):
+        losses, regions = _run(cfg, bits, 3, poison=True, delay_seed=seed, **kw)
+        assert losses == ref_losses, (variant, seed, losses, ref_losses)
+        for key, a in ref.items():
+            assert np.array_equal(regions[key], a), (variant, seed, key)
+
+
+def test_device_peak_independent_of_depth(gpu):
+    """The 7B layer shape (hidden 4096, batch 4 x 2048) streamed with
+    checkpoints every 4 layers and 2 slots, at 8 and at 16 layers: the device
+    peak differs by exactly the two extra block checkpoints ([T, h] bf16,
+    64 MiB each); the weight slots, gradient slots, one block's internals and
+    the workspace are sized per layer."""
+    import torch
+
+    from host_memory_centric_amd.engine import Trainer
+    peaks = {}
+    for L in (8, 16):
+        cfg = synth.preset("7b", layers=L)
+        torch.cuda.empty_cache()
+        torch.cuda.reset_peak_memory_stats()
+        base = torch.cuda.memory_allocated()
+        tr = Trainer(cfg, synth.AdamCfg(), n_slots=2)
+        try:
+            tr.step(synth.make_tokens(cfg, 0))
+            tr.finish()
+            torch.cuda.synchronize()
+            peaks[L] = torch.cuda.max_memory_allocated() - base
+        finally:
+            tr.close()
+            del tr
+    ckpt = 4 * 2048 * 4096 * 2
+    blocks = {L: (L + 3) // 4 for L in peaks}
+    print(f"device peaks: {peaks}, block checkpoint {ckpt} bytes", flush=True)
+    assert peaks[16] - peaks[8] == (blocks[16] - blocks[8]) * ckpt, peaks
