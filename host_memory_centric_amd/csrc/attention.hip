@@ -48,6 +48,16 @@ constexpr int ATT_BQ = ATT_WAVES * 32;  // queries per workgroup (fwd, dQ)
 constexpr int ATT_BK = ATT_WAVES * 32;  // keys per workgroup (dK/dV)
 constexpr int ATT_T = 64;               // rows per streamed tile
 constexpr float LOG2E = 1.4426950408889634f;
+// fp16 attention: the probabilities enter the fp16 products multiplied by
+// 2^P16_EXP (they are at most 1, so at most 16384: far below fp16's 65504,
+// and a probability of 1/2^19 becomes 2^-5, a normal fp16 number)
+constexpr float P16_EXP = 14.f;
+constexpr float P16_SCALE = 16384.f;  // 2^P16_EXP
+// fp16 backward: dO is scaled per (batch, head) so that its largest element
+// lies in [2^11, 2^12), and dS so that its bound 2 |dO_q|_1 max|v| lies in
+// [2^12, 2^13) (fp16 holds up to 65504); both scales are powers of two.
+constexpr int DO16_TOP = 11;
+constexpr int DS16_TOP = 12;
 constexpr float LN2 = 0.6931471805599453f;
 
 typedef short att_v4s __attribute__((ext_vector_type(4)));
@@ -115,10 +125,32 @@ struct ATile {
     }
 };
 
-// B-operand fragment from 8 accumulator values (elements r0 .. r0+7 of a tile)
+// B-operand fragment from 8 accumulator values (elements r0 .. r0+7 of a
+// tile), rounded to bf16 (F16 = false) or fp16
+template <bool F16 = false>
 __device__ __forceinline__ bf16x8 frag_acc(const f32x16& a, int r0) {
-    return as_bf16x8(make_uint4(pack_bf2(a[r0 + 0], a[r0 + 1]), pack_bf2(a[r0 + 2], a[r0 + 3]),
-                                pack_bf2(a[r0 + 4], a[r0 + 5]), pack_bf2(a[r0 + 6], a[r0 + 7])));
+    if constexpr (F16)
+        return as_bf16x8(make_uint4(pack_h2(a[r0 + 0], a[r0 + 1]), pack_h2(a[r0 + 2], a[r0 + 3]),
+                                    pack_h2(a[r0 + 4], a[r0 + 5]), pack_h2(a[r0 + 6], a[r0 + 7])));
+    else
+        return as_bf16x8(make_uint4(pack_bf2(a[r0 + 0], a[r0 + 1]), pack_bf2(a[r0 + 2], a[r0 + 3]),
+                                    pack_bf2(a[r0 + 4], a[r0 + 5]), pack_bf2(a[r0 + 6], a[r0 + 7])));
+}
+
+// The forward's output rows: bf16 o and, when o16 is given, fp16 o16 (both
+// rounded from the same normalised fp32 accumulators).
+template <int HD>
+__device__ __forceinline__ void store_o(const f32x16* oacc, float inv_l, uint16_t* orow, uint16_t* orow16, int half) {
+#pragma unroll
+    for (int dt = 0; dt < HD / 32; ++dt)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int d = dt * 32 + 8 * g + 4 * half;
+            const float v0 = oacc[dt][4 * g] * inv_l, v1 = oacc[dt][4 * g + 1] * inv_l;
+            const float v2 = oacc[dt][4 * g + 2] * inv_l, v3 = oacc[dt][4 * g + 3] * inv_l;
+            *(uint2*)(orow + d) = make_uint2(pack_bf2(v0, v1), pack_bf2(v2, v3));
+            if (orow16) *(uint2*)(orow16 + d) = make_uint2(pack_h2(v0, v1), pack_h2(v2, v3));
+        }
 }
 
 __device__ __forceinline__ int acc_row(int r, int half) { return 8 * (r >> 2) + 4 * half + (r & 3); }
@@ -135,10 +167,10 @@ __device__ __forceinline__ void zero(f32x16& a) {
 // vector ALUs, the MFMAs of tile j+1's scores are already in flight.  K and V
 // have separate double buffers with staggered loads: during step j the LDS
 // holds K_{j+1} and V_j (read) while K_{j+2} and V_{j+1} arrive.
-template <int HD>
+template <int HD, bool F16 = false>
 __global__ __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_kernel(const uint16_t* __restrict__ qkv,
-                                                               uint16_t* __restrict__ o, float* __restrict__ lse, int S,
-                                                               int heads, float sl2) {
+                                                               uint16_t* __restrict__ o, uint16_t* __restrict__ o16,
+                                                               float* __restrict__ lse, int S, int heads, float sl2) {
     using TL = ATile<HD>;
     __shared__ __attribute__((aligned(1024))) uint16_t kbuf[2][TL::ELEMS];
     __shared__ __attribute__((aligned(1024))) uint16_t vbuf[2][TL::ELEMS];
@@ -178,8 +210,8 @@ __global__ __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(2, 
             zero(st[kt]);
 #pragma unroll
             for (int ds = 0; ds < HD / 16; ++ds)
-                st[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(TL::frag_row(Ks, kt * 32 + (lane & 31), ds, half),
-                                                                 as_bf16x8(qf[ds]), st[kt], 0, 0, 0);
+                st[kt] = mfma32x16<F16>(TL::frag_row(Ks, kt * 32 + (lane & 31), ds, half), as_bf16x8(qf[ds]),
+                                        st[kt]);
         }
     };
     auto softmax_pv = [&](f32x16* st, const uint16_t* Vs, int k0) {
@@ -201,12 +233,15 @@ __global__ __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(2, 
         mx = fmaxf(mx, __shfl_xor(mx, 32));
         const float m_new = fmaxf(m_run, mx * sl2);
         const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        // fp16 path: probabilities scaled by 2^P16_EXP (exact), so that the
+        // small ones of long rows stay normal fp16 numbers
+        const float m_sub = F16 ? m_new - P16_EXP : m_new;
         float ps = 0.f;
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const float p = __builtin_amdgcn_exp2f(fmaf(st[kt][r], sl2, -m_new));
+                const float p = __builtin_amdgcn_exp2f(fmaf(st[kt][r], sl2, -m_sub));
                 st[kt][r] = p;
                 ps += p;
             }
@@ -225,11 +260,10 @@ __global__ __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(2, 
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
-                const bf16x8 pb = frag_acc(st[kt], ks * 8);
+                const bf16x8 pb = frag_acc<F16>(st[kt], ks * 8);
 #pragma unroll
                 for (int dt = 0; dt < HD / 32; ++dt)
-                    oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(TL::frag_tr(Vs, dt * 32, kt * 2 + ks, lane), pb,
-                                                                       oacc[dt], 0, 0, 0);
+                    oacc[dt] = mfma32x16<F16>(TL::frag_tr(Vs, dt * 32, kt * 2 + ks, lane), pb, oacc[dt]);
             }
     };
 
@@ -261,17 +295,9 @@ __global__ __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(2, 
         __syncthreads();
     }
     if (qi < S) {
-        const float inv_l = 1.0f / l_run;
-        uint16_t* orow = o + ((int64_t)b * S + qi) * H + (int64_t)head * HD;
-#pragma unroll
-        for (int dt = 0; dt < HD / 32; ++dt)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int d = dt * 32 + 8 * g + 4 * half;
-                *(uint2*)(orow + d) = make_uint2(pack_bf2(oacc[dt][4 * g] * inv_l, oacc[dt][4 * g + 1] * inv_l),
-                                                 pack_bf2(oacc[dt][4 * g + 2] * inv_l, oacc[dt][4 * g + 3] * inv_l));
-            }
-        if (half == 0) lse[(int64_t)bh * S + qi] = (m_run + log2f(l_run)) * LN2;
+        const int64_t ro = ((int64_t)b * S + qi) * H + (int64_t)head * HD;
+        store_o<HD>(oacc, 1.0f / l_run, o + ro, o16 ? o16 + ro : nullptr, half);
+        if (half == 0) lse[(int64_t)bh * S + qi] = (m_run + log2f(l_run) - (F16 ? P16_EXP : 0.f)) * LN2;
     }
 }
 
@@ -296,9 +322,10 @@ constexpr int ATT_PP_WAVES = 8;
 constexpr int ATT_PP_THREADS = ATT_PP_WAVES * 64;
 constexpr int ATT_PP_BQ = ATT_PP_WAVES * 32;
 
-template <int HD>
+template <int HD, bool F16 = false>
 __global__ __launch_bounds__(ATT_PP_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_pp_kernel(
-    const uint16_t* __restrict__ qkv, uint16_t* __restrict__ o, float* __restrict__ lse, int S, int heads, float sl2) {
+    const uint16_t* __restrict__ qkv, uint16_t* __restrict__ o, uint16_t* __restrict__ o16, float* __restrict__ lse,
+    int S, int heads, float sl2) {
     using TL = ATile<HD>;
     __shared__ __attribute__((aligned(1024))) uint16_t kbuf[2][TL::ELEMS];
     __shared__ __attribute__((aligned(1024))) uint16_t vbuf[2][TL::ELEMS];
@@ -372,8 +399,8 @@ __global__ __launch_bounds__(ATT_PP_THREADS) __attribute__((amdgpu_waves_per_eu(
                 for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
                     for (int dt = 0; dt < HD / 32; ++dt)
-                        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                            TL::frag_tr(Vs, dt * 32, kt * 2 + ks, lane), pb[kt * 2 + ks], oacc[dt], 0, 0, 0);
+                        oacc[dt] = mfma32x16<F16>(TL::frag_tr(Vs, dt * 32, kt * 2 + ks, lane), pb[kt * 2 + ks],
+                                                  oacc[dt]);
         }
         __builtin_amdgcn_sched_barrier(0);
         if (j + 1 < nk_wave) {
@@ -382,8 +409,8 @@ __global__ __launch_bounds__(ATT_PP_THREADS) __attribute__((amdgpu_waves_per_eu(
                 zero(st[kt]);
 #pragma unroll
                 for (int ds = 0; ds < HD / 16; ++ds)
-                    st[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        TL::frag_row(Ks, kt * 32 + (lane & 31), ds, half), as_bf16x8(qf[ds]), st[kt], 0, 0, 0);
+                    st[kt] = mfma32x16<F16>(TL::frag_row(Ks, kt * 32 + (lane & 31), ds, half), as_bf16x8(qf[ds]),
+                                            st[kt]);
             }
         }
     };
@@ -408,12 +435,15 @@ __global__ __launch_bounds__(ATT_PP_THREADS) __attribute__((amdgpu_waves_per_eu(
         mx = fmaxf(mx, __shfl_xor(mx, 32));
         const float m_new = fmaxf(m_run, mx * sl2);
         const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        // fp16 path: probabilities scaled by 2^P16_EXP (exact), so that the
+        // small ones of long rows stay normal fp16 numbers
+        const float m_sub = F16 ? m_new - P16_EXP : m_new;
         float ps = 0.f;
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const float p = __builtin_amdgcn_exp2f(fmaf(st[kt][r], sl2, -m_new));
+                const float p = __builtin_amdgcn_exp2f(fmaf(st[kt][r], sl2, -m_sub));
                 st[kt][r] = p;
                 ps += p;
             }
@@ -429,7 +459,7 @@ __global__ __launch_bounds__(ATT_PP_THREADS) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) pb[kt * 2 + ks] = frag_acc(st[kt], ks * 8);
+            for (int ks = 0; ks < 2; ++ks) pb[kt * 2 + ks] = frag_acc<F16>(st[kt], ks * 8);
     };
 
     load_slot(0, kbuf[0], vbuf[0]);
@@ -473,17 +503,9 @@ __global__ __launch_bounds__(ATT_PP_THREADS) __attribute__((amdgpu_waves_per_eu(
     }
     if (grp == 0) fence(false);
     if (qi < S) {
-        const float inv_l = 1.0f / l_run;
-        uint16_t* orow = o + ((int64_t)b * S + qi) * H + (int64_t)head * HD;
-#pragma unroll
-        for (int dt = 0; dt < HD / 32; ++dt)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int d = dt * 32 + 8 * g + 4 * half;
-                *(uint2*)(orow + d) = make_uint2(pack_bf2(oacc[dt][4 * g] * inv_l, oacc[dt][4 * g + 1] * inv_l),
-                                                 pack_bf2(oacc[dt][4 * g + 2] * inv_l, oacc[dt][4 * g + 3] * inv_l));
-            }
-        if (half == 0) lse[(int64_t)bh * S + qi] = (m_run + log2f(l_run)) * LN2;
+        const int64_t ro = ((int64_t)b * S + qi) * H + (int64_t)head * HD;
+        store_o<HD>(oacc, 1.0f / l_run, o + ro, o16 ? o16 + ro : nullptr, half);
+        if (half == 0) lse[(int64_t)bh * S + qi] = (m_run + log2f(l_run) - (F16 ? P16_EXP : 0.f)) * LN2;
     }
 }
 
@@ -512,15 +534,124 @@ __global__ __launch_bounds__(256) void attn_bwd_pre_kernel(const uint16_t* __res
     dvec[(b * heads + head) * S + sidx] = s;
 }
 
+// fp16 backward, first pass, one thread per (token, head): D = rowsum(dO * O)
+// and the row statistics that bound the scaled operands: |dO_row|_1,
+// max |dO_row|, max |v_row| (v: the saved fp16 projection).
+template <int HD>
+__global__ __launch_bounds__(256) void attn_bwd_stats_kernel(const uint16_t* __restrict__ qkv16,
+                                                             const uint16_t* __restrict__ o,
+                                                             const uint16_t* __restrict__ dout,
+                                                             float* __restrict__ stats, int64_t T, int S, int heads) {
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= T * heads) return;
+    const int64_t t = idx / heads;
+    const int head = (int)(idx % heads);
+    const int64_t H = (int64_t)heads * HD;
+    const uint16_t* a = o + t * H + (int64_t)head * HD;
+    const uint16_t* c = dout + t * H + (int64_t)head * HD;
+    const uint16_t* vv = qkv16 + t * 3 * H + 2 * H + (int64_t)head * HD;
+    float d = 0.f, l1 = 0.f, mdo = 0.f, mv = 0.f;
+#pragma unroll
+    for (int i = 0; i < HD; i += 8) {
+        const uint4 x = *(const uint4*)(a + i), y = *(const uint4*)(c + i), z = *(const uint4*)(vv + i);
+        const uint32_t xw[4] = {x.x, x.y, x.z, x.w}, yw[4] = {y.x, y.y, y.z, y.w}, zw[4] = {z.x, z.y, z.z, z.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float y0 = bf_lo(yw[q]), y1 = bf_hi(yw[q]);
+            d += bf_lo(xw[q]) * y0 + bf_hi(xw[q]) * y1;
+            l1 += fabsf(y0) + fabsf(y1);
+            mdo = fmaxf(mdo, fmaxf(fabsf(y0), fabsf(y1)));
+            mv = fmaxf(mv, fmaxf(fabsf(h2f((uint16_t)(zw[q] & 0xffff))), fabsf(h2f((uint16_t)(zw[q] >> 16)))));
+        }
+    }
+    const int64_t b = t / S, sidx = t % S;
+    const int64_t r = (b * heads + head) * S + sidx;
+    const int64_t n = T * heads;
+    stats[r] = d;
+    stats[n + r] = l1;
+    stats[2 * n + r] = mdo;
+    stats[3 * n + r] = mv;
+}
+
+// 2^k with k an integer such that x * 2^k lies in [2^top, 2^(top+1)); 1 for x == 0.
+__device__ __forceinline__ float pow2_scale(float x, int top) {
+    if (!(x > 0.f)) return 1.f;
+    const int e = __builtin_amdgcn_frexp_expf(x) - 1;  // floor(log2 x)
+    return ldexpf(1.f, max(-120, min(120, top - e)));
+}
+
+// fp16 backward, second pass, one workgroup per (batch, head): the maxima of
+// the row statistics over the sequence and the two scales (dO, dS).
+__global__ __launch_bounds__(256) void attn_bwd_scale_kernel(const float* __restrict__ stats, float* __restrict__ sc,
+                                                             int64_t n, int S) {
+    __shared__ float red[3][4];
+    const int bh = blockIdx.x;
+    const float* l1 = stats + n + (int64_t)bh * S;
+    const float* mdo = stats + 2 * n + (int64_t)bh * S;
+    const float* mv = stats + 3 * n + (int64_t)bh * S;
+    float a = 0.f, b = 0.f, c = 0.f;
+    for (int i = threadIdx.x; i < S; i += 256) {
+        a = fmaxf(a, l1[i]);
+        b = fmaxf(b, mdo[i]);
+        c = fmaxf(c, mv[i]);
+    }
+    a = wave_max(a);
+    b = wave_max(b);
+    c = wave_max(c);
+    const int w = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) {
+        red[0][w] = a;
+        red[1][w] = b;
+        red[2][w] = c;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float l1m = 0.f, dom = 0.f, vm = 0.f;
+        for (int i = 0; i < 4; ++i) {
+            l1m = fmaxf(l1m, red[0][i]);
+            dom = fmaxf(dom, red[1][i]);
+            vm = fmaxf(vm, red[2][i]);
+        }
+        const float so = pow2_scale(dom, DO16_TOP);
+        const float ss = pow2_scale(2.f * l1m * so * vm, DS16_TOP);
+        sc[4 * bh] = so;
+        sc[4 * bh + 1] = ss;
+        sc[4 * bh + 2] = (float)(__builtin_amdgcn_frexp_expf(ss) - 1);  // log2 ss, exact
+        sc[4 * bh + 3] = 0.f;
+    }
+}
+
+// fp16 backward, third pass: dO16 = dO * so(batch, head), exact (a power of
+// two times a bf16 value inside fp16's range).
+__global__ void attn_bwd_do16_kernel(const uint16_t* __restrict__ dout, const float* __restrict__ sc,
+                                     uint16_t* __restrict__ do16, int64_t T, int S, int heads, int hd) {
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t H = (int64_t)heads * hd;
+    if (idx >= T * H / 8) return;
+    const int64_t e = idx * 8;
+    const int64_t t = e / H;
+    const int head = (int)((e % H) / hd);
+    const float so = sc[4 * ((t / S) * heads + head)];
+    const uint4 v = *(const uint4*)(dout + e);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    uint32_t out[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) out[q] = pack_h2(bf_lo(w[q]) * so, bf_hi(w[q]) * so);
+    *(uint4*)(do16 + e) = make_uint4(out[0], out[1], out[2], out[3]);
+}
+
 // ---------------------------------------------------------------------------
 // backward: dQ, one workgroup per 128 queries, loop over key tiles
 // ---------------------------------------------------------------------------
 // Two workgroups per CU (the LDS allows it; 256 registers per lane suffice).
-template <int HD>
+// F16: q, k, v, dO (scaled by so) and dS (scaled by so * ss) are fp16 (sc:
+// [batch*heads][so, ss, log2 ss, 0]); else all bf16 and sc unused.
+template <int HD, bool F16 = false>
 __global__ __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bwd_dq_kernel(const uint16_t* __restrict__ qkv,
                                                                   const float* __restrict__ lse,
                                                                   const uint16_t* __restrict__ dout,
                                                                   const float* __restrict__ dvec,
+                                                                  const float* __restrict__ sc,
                                                                   uint16_t* __restrict__ dqkv, int S, int heads,
                                                                   float sl2, float scale) {
     using TL = ATile<HD>;
@@ -551,8 +682,10 @@ __global__ __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(2, 
         }
     }
     const int64_t rowbase = (int64_t)bh * S;
-    const float lse2 = qi < S ? lse[rowbase + qi] * LOG2E : 0.f;
-    const float Dq = qi < S ? dvec[rowbase + qi] : 0.f;
+    const float so = F16 ? sc[4 * bh] : 1.f, ss = F16 ? sc[4 * bh + 1] : 1.f;
+    // (fp16: the scale of dS folded into the exponent of P, exactly)
+    const float lse2 = qi < S ? lse[rowbase + qi] * LOG2E - (F16 ? sc[4 * bh + 2] : 0.f) : 0.f;
+    const float Dq = qi < S ? dvec[rowbase + qi] * so : 0.f;
     f32x16 dq[HD / 32];
 #pragma unroll
     for (int dt = 0; dt < HD / 32; ++dt) zero(dq[dt]);
@@ -577,10 +710,8 @@ __global__ __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(2, 
 #pragma unroll
             for (int ds = 0; ds < HD / 16; ++ds) {
                 const int row = kt * 32 + (lane & 31);
-                st[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(TL::frag_row(Ks, row, ds, half), as_bf16x8(qf[ds]),
-                                                                 st[kt], 0, 0, 0);
-                dp[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(TL::frag_row(Vs, row, ds, half), as_bf16x8(df[ds]),
-                                                                 dp[kt], 0, 0, 0);
+                st[kt] = mfma32x16<F16>(TL::frag_row(Ks, row, ds, half), as_bf16x8(qf[ds]), st[kt]);
+                dp[kt] = mfma32x16<F16>(TL::frag_row(Vs, row, ds, half), as_bf16x8(df[ds]), dp[kt]);
             }
             if (k0 + ATT_T - 1 > q0 || k0 + ATT_T > S || q0 + 32 > S) {
 #pragma unroll
@@ -599,11 +730,10 @@ __global__ __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(2, 
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
-                const bf16x8 sb = frag_acc(st[kt], ks * 8);
+                const bf16x8 sb = frag_acc<F16>(st[kt], ks * 8);
 #pragma unroll
                 for (int dt = 0; dt < HD / 32; ++dt)
-                    dq[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(TL::frag_tr(Ks, dt * 32, kt * 2 + ks, lane), sb,
-                                                                     dq[dt], 0, 0, 0);
+                    dq[dt] = mfma32x16<F16>(TL::frag_tr(Ks, dt * 32, kt * 2 + ks, lane), sb, dq[dt]);
             }
     };
 
@@ -618,13 +748,14 @@ __global__ __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(2, 
     }
     if (qi < S) {
         uint16_t* row = dqkv + ((int64_t)b * S + qi) * ld + (int64_t)head * HD;
+        const float sq = F16 ? scale / (so * ss) : scale;
 #pragma unroll
         for (int dt = 0; dt < HD / 32; ++dt)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int d = dt * 32 + 8 * g + 4 * half;
-                *(uint2*)(row + d) = make_uint2(pack_bf2(dq[dt][4 * g] * scale, dq[dt][4 * g + 1] * scale),
-                                                pack_bf2(dq[dt][4 * g + 2] * scale, dq[dt][4 * g + 3] * scale));
+                *(uint2*)(row + d) = make_uint2(pack_bf2(dq[dt][4 * g] * sq, dq[dt][4 * g + 1] * sq),
+                                                pack_bf2(dq[dt][4 * g + 2] * sq, dq[dt][4 * g + 3] * sq));
             }
     }
 }
@@ -636,10 +767,11 @@ __global__ __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(2, 
 // lane (one wave per SIMD); apart, each runs two workgroups per CU, which more
 // than pays for recomputing Q K^T once more.
 // ---------------------------------------------------------------------------
-template <int HD, bool GRAD_K>
+template <int HD, bool GRAD_K, bool F16 = false>
 __global__ __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bwd_kv_kernel(
     const uint16_t* __restrict__ qkv, const float* __restrict__ lse, const uint16_t* __restrict__ dout,
-    const float* __restrict__ dvec, uint16_t* __restrict__ dqkv, int S, int heads, float sl2, float scale) {
+    const float* __restrict__ dvec, const float* __restrict__ sc, uint16_t* __restrict__ dqkv, int S, int heads,
+    float sl2, float scale) {
     using TL = ATile<HD>;
     __shared__ __attribute__((aligned(1024))) uint16_t smem[2][2 * TL::ELEMS];  // [buffer][Q | dO]
     __shared__ float rs[2][2][ATT_T];  // [buffer][lse*log2(e) | D] of the tile's queries
@@ -655,6 +787,10 @@ __global__ __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(2, 
     const uint16_t* Vg = Qg + 2 * H;
     const uint16_t* dOg = dout + (int64_t)b * S * H + (int64_t)head * HD;
     const int64_t rowbase = (int64_t)bh * S;
+    const float so = F16 ? sc[4 * bh] : 1.f, ss = F16 ? sc[4 * bh + 1] : 1.f;
+    // fp16: the scale of the fp16 operand (dS for dK, P for dV) folded into
+    // the exponent of P, exactly
+    const float pexp = F16 ? (GRAD_K ? sc[4 * bh + 2] : P16_EXP) : 0.f;
     const int kw0 = kbk * ATT_BK;     // first key of the workgroup
     const int k0 = kw0 + wave * 32;   // first key of this wave
     const int kj = k0 + (lane & 31);  // key owned by this lane
@@ -681,8 +817,8 @@ __global__ __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(2, 
     auto fetch_rows = [&](int q0) {
         if (threadIdx.x < ATT_T) {
             const int q = min(q0 + (int)threadIdx.x, S - 1);
-            rl = lse[rowbase + q] * LOG2E;
-            rd = dvec[rowbase + q];
+            rl = lse[rowbase + q] * LOG2E - pexp;
+            rd = dvec[rowbase + q] * so;
         }
     };
     auto load = [&](int t, uint16_t* __restrict__ buf) {
@@ -703,14 +839,12 @@ __global__ __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(2, 
             zero(s);
 #pragma unroll
             for (int ds = 0; ds < HD / 16; ++ds)
-                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(TL::frag_row(Qs, row, ds, half), as_bf16x8(kf[ds]), s, 0,
-                                                            0, 0);
+                s = mfma32x16<F16>(TL::frag_row(Qs, row, ds, half), as_bf16x8(kf[ds]), s);
             if constexpr (GRAD_K) {
                 zero(dp);
 #pragma unroll
                 for (int ds = 0; ds < HD / 16; ++ds)
-                    dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(TL::frag_row(dOs, row, ds, half), as_bf16x8(vf[ds]),
-                                                                 dp, 0, 0, 0);
+                    dp = mfma32x16<F16>(TL::frag_row(dOs, row, ds, half), as_bf16x8(vf[ds]), dp);
             }
             // mask only where this 32-query sub-tile reaches below this wave's keys or past the end
             // (a uniform condition: one branch around the whole mask)
@@ -732,11 +866,10 @@ __global__ __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(2, 
             }
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
-                const bf16x8 sb = frag_acc(s, ks * 8);
+                const bf16x8 sb = frag_acc<F16>(s, ks * 8);
 #pragma unroll
                 for (int dt = 0; dt < HD / 32; ++dt)
-                    acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        TL::frag_tr(GRAD_K ? Qs : dOs, dt * 32, qt * 2 + ks, lane), sb, acc[dt], 0, 0, 0);
+                    acc[dt] = mfma32x16<F16>(TL::frag_tr(GRAD_K ? Qs : dOs, dt * 32, qt * 2 + ks, lane), sb, acc[dt]);
             }
         }
     };
@@ -762,14 +895,15 @@ __global__ __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(2, 
     }
     if (kj < S) {
         uint16_t* orow = dqkv + ((int64_t)b * S + kj) * ld + (GRAD_K ? H : 2 * H) + (int64_t)head * HD;
-        const float sc = GRAD_K ? scale : 1.0f;
+        // undo the operand scales: dK carries so * ss, dV carries so * 2^P16_EXP
+        const float fs = GRAD_K ? (F16 ? scale / (so * ss) : scale) : (F16 ? 1.0f / (so * P16_SCALE) : 1.0f);
 #pragma unroll
         for (int dt = 0; dt < HD / 32; ++dt)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int d = dt * 32 + 8 * g + 4 * half;
-                *(uint2*)(orow + d) = make_uint2(pack_bf2(acc[dt][4 * g] * sc, acc[dt][4 * g + 1] * sc),
-                                                 pack_bf2(acc[dt][4 * g + 2] * sc, acc[dt][4 * g + 3] * sc));
+                *(uint2*)(orow + d) = make_uint2(pack_bf2(acc[dt][4 * g] * fs, acc[dt][4 * g + 1] * fs),
+                                                 pack_bf2(acc[dt][4 * g + 2] * fs, acc[dt][4 * g + 3] * fs));
             }
     }
 }
@@ -787,8 +921,42 @@ size_t attention_fwd_ws_bytes(int, int, int, int) { return 0; }
 
 size_t attention_bwd_ws_bytes(int B, int S, int heads, int) { return round_up((size_t)B * heads * S * 4, 256); }
 
-void attention_fwd(const uint16_t* qkv, uint16_t* o, float* lse, int B, int S, int heads, int hd, void*, size_t,
-                   hipStream_t s) {
+// fp16 backward: row statistics [4][B*heads*S] fp32, scales [B*heads][4]
+// fp32, scaled dO [B*S, heads*hd] fp16.
+size_t attention_bwd16_ws_bytes(int B, int S, int heads, int hd) {
+    const size_t n = (size_t)B * heads * S;
+    return round_up(4 * n * 4, 256) + round_up((size_t)B * heads * 16, 256) + round_up(n * hd * 2, 256);
+}
+
+template <bool F16>
+static void launch_attn_fwd(const uint16_t* qkv, uint16_t* o, uint16_t* o16, float* lse, int B, int S, int heads,
+                            int hd, bool pipe, float sl2, hipStream_t s) {
+    if (pipe) {
+        const dim3 grid((S + ATT_BQ - 1) / ATT_BQ, B * heads);
+        if (hd == 128)
+            hipLaunchKernelGGL((attn_fwd_kernel<128, F16>), grid, dim3(ATT_THREADS), 0, s, qkv, o, o16, lse, S, heads,
+                               sl2);
+        else
+            hipLaunchKernelGGL((attn_fwd_kernel<64, F16>), grid, dim3(ATT_THREADS), 0, s, qkv, o, o16, lse, S, heads,
+                               sl2);
+    } else {
+        const dim3 grid((S + ATT_PP_BQ - 1) / ATT_PP_BQ, B * heads);
+        if (hd == 128)
+            hipLaunchKernelGGL((attn_fwd_pp_kernel<128, F16>), grid, dim3(ATT_PP_THREADS), 0, s, qkv, o, o16, lse, S,
+                               heads, sl2);
+        else
+            hipLaunchKernelGGL((attn_fwd_pp_kernel<64, F16>), grid, dim3(ATT_PP_THREADS), 0, s, qkv, o, o16, lse, S,
+                               heads, sl2);
+    }
+}
+
+void attention_fwd(const uint16_t* qkv, uint16_t* o, float* lse, int B, int S, int heads, int hd, void* ws,
+                   size_t ws_bytes, hipStream_t s) {
+    attention_fwd_ex(qkv, false, o, nullptr, lse, B, S, heads, hd, s);
+}
+
+void attention_fwd_ex(const uint16_t* qkv, bool f16, uint16_t* o, uint16_t* o16, float* lse, int B, int S, int heads,
+                      int hd, hipStream_t s) {
     check_attn(B, S, heads, hd);
     const float sl2 = LOG2E / sqrtf((float)hd);
     // causal: S(S+1)/2 score entries, each 2*hd flops for QK^T and 2*hd for PV
@@ -799,19 +967,10 @@ void attention_fwd(const uint16_t* qkv, uint16_t* o, float* lse, int B, int S, i
         const char* e = getenv("MT_ATTN_FWD");
         return e && strcmp(e, "pipe") == 0;
     }();
-    if (pipe) {
-        const dim3 grid((S + ATT_BQ - 1) / ATT_BQ, B * heads);
-        if (hd == 128)
-            hipLaunchKernelGGL(attn_fwd_kernel<128>, grid, dim3(ATT_THREADS), 0, s, qkv, o, lse, S, heads, sl2);
-        else
-            hipLaunchKernelGGL(attn_fwd_kernel<64>, grid, dim3(ATT_THREADS), 0, s, qkv, o, lse, S, heads, sl2);
-    } else {
-        const dim3 grid((S + ATT_PP_BQ - 1) / ATT_PP_BQ, B * heads);
-        if (hd == 128)
-            hipLaunchKernelGGL(attn_fwd_pp_kernel<128>, grid, dim3(ATT_PP_THREADS), 0, s, qkv, o, lse, S, heads, sl2);
-        else
-            hipLaunchKernelGGL(attn_fwd_pp_kernel<64>, grid, dim3(ATT_PP_THREADS), 0, s, qkv, o, lse, S, heads, sl2);
-    }
+    if (f16)
+        launch_attn_fwd<true>(qkv, o, o16, lse, B, S, heads, hd, pipe, sl2, s);
+    else
+        launch_attn_fwd<false>(qkv, o, o16, lse, B, S, heads, hd, pipe, sl2, s);
     launch_check("attention_fwd", s);
 }
 
@@ -831,23 +990,60 @@ void attention_bwd(const uint16_t* qkv, const uint16_t* o, const float* lse, con
     if (hd == 128) {
         hipLaunchKernelGGL(attn_bwd_pre_kernel<128>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, o, dout, dvec,
                            T, S, heads);
-        hipLaunchKernelGGL((attn_bwd_kv_kernel<128, false>), gk, dim3(ATT_THREADS), 0, s, qkv, lse, dout, dvec, dqkv, S,
+        hipLaunchKernelGGL((attn_bwd_kv_kernel<128, false>), gk, dim3(ATT_THREADS), 0, s, qkv, lse, dout, dvec, nullptr,
+                           dqkv, S, heads, sl2, scale);
+        hipLaunchKernelGGL((attn_bwd_kv_kernel<128, true>), gk, dim3(ATT_THREADS), 0, s, qkv, lse, dout, dvec, nullptr,
+                           dqkv, S, heads, sl2, scale);
+        hipLaunchKernelGGL(attn_bwd_dq_kernel<128>, gq, dim3(ATT_THREADS), 0, s, qkv, lse, dout, dvec, nullptr, dqkv, S,
                            heads, sl2, scale);
-        hipLaunchKernelGGL((attn_bwd_kv_kernel<128, true>), gk, dim3(ATT_THREADS), 0, s, qkv, lse, dout, dvec, dqkv, S,
-                           heads, sl2, scale);
-        hipLaunchKernelGGL(attn_bwd_dq_kernel<128>, gq, dim3(ATT_THREADS), 0, s, qkv, lse, dout, dvec, dqkv, S, heads,
-                           sl2, scale);
     } else {
         hipLaunchKernelGGL(attn_bwd_pre_kernel<64>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, o, dout, dvec, T,
                            S, heads);
-        hipLaunchKernelGGL((attn_bwd_kv_kernel<64, false>), gk, dim3(ATT_THREADS), 0, s, qkv, lse, dout, dvec, dqkv, S,
+        hipLaunchKernelGGL((attn_bwd_kv_kernel<64, false>), gk, dim3(ATT_THREADS), 0, s, qkv, lse, dout, dvec, nullptr,
+                           dqkv, S, heads, sl2, scale);
+        hipLaunchKernelGGL((attn_bwd_kv_kernel<64, true>), gk, dim3(ATT_THREADS), 0, s, qkv, lse, dout, dvec, nullptr,
+                           dqkv, S, heads, sl2, scale);
+        hipLaunchKernelGGL(attn_bwd_dq_kernel<64>, gq, dim3(ATT_THREADS), 0, s, qkv, lse, dout, dvec, nullptr, dqkv, S,
                            heads, sl2, scale);
-        hipLaunchKernelGGL((attn_bwd_kv_kernel<64, true>), gk, dim3(ATT_THREADS), 0, s, qkv, lse, dout, dvec, dqkv, S,
-                           heads, sl2, scale);
-        hipLaunchKernelGGL(attn_bwd_dq_kernel<64>, gq, dim3(ATT_THREADS), 0, s, qkv, lse, dout, dvec, dqkv, S, heads,
-                           sl2, scale);
     }
     launch_check("attention_bwd", s);
+}
+
+template <int HD>
+static void launch_attn_bwd16(const uint16_t* qkv16, const uint16_t* o, const float* lse, const uint16_t* dout,
+                              uint16_t* dqkv, int B, int S, int heads, char* ws, float sl2, float scale, hipStream_t s) {
+    const int64_t T = (int64_t)B * S, n = T * heads;
+    float* stats = (float*)ws;
+    float* sc = (float*)(ws + round_up(4 * (size_t)n * 4, 256));
+    uint16_t* do16 = (uint16_t*)((char*)sc + round_up((size_t)B * heads * 16, 256));
+    const dim3 gq((S + ATT_BQ - 1) / ATT_BQ, B * heads), gk((S + ATT_BK - 1) / ATT_BK, B * heads);
+    hipLaunchKernelGGL(attn_bwd_stats_kernel<HD>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, qkv16, o, dout,
+                       stats, T, S, heads);
+    hipLaunchKernelGGL(attn_bwd_scale_kernel, dim3((unsigned)(B * heads)), dim3(256), 0, s, stats, sc, n, S);
+    const int64_t n8 = n * HD / 8;
+    hipLaunchKernelGGL(attn_bwd_do16_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s, dout, sc, do16, T, S,
+                       heads, HD);
+    hipLaunchKernelGGL((attn_bwd_kv_kernel<HD, false, true>), gk, dim3(ATT_THREADS), 0, s, qkv16, lse, do16, stats, sc,
+                       dqkv, S, heads, sl2, scale);
+    hipLaunchKernelGGL((attn_bwd_kv_kernel<HD, true, true>), gk, dim3(ATT_THREADS), 0, s, qkv16, lse, do16, stats, sc,
+                       dqkv, S, heads, sl2, scale);
+    hipLaunchKernelGGL((attn_bwd_dq_kernel<HD, true>), gq, dim3(ATT_THREADS), 0, s, qkv16, lse, do16, stats, sc, dqkv,
+                       S, heads, sl2, scale);
+}
+
+void attention_bwd16(const uint16_t* qkv16, const uint16_t* o, const float* lse, const uint16_t* dout,
+                     uint16_t* dqkv, int B, int S, int heads, int hd, void* ws, size_t ws_bytes, hipStream_t s) {
+    check_attn(B, S, heads, hd);
+    if (!ws || ws_bytes < attention_bwd16_ws_bytes(B, S, heads, hd))
+        MT_FAIL(MT_E_ARG, "attention (fp16): workspace too small");
+    const float scale = 1.0f / sqrtf((float)hd);
+    const float sl2 = LOG2E * scale;
+    ProfScope prof(PROF_ATTN_BWD, 10.0 * hd * (double)B * heads * ((double)S * (S + 1) / 2), s);
+    if (hd == 128)
+        launch_attn_bwd16<128>(qkv16, o, lse, dout, dqkv, B, S, heads, (char*)ws, sl2, scale, s);
+    else
+        launch_attn_bwd16<64>(qkv16, o, lse, dout, dqkv, B, S, heads, (char*)ws, sl2, scale, s);
+    launch_check("attention_bwd16", s);
 }
 
 }  // namespace mt

@@ -25,19 +25,24 @@ constexpr int NORM_THREADS = 256;
 constexpr int NORM_MAXC = 8;  // supports h <= 8 * 256 * 8 = 16384; kernels are instantiated per chunk count
 constexpr int NORM_ROWS = 16; // rows per workgroup in the backward
 
-template <int NC>
-__global__ __launch_bounds__(NORM_THREADS) void rmsnorm_fwd_kernel(const uint16_t* __restrict__ x,
-                                                                    const uint16_t* __restrict__ g,
-                                                                    uint16_t* __restrict__ y,
-                                                                    float* __restrict__ rstd, int h, float eps) {
-    __shared__ float red[NORM_THREADS / 64];
-    const int64_t row = blockIdx.x;
+// RMSNorm forward, one wave per row (four rows per workgroup): each lane
+// holds NV 16-byte chunks of the row (columns 8 * (lane + 64 i)), the sum of
+// squares is one wave reduction, and the output goes to bf16 y and, when y16
+// is given, to fp16 y16 as well (both rounded from the same fp32 value).
+template <int NV>
+__global__ __launch_bounds__(256) void rmsnorm_fwd_wave_kernel(const uint16_t* __restrict__ x,
+                                                               const uint16_t* __restrict__ g,
+                                                               uint16_t* __restrict__ y, uint16_t* __restrict__ y16,
+                                                               float* __restrict__ rstd, int64_t T, int h, float eps) {
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= T) return;  // whole waves
     const uint16_t* xr = x + row * h;
-    uint4 xv[NC];
+    uint4 xv[NV];
     float ss = 0.f;
 #pragma unroll
-    for (int it = 0; it < NC; ++it) {
-        const int c = (threadIdx.x + it * NORM_THREADS) * 8;
+    for (int it = 0; it < NV; ++it) {
+        const int c = (lane + 64 * it) * 8;
         xv[it] = make_uint4(0, 0, 0, 0);
         if (c < h) {
             xv[it] = *(const uint4*)(xr + c);
@@ -49,35 +54,45 @@ __global__ __launch_bounds__(NORM_THREADS) void rmsnorm_fwd_kernel(const uint16_
             }
         }
     }
-    const float tot = block_sum<NORM_THREADS>(ss, red);
-    const float r = 1.0f / sqrtf(tot / (float)h + eps);
-    if (threadIdx.x == 0) rstd[row] = r;
+    const float r = 1.0f / sqrtf(wave_sum(ss) / (float)h + eps);
+    if (lane == 0) rstd[row] = r;
 #pragma unroll
-    for (int it = 0; it < NC; ++it) {
-        const int c = (threadIdx.x + it * NORM_THREADS) * 8;
+    for (int it = 0; it < NV; ++it) {
+        const int c = (lane + 64 * it) * 8;
         if (c < h) {
             const uint4 gv = *(const uint4*)(g + c);
             const uint32_t w[4] = {xv[it].x, xv[it].y, xv[it].z, xv[it].w};
             const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
-            uint32_t o[4];
+            float v[8];
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-                o[q] = pack_bf2((bf_lo(w[q]) * r) * bf_lo(gw[q]), (bf_hi(w[q]) * r) * bf_hi(gw[q]));
-            *(uint4*)(y + row * h + c) = make_uint4(o[0], o[1], o[2], o[3]);
+            for (int q = 0; q < 4; ++q) {
+                v[2 * q] = (bf_lo(w[q]) * r) * bf_lo(gw[q]);
+                v[2 * q + 1] = (bf_hi(w[q]) * r) * bf_hi(gw[q]);
+            }
+            *(uint4*)(y + row * h + c) = make_uint4(pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3]), pack_bf2(v[4], v[5]),
+                                                    pack_bf2(v[6], v[7]));
+            if (y16)
+                *(uint4*)(y16 + row * h + c) = make_uint4(pack_h2(v[0], v[1]), pack_h2(v[2], v[3]),
+                                                          pack_h2(v[4], v[5]), pack_h2(v[6], v[7]));
         }
     }
 }
 
-void rmsnorm_fwd(const uint16_t* x, const uint16_t* g, uint16_t* y, float* rstd, int64_t T, int h, float eps,
-                 hipStream_t s) {
-    if (h % 8 || h > NORM_THREADS * 8 * NORM_MAXC) MT_FAIL(MT_E_SHAPE, "rmsnorm: unsupported h=%d", h);
+void rmsnorm_fwd2(const uint16_t* x, const uint16_t* g, uint16_t* y, uint16_t* y16, float* rstd, int64_t T, int h,
+                  float eps, hipStream_t s) {
+    if (h % 8 || h > 64 * 8 * 32) MT_FAIL(MT_E_SHAPE, "rmsnorm: unsupported h=%d", h);
     if (T <= 0) return;
-    const int nc = (h + NORM_THREADS * 8 - 1) / (NORM_THREADS * 8);
-#define MT_NORM_FWD(NCV) \
-    case NCV: hipLaunchKernelGGL(rmsnorm_fwd_kernel<NCV>, dim3((unsigned)T), dim3(NORM_THREADS), 0, s, x, g, y, rstd, h, eps); break;
-    switch (nc) { MT_NORM_FWD(1) MT_NORM_FWD(2) MT_NORM_FWD(3) MT_NORM_FWD(4) MT_NORM_FWD(5) MT_NORM_FWD(6) MT_NORM_FWD(7) MT_NORM_FWD(8) }
-#undef MT_NORM_FWD
-    launch_check("rmsnorm_fwd", s);
+    const int nv = (h + 511) / 512;
+    const dim3 grid((unsigned)((T + 3) / 4));
+#define MT_NORM_FWD2(NVV)                                                                                     \
+    if (nv <= NVV) {                                                                                          \
+        hipLaunchKernelGGL(rmsnorm_fwd_wave_kernel<NVV>, grid, dim3(256), 0, s, x, g, y, y16, rstd, T, h, eps); \
+        launch_check("rmsnorm_fwd", s);                                                                       \
+        return;                                                                                               \
+    }
+    MT_NORM_FWD2(1) MT_NORM_FWD2(2) MT_NORM_FWD2(4) MT_NORM_FWD2(8) MT_NORM_FWD2(10) MT_NORM_FWD2(12)
+    MT_NORM_FWD2(16) MT_NORM_FWD2(20) MT_NORM_FWD2(24) MT_NORM_FWD2(32)
+#undef MT_NORM_FWD2
 }
 
 template <int NC>
@@ -246,6 +261,65 @@ __global__ void rope_kernel(uint16_t* __restrict__ qkv, const float* __restrict_
     *(uint4*)(base + half) = make_uint4(bo[0], bo[1], bo[2], bo[3]);
 }
 
+// The fused projection's fp32 output, finished: rows t0 .. t0+rows-1 of
+// qkv32 ([rows, 3h], fp32) hold tokens t0 ... of the batch; q and k are
+// rotated by RoPE in fp32 and every value is rounded once, to bf16 into qkv
+// and to fp16 into qkv16 (both [T, 3h]).  One thread: 8 pairs (i, i + hd/2)
+// of one head of q, k or v (v is only converted).
+__global__ void qkv_finish_kernel(const float* __restrict__ qkv32, uint16_t* __restrict__ qkv,
+                                  uint16_t* __restrict__ qkv16, const float* __restrict__ cs,
+                                  const float* __restrict__ sn, int64_t t0, int64_t rows, int S, int heads, int hd) {
+    const int half = hd / 2, groups = half / 8;
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t per_tok = (int64_t)3 * heads * groups;
+    if (idx >= rows * per_tok) return;
+    const int64_t tr = idx / per_tok;
+    int rem = (int)(idx % per_tok);
+    const int which = rem / (heads * groups);  // 0: q, 1: k, 2: v
+    rem %= heads * groups;
+    const int head = rem / groups, gi = rem % groups;
+    const int64_t t = t0 + tr;
+    const int s = (int)(t % S);
+    const int64_t h3 = (int64_t)3 * heads * hd;
+    const int64_t col = (int64_t)which * heads * hd + (int64_t)head * hd + gi * 8;
+    const float* src = qkv32 + tr * h3 + col;
+    const float4 a0 = *(const float4*)src, a1 = *(const float4*)(src + 4);
+    const float4 b0 = *(const float4*)(src + half), b1 = *(const float4*)(src + half + 4);
+    float a[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+    float b[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+    if (which < 2) {
+        const float* cp = cs + (int64_t)s * half + gi * 8;
+        const float* sp = sn + (int64_t)s * half + gi * 8;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float c = cp[e], si = sp[e];
+            const float ra = a[e] * c - b[e] * si, rb = b[e] * c + a[e] * si;
+            a[e] = ra;
+            b[e] = rb;
+        }
+    }
+    if (qkv) {
+        uint16_t* d = qkv + t * h3 + col;
+        *(uint4*)d = make_uint4(pack_bf2(a[0], a[1]), pack_bf2(a[2], a[3]), pack_bf2(a[4], a[5]), pack_bf2(a[6], a[7]));
+        *(uint4*)(d + half) =
+            make_uint4(pack_bf2(b[0], b[1]), pack_bf2(b[2], b[3]), pack_bf2(b[4], b[5]), pack_bf2(b[6], b[7]));
+    }
+    uint16_t* d16 = qkv16 + t * h3 + col;
+    *(uint4*)d16 = make_uint4(pack_h2(a[0], a[1]), pack_h2(a[2], a[3]), pack_h2(a[4], a[5]), pack_h2(a[6], a[7]));
+    *(uint4*)(d16 + half) =
+        make_uint4(pack_h2(b[0], b[1]), pack_h2(b[2], b[3]), pack_h2(b[4], b[5]), pack_h2(b[6], b[7]));
+}
+
+void qkv_finish(const float* qkv32, uint16_t* qkv, uint16_t* qkv16, const float* cos, const float* sin, int64_t t0,
+                int64_t rows, int S, int heads, int hd, hipStream_t s) {
+    if (hd % 16) MT_FAIL(MT_E_SHAPE, "qkv_finish: head_dim %d must be a multiple of 16", hd);
+    const int64_t n = rows * 3 * heads * (hd / 16);
+    if (n == 0) return;
+    hipLaunchKernelGGL(qkv_finish_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, qkv32, qkv, qkv16, cos,
+                       sin, t0, rows, S, heads, hd);
+    launch_check("qkv_finish", s);
+}
+
 void rope_apply(uint16_t* qkv, const float* cos, const float* sin, int64_t T, int S, int heads, int hd, bool inverse,
                 hipStream_t s) {
     if (hd % 16) MT_FAIL(MT_E_SHAPE, "rope: head_dim %d must be a multiple of 16", hd);
@@ -305,6 +379,58 @@ __global__ void swiglu_bwd_kernel(const uint16_t* __restrict__ da, const uint16_
     }
     *(uint4*)(dgu + t * 2 * f + c) = make_uint4(og[0], og[1], og[2], og[3]);
     *(uint4*)(dgu + t * 2 * f + f + c) = make_uint4(ou[0], ou[1], ou[2], ou[3]);
+}
+
+// SwiGLU from the gate/up projection's fp32 output gu32 [rows, 2f]:
+// a = silu(gate) * up in fp32, rounded once to bf16 (a, [rows, f]) and to
+// fp16 (a16, [rows, f]).
+__global__ void swiglu_fwd32_kernel(const float* __restrict__ gu, uint16_t* __restrict__ a,
+                                    uint16_t* __restrict__ a16, int64_t rows, int f) {
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int per = f / 8;
+    if (idx >= rows * per) return;
+    const int64_t t = idx / per;
+    const int c = (int)(idx % per) * 8;
+    const float* gr = gu + t * 2 * f + c;
+    const float4 g0 = *(const float4*)gr, g1 = *(const float4*)(gr + 4);
+    const float4 u0 = *(const float4*)(gr + f), u1 = *(const float4*)(gr + f + 4);
+    const float gv[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+    const float uv[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = gv[e] * sigmoidf_(gv[e]) * uv[e];
+    *(uint4*)(a + t * f + c) =
+        make_uint4(pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3]), pack_bf2(v[4], v[5]), pack_bf2(v[6], v[7]));
+    *(uint4*)(a16 + t * f + c) =
+        make_uint4(pack_h2(v[0], v[1]), pack_h2(v[2], v[3]), pack_h2(v[4], v[5]), pack_h2(v[6], v[7]));
+}
+
+void swiglu_fwd32(const float* gu, uint16_t* a, uint16_t* a16, int64_t rows, int f, hipStream_t s) {
+    const int64_t n = rows * (f / 8);
+    if (n == 0) return;
+    hipLaunchKernelGGL(swiglu_fwd32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, gu, a, a16, rows, f);
+    launch_check("swiglu_fwd32", s);
+}
+
+// bf16 -> fp16 (exact for every bf16 value inside fp16's range; weights of
+// the layer template, |w| << 65504), 8 values per thread.
+__global__ void bf16_to_f16_kernel(const uint16_t* __restrict__ x, uint16_t* __restrict__ y, int64_t n8) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n8) return;
+    const uint4 v = *(const uint4*)(x + 8 * i);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) o[q] = pack_h2(bf_lo(w[q]), bf_hi(w[q]));
+    *(uint4*)(y + 8 * i) = make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+void bf16_to_f16(const uint16_t* x, uint16_t* y, int64_t n, hipStream_t s) {
+    if (n % 8) MT_FAIL(MT_E_SHAPE, "bf16_to_f16: %lld elements, not a multiple of 8", (long long)n);
+    const int64_t n8 = n / 8;
+    if (n8 == 0) return;
+    hipLaunchKernelGGL(bf16_to_f16_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s, x, y, n8);
+    launch_check("bf16_to_f16", s);
 }
 
 void swiglu_fwd(const uint16_t* gu, uint16_t* a, int64_t T, int f, hipStream_t s) {

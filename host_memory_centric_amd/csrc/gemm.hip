@@ -1,5 +1,7 @@
 // bf16 GEMM on gfx950 matrix cores (v_mfma_f32_32x32x16_bf16), fp32
-// accumulation, for the layer template's linear maps (QKV, output, gate/up and
+// accumulation (and the same kernels on fp16 operands, v_mfma_f32_32x32x16_f16,
+// for the forward maps, whose activations are kept in fp16), for the layer
+// template's linear maps (QKV, output, gate/up and
 // down projections and the LM head) in the three orientations the forward and
 // backward need:
 //   forward      Y[T, out]  = X[T, in] * W[out, in]^T   A K-major, B K-major
@@ -88,7 +90,9 @@ static void launch_tiles(const GemmDesc& d, hipStream_t s, float* part, int spli
     const GemmArgs p = make_args(d, part, splits, kps, BM, BN);
     dim3 grid(p.tiles_m * p.tiles_n, splits);
     dim3 block(WM * WN * 64);
-    if (d.a_kmajor && d.b_kmajor)
+    if (d.f16)
+        hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, true, true, true>), grid, block, 0, s, p);
+    else if (d.a_kmajor && d.b_kmajor)
         hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, true, true>), grid, block, 0, s, p);
     else if (d.a_kmajor && !d.b_kmajor)
         hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, true, false>), grid, block, 0, s, p);
@@ -116,7 +120,9 @@ static void launch_pp(const GemmDesc& d, hipStream_t s, float* part, int splits,
     const GemmArgs p = make_args(d, part, splits, kps, 256, 256);
     dim3 grid(p.tiles_m * p.tiles_n, splits);
     dim3 block(512);
-    if (d.a_kmajor && d.b_kmajor)
+    if (d.f16)
+        hipLaunchKernelGGL((gemm_pp_kernel<true, true, true>), grid, block, 0, s, p);
+    else if (d.a_kmajor && d.b_kmajor)
         hipLaunchKernelGGL((gemm_pp_kernel<true, true>), grid, block, 0, s, p);
     else if (d.a_kmajor && !d.b_kmajor)
         hipLaunchKernelGGL((gemm_pp_kernel<true, false>), grid, block, 0, s, p);
@@ -184,8 +190,9 @@ void gemm(const GemmDesc& d, hipStream_t s) {
     float* part = splits > 1 ? (float*)d.ws : nullptr;
     const ProfClass pc = d.a_kmajor ? (d.b_kmajor ? PROF_GEMM_NT : PROF_GEMM_NN) : PROF_GEMM_TN;
     ProfScope prof(pc, 2.0 * (double)d.M * (double)d.N * (double)d.K, s);
+    if (d.f16 && !(d.a_kmajor && d.b_kmajor)) MT_FAIL(MT_E_ARG, "gemm: fp16 operands are supported K-major only");
     if (pipe_ok(d, kps)) {
-        if (use_pp()) launch_pp(d, s, part, splits, kps);
+        if (use_pp() || d.f16) launch_pp(d, s, part, splits, kps);
         else launch_pipe(d, s, part, splits, kps);
     }
     else if (use_big(d.M, d.N))

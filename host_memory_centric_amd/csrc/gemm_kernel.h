@@ -159,7 +159,7 @@ __device__ __forceinline__ void store_acc(const f32x16& a, const GemmArgs& p, fl
     }
 }
 
-template <int BM, int BN, int WM, int WN, bool AK, bool BKM>
+template <int BM, int BN, int WM, int WN, bool AK, bool BKM, bool F16 = false>
 __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(GemmArgs p) {
     constexpr int NT = WM * WN * 64, NW = NT / 64, SW = NW / 2;
     constexpr int WTM = BM / WM, WTN = BN / WN;
@@ -224,7 +224,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(GemmArgs p) {
         for (int i = 0; i < TM; ++i)
 #pragma unroll
             for (int j = 0; j < TN; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfm[j], acc[i][j], 0, 0, 0);
+                acc[i][j] = mfma32x16<F16>(af[i], bfm[j], acc[i][j]);
     };
 
     // One K step: start the direct loads of the next tile into the other

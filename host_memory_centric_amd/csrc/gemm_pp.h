@@ -13,7 +13,7 @@
 
 namespace mt {
 
-template <bool AK, bool BKM>
+template <bool AK, bool BKM, bool F16 = false>
 __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmArgs p) {
     constexpr int BM = 256, BN = 256;
     constexpr int TE = 256 * PBK;
@@ -125,7 +125,7 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmArgs p) {
             for (int i = 0; i < 4; ++i)
 #pragma unroll
                 for (int j = 0; j < 2; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[kk][j], fa[kk][i], acc[i][j], 0, 0, 0);
+                    acc[i][j] = mfma32x16<F16>(fb[kk][j], fa[kk][i], acc[i][j]);
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_barrier();
     }

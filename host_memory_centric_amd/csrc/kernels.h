@@ -37,14 +37,12 @@ struct GemmDesc {
     int accumulate = 0;         // Cf += result
     void* ws = nullptr;         // split-K scratch (fp32)
     size_t ws_bytes = 0;
+    bool f16 = false;           // A and B hold fp16 (not bf16) values; A and B K-major only
 };
 void gemm(const GemmDesc& d, hipStream_t s);
 int gemm_pick_splits(int64_t M, int64_t N, int64_t K);
 size_t gemm_splitk_bytes(int64_t M, int64_t N, int64_t K);
 
-// RMSNorm over rows of length h: y = x * rstd * g (bf16 out), rstd fp32 [T].
-void rmsnorm_fwd(const uint16_t* x, const uint16_t* g, uint16_t* y, float* rstd, int64_t T, int h, float eps,
-                 hipStream_t s);
 // Backward: dx = resid + rstd * (dy*g - xh * mean(dy*g*xh)); writes fp32 and
 // bf16 dx (either may be NULL), and per-row-block partials of dg.
 int64_t rmsnorm_bwd_blocks(int64_t T);
@@ -58,6 +56,20 @@ void colsum_to_bf16(const float* part, int64_t nblk, int h, uint16_t* out, hipSt
 void rope_apply(uint16_t* qkv, const float* cos, const float* sin, int64_t T, int S, int heads, int hd,
                 bool inverse, hipStream_t s);
 
+// RMSNorm forward, one wave per row: bf16 y and (when y16 != NULL) fp16 y16
+// from the same fp32 values; rstd fp32 [T].
+void rmsnorm_fwd2(const uint16_t* x, const uint16_t* g, uint16_t* y, uint16_t* y16, float* rstd, int64_t T, int h,
+                  float eps, hipStream_t s);
+// The fused projection's fp32 output of tokens t0 .. t0+rows-1 ([rows, 3h]):
+// RoPE on q and k in fp32, then bf16 into qkv (skipped when NULL) and fp16
+// into qkv16 ([T, 3h]).
+void qkv_finish(const float* qkv32, uint16_t* qkv, uint16_t* qkv16, const float* cos, const float* sin, int64_t t0,
+                int64_t rows, int S, int heads, int hd, hipStream_t s);
+// SwiGLU from an fp32 gate/up [rows, 2f]: a (bf16) and a16 (fp16), [rows, f].
+void swiglu_fwd32(const float* gu, uint16_t* a, uint16_t* a16, int64_t rows, int f, hipStream_t s);
+// bf16 -> fp16 elementwise (n a multiple of 8).
+void bf16_to_f16(const uint16_t* x, uint16_t* y, int64_t n, hipStream_t s);
+
 // SwiGLU: a = silu(gate) * up from gu [T, 2f]; and its backward.
 void swiglu_fwd(const uint16_t* gu, uint16_t* a, int64_t T, int f, hipStream_t s);
 void swiglu_bwd(const uint16_t* da, const uint16_t* gu, uint16_t* dgu, int64_t T, int f, hipStream_t s);
@@ -68,8 +80,19 @@ size_t attention_fwd_ws_bytes(int B, int S, int heads, int hd);
 size_t attention_bwd_ws_bytes(int B, int S, int heads, int hd);
 void attention_fwd(const uint16_t* qkv, uint16_t* o, float* lse, int B, int S, int heads, int hd, void* ws,
                    size_t ws_bytes, hipStream_t s);
+// The forward on q, k, v held as fp16 (f16 = true; the probabilities enter
+// P V as fp16 too) or bf16, writing bf16 o and, when o16 != NULL, fp16 o16.
+void attention_fwd_ex(const uint16_t* qkv, bool f16, uint16_t* o, uint16_t* o16, float* lse, int B, int S, int heads,
+                      int hd, hipStream_t s);
 void attention_bwd(const uint16_t* qkv, const uint16_t* o, const float* lse, const uint16_t* dout, uint16_t* dqkv,
                    int B, int S, int heads, int hd, void* ws, size_t ws_bytes, hipStream_t s);
+// The backward on the forward's fp16 q, k, v (qkv16, as attention_fwd_ex with
+// f16 = true read them, so that the recomputed scores equal the forward's):
+// dO and dS enter the products as fp16 under per-(batch, head) power-of-two
+// scales taken from bounds of their magnitudes; o and dout bf16, dqkv bf16.
+size_t attention_bwd16_ws_bytes(int B, int S, int heads, int hd);
+void attention_bwd16(const uint16_t* qkv16, const uint16_t* o, const float* lse, const uint16_t* dout,
+                     uint16_t* dqkv, int B, int S, int heads, int hd, void* ws, size_t ws_bytes, hipStream_t s);
 
 // Cross entropy over a chunk of logits z [rows, V] (fp32) for tokens
 // t0..t0+rows-1 of the batch: per-row loss and dz (bf16) = (softmax - onehot)/N.

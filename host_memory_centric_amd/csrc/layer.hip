@@ -30,7 +30,7 @@ struct Carve {
 struct Saved {
     uint16_t* n1;    // RMSNorm output before attention [T, h]
     float* rstd1;    // [T]
-    uint16_t* qkv;   // fused projection, q and k rotated [T, 3h]
+    uint16_t* qkv;   // fused projection as fp16, q and k rotated [T, 3h]
     uint16_t* o;     // attention output [T, h]
     float* lse;      // [B, heads, S]
     uint16_t* xm;    // residual stream after attention [T, h]
@@ -56,7 +56,36 @@ Saved carve_saved(Carve& c, const mt_model_cfg* cfg, int64_t B, int64_t S) {
     return s;
 }
 
+// Forward transients (fp16 GEMM operands and fp32 GEMM outputs); they share
+// memory with the backward temporaries below, which are dead during a forward.
+struct FwdWs {
+    uint16_t* w16;    // the layer's four matrices as fp16, W-region order [3h*h | h*h | 2f*h | h*f]
+    uint16_t* n16;    // RMSNorm output of a token chunk, fp16 [Tc, h]
+    float* qkv32;     // fused projection of a token chunk, fp32 [Tc, 3h]
+    uint16_t* o16;    // attention output as fp16, whole batch [T, h]
+    float* gu32;      // gate | up of a token chunk, fp32 [Tc, 2f]
+    uint16_t* a16;    // SwiGLU output of a token chunk, fp16 [Tc, f]
+};
+
+// Token chunk of the forward's per-token phases: the whole batch up to 32768
+// tokens, else chunks of 32768 (a function of the shape only, so every run of
+// a configuration computes identically).
+int64_t fwd_chunk(int64_t T) { return std::min<int64_t>(T, 32768); }
+
+FwdWs carve_fwd(Carve& c, const mt_model_cfg* cfg, int64_t T) {
+    const int64_t h = cfg->hidden, f = cfg->ffn, Tc = fwd_chunk(T);
+    FwdWs w;
+    w.w16 = c.take<uint16_t>(4 * h * h + 3 * h * f);
+    w.n16 = c.take<uint16_t>(Tc * h);
+    w.qkv32 = c.take<float>(Tc * 3 * h);
+    w.o16 = c.take<uint16_t>(T * h);
+    w.gu32 = c.take<float>(Tc * 2 * f);
+    w.a16 = c.take<uint16_t>(Tc * f);
+    return w;
+}
+
 struct BwdWs {
+    FwdWs fw;         // forward transients, overlapping the backward temporaries after xtmp
     uint16_t* xtmp;   // forward output during recompute [T, h]
     uint16_t* da;     // [T, f]
     uint16_t* dgu;    // [T, 2f]
@@ -65,7 +94,7 @@ struct BwdWs {
     uint16_t* dxm_b;  // its bf16 copy
     uint16_t* dout;   // gradient of the attention output [T, h]
     uint16_t* dqkv;   // [T, 3h]
-    void* attn;       // attention scratch (the backward's row dot products)
+    void* attn;       // attention scratch (the backward's row statistics, scales, scaled dO)
     size_t attn_bytes;
     float* dg_part;   // RMSNorm gain partials [blocks, h]
     void* splitk;     // split-K partials
@@ -86,8 +115,15 @@ size_t splitk_need(const mt_model_cfg* cfg, int64_t T) {
 // without one carves the internals right after these pieces.
 BwdWs carve_ws(Carve& c, const mt_model_cfg* cfg, int64_t B, int64_t S) {
     const int64_t T = B * S, h = cfg->hidden, f = cfg->ffn;
+    size_t fwd_bytes = 0;
     BwdWs w;
     w.xtmp = c.take<uint16_t>(T * h);
+    const size_t union_off = c.off;
+    {
+        Carve cf(c.base ? c.base + union_off : nullptr);
+        w.fw = carve_fwd(cf, cfg, T);
+        fwd_bytes = cf.off;
+    }
     w.da = c.take<uint16_t>(T * f);
     w.dgu = c.take<uint16_t>(T * 2 * f);
     w.dn = c.take<float>(T * h);
@@ -96,11 +132,12 @@ BwdWs carve_ws(Carve& c, const mt_model_cfg* cfg, int64_t B, int64_t S) {
     w.dout = c.take<uint16_t>(T * h);
     w.dqkv = c.take<uint16_t>(T * 3 * h);
     w.attn_bytes = std::max(attention_fwd_ws_bytes((int)B, (int)S, cfg->heads, cfg->head_dim),
-                            attention_bwd_ws_bytes((int)B, (int)S, cfg->heads, cfg->head_dim));
+                            attention_bwd16_ws_bytes((int)B, (int)S, cfg->heads, cfg->head_dim));
     w.attn = c.take<char>(w.attn_bytes);
     w.dg_part = c.take<float>(rmsnorm_bwd_blocks(T) * h);
     w.splitk_bytes = splitk_need(cfg, T);
     w.splitk = c.take<char>(w.splitk_bytes);
+    if (c.off < union_off + fwd_bytes) c.off = union_off + fwd_bytes;  // the union's larger part
     return w;
 }
 
@@ -133,36 +170,58 @@ GemmDesc gd(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, bool ak
     return d;
 }
 
-// Forward of one layer: x -> y, internals into sv.
+// Forward of one layer: x -> y, internals into sv.  The GEMM operands of the
+// forward are fp16 (the weights converted exactly, the activations rounded
+// once from fp32: three more significand bits than bf16).  The backward reads
+// q, k, v as the same fp16 values, so that its recomputed attention scores are
+// the forward's; its other internals are stored bf16, from the same fp32 values.  Per-token work
+// runs over token chunks (fwd_chunk), attention over the whole batch.
 void layer_forward(const mt_layer_view* v, const mt_model_cfg* cfg, int B, int S, const uint16_t* x, uint16_t* y,
-                   const float* cs, const float* sn, const Saved& sv, void* attn_ws, size_t attn_bytes, hipStream_t s) {
-    const int64_t T = (int64_t)B * S, h = cfg->hidden, f = cfg->ffn;
+                   const float* cs, const float* sn, const Saved& sv, const FwdWs& fw, hipStream_t s) {
+    const int64_t T = (int64_t)B * S, h = cfg->hidden, f = cfg->ffn, Tc = fwd_chunk(T);
     const uint16_t* g_attn = (const uint16_t*)v->w[0];
-    const uint16_t* wqkv = (const uint16_t*)v->w[1];
-    const uint16_t* wo = (const uint16_t*)v->w[2];
     const uint16_t* g_mlp = (const uint16_t*)v->w[3];
-    const uint16_t* wgu = (const uint16_t*)v->w[4];
-    const uint16_t* wd = (const uint16_t*)v->w[5];
+    uint16_t* wqkv = fw.w16;
+    uint16_t* wo = wqkv + 3 * h * h;
+    uint16_t* wgu = wo + h * h;
+    uint16_t* wd = wgu + 2 * f * h;
+    bf16_to_f16((const uint16_t*)v->w[1], wqkv, 3 * h * h, s);
+    bf16_to_f16((const uint16_t*)v->w[2], wo, h * h, s);
+    bf16_to_f16((const uint16_t*)v->w[4], wgu, 2 * f * h, s);
+    bf16_to_f16((const uint16_t*)v->w[5], wd, h * f, s);
 
-    rmsnorm_fwd(x, g_attn, sv.n1, sv.rstd1, T, (int)h, cfg->eps, s);
-    GemmDesc d = gd(T, 3 * h, h, sv.n1, h, true, wqkv, h, true, 3 * h);
-    d.Cb = sv.qkv;
-    gemm(d, s);
-    rope_apply(sv.qkv, cs, sn, T, S, cfg->heads, cfg->head_dim, false, s);
-    attention_fwd(sv.qkv, sv.o, sv.lse, B, S, cfg->heads, cfg->head_dim, attn_ws, attn_bytes, s);
-    d = gd(T, h, h, sv.o, h, true, wo, h, true, h);
-    d.R = x;
-    d.Cb = sv.xm;
-    gemm(d, s);
-    rmsnorm_fwd(sv.xm, g_mlp, sv.n2, sv.rstd2, T, (int)h, cfg->eps, s);
-    d = gd(T, 2 * f, h, sv.n2, h, true, wgu, h, true, 2 * f);
-    d.Cb = sv.gu;
-    gemm(d, s);
-    swiglu_fwd(sv.gu, sv.a, T, (int)f, s);
-    d = gd(T, h, f, sv.a, f, true, wd, f, true, h);
-    d.R = sv.xm;
-    d.Cb = y;
-    gemm(d, s);
+    // attention RMSNorm, QKV projection, RoPE: per token chunk
+    for (int64_t t0 = 0; t0 < T; t0 += Tc) {
+        const int64_t rows = std::min(Tc, T - t0);
+        rmsnorm_fwd2(x + t0 * h, g_attn, sv.n1 + t0 * h, fw.n16, sv.rstd1 + t0, rows, (int)h, cfg->eps, s);
+        GemmDesc d = gd(rows, 3 * h, h, fw.n16, h, true, wqkv, h, true, 3 * h);
+        d.f16 = true;
+        d.Cf = fw.qkv32;
+        gemm(d, s);
+        qkv_finish(fw.qkv32, nullptr, sv.qkv, cs, sn, t0, rows, S, cfg->heads, cfg->head_dim, s);
+    }
+    attention_fwd_ex(sv.qkv, true, sv.o, fw.o16, sv.lse, B, S, cfg->heads, cfg->head_dim, s);
+    // output projection + residual, MLP RMSNorm, gate/up, SwiGLU, down + residual: per token chunk
+    for (int64_t t0 = 0; t0 < T; t0 += Tc) {
+        const int64_t rows = std::min(Tc, T - t0);
+        GemmDesc d = gd(rows, h, h, fw.o16 + t0 * h, h, true, wo, h, true, h);
+        d.f16 = true;
+        d.R = x + t0 * h;
+        d.Cb = sv.xm + t0 * h;
+        gemm(d, s);
+        rmsnorm_fwd2(sv.xm + t0 * h, g_mlp, sv.n2 + t0 * h, fw.n16, sv.rstd2 + t0, rows, (int)h, cfg->eps, s);
+        d = gd(rows, 2 * f, h, fw.n16, h, true, wgu, h, true, 2 * f);
+        d.f16 = true;
+        d.Cf = fw.gu32;
+        d.Cb = sv.gu + t0 * 2 * f;
+        gemm(d, s);
+        swiglu_fwd32(fw.gu32, sv.a + t0 * f, fw.a16, rows, (int)f, s);
+        d = gd(rows, h, f, fw.a16, f, true, wd, f, true, h);
+        d.f16 = true;
+        d.R = sv.xm + t0 * h;
+        d.Cb = y + t0 * h;
+        gemm(d, s);
+    }
 }
 
 void layer_backward(const mt_layer_view* v, const mt_model_cfg* cfg, const mt_act* io, const Saved& sv, BwdWs& w,
@@ -207,7 +266,7 @@ void layer_backward(const mt_layer_view* v, const mt_model_cfg* cfg, const mt_ac
     d.Cb = w.dout;
     gemm(d, s);
     // attention and RoPE
-    attention_bwd(sv.qkv, sv.o, sv.lse, w.dout, w.dqkv, B, S, cfg->heads, cfg->head_dim, w.attn, w.attn_bytes, s);
+    attention_bwd16(sv.qkv, sv.o, sv.lse, w.dout, w.dqkv, B, S, cfg->heads, cfg->head_dim, w.attn, w.attn_bytes, s);
     rope_apply(w.dqkv, io->rope_cos, io->rope_sin, T, S, cfg->heads, cfg->head_dim, true, s);
     // QKV projection
     d = gd(3 * h, h, T, w.dqkv, 3 * h, false, sv.n1, h, false, h);
@@ -339,7 +398,7 @@ int mt_layer_fwd(const mt_layer_view* v, const mt_model_cfg* cfg, const mt_act* 
         Saved sv;
         carve_call(cfg, io, w, sv);
         layer_forward(v, cfg, io->batch, io->seq, (const uint16_t*)io->x_in, (uint16_t*)io->x_out, io->rope_cos,
-                      io->rope_sin, sv, w.attn, w.attn_bytes, as_stream(stream));
+                      io->rope_sin, sv, w.fw, as_stream(stream));
     });
 }
 
@@ -364,7 +423,7 @@ int mt_layer_recompute_bwd(const mt_layer_view* v, const mt_model_cfg* cfg, cons
         const hipStream_t s = as_stream(stream);
         if (!io->saved) {
             layer_forward(v, cfg, io->batch, io->seq, (const uint16_t*)io->x_in, w.xtmp, io->rope_cos, io->rope_sin, sv,
-                          w.attn, w.attn_bytes, s);
+                          w.fw, s);
         }
         layer_backward(v, cfg, io, sv, w, s);
     });
@@ -411,7 +470,7 @@ int mt_head_fwd_bwd(const mt_layer_view* v, const mt_model_cfg* cfg, const mt_he
         int64_t nblk = 0;
         for (int64_t t0 = 0, ci = 0; t0 < T; t0 += Tc, ++ci) {
             const int64_t rows = std::min(Tc, T - t0);
-            rmsnorm_fwd(x + t0 * h, gf, w.xf, w.rstd, rows, (int)h, cfg->eps, s);
+            rmsnorm_fwd2(x + t0 * h, gf, w.xf, nullptr, w.rstd, rows, (int)h, cfg->eps, s);
             GemmDesc d = gd(rows, V, h, w.xf, h, true, wh, h, true, V);
             d.Cf = w.z;
             gemm(d, s);
