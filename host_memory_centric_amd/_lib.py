@@ -108,6 +108,8 @@ _SIGS = {
                             c_void_p],
     "mt_op_attention_bwd": [c_int32, c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                             c_void_p, c_size_t, c_void_p],
+    "mt_op_attention_bwd_noalloc": [c_int32, c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
+                                    c_void_p, c_void_p],
     "mt_op_attention_ws_bytes": [c_int32, c_int32, c_int32, c_int32, POINTER(c_size_t)],
 }
 VOID_FUNCS = {"mt_store_destroy": [c_void_p]}

@@ -34,6 +34,7 @@
 // [B, heads, S] natural-log row logsumexp of the scaled scores.
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <type_traits>
 
 #include "common.h"
@@ -1044,6 +1045,56 @@ void attention_bwd16(const uint16_t* qkv16, const uint16_t* o, const float* lse,
     else
         launch_attn_bwd16<64>(qkv16, o, lse, dout, dqkv, B, S, heads, (char*)ws, sl2, scale, s);
     launch_check("attention_bwd16", s);
+}
+
+// ---------------------------------------------------------------------------
+// Allocation-free attention backward: the same kernels with the row dot
+// products D = rowsum(dO * O) in a file-scope device array instead of a
+// caller workspace, for callers that cannot allocate device memory.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[ATTN_STATIC_SCRATCH_BYTES];
+
+// Device address of `scratch` on the stream's device.  The array's name in
+// host code is only a handle for the runtime; its address on a device comes
+// from hipGetSymbolAddress, taken once per device with that device current.
+static void* static_scratch(hipStream_t s) {
+    constexpr int MAX_DEV = 64;
+    static std::mutex mu;
+    static void* addr[MAX_DEV] = {};
+    int dev = 0;
+    hipError_t e = s ? hipStreamGetDevice(s, &dev) : hipGetDevice(&dev);
+    if (e != hipSuccess) MT_FAIL(MT_E_HIP, "attention (no-alloc): device of the stream: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= MAX_DEV) MT_FAIL(MT_E_ARG, "attention (no-alloc): device %d out of range", dev);
+    std::lock_guard<std::mutex> lk(mu);
+    if (!addr[dev]) {
+        int cur = 0;
+        e = hipGetDevice(&cur);
+        if (e != hipSuccess) MT_FAIL(MT_E_HIP, "attention (no-alloc): hipGetDevice: %s", hipGetErrorString(e));
+        if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess)
+            MT_FAIL(MT_E_HIP, "attention (no-alloc): hipSetDevice(%d): %s", dev, hipGetErrorString(e));
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        const hipError_t e2 = cur != dev ? hipSetDevice(cur) : hipSuccess;
+        if (e != hipSuccess || p == nullptr)
+            MT_FAIL(MT_E_HIP, "attention (no-alloc): hipGetSymbolAddress: %s", hipGetErrorString(e));
+        if (e2 != hipSuccess) MT_FAIL(MT_E_HIP, "attention (no-alloc): hipSetDevice(%d): %s", cur, hipGetErrorString(e2));
+        addr[dev] = p;
+    }
+    return addr[dev];
+}
+
+void attention_bwd_noalloc(const uint16_t* qkv, const uint16_t* o, const float* lse, const uint16_t* dout,
+                           uint16_t* dqkv, int B, int S, int heads, int hd, hipStream_t s) {
+    check_attn(B, S, heads, hd);
+    const size_t need = attention_bwd_ws_bytes(B, S, heads, hd);
+    if (need > ATTN_STATIC_SCRATCH_BYTES)
+        MT_FAIL(MT_E_ARG,
+                "attention (no-alloc): batch*heads*seq = %lld rows need %zu bytes of scratch, above the %zu-byte "
+                "static buffer (at most %zu rows)",
+                (long long)B * heads * S, need, (size_t)ATTN_STATIC_SCRATCH_BYTES, (size_t)ATTN_STATIC_SCRATCH_BYTES / 4);
+    // every element of D is written by the first kernel before it is read,
+    // so the buffer needs no clearing between calls
+    attention_bwd(qkv, o, lse, dout, dqkv, B, S, heads, hd, static_scratch(s), ATTN_STATIC_SCRATCH_BYTES, s);
 }
 
 }  // namespace mt

@@ -93,6 +93,11 @@ void attention_bwd(const uint16_t* qkv, const uint16_t* o, const float* lse, con
 size_t attention_bwd16_ws_bytes(int B, int S, int heads, int hd);
 void attention_bwd16(const uint16_t* qkv16, const uint16_t* o, const float* lse, const uint16_t* dout,
                      uint16_t* dqkv, int B, int S, int heads, int hd, void* ws, size_t ws_bytes, hipStream_t s);
+// The same backward with its scratch in a file-scope device array of
+// ATTN_STATIC_SCRATCH_BYTES per device (no workspace argument, no allocation).
+constexpr size_t ATTN_STATIC_SCRATCH_BYTES = 64ull << 20;
+void attention_bwd_noalloc(const uint16_t* qkv, const uint16_t* o, const float* lse, const uint16_t* dout,
+                           uint16_t* dqkv, int B, int S, int heads, int hd, hipStream_t s);
 
 // Cross entropy over a chunk of logits z [rows, V] (fp32) for tokens
 // t0..t0+rows-1 of the batch: per-row loss and dz (bf16) = (softmax - onehot)/N.

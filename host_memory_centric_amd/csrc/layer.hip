@@ -534,6 +534,19 @@ int mt_op_attention_bwd(int32_t batch, int32_t seq, int32_t heads, int32_t hd, c
     });
 }
 
+int mt_op_attention_bwd_noalloc(int32_t batch, int32_t seq, int32_t heads, int32_t hd, const void* qkv,
+                                const void* o, const float* lse, const void* d_o, void* dqkv, void* stream) {
+    return guard([&] {
+        need(qkv, "qkv");
+        need(o, "o");
+        need(d_o, "d_o");
+        need(dqkv, "dqkv");
+        MT_CHECK_ARG(lse != nullptr, "lse is NULL");
+        attention_bwd_noalloc((const uint16_t*)qkv, (const uint16_t*)o, lse, (const uint16_t*)d_o, (uint16_t*)dqkv,
+                              batch, seq, heads, hd, as_stream(stream));
+    });
+}
+
 int mt_op_attention_ws_bytes(int32_t batch, int32_t seq, int32_t heads, int32_t hd, size_t* out) {
     return guard([&] {
         MT_CHECK_ARG(out != nullptr, "out is NULL");

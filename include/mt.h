@@ -392,6 +392,18 @@ int mt_op_attention_fwd(int32_t batch, int32_t seq, int32_t heads, int32_t hd, c
 int mt_op_attention_bwd(int32_t batch, int32_t seq, int32_t heads, int32_t hd, const void* qkv,
                         const void* o, const float* lse, const void* d_o, void* dqkv, void* ws,
                         size_t ws_bytes, void* stream);
+/* The same attention backward without a workspace argument, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc).  Its scratch (the row dot
+ * products, 4 bytes per batch*heads*seq row) lives in a file-scope device
+ * array of 64 MiB that every GPU the library runs on holds until the process
+ * ends: MT_E_ARG when batch*heads*seq exceeds 16777216 rows (16M), and no
+ * allocation of any kind is made.  Results are bit-identical to
+ * mt_op_attention_bwd.  All calls on one GPU share that array: calls that
+ * overlap in time on one GPU (e.g. on two streams) race and must be ordered
+ * by the caller. */
+int mt_op_attention_bwd_noalloc(int32_t batch, int32_t seq, int32_t heads, int32_t hd, const void* qkv,
+                                const void* o, const float* lse, const void* d_o, void* dqkv, void* stream);
 /* Scratch bytes either attention call needs. */
 int mt_op_attention_ws_bytes(int32_t batch, int32_t seq, int32_t heads, int32_t hd, size_t* out);
 
