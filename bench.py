@@ -65,11 +65,11 @@ def gemm_source_hash():
 
 def measured_traffic(kernel, workload):
     """HBM bytes per launch of a GEMM class from the committed rocprofv3 PMC
-    summary (profiles/gemm_7b_traffic.md), or None if that summary is for
-    another workload or the GEMM sources changed since it was taken."""
+    summary of the workload (profiles/gemm_<workload>_traffic.md), or None if
+    there is none or the GEMM sources changed since it was taken."""
     import re
-    path = os.path.join(ROOT, "profiles", "gemm_7b_traffic.md")
-    if workload != "7b" or not os.path.exists(path):
+    path = os.path.join(ROOT, "profiles", f"gemm_{workload}_traffic.md")
+    if not os.path.exists(path):
         return None
     m = re.search(r"```json\n(.*?)\n```", open(path).read(), re.S)
     if not m:
@@ -83,11 +83,12 @@ def measured_traffic(kernel, workload):
 
 def measured_mfma_busy(kernel, workload):
     """Fraction of cycles the MFMA units are busy in a GEMM class, from the
-    committed rocprofv3 PMC summary (profiles/mfma_util_7b_gemm_attention.md),
-    or None for another workload or once the GEMM sources changed."""
+    committed rocprofv3 PMC summary of the workload
+    (profiles/mfma_util_<workload>_gemm_attention.md), or None if there is
+    none or the GEMM sources changed since it was taken."""
     import re
-    path = os.path.join(ROOT, "profiles", "mfma_util_7b_gemm_attention.md")
-    if workload != "7b" or not os.path.exists(path):
+    path = os.path.join(ROOT, "profiles", f"mfma_util_{workload}_gemm_attention.md")
+    if not os.path.exists(path):
         return None
     m = re.search(r"```json\n(.*?)\n```", open(path).read(), re.S)
     if not m:
@@ -310,13 +311,13 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="14b", choices=WORKLOADS)
     ap.add_argument("--mode", default="streamed", choices=["streamed", "resident"])
-    ap.add_argument("--slots", type=int, default=2)
+    ap.add_argument("--slots", type=int, default=5)
     ap.add_argument("--grad-slabs", type=int, default=16)
     ap.add_argument("--update-order", default="arrival", choices=["arrival", "urgent"],
                     help="order of the host updates: as gradients arrive, or most urgent for the next step first")
-    ap.add_argument("--pinned-store", action="store_true",
-                    help="page-lock the store's W and G regions and copy weights and gradients directly (no packer "
-                         "copy, no gradient slabs); default: the pageable store with the packer and slabs")
+    ap.add_argument("--pageable-store", dest="pinned_store", action="store_false",
+                    help="keep the whole store pageable and stream through the packer and the gradient slabs; "
+                         "default: the store's W and G regions page-locked, weights and gradients copied directly")
     ap.add_argument("--ckpt-every", type=int, default=None, help="override the workload's checkpoint interval")
     ap.add_argument("--micro-batches", type=int, default=1,
                     help="micro-batches per optimizer step (gradients accumulated on the host)")

@@ -433,6 +433,46 @@ void bf16_to_f16(const uint16_t* x, uint16_t* y, int64_t n, hipStream_t s) {
     launch_check("bf16_to_f16", s);
 }
 
+// bf16 -> fp16 with a transpose: each lane moves one 8x8 block (eight
+// 16-byte row loads, an in-register transpose, eight 16-byte stores); the 64
+// lanes of a wave cover a 64x64 tile, so that every load and store
+// instruction touches eight whole 128-byte rows.  Four waves per workgroup
+// take four consecutive column tiles.
+__global__ __launch_bounds__(256) void bf16_to_f16_t_kernel(const uint16_t* __restrict__ x,
+                                                            uint16_t* __restrict__ y, int64_t rows,
+                                                            int64_t cols) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t r0 = (int64_t)blockIdx.y * 64 + 8 * (lane >> 3);
+    const int64_t c0 = ((int64_t)blockIdx.x * 4 + wave) * 64 + 8 * (lane & 7);
+    if (r0 >= rows || c0 >= cols) return;
+    uint32_t in[8][4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint4 v = *(const uint4*)(x + (r0 + i) * cols + c0);
+        in[i][0] = v.x;
+        in[i][1] = v.y;
+        in[i][2] = v.z;
+        in[i][3] = v.w;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        float f[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) f[i] = (j & 1) ? bf_hi(in[i][j >> 1]) : bf_lo(in[i][j >> 1]);
+        *(uint4*)(y + (c0 + j) * rows + r0) =
+            make_uint4(pack_h2(f[0], f[1]), pack_h2(f[2], f[3]), pack_h2(f[4], f[5]), pack_h2(f[6], f[7]));
+    }
+}
+
+void bf16_to_f16_t(const uint16_t* x, uint16_t* y, int64_t rows, int64_t cols, hipStream_t s) {
+    if (rows % 8 || cols % 8)
+        MT_FAIL(MT_E_SHAPE, "bf16_to_f16_t: %lld x %lld, not multiples of 8", (long long)rows, (long long)cols);
+    if (rows == 0 || cols == 0) return;
+    const dim3 grid((unsigned)((cols + 255) / 256), (unsigned)((rows + 63) / 64));
+    hipLaunchKernelGGL(bf16_to_f16_t_kernel, grid, dim3(256), 0, s, x, y, rows, cols);
+    launch_check("bf16_to_f16_t", s);
+}
+
 void swiglu_fwd(const uint16_t* gu, uint16_t* a, int64_t T, int f, hipStream_t s) {
     const int64_t n = T * (f / 8);
     if (n == 0) return;

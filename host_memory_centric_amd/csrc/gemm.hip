@@ -1,6 +1,8 @@
 // bf16 GEMM on gfx950 matrix cores (v_mfma_f32_32x32x16_bf16), fp32
 // accumulation (and the same kernels on fp16 operands, v_mfma_f32_32x32x16_f16,
-// for the forward maps, whose activations are kept in fp16), for the layer
+// for the forward maps, whose activations are kept in fp16 and whose weights
+// are converted to fp16 and transposed to [in, out], so that the forward runs
+// in the input-gradient orientation below), for the layer
 // template's linear maps (QKV, output, gate/up and
 // down projections and the LM head) in the three orientations the forward and
 // backward need:
@@ -90,8 +92,10 @@ static void launch_tiles(const GemmDesc& d, hipStream_t s, float* part, int spli
     const GemmArgs p = make_args(d, part, splits, kps, BM, BN);
     dim3 grid(p.tiles_m * p.tiles_n, splits);
     dim3 block(WM * WN * 64);
-    if (d.f16)
+    if (d.f16 && d.b_kmajor)
         hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, true, true, true>), grid, block, 0, s, p);
+    else if (d.f16)
+        hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, true, false, true>), grid, block, 0, s, p);
     else if (d.a_kmajor && d.b_kmajor)
         hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, true, true>), grid, block, 0, s, p);
     else if (d.a_kmajor && !d.b_kmajor)
@@ -120,8 +124,10 @@ static void launch_pp(const GemmDesc& d, hipStream_t s, float* part, int splits,
     const GemmArgs p = make_args(d, part, splits, kps, 256, 256);
     dim3 grid(p.tiles_m * p.tiles_n, splits);
     dim3 block(512);
-    if (d.f16)
+    if (d.f16 && d.b_kmajor)
         hipLaunchKernelGGL((gemm_pp_kernel<true, true, true>), grid, block, 0, s, p);
+    else if (d.f16)
+        hipLaunchKernelGGL((gemm_pp_kernel<true, false, true>), grid, block, 0, s, p);
     else if (d.a_kmajor && d.b_kmajor)
         hipLaunchKernelGGL((gemm_pp_kernel<true, true>), grid, block, 0, s, p);
     else if (d.a_kmajor && !d.b_kmajor)
@@ -190,7 +196,7 @@ void gemm(const GemmDesc& d, hipStream_t s) {
     float* part = splits > 1 ? (float*)d.ws : nullptr;
     const ProfClass pc = d.a_kmajor ? (d.b_kmajor ? PROF_GEMM_NT : PROF_GEMM_NN) : PROF_GEMM_TN;
     ProfScope prof(pc, 2.0 * (double)d.M * (double)d.N * (double)d.K, s);
-    if (d.f16 && !(d.a_kmajor && d.b_kmajor)) MT_FAIL(MT_E_ARG, "gemm: fp16 operands are supported K-major only");
+    if (d.f16 && !d.a_kmajor) MT_FAIL(MT_E_ARG, "gemm: fp16 operands need a K-major A");
     if (pipe_ok(d, kps)) {
         if (use_pp() || d.f16) launch_pp(d, s, part, splits, kps);
         else launch_pipe(d, s, part, splits, kps);

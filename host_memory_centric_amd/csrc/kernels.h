@@ -37,7 +37,7 @@ struct GemmDesc {
     int accumulate = 0;         // Cf += result
     void* ws = nullptr;         // split-K scratch (fp32)
     size_t ws_bytes = 0;
-    bool f16 = false;           // A and B hold fp16 (not bf16) values; A and B K-major only
+    bool f16 = false;           // A and B hold fp16 (not bf16) values; A K-major only
 };
 void gemm(const GemmDesc& d, hipStream_t s);
 int gemm_pick_splits(int64_t M, int64_t N, int64_t K);
@@ -69,6 +69,8 @@ void qkv_finish(const float* qkv32, uint16_t* qkv, uint16_t* qkv16, const float*
 void swiglu_fwd32(const float* gu, uint16_t* a, uint16_t* a16, int64_t rows, int f, hipStream_t s);
 // bf16 -> fp16 elementwise (n a multiple of 8).
 void bf16_to_f16(const uint16_t* x, uint16_t* y, int64_t n, hipStream_t s);
+// bf16 x [rows, cols] -> fp16 y = x^T [cols, rows] (rows, cols multiples of 8).
+void bf16_to_f16_t(const uint16_t* x, uint16_t* y, int64_t rows, int64_t cols, hipStream_t s);
 
 // SwiGLU: a = silu(gate) * up from gu [T, 2f]; and its backward.
 void swiglu_fwd(const uint16_t* gu, uint16_t* a, int64_t T, int f, hipStream_t s);

@@ -59,7 +59,7 @@ Saved carve_saved(Carve& c, const mt_model_cfg* cfg, int64_t B, int64_t S) {
 // Forward transients (fp16 GEMM operands and fp32 GEMM outputs); they share
 // memory with the backward temporaries below, which are dead during a forward.
 struct FwdWs {
-    uint16_t* w16;    // the layer's four matrices as fp16, W-region order [3h*h | h*h | 2f*h | h*f]
+    uint16_t* w16;    // the layer's four matrices as fp16, transposed to [in, out]: [h*3h | h*h | h*2f | f*h]
     uint16_t* n16;    // RMSNorm output of a token chunk, fp16 [Tc, h]
     float* qkv32;     // fused projection of a token chunk, fp32 [Tc, 3h]
     uint16_t* o16;    // attention output as fp16, whole batch [T, h]
@@ -171,11 +171,12 @@ GemmDesc gd(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, bool ak
 }
 
 // Forward of one layer: x -> y, internals into sv.  The GEMM operands of the
-// forward are fp16 (the weights converted exactly, the activations rounded
-// once from fp32: three more significand bits than bf16).  The backward reads
-// q, k, v as the same fp16 values, so that its recomputed attention scores are
-// the forward's; its other internals are stored bf16, from the same fp32 values.  Per-token work
-// runs over token chunks (fwd_chunk), attention over the whole batch.
+// forward are fp16 (the weights converted exactly and transposed to [in, out],
+// the activations rounded once from fp32: three more significand bits than
+// bf16).  The backward reads q, k, v as the same fp16 values, so that its
+// recomputed attention scores are the forward's; its other internals are
+// stored bf16, from the same fp32 values.  Per-token work runs over token
+// chunks (fwd_chunk), attention over the whole batch.
 void layer_forward(const mt_layer_view* v, const mt_model_cfg* cfg, int B, int S, const uint16_t* x, uint16_t* y,
                    const float* cs, const float* sn, const Saved& sv, const FwdWs& fw, hipStream_t s) {
     const int64_t T = (int64_t)B * S, h = cfg->hidden, f = cfg->ffn, Tc = fwd_chunk(T);
@@ -185,16 +186,16 @@ void layer_forward(const mt_layer_view* v, const mt_model_cfg* cfg, int B, int S
     uint16_t* wo = wqkv + 3 * h * h;
     uint16_t* wgu = wo + h * h;
     uint16_t* wd = wgu + 2 * f * h;
-    bf16_to_f16((const uint16_t*)v->w[1], wqkv, 3 * h * h, s);
-    bf16_to_f16((const uint16_t*)v->w[2], wo, h * h, s);
-    bf16_to_f16((const uint16_t*)v->w[4], wgu, 2 * f * h, s);
-    bf16_to_f16((const uint16_t*)v->w[5], wd, h * f, s);
+    bf16_to_f16_t((const uint16_t*)v->w[1], wqkv, 3 * h, h, s);
+    bf16_to_f16_t((const uint16_t*)v->w[2], wo, h, h, s);
+    bf16_to_f16_t((const uint16_t*)v->w[4], wgu, 2 * f, h, s);
+    bf16_to_f16_t((const uint16_t*)v->w[5], wd, h, f, s);
 
     // attention RMSNorm, QKV projection, RoPE: per token chunk
     for (int64_t t0 = 0; t0 < T; t0 += Tc) {
         const int64_t rows = std::min(Tc, T - t0);
         rmsnorm_fwd2(x + t0 * h, g_attn, sv.n1 + t0 * h, fw.n16, sv.rstd1 + t0, rows, (int)h, cfg->eps, s);
-        GemmDesc d = gd(rows, 3 * h, h, fw.n16, h, true, wqkv, h, true, 3 * h);
+        GemmDesc d = gd(rows, 3 * h, h, fw.n16, h, true, wqkv, 3 * h, false, 3 * h);
         d.f16 = true;
         d.Cf = fw.qkv32;
         gemm(d, s);
@@ -204,19 +205,19 @@ void layer_forward(const mt_layer_view* v, const mt_model_cfg* cfg, int B, int S
     // output projection + residual, MLP RMSNorm, gate/up, SwiGLU, down + residual: per token chunk
     for (int64_t t0 = 0; t0 < T; t0 += Tc) {
         const int64_t rows = std::min(Tc, T - t0);
-        GemmDesc d = gd(rows, h, h, fw.o16 + t0 * h, h, true, wo, h, true, h);
+        GemmDesc d = gd(rows, h, h, fw.o16 + t0 * h, h, true, wo, h, false, h);
         d.f16 = true;
         d.R = x + t0 * h;
         d.Cb = sv.xm + t0 * h;
         gemm(d, s);
         rmsnorm_fwd2(sv.xm + t0 * h, g_mlp, sv.n2 + t0 * h, fw.n16, sv.rstd2 + t0, rows, (int)h, cfg->eps, s);
-        d = gd(rows, 2 * f, h, fw.n16, h, true, wgu, h, true, 2 * f);
+        d = gd(rows, 2 * f, h, fw.n16, h, true, wgu, 2 * f, false, 2 * f);
         d.f16 = true;
         d.Cf = fw.gu32;
         d.Cb = sv.gu + t0 * 2 * f;
         gemm(d, s);
         swiglu_fwd32(fw.gu32, sv.a + t0 * f, fw.a16, rows, (int)f, s);
-        d = gd(rows, h, f, fw.a16, f, true, wd, f, true, h);
+        d = gd(rows, h, f, fw.a16, f, true, wd, h, false, h);
         d.f16 = true;
         d.R = sv.xm + t0 * h;
         d.Cb = y + t0 * h;
