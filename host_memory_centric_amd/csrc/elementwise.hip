@@ -55,7 +55,7 @@ __global__ __launch_bounds__(256) void rmsnorm_fwd_wave_kernel(const uint16_t* _
         }
     }
     const float r = 1.0f / sqrtf(wave_sum(ss) / (float)h + eps);
-    if (lane == 0) rstd[row] = r;
+    if (lane == 0 && rstd) rstd[row] = r;
 #pragma unroll
     for (int it = 0; it < NV; ++it) {
         const int c = (lane + 64 * it) * 8;
@@ -69,8 +69,9 @@ __global__ __launch_bounds__(256) void rmsnorm_fwd_wave_kernel(const uint16_t* _
                 v[2 * q] = (bf_lo(w[q]) * r) * bf_lo(gw[q]);
                 v[2 * q + 1] = (bf_hi(w[q]) * r) * bf_hi(gw[q]);
             }
-            *(uint4*)(y + row * h + c) = make_uint4(pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3]), pack_bf2(v[4], v[5]),
-                                                    pack_bf2(v[6], v[7]));
+            if (y)
+                *(uint4*)(y + row * h + c) = make_uint4(pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3]),
+                                                        pack_bf2(v[4], v[5]), pack_bf2(v[6], v[7]));
             if (y16)
                 *(uint4*)(y16 + row * h + c) = make_uint4(pack_h2(v[0], v[1]), pack_h2(v[2], v[3]),
                                                           pack_h2(v[4], v[5]), pack_h2(v[6], v[7]));
@@ -399,10 +400,12 @@ __global__ void swiglu_fwd32_kernel(const float* __restrict__ gu, uint16_t* __re
     float v[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[e] = gv[e] * sigmoidf_(gv[e]) * uv[e];
-    *(uint4*)(a + t * f + c) =
-        make_uint4(pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3]), pack_bf2(v[4], v[5]), pack_bf2(v[6], v[7]));
-    *(uint4*)(a16 + t * f + c) =
-        make_uint4(pack_h2(v[0], v[1]), pack_h2(v[2], v[3]), pack_h2(v[4], v[5]), pack_h2(v[6], v[7]));
+    if (a)
+        *(uint4*)(a + t * f + c) =
+            make_uint4(pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3]), pack_bf2(v[4], v[5]), pack_bf2(v[6], v[7]));
+    if (a16)
+        *(uint4*)(a16 + t * f + c) =
+            make_uint4(pack_h2(v[0], v[1]), pack_h2(v[2], v[3]), pack_h2(v[4], v[5]), pack_h2(v[6], v[7]));
 }
 
 void swiglu_fwd32(const float* gu, uint16_t* a, uint16_t* a16, int64_t rows, int f, hipStream_t s) {

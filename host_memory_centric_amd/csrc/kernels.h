@@ -56,8 +56,8 @@ void colsum_to_bf16(const float* part, int64_t nblk, int h, uint16_t* out, hipSt
 void rope_apply(uint16_t* qkv, const float* cos, const float* sin, int64_t T, int S, int heads, int hd,
                 bool inverse, hipStream_t s);
 
-// RMSNorm forward, one wave per row: bf16 y and (when y16 != NULL) fp16 y16
-// from the same fp32 values; rstd fp32 [T].
+// RMSNorm forward, one wave per row: bf16 y and fp16 y16 from the same fp32
+// values, and rstd fp32 [T] (each output skipped when NULL).
 void rmsnorm_fwd2(const uint16_t* x, const uint16_t* g, uint16_t* y, uint16_t* y16, float* rstd, int64_t T, int h,
                   float eps, hipStream_t s);
 // The fused projection's fp32 output of tokens t0 .. t0+rows-1 ([rows, 3h]):
@@ -65,7 +65,8 @@ void rmsnorm_fwd2(const uint16_t* x, const uint16_t* g, uint16_t* y, uint16_t* y
 // into qkv16 ([T, 3h]).
 void qkv_finish(const float* qkv32, uint16_t* qkv, uint16_t* qkv16, const float* cos, const float* sin, int64_t t0,
                 int64_t rows, int S, int heads, int hd, hipStream_t s);
-// SwiGLU from an fp32 gate/up [rows, 2f]: a (bf16) and a16 (fp16), [rows, f].
+// SwiGLU from an fp32 gate/up [rows, 2f]: a (bf16) and a16 (fp16), [rows, f]
+// (either skipped when NULL).
 void swiglu_fwd32(const float* gu, uint16_t* a, uint16_t* a16, int64_t rows, int f, hipStream_t s);
 // bf16 -> fp16 elementwise (n a multiple of 8).
 void bf16_to_f16(const uint16_t* x, uint16_t* y, int64_t n, hipStream_t s);

@@ -26,6 +26,17 @@ struct Carve {
     }
 };
 
+// Token chunk of the per-token phases: the whole batch up to 32768 tokens,
+// else chunks of 32768 (a function of the shape only, so every run of a
+// configuration computes identically; a multiple of the RMSNorm backward's
+// row blocks, so the gain partials of the chunks are those of the whole).
+int64_t fwd_chunk(int64_t T) { return std::min<int64_t>(T, 32768); }
+// Above one chunk the MLP runs chunked in the backward too: its [T, 2f] and
+// [T, f] internals are not kept but recomputed per chunk from the saved
+// residual stream, and its weight gradients accumulate in fp32 over the
+// chunks in order.
+bool mlp_chunked(int64_t T) { return T > fwd_chunk(T); }
+
 // Internals of one layer's forward that its backward reads.
 struct Saved {
     uint16_t* n1;    // RMSNorm output before attention [T, h]
@@ -34,10 +45,10 @@ struct Saved {
     uint16_t* o;     // attention output [T, h]
     float* lse;      // [B, heads, S]
     uint16_t* xm;    // residual stream after attention [T, h]
-    uint16_t* n2;    // RMSNorm output before the MLP [T, h]
+    uint16_t* n2;    // RMSNorm output before the MLP [T, h] (NULL when the MLP is chunked)
     float* rstd2;    // [T]
-    uint16_t* gu;    // gate | up [T, 2f]
-    uint16_t* a;     // silu(gate) * up [T, f]
+    uint16_t* gu;    // gate | up [T, 2f] (NULL when the MLP is chunked)
+    uint16_t* a;     // silu(gate) * up [T, f] (NULL when the MLP is chunked)
 };
 
 Saved carve_saved(Carve& c, const mt_model_cfg* cfg, int64_t B, int64_t S) {
@@ -49,10 +60,13 @@ Saved carve_saved(Carve& c, const mt_model_cfg* cfg, int64_t B, int64_t S) {
     s.o = c.take<uint16_t>(T * h);
     s.lse = c.take<float>(B * cfg->heads * S);
     s.xm = c.take<uint16_t>(T * h);
-    s.n2 = c.take<uint16_t>(T * h);
     s.rstd2 = c.take<float>(T);
-    s.gu = c.take<uint16_t>(T * 2 * f);
-    s.a = c.take<uint16_t>(T * f);
+    s.n2 = s.gu = s.a = nullptr;
+    if (!mlp_chunked(T)) {
+        s.n2 = c.take<uint16_t>(T * h);
+        s.gu = c.take<uint16_t>(T * 2 * f);
+        s.a = c.take<uint16_t>(T * f);
+    }
     return s;
 }
 
@@ -66,11 +80,6 @@ struct FwdWs {
     float* gu32;      // gate | up of a token chunk, fp32 [Tc, 2f]
     uint16_t* a16;    // SwiGLU output of a token chunk, fp16 [Tc, f]
 };
-
-// Token chunk of the forward's per-token phases: the whole batch up to 32768
-// tokens, else chunks of 32768 (a function of the shape only, so every run of
-// a configuration computes identically).
-int64_t fwd_chunk(int64_t T) { return std::min<int64_t>(T, 32768); }
 
 FwdWs carve_fwd(Carve& c, const mt_model_cfg* cfg, int64_t T) {
     const int64_t h = cfg->hidden, f = cfg->ffn, Tc = fwd_chunk(T);
@@ -99,13 +108,24 @@ struct BwdWs {
     float* dg_part;   // RMSNorm gain partials [blocks, h]
     void* splitk;     // split-K partials
     size_t splitk_bytes;
+    // chunked MLP only (else NULL): one chunk's recomputed internals, the
+    // fp16 gate/up weight transposed to [h, 2f], the fp32 weight-gradient sums
+    uint16_t* mc_n2;  // [Tc, h] bf16
+    uint16_t* mc_n16; // [Tc, h] fp16
+    float* mc_rstd;   // [Tc]
+    float* mc_gu32;   // [Tc, 2f]
+    uint16_t* mc_gu;  // [Tc, 2f] bf16
+    uint16_t* mc_a;   // [Tc, f] bf16
+    uint16_t* mc_wgu; // [h, 2f] fp16
+    float* mc_dwd;    // [h, f]
+    float* mc_dwgu;   // [2f, h]
 };
 
 size_t splitk_need(const mt_model_cfg* cfg, int64_t T) {
-    const int64_t h = cfg->hidden, f = cfg->ffn;
+    const int64_t h = cfg->hidden, f = cfg->ffn, Tm = mlp_chunked(T) ? fwd_chunk(T) : T;
     size_t m = 0;
-    m = std::max(m, gemm_splitk_bytes(h, f, T));
-    m = std::max(m, gemm_splitk_bytes(2 * f, h, T));
+    m = std::max(m, gemm_splitk_bytes(h, f, Tm));
+    m = std::max(m, gemm_splitk_bytes(2 * f, h, Tm));
     m = std::max(m, gemm_splitk_bytes(h, h, T));
     m = std::max(m, gemm_splitk_bytes(3 * h, h, T));
     return m;
@@ -124,8 +144,9 @@ BwdWs carve_ws(Carve& c, const mt_model_cfg* cfg, int64_t B, int64_t S) {
         w.fw = carve_fwd(cf, cfg, T);
         fwd_bytes = cf.off;
     }
-    w.da = c.take<uint16_t>(T * f);
-    w.dgu = c.take<uint16_t>(T * 2 * f);
+    const int64_t Tm = mlp_chunked(T) ? fwd_chunk(T) : T;  // rows of the MLP's backward temporaries
+    w.da = c.take<uint16_t>(Tm * f);
+    w.dgu = c.take<uint16_t>(Tm * 2 * f);
     w.dn = c.take<float>(T * h);
     w.dxm = c.take<float>(T * h);
     w.dxm_b = c.take<uint16_t>(T * h);
@@ -137,6 +158,19 @@ BwdWs carve_ws(Carve& c, const mt_model_cfg* cfg, int64_t B, int64_t S) {
     w.dg_part = c.take<float>(rmsnorm_bwd_blocks(T) * h);
     w.splitk_bytes = splitk_need(cfg, T);
     w.splitk = c.take<char>(w.splitk_bytes);
+    w.mc_n2 = w.mc_n16 = w.mc_gu = w.mc_a = w.mc_wgu = nullptr;
+    w.mc_rstd = w.mc_gu32 = w.mc_dwd = w.mc_dwgu = nullptr;
+    if (mlp_chunked(T)) {
+        w.mc_n2 = c.take<uint16_t>(Tm * h);
+        w.mc_n16 = c.take<uint16_t>(Tm * h);
+        w.mc_rstd = c.take<float>(Tm);
+        w.mc_gu32 = c.take<float>(Tm * 2 * f);
+        w.mc_gu = c.take<uint16_t>(Tm * 2 * f);
+        w.mc_a = c.take<uint16_t>(Tm * f);
+        w.mc_wgu = c.take<uint16_t>(h * 2 * f);
+        w.mc_dwd = c.take<float>(h * f);
+        w.mc_dwgu = c.take<float>(2 * f * h);
+    }
     if (c.off < union_off + fwd_bytes) c.off = union_off + fwd_bytes;  // the union's larger part
     return w;
 }
@@ -210,13 +244,14 @@ void layer_forward(const mt_layer_view* v, const mt_model_cfg* cfg, int B, int S
         d.R = x + t0 * h;
         d.Cb = sv.xm + t0 * h;
         gemm(d, s);
-        rmsnorm_fwd2(sv.xm + t0 * h, g_mlp, sv.n2 + t0 * h, fw.n16, sv.rstd2 + t0, rows, (int)h, cfg->eps, s);
+        rmsnorm_fwd2(sv.xm + t0 * h, g_mlp, sv.n2 ? sv.n2 + t0 * h : nullptr, fw.n16, sv.rstd2 + t0, rows, (int)h,
+                     cfg->eps, s);
         d = gd(rows, 2 * f, h, fw.n16, h, true, wgu, 2 * f, false, 2 * f);
         d.f16 = true;
         d.Cf = fw.gu32;
-        d.Cb = sv.gu + t0 * 2 * f;
+        d.Cb = sv.gu ? sv.gu + t0 * 2 * f : nullptr;
         gemm(d, s);
-        swiglu_fwd32(fw.gu32, sv.a + t0 * f, fw.a16, rows, (int)f, s);
+        swiglu_fwd32(fw.gu32, sv.a ? sv.a + t0 * f : nullptr, fw.a16, rows, (int)f, s);
         d = gd(rows, h, f, fw.a16, f, true, wd, h, false, h);
         d.f16 = true;
         d.R = sv.xm + t0 * h;
@@ -235,27 +270,76 @@ void layer_backward(const mt_layer_view* v, const mt_model_cfg* cfg, const mt_ac
     const uint16_t* wd = (const uint16_t*)v->w[5];
     const uint16_t* dyb = (const uint16_t*)io->dy_bf16;
 
-    // down projection
-    GemmDesc d = gd(h, f, T, dyb, h, false, sv.a, f, false, f);
-    d.Cb = v->g[5];
-    d.ws = w.splitk;
-    d.ws_bytes = w.splitk_bytes;
-    gemm(d, s);
-    d = gd(T, f, h, dyb, h, true, wd, f, false, f);
-    d.Cb = w.da;
-    gemm(d, s);
-    swiglu_bwd(w.da, sv.gu, w.dgu, T, (int)f, s);
-    // gate/up projection
-    d = gd(2 * f, h, T, w.dgu, 2 * f, false, sv.n2, h, false, h);
-    d.Cb = v->g[4];
-    d.ws = w.splitk;
-    d.ws_bytes = w.splitk_bytes;
-    gemm(d, s);
-    d = gd(T, h, 2 * f, w.dgu, 2 * f, true, wgu, h, false, h);
-    d.Cf = w.dn;
-    gemm(d, s);
-    // MLP RMSNorm (+ residual)
-    rmsnorm_bwd(w.dn, sv.xm, sv.rstd2, (const uint16_t*)v->w[3], io->dy, w.dxm, w.dxm_b, w.dg_part, T, (int)h, s);
+    const uint16_t* g_mlp = (const uint16_t*)v->w[3];
+    GemmDesc d;
+    if (!mlp_chunked(T)) {
+        // down projection
+        d = gd(h, f, T, dyb, h, false, sv.a, f, false, f);
+        d.Cb = v->g[5];
+        d.ws = w.splitk;
+        d.ws_bytes = w.splitk_bytes;
+        gemm(d, s);
+        d = gd(T, f, h, dyb, h, true, wd, f, false, f);
+        d.Cb = w.da;
+        gemm(d, s);
+        swiglu_bwd(w.da, sv.gu, w.dgu, T, (int)f, s);
+        // gate/up projection
+        d = gd(2 * f, h, T, w.dgu, 2 * f, false, sv.n2, h, false, h);
+        d.Cb = v->g[4];
+        d.ws = w.splitk;
+        d.ws_bytes = w.splitk_bytes;
+        gemm(d, s);
+        d = gd(T, h, 2 * f, w.dgu, 2 * f, true, wgu, h, false, h);
+        d.Cf = w.dn;
+        gemm(d, s);
+        // MLP RMSNorm (+ residual)
+        rmsnorm_bwd(w.dn, sv.xm, sv.rstd2, g_mlp, io->dy, w.dxm, w.dxm_b, w.dg_part, T, (int)h, s);
+    } else {
+        // Per token chunk: recompute the chunk's MLP input (RMSNorm), gate/up
+        // (the forward's fp16 GEMM) and SwiGLU exactly as the forward computed
+        // them, then its backward; the weight gradients are summed over the
+        // chunks in order in fp32 and rounded once.
+        const int64_t Tc = fwd_chunk(T);
+        bf16_to_f16_t(wgu, w.mc_wgu, 2 * f, h, s);
+        for (int64_t t0 = 0; t0 < T; t0 += Tc) {
+            const int64_t rows = std::min(Tc, T - t0);
+            const int acc = t0 > 0;
+            rmsnorm_fwd2(sv.xm + t0 * h, g_mlp, w.mc_n2, w.mc_n16, w.mc_rstd, rows, (int)h, cfg->eps, s);
+            d = gd(rows, 2 * f, h, w.mc_n16, h, true, w.mc_wgu, 2 * f, false, 2 * f);
+            d.f16 = true;
+            d.Cf = w.mc_gu32;
+            d.Cb = w.mc_gu;
+            gemm(d, s);
+            swiglu_fwd32(w.mc_gu32, w.mc_a, nullptr, rows, (int)f, s);
+            // down projection
+            d = gd(h, f, rows, dyb + t0 * h, h, false, w.mc_a, f, false, f);
+            d.Cf = w.mc_dwd;
+            d.accumulate = acc;
+            d.ws = w.splitk;
+            d.ws_bytes = w.splitk_bytes;
+            gemm(d, s);
+            d = gd(rows, f, h, dyb + t0 * h, h, true, wd, f, false, f);
+            d.Cb = w.da;
+            gemm(d, s);
+            swiglu_bwd(w.da, w.mc_gu, w.dgu, rows, (int)f, s);
+            // gate/up projection
+            d = gd(2 * f, h, rows, w.dgu, 2 * f, false, w.mc_n2, h, false, h);
+            d.Cf = w.mc_dwgu;
+            d.accumulate = acc;
+            d.ws = w.splitk;
+            d.ws_bytes = w.splitk_bytes;
+            gemm(d, s);
+            d = gd(rows, h, 2 * f, w.dgu, 2 * f, true, wgu, h, false, h);
+            d.Cf = w.dn + t0 * h;
+            gemm(d, s);
+            // MLP RMSNorm (+ residual); the chunk's gain partials are row
+            // blocks t0 / 16 .. of the whole
+            rmsnorm_bwd(w.dn + t0 * h, sv.xm + t0 * h, sv.rstd2 + t0, g_mlp, io->dy + t0 * h, w.dxm + t0 * h,
+                        w.dxm_b + t0 * h, w.dg_part + rmsnorm_bwd_blocks(t0) * h, rows, (int)h, s);
+        }
+        f32_to_bf16(w.mc_dwd, (uint16_t*)v->g[5], h * f, s);
+        f32_to_bf16(w.mc_dwgu, (uint16_t*)v->g[4], 2 * f * h, s);
+    }
     colsum_to_bf16(w.dg_part, rmsnorm_bwd_blocks(T), (int)h, (uint16_t*)v->g[3], s);
     // output projection
     d = gd(h, h, T, w.dxm_b, h, false, sv.o, h, false, h);

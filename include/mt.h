@@ -316,7 +316,10 @@ typedef struct mt_act {
 } mt_act;
 
 /* Bytes of a layer's saved internals (n1, rstd1, qkv, o, lse, x_mid, n2,
- * rstd2, gate|up, a).  Workspace of a layer call: mt_layer_workspace_bytes
+ * rstd2, gate|up, a; above 32768 tokens per call the MLP runs in token chunks
+ * of 32768 and n2, gate|up and a are not kept: the backward recomputes them
+ * chunk by chunk, as the pages' chunked MLP execution for long contexts
+ * keeps the [tokens, ffn] buffers bounded).  Workspace of a layer call: mt_layer_workspace_bytes
  * when io->saved is given; a call without a saved buffer keeps the internals
  * in the workspace too and needs workspace + saved bytes.  MT_E_ARG when a
  * buffer is too small. */

@@ -318,13 +318,16 @@ def test_layer_full_shape_vs_oracle(gpu, name):
     assert not fails, fails
 
 
-@pytest.mark.parametrize("name", ["tiny", "7b"])
-def test_layer_recompute_path_equals_saved_path(gpu, name):
+@pytest.mark.parametrize("name,kw", [("tiny", {}), ("tiny", dict(batch=20, seq=2048)), ("7b", {})],
+                         ids=["tiny", "tiny_mlp_chunked", "7b"])
+def test_layer_recompute_path_equals_saved_path(gpu, name, kw):
     """mt_layer_recompute_bwd without a saved buffer recomputes the internals
     in the workspace; with one it reads them from an earlier mt_layer_fwd.
-    Both run the same kernels: the gradients must be bit-identical."""
+    Both run the same kernels: the gradients must be bit-identical.  At
+    20 x 2048 tokens (one 32768-token chunk and a ragged one) the MLP's
+    backward recomputes its internals chunk by chunk in both."""
     import torch
-    cfg = synth.preset(name)
+    cfg = synth.preset(name, **kw)
     B, S, h = cfg.batch, cfg.seq, cfg.hidden
     T = B * S
     W, x, dy = _layer_inputs(cfg, seed=81)

@@ -66,6 +66,42 @@ def test_streamed_equals_resident_bitwise(gpu):
             assert np.array_equal(regions[key], a), (name, key)
 
 
+def test_chunked_mlp_step_matches_oracle_and_resident(gpu):
+    """Above 32768 tokens per layer call the MLP runs in token chunks and its
+    backward recomputes the chunk's RMSNorm, gate/up and SwiGLU (20 x 2048 =
+    40960 tokens: one whole chunk and a ragged one of 8192).  Two streamed
+    steps (K = 1, 2 slots) equal the resident steps bit for bit, and the
+    streamed step matches the oracle's full-batch step."""
+    cfg = synth.preset("tiny", batch=20, seq=2048)
+    bits = synth.make_weights(cfg)
+    adam = synth.AdamCfg()
+    runs = {}
+    for name, kw in {"resident": dict(mode="resident"), "k1_2slot": dict(ckpt_every=1, n_slots=2)}.items():
+        print(f"chunked MLP step: {name}", flush=True)
+        tr = _trainer(cfg, bits, **kw)
+        try:
+            losses = [tr.step(synth.make_tokens(cfg, s)) for s in range(2)]
+            runs[name] = (losses, _store_regions(tr))
+        finally:
+            tr.close()
+    ref_losses, ref_regions = runs["resident"]
+    losses, regions = runs["k1_2slot"]
+    assert losses == ref_losses
+    for key, a in ref_regions.items():
+        assert np.array_equal(regions[key], a), key
+    print("chunked MLP step: oracle", flush=True)
+    st = oracle.HostState(bits)
+    tr = _trainer(cfg, bits, ckpt_every=1, n_slots=2)
+    try:
+        tok = synth.make_tokens(cfg, 0)
+        loss = tr.step(tok)
+        prev = snapshot_weights(st)
+        res = oracle.train_step(st, tok, cfg, adam, mode="resident")
+        check_step(tr, loss, res, cfg, w_prev=prev)
+    finally:
+        tr.close()
+
+
 def test_ragged_blocks_and_sequence(gpu):
     """Five layers (blocks of 2, 2, 1 and of 3, 2) at a sequence of 100
     (partial attention and GEMM tiles): every schedule gives the resident
