@@ -194,7 +194,8 @@ void gemm(const GemmDesc& d, hipStream_t s) {
         splits = (int)((d.K + kps - 1) / kps);
     }
     float* part = splits > 1 ? (float*)d.ws : nullptr;
-    const ProfClass pc = d.a_kmajor ? (d.b_kmajor ? PROF_GEMM_NT : PROF_GEMM_NN) : PROF_GEMM_TN;
+    const ProfClass pc =
+        d.f16 ? PROF_GEMM_FWD16 : d.a_kmajor ? (d.b_kmajor ? PROF_GEMM_NT : PROF_GEMM_NN) : PROF_GEMM_TN;
     ProfScope prof(pc, 2.0 * (double)d.M * (double)d.N * (double)d.K, s);
     if (d.f16 && !d.a_kmajor) MT_FAIL(MT_E_ARG, "gemm: fp16 operands need a K-major A");
     if (pipe_ok(d, kps)) {

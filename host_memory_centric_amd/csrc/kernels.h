@@ -14,7 +14,7 @@ void launch_check(const char* what, hipStream_t s = nullptr);
 
 // Kernel timing (see mt_prof_enable): a scope that records a start event on
 // construction and an end event on destruction, when timing is on.
-enum ProfClass { PROF_GEMM_NT = 0, PROF_GEMM_NN, PROF_GEMM_TN, PROF_ATTN_FWD, PROF_ATTN_BWD, PROF_N };
+enum ProfClass { PROF_GEMM_NT = 0, PROF_GEMM_NN, PROF_GEMM_TN, PROF_ATTN_FWD, PROF_ATTN_BWD, PROF_GEMM_FWD16, PROF_N };
 struct ProfScope {
     ProfScope(ProfClass c, double flops, hipStream_t s);
     ~ProfScope();

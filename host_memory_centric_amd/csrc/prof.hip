@@ -14,7 +14,7 @@
 namespace mt {
 
 namespace {
-const char* kNames[PROF_N] = {"gemm_nt", "gemm_nn", "gemm_tn", "attn_fwd", "attn_bwd"};
+const char* kNames[PROF_N] = {"gemm_nt", "gemm_nn", "gemm_tn", "attn_fwd", "attn_bwd", "gemm_fwd16"};
 
 struct Rec {
     int cls;

@@ -414,7 +414,8 @@ int mt_op_attention_ws_bytes(int32_t batch, int32_t seq, int32_t heads, int32_t 
 /* Kernel timing                                                            */
 /* ------------------------------------------------------------------------ */
 
-/* One kernel class: GEMMs by operand orientation ("gemm_nt" forward,
+/* One kernel class: GEMMs by operand orientation and type ("gemm_fwd16" the
+ * layer forward's fp16 projections, "gemm_nt" the LM head's forward,
  * "gemm_nn" input gradient, "gemm_tn" weight gradient, each including its
  * split-K reduction) and attention ("attn_fwd", "attn_bwd").  flops are the
  * algorithmic flops of the recorded launches (2*M*N*K per GEMM; causal
