@@ -269,7 +269,8 @@ __global__ void rope_kernel(uint16_t* __restrict__ qkv, const float* __restrict_
 // of one head of q, k or v (v is only converted).
 __global__ void qkv_finish_kernel(const float* __restrict__ qkv32, uint16_t* __restrict__ qkv,
                                   uint16_t* __restrict__ qkv16, const float* __restrict__ cs,
-                                  const float* __restrict__ sn, int64_t t0, int64_t rows, int S, int heads, int hd) {
+                                  const float* __restrict__ sn, int64_t t0, int64_t rows, int S, int heads, int hd,
+                                  int interleaved) {
     const int half = hd / 2, groups = half / 8;
     const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t per_tok = (int64_t)3 * heads * groups;
@@ -283,11 +284,25 @@ __global__ void qkv_finish_kernel(const float* __restrict__ qkv32, uint16_t* __r
     const int s = (int)(t % S);
     const int64_t h3 = (int64_t)3 * heads * hd;
     const int64_t col = (int64_t)which * heads * hd + (int64_t)head * hd + gi * 8;
-    const float* src = qkv32 + tr * h3 + col;
-    const float4 a0 = *(const float4*)src, a1 = *(const float4*)(src + 4);
-    const float4 b0 = *(const float4*)(src + half), b1 = *(const float4*)(src + half + 4);
-    float a[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-    float b[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+    float a[8], b[8];
+    if (interleaved && which < 2) {
+        // features (p, p + hd/2) of pair p at columns 2p, 2p + 1 of the head
+        const float* src = qkv32 + tr * h3 + (int64_t)which * heads * hd + (int64_t)head * hd + 2 * (gi * 8);
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+            const float4 v = *(const float4*)(src + 2 * e);
+            a[e] = v.x;
+            b[e] = v.y;
+            a[e + 1] = v.z;
+            b[e + 1] = v.w;
+        }
+    } else {
+        const float* src = qkv32 + tr * h3 + col;
+        const float4 a0 = *(const float4*)src, a1 = *(const float4*)(src + 4);
+        const float4 b0 = *(const float4*)(src + half), b1 = *(const float4*)(src + half + 4);
+        a[0] = a0.x; a[1] = a0.y; a[2] = a0.z; a[3] = a0.w; a[4] = a1.x; a[5] = a1.y; a[6] = a1.z; a[7] = a1.w;
+        b[0] = b0.x; b[1] = b0.y; b[2] = b0.z; b[3] = b0.w; b[4] = b1.x; b[5] = b1.y; b[6] = b1.z; b[7] = b1.w;
+    }
     if (which < 2) {
         const float* cp = cs + (int64_t)s * half + gi * 8;
         const float* sp = sn + (int64_t)s * half + gi * 8;
@@ -312,12 +327,12 @@ __global__ void qkv_finish_kernel(const float* __restrict__ qkv32, uint16_t* __r
 }
 
 void qkv_finish(const float* qkv32, uint16_t* qkv, uint16_t* qkv16, const float* cos, const float* sin, int64_t t0,
-                int64_t rows, int S, int heads, int hd, hipStream_t s) {
+                int64_t rows, int S, int heads, int hd, bool interleaved, hipStream_t s) {
     if (hd % 16) MT_FAIL(MT_E_SHAPE, "qkv_finish: head_dim %d must be a multiple of 16", hd);
     const int64_t n = rows * 3 * heads * (hd / 16);
     if (n == 0) return;
     hipLaunchKernelGGL(qkv_finish_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, qkv32, qkv, qkv16, cos,
-                       sin, t0, rows, S, heads, hd);
+                       sin, t0, rows, S, heads, hd, interleaved ? 1 : 0);
     launch_check("qkv_finish", s);
 }
 
@@ -331,7 +346,6 @@ void rope_apply(uint16_t* qkv, const float* cos, const float* sin, int64_t T, in
     launch_check("rope", s);
 }
 
-__device__ __forceinline__ float sigmoidf_(float z) { return 1.0f / (1.0f + __expf(-z)); }
 
 __global__ void swiglu_fwd_kernel(const uint16_t* __restrict__ gu, uint16_t* __restrict__ a, int64_t T, int f) {
     const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -385,21 +399,41 @@ __global__ void swiglu_bwd_kernel(const uint16_t* __restrict__ da, const uint16_
 // SwiGLU from the gate/up projection's fp32 output gu32 [rows, 2f]:
 // a = silu(gate) * up in fp32, rounded once to bf16 (a, [rows, f]) and to
 // fp16 (a16, [rows, f]).
-__global__ void swiglu_fwd32_kernel(const float* __restrict__ gu, uint16_t* __restrict__ a,
-                                    uint16_t* __restrict__ a16, int64_t rows, int f) {
+__global__ void swiglu_fwd32_kernel(const float* __restrict__ gu32, uint16_t* __restrict__ gu,
+                                    uint16_t* __restrict__ a, uint16_t* __restrict__ a16, int64_t rows, int f,
+                                    int interleaved) {
     const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int per = f / 8;
     if (idx >= rows * per) return;
     const int64_t t = idx / per;
     const int c = (int)(idx % per) * 8;
-    const float* gr = gu + t * 2 * f + c;
-    const float4 g0 = *(const float4*)gr, g1 = *(const float4*)(gr + 4);
-    const float4 u0 = *(const float4*)(gr + f), u1 = *(const float4*)(gr + f + 4);
-    const float gv[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
-    const float uv[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+    float gv[8], uv[8];
+    if (interleaved) {
+        const float* src = gu32 + t * 2 * f + 2 * c;
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+            const float4 v = *(const float4*)(src + 2 * e);
+            gv[e] = v.x;
+            uv[e] = v.y;
+            gv[e + 1] = v.z;
+            uv[e + 1] = v.w;
+        }
+    } else {
+        const float* gr = gu32 + t * 2 * f + c;
+        const float4 g0 = *(const float4*)gr, g1 = *(const float4*)(gr + 4);
+        const float4 u0 = *(const float4*)(gr + f), u1 = *(const float4*)(gr + f + 4);
+        gv[0] = g0.x; gv[1] = g0.y; gv[2] = g0.z; gv[3] = g0.w; gv[4] = g1.x; gv[5] = g1.y; gv[6] = g1.z; gv[7] = g1.w;
+        uv[0] = u0.x; uv[1] = u0.y; uv[2] = u0.z; uv[3] = u0.w; uv[4] = u1.x; uv[5] = u1.y; uv[6] = u1.z; uv[7] = u1.w;
+    }
+    if (gu) {
+        *(uint4*)(gu + t * 2 * f + c) = make_uint4(pack_bf2(gv[0], gv[1]), pack_bf2(gv[2], gv[3]),
+                                                   pack_bf2(gv[4], gv[5]), pack_bf2(gv[6], gv[7]));
+        *(uint4*)(gu + t * 2 * f + f + c) = make_uint4(pack_bf2(uv[0], uv[1]), pack_bf2(uv[2], uv[3]),
+                                                       pack_bf2(uv[4], uv[5]), pack_bf2(uv[6], uv[7]));
+    }
     float v[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = gv[e] * sigmoidf_(gv[e]) * uv[e];
+    for (int e = 0; e < 8; ++e) v[e] = swiglu_f(gv[e], uv[e]);
     if (a)
         *(uint4*)(a + t * f + c) =
             make_uint4(pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3]), pack_bf2(v[4], v[5]), pack_bf2(v[6], v[7]));
@@ -408,10 +442,12 @@ __global__ void swiglu_fwd32_kernel(const float* __restrict__ gu, uint16_t* __re
             make_uint4(pack_h2(v[0], v[1]), pack_h2(v[2], v[3]), pack_h2(v[4], v[5]), pack_h2(v[6], v[7]));
 }
 
-void swiglu_fwd32(const float* gu, uint16_t* a, uint16_t* a16, int64_t rows, int f, hipStream_t s) {
+void swiglu_fwd32(const float* gu32, uint16_t* gu, uint16_t* a, uint16_t* a16, int64_t rows, int f, bool interleaved,
+                  hipStream_t s) {
     const int64_t n = rows * (f / 8);
     if (n == 0) return;
-    hipLaunchKernelGGL(swiglu_fwd32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, gu, a, a16, rows, f);
+    hipLaunchKernelGGL(swiglu_fwd32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, gu32, gu, a, a16, rows,
+                       f, interleaved ? 1 : 0);
     launch_check("swiglu_fwd32", s);
 }
 
@@ -441,9 +477,19 @@ void bf16_to_f16(const uint16_t* x, uint16_t* y, int64_t n, hipStream_t s) {
 // lanes of a wave cover a 64x64 tile, so that every load and store
 // instruction touches eight whole 128-byte rows.  Four waves per workgroup
 // take four consecutive column tiles.
+// Source row of output column c of the permuted transpose (see bf16_to_f16_t).
+__device__ __forceinline__ int64_t perm_src(int64_t c, int perm, int64_t pa, int64_t pb, int64_t rows) {
+    if (perm == 1 && c < pa) {
+        const int64_t o = c % pb;
+        return c - o + o / 2 + (o & 1) * (pb / 2);
+    }
+    if (perm == 2) return c / 2 + (c & 1) * (rows / 2);
+    return c;
+}
+
 __global__ __launch_bounds__(256) void bf16_to_f16_t_kernel(const uint16_t* __restrict__ x,
                                                             uint16_t* __restrict__ y, int64_t rows,
-                                                            int64_t cols) {
+                                                            int64_t cols, int perm, int64_t pa, int64_t pb) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int64_t r0 = (int64_t)blockIdx.y * 64 + 8 * (lane >> 3);
     const int64_t c0 = ((int64_t)blockIdx.x * 4 + wave) * 64 + 8 * (lane & 7);
@@ -451,7 +497,7 @@ __global__ __launch_bounds__(256) void bf16_to_f16_t_kernel(const uint16_t* __re
     uint32_t in[8][4];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        const uint4 v = *(const uint4*)(x + (r0 + i) * cols + c0);
+        const uint4 v = *(const uint4*)(x + perm_src(r0 + i, perm, pa, pb, rows) * cols + c0);
         in[i][0] = v.x;
         in[i][1] = v.y;
         in[i][2] = v.z;
@@ -467,12 +513,15 @@ __global__ __launch_bounds__(256) void bf16_to_f16_t_kernel(const uint16_t* __re
     }
 }
 
-void bf16_to_f16_t(const uint16_t* x, uint16_t* y, int64_t rows, int64_t cols, hipStream_t s) {
+void bf16_to_f16_t(const uint16_t* x, uint16_t* y, int64_t rows, int64_t cols, int perm, int64_t pa, int64_t pb,
+                   hipStream_t s) {
     if (rows % 8 || cols % 8)
         MT_FAIL(MT_E_SHAPE, "bf16_to_f16_t: %lld x %lld, not multiples of 8", (long long)rows, (long long)cols);
+    if ((perm == 1 && (pb < 2 || pb % 2 || pa % pb || pa > rows)) || (perm == 2 && rows % 2) || perm < 0 || perm > 2)
+        MT_FAIL(MT_E_ARG, "bf16_to_f16_t: bad permutation %d (%lld, %lld)", perm, (long long)pa, (long long)pb);
     if (rows == 0 || cols == 0) return;
     const dim3 grid((unsigned)((cols + 255) / 256), (unsigned)((rows + 63) / 64));
-    hipLaunchKernelGGL(bf16_to_f16_t_kernel, grid, dim3(256), 0, s, x, y, rows, cols);
+    hipLaunchKernelGGL(bf16_to_f16_t_kernel, grid, dim3(256), 0, s, x, y, rows, cols, perm, pa, pb);
     launch_check("bf16_to_f16_t", s);
 }
 

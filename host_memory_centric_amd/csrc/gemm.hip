@@ -69,6 +69,15 @@ static GemmArgs make_args(const GemmDesc& d, float* part, int splits, int64_t kp
     p.tiles_m = (int)((d.M + bm - 1) / bm);
     p.tiles_n = (int)((d.N + bn - 1) / bn);
     p.k_per_split = kps;
+    p.epi = d.epi;
+    p.rope_cos = d.rope_cos;
+    p.rope_sin = d.rope_sin;
+    p.rope_S = d.rope_S;
+    p.rope_hd = d.rope_hd;
+    p.rope_t0 = d.rope_t0;
+    p.rope_cols = d.rope_cols;
+    p.Ca = (uint16_t*)d.Ca;
+    p.Ca16 = (uint16_t*)d.Ca16;
     if (splits > 1) {
         p.Cf = part;
         p.Cb = nullptr;
@@ -156,6 +165,11 @@ static bool pipe_ok(const GemmDesc& d, int64_t kps) {
            d.ldb < (1 << 22);
 }
 
+bool gemm_epi_ok(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb) {
+    return M >= 256 && N >= 256 && N % 256 == 0 && K % PBK == 0 && lda < (1 << 22) && ldb < (1 << 22) &&
+           gemm_pick_splits(M, N, K) == 1;
+}
+
 size_t gemm_splitk_bytes(int64_t M, int64_t N, int64_t K) {
     const int s = gemm_pick_splits(M, N, K);
     return s > 1 ? (size_t)s * M * N * 4 : 0;
@@ -180,12 +194,22 @@ void gemm(const GemmDesc& d, hipStream_t s) {
         MT_FAIL(MT_E_SHAPE, "gemm: M=%lld N=%lld K=%lld lda=%lld ldb=%lld ldc=%lld must be positive multiples of 8",
                 (long long)d.M, (long long)d.N, (long long)d.K, (long long)d.lda, (long long)d.ldb,
                 (long long)d.ldc);
-    if (!d.A || !d.B || (!d.Cf && !d.Cb)) MT_FAIL(MT_E_ARG, "gemm: NULL operand");
+    if (!d.A || !d.B || (!d.Cf && !d.Cb && !d.epi)) MT_FAIL(MT_E_ARG, "gemm: NULL operand");
     if (((uintptr_t)d.A | (uintptr_t)d.B | (uintptr_t)d.Cf | (uintptr_t)d.Cb | (uintptr_t)d.R) & 15)
         MT_FAIL(MT_E_ALIGN, "gemm: operands must be 16-byte aligned");
     const int64_t a_rows_ld = d.a_kmajor ? d.K : d.M, b_rows_ld = d.b_kmajor ? d.K : d.N;
     if (d.lda < a_rows_ld || d.ldb < b_rows_ld || d.ldc < d.N) MT_FAIL(MT_E_SHAPE, "gemm: leading dimension too small");
-    int splits = gemm_pick_splits(d.M, d.N, d.K);
+    if (d.epi) {
+        if (!d.f16 || d.epi > 2 || d.Cf || d.R || d.accumulate || !gemm_epi_ok(d.M, d.N, d.K, d.lda, d.ldb))
+            MT_FAIL(MT_E_ARG, "gemm: fused epilogue %d not available for M=%lld N=%lld K=%lld", d.epi, (long long)d.M,
+                    (long long)d.N, (long long)d.K);
+        if (((uintptr_t)d.Ca | (uintptr_t)d.Ca16) & 15) MT_FAIL(MT_E_ALIGN, "gemm: outputs must be 16-byte aligned");
+        if (d.epi == 1 && (!d.Cb || !d.rope_cos || !d.rope_sin || d.rope_S < 1 || (d.rope_hd != 64 && d.rope_hd != 128) ||
+                           d.rope_cols % d.rope_hd || d.rope_cols > d.N))
+            MT_FAIL(MT_E_ARG, "gemm: bad RoPE epilogue arguments");
+        if (d.epi == 2 && !d.Cb && !d.Ca && !d.Ca16) MT_FAIL(MT_E_ARG, "gemm: SwiGLU epilogue without outputs");
+    }
+    int splits = d.epi ? 1 : gemm_pick_splits(d.M, d.N, d.K);
     if (splits > 1 && (!d.ws || d.ws_bytes < (size_t)splits * d.M * d.N * 4)) splits = 1;
     const int BK = GBK;
     int64_t kps = d.K;
@@ -199,7 +223,7 @@ void gemm(const GemmDesc& d, hipStream_t s) {
     ProfScope prof(pc, 2.0 * (double)d.M * (double)d.N * (double)d.K, s);
     if (d.f16 && !d.a_kmajor) MT_FAIL(MT_E_ARG, "gemm: fp16 operands need a K-major A");
     if (pipe_ok(d, kps)) {
-        if (use_pp() || d.f16) launch_pp(d, s, part, splits, kps);
+        if (use_pp() || d.f16 || d.epi) launch_pp(d, s, part, splits, kps);
         else launch_pipe(d, s, part, splits, kps);
     }
     else if (use_big(d.M, d.N))

@@ -21,6 +21,21 @@ struct GemmArgs {
     int64_t k_per_split;   // multiple of BK; K slice of blockIdx.y
     int64_t split_stride;  // elements between partial outputs of successive slices (0: no split)
     int tiles_m, tiles_n;
+    // Fused epilogues of the fp16 forward (gemm_pp_kernel only; whole 256-column tiles):
+    //  epi 1: RoPE.  Output columns below rope_cols come in interleaved pairs, column
+    //    2j + e of a head being feature j + e*hd/2; they are rotated by the angle of
+    //    pair j at position (rope_t0 + row) % rope_S and stored de-interleaved, every
+    //    column as fp16, into Cb.
+    //  epi 2: SwiGLU.  Output column 2j + e is gate (e = 0) or up (e = 1) of feature j;
+    //    Cb receives gate | up de-interleaved as bf16 ([M, N], optional), Ca silu(gate)*up
+    //    as bf16 and Ca16 the same as fp16 ([M, N/2], optional).
+    int epi;
+    const float* rope_cos;
+    const float* rope_sin;
+    int rope_S, rope_hd;
+    int64_t rope_t0, rope_cols;
+    uint16_t* Ca;
+    uint16_t* Ca16;
 };
 
 // ---------------------------------------------------------------------------

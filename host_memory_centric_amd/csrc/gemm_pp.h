@@ -13,6 +13,106 @@
 
 namespace mt {
 
+// Staging of a 256 x 256 tile of 16-bit values in LDS: 16-byte chunk c of row
+// r at chunk c ^ (r & 31), so that both the per-lane stores (32 rows, one
+// chunk) and the row reads of the write-out are conflict free.
+__device__ __forceinline__ int stage_off(int r, int col) { return r * 256 + 8 * ((col >> 3) ^ (r & 31)) + (col & 7); }
+
+// Write the staged tile's rows m0 + r (r < 256, rows below m_lo belong to the
+// previous tile) as 16-byte pieces: the thread's chunk c (0..31) goes to
+// lo + m * ld + 8c for c < 16, else to hi + m * ld + 8(c - 16) (either base NULL:
+// skipped).
+__device__ __forceinline__ void write_halves(const uint16_t* st, uint16_t* lo, uint16_t* hi, int64_t ld, int64_t m0,
+                                             int64_t m_lo, int64_t M, int tid) {
+    const int c = tid & 31;
+    uint16_t* base = c < 16 ? lo : hi;
+    if (!base) return;
+    const int cc = c & 15;
+#pragma unroll 4
+    for (int it = 0; it < 16; ++it) {
+        const int r = 16 * it + (tid >> 5);
+        const int64_t m = m0 + r;
+        if (m < m_lo || m >= M) continue;
+        *(uint4*)(base + m * ld + 8 * cc) = *(const uint4*)(st + r * 256 + 8 * (c ^ (r & 31)));
+    }
+}
+
+// The fused epilogues (GemmArgs::epi) of a 256 x 256 tile at (m0, n0); N is a
+// multiple of 256, so n0 is the tile's own origin and every head (or gate/up
+// pair block) lies inside the tile.
+__device__ __forceinline__ void epilogue_fused(const GemmArgs& p, const f32x16 (&acc)[4][2], int64_t m0, int64_t n0,
+                                               int64_t m_lo, int wm, int wn, int lane, int tid, uint16_t* st) {
+    __syncthreads();  // every wave is past its last fragment read: LDS is free
+    if (p.epi == 1) {
+        const int hd = p.rope_hd, half = hd / 2;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = wm * 128 + i * 32 + (lane & 31);
+            const int64_t pos = (p.rope_t0 + m0 + r) % p.rope_S;
+            const float* cs = p.rope_cos + pos * half;
+            const float* sn = p.rope_sin + pos * half;
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int cl = wn * 64 + j * 32 + 8 * q + 4 * (lane >> 5);
+                    const float v0 = acc[i][j][4 * q], v1 = acc[i][j][4 * q + 1], v2 = acc[i][j][4 * q + 2],
+                                v3 = acc[i][j][4 * q + 3];
+                    if (n0 + cl < p.rope_cols) {
+                        // (v0, v1) = features (pr, pr + hd/2) of pair pr, (v2, v3) pair pr + 1
+                        const int o = (int)((n0 + cl) % hd), pr = o / 2;
+                        const int la = cl - o + pr;  // local column of feature pr of this head
+                        const float2 c2 = *(const float2*)(cs + pr), s2 = *(const float2*)(sn + pr);
+                        const float ra0 = v0 * c2.x - v1 * s2.x, rb0 = v1 * c2.x + v0 * s2.x;
+                        const float ra1 = v2 * c2.y - v3 * s2.y, rb1 = v3 * c2.y + v2 * s2.y;
+                        *(uint32_t*)(st + stage_off(r, la)) = pack_h2(ra0, ra1);
+                        *(uint32_t*)(st + stage_off(r, la + half)) = pack_h2(rb0, rb1);
+                    } else {
+                        *(uint2*)(st + stage_off(r, cl)) = make_uint2(pack_h2(v0, v1), pack_h2(v2, v3));
+                    }
+                }
+        }
+        __syncthreads();
+        write_halves(st, p.Cb + n0, p.Cb + n0 + 128, p.ldc, m0, m_lo, p.M, tid);
+        return;
+    }
+    // SwiGLU: (v0, v1, v2, v3) = gate, up of feature jf and of jf + 1, jf = (n0 + cl) / 2
+    const int64_t f = p.N / 2, j0 = n0 / 2;
+    if (p.Cb) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = wm * 128 + i * 32 + (lane & 31);
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int cl = wn * 64 + j * 32 + 8 * q + 4 * (lane >> 5), lg = cl / 2;
+                    *(uint32_t*)(st + stage_off(r, lg)) = pack_bf2(acc[i][j][4 * q], acc[i][j][4 * q + 2]);
+                    *(uint32_t*)(st + stage_off(r, 128 + lg)) = pack_bf2(acc[i][j][4 * q + 1], acc[i][j][4 * q + 3]);
+                }
+        }
+        __syncthreads();
+        write_halves(st, p.Cb + j0, p.Cb + f + j0, p.ldc, m0, m_lo, p.M, tid);
+        __syncthreads();
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = wm * 128 + i * 32 + (lane & 31);
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int cl = wn * 64 + j * 32 + 8 * q + 4 * (lane >> 5), lg = cl / 2;
+                const float a0 = swiglu_f(acc[i][j][4 * q], acc[i][j][4 * q + 1]);
+                const float a1 = swiglu_f(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+                *(uint32_t*)(st + stage_off(r, lg)) = pack_bf2(a0, a1);
+                *(uint32_t*)(st + stage_off(r, 128 + lg)) = pack_h2(a0, a1);
+            }
+    }
+    __syncthreads();
+    write_halves(st, p.Ca ? p.Ca + j0 : nullptr, p.Ca16 ? p.Ca16 + j0 : nullptr, f, m0, m_lo, p.M, tid);
+}
+
 template <bool AK, bool BKM, bool F16 = false>
 __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmArgs p) {
     constexpr int BM = 256, BN = 256;
@@ -134,6 +234,12 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmArgs p) {
 
     // acc[i][j] is the transposed 32x32 block (i, j) of the wave tile: a lane
     // holds output row (lane % 32) and runs of 4 consecutive columns.
+    if constexpr (F16) {
+        if (p.epi) {
+            epilogue_fused(p, acc, m0, n0, m_lo, wm, wn, lane, tid, &smem[0][0]);
+            return;
+        }
+    }
     float* Cf = p.Cf ? p.Cf + (int64_t)blockIdx.y * p.split_stride : nullptr;
     if (!Cf) {
         // bf16 output: residual, round, stage [256][256] in LDS (16-byte chunk

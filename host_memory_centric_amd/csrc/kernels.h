@@ -38,8 +38,23 @@ struct GemmDesc {
     void* ws = nullptr;         // split-K scratch (fp32)
     size_t ws_bytes = 0;
     bool f16 = false;           // A and B hold fp16 (not bf16) values; A K-major only
+    // Fused epilogue (fp16 operands, gemm_epi_ok shapes; no Cf, R, accumulation):
+    //  epi 1: RoPE on interleaved q/k pairs (columns below rope_cols), every column
+    //    stored de-interleaved as fp16 into Cb;
+    //  epi 2: SwiGLU on interleaved gate/up pairs: Cb = gate | up (bf16, optional),
+    //    Ca = silu(gate) * up (bf16, optional), Ca16 the same as fp16 (optional),
+    //    both [M, N/2].
+    int epi = 0;
+    const float* rope_cos = nullptr;
+    const float* rope_sin = nullptr;
+    int rope_S = 0, rope_hd = 0;
+    int64_t rope_t0 = 0, rope_cols = 0;
+    void* Ca = nullptr;
+    void* Ca16 = nullptr;
 };
 void gemm(const GemmDesc& d, hipStream_t s);
+// Whether an M x N x K GEMM (A K-major) can take a fused epilogue.
+bool gemm_epi_ok(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb);
 int gemm_pick_splits(int64_t M, int64_t N, int64_t K);
 size_t gemm_splitk_bytes(int64_t M, int64_t N, int64_t K);
 
@@ -60,18 +75,27 @@ void rope_apply(uint16_t* qkv, const float* cos, const float* sin, int64_t T, in
 // values, and rstd fp32 [T] (each output skipped when NULL).
 void rmsnorm_fwd2(const uint16_t* x, const uint16_t* g, uint16_t* y, uint16_t* y16, float* rstd, int64_t T, int h,
                   float eps, hipStream_t s);
-// The fused projection's fp32 output of tokens t0 .. t0+rows-1 ([rows, 3h]):
-// RoPE on q and k in fp32, then bf16 into qkv (skipped when NULL) and fp16
-// into qkv16 ([T, 3h]).
+// The fused projection's fp32 output of tokens t0 .. t0+rows-1 ([rows, 3h];
+// with `interleaved`, the q and k pairs of each head interleaved as the
+// epilogue of gemm epi 1 takes them): RoPE on q and k in fp32, then bf16 into
+// qkv (skipped when NULL) and fp16 into qkv16 ([T, 3h], features in order).
 void qkv_finish(const float* qkv32, uint16_t* qkv, uint16_t* qkv16, const float* cos, const float* sin, int64_t t0,
-                int64_t rows, int S, int heads, int hd, hipStream_t s);
-// SwiGLU from an fp32 gate/up [rows, 2f]: a (bf16) and a16 (fp16), [rows, f]
-// (either skipped when NULL).
-void swiglu_fwd32(const float* gu, uint16_t* a, uint16_t* a16, int64_t rows, int f, hipStream_t s);
+                int64_t rows, int S, int heads, int hd, bool interleaved, hipStream_t s);
+// SwiGLU from an fp32 gate/up [rows, 2f] (with `interleaved`, gate and up of
+// feature j in columns 2j and 2j + 1): gu = gate | up (bf16 [rows, 2f]), a
+// (bf16) and a16 (fp16), [rows, f] (each skipped when NULL).
+void swiglu_fwd32(const float* gu32, uint16_t* gu, uint16_t* a, uint16_t* a16, int64_t rows, int f, bool interleaved,
+                  hipStream_t s);
 // bf16 -> fp16 elementwise (n a multiple of 8).
 void bf16_to_f16(const uint16_t* x, uint16_t* y, int64_t n, hipStream_t s);
-// bf16 x [rows, cols] -> fp16 y = x^T [cols, rows] (rows, cols multiples of 8).
-void bf16_to_f16_t(const uint16_t* x, uint16_t* y, int64_t rows, int64_t cols, hipStream_t s);
+// bf16 x [rows, cols] -> fp16 y = x^T [cols, rows] (rows, cols multiples of 8),
+// with the columns of y optionally permuted: y[k][c] = x[src(c)][k] where
+//  perm 0: src(c) = c;
+//  perm 1 (RoPE pairs): for c < pa, c = g*pb + 2j + e -> g*pb + j + e*pb/2 (pb = head
+//    dim; pairs of a head interleaved), src(c) = c above pa;
+//  perm 2 (gate/up pairs): c = 2j + e -> j + e*rows/2.
+void bf16_to_f16_t(const uint16_t* x, uint16_t* y, int64_t rows, int64_t cols, int perm, int64_t pa, int64_t pb,
+                   hipStream_t s);
 
 // SwiGLU: a = silu(gate) * up from gu [T, 2f]; and its backward.
 void swiglu_fwd(const uint16_t* gu, uint16_t* a, int64_t T, int f, hipStream_t s);

@@ -74,6 +74,7 @@ Saved carve_saved(Carve& c, const mt_model_cfg* cfg, int64_t B, int64_t S) {
 // memory with the backward temporaries below, which are dead during a forward.
 struct FwdWs {
     uint16_t* w16;    // the layer's four matrices as fp16, transposed to [in, out]: [h*3h | h*h | h*2f | f*h]
+                      // (q/k pairs and gate/up pairs interleaved, see qkv_project and gate_up_project)
     uint16_t* n16;    // RMSNorm output of a token chunk, fp16 [Tc, h]
     float* qkv32;     // fused projection of a token chunk, fp32 [Tc, 3h]
     uint16_t* o16;    // attention output as fp16, whole batch [T, h]
@@ -204,6 +205,57 @@ GemmDesc gd(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, bool ak
     return d;
 }
 
+// QKV projection of tokens t0 .. t0 + rows - 1 from their fp16 RMSNorm output:
+// q and k rotated, then q, k, v as fp16 into qkv16 ([T, 3h]).  wqkv16 is the
+// fp16 weight transposed to [h, 3h] with the (p, p + hd/2) feature pairs of
+// every q and k head interleaved, so that the GEMM's epilogue rotates each pair
+// inside one lane; shapes that the fused epilogue does not take go through
+// fp32 (qkv32, [rows, 3h]) and a separate kernel with the same arithmetic.
+void qkv_project(const mt_model_cfg* cfg, const uint16_t* n16, const uint16_t* wqkv16, int64_t rows, int64_t t0, int S,
+                 const float* cs, const float* sn, uint16_t* qkv16, float* qkv32, hipStream_t s) {
+    const int64_t h = cfg->hidden;
+    GemmDesc d = gd(rows, 3 * h, h, n16, h, true, wqkv16, 3 * h, false, 3 * h);
+    d.f16 = true;
+    if (gemm_epi_ok(rows, 3 * h, h, h, 3 * h)) {
+        d.epi = 1;
+        d.Cb = qkv16 + t0 * 3 * h;
+        d.rope_cos = cs;
+        d.rope_sin = sn;
+        d.rope_S = S;
+        d.rope_hd = cfg->head_dim;
+        d.rope_t0 = t0;
+        d.rope_cols = 2 * h;
+        gemm(d, s);
+    } else {
+        d.Cf = qkv32;
+        gemm(d, s);
+        qkv_finish(qkv32, nullptr, qkv16, cs, sn, t0, rows, S, cfg->heads, cfg->head_dim, true, s);
+    }
+}
+
+// Gate/up projection and SwiGLU of rows tokens from their fp16 RMSNorm output:
+// gu = gate | up (bf16 [rows, 2f]), a = silu(gate) * up (bf16) and a16 (fp16)
+// [rows, f], each skipped when NULL.  wgu16 is the fp16 weight transposed to
+// [h, 2f] with gate and up of every feature interleaved; shapes that the fused
+// epilogue does not take go through fp32 (gu32, [rows, 2f]).
+void gate_up_project(const mt_model_cfg* cfg, const uint16_t* n16, const uint16_t* wgu16, int64_t rows, uint16_t* gu,
+                     uint16_t* a, uint16_t* a16, float* gu32, hipStream_t s) {
+    const int64_t h = cfg->hidden, f = cfg->ffn;
+    GemmDesc d = gd(rows, 2 * f, h, n16, h, true, wgu16, 2 * f, false, 2 * f);
+    d.f16 = true;
+    if (gemm_epi_ok(rows, 2 * f, h, h, 2 * f)) {
+        d.epi = 2;
+        d.Cb = gu;
+        d.Ca = a;
+        d.Ca16 = a16;
+        gemm(d, s);
+    } else {
+        d.Cf = gu32;
+        gemm(d, s);
+        swiglu_fwd32(gu32, gu, a, a16, rows, (int)f, true, s);
+    }
+}
+
 // Forward of one layer: x -> y, internals into sv.  The GEMM operands of the
 // forward are fp16 (the weights converted exactly and transposed to [in, out],
 // the activations rounded once from fp32: three more significand bits than
@@ -220,20 +272,16 @@ void layer_forward(const mt_layer_view* v, const mt_model_cfg* cfg, int B, int S
     uint16_t* wo = wqkv + 3 * h * h;
     uint16_t* wgu = wo + h * h;
     uint16_t* wd = wgu + 2 * f * h;
-    bf16_to_f16_t((const uint16_t*)v->w[1], wqkv, 3 * h, h, s);
-    bf16_to_f16_t((const uint16_t*)v->w[2], wo, h, h, s);
-    bf16_to_f16_t((const uint16_t*)v->w[4], wgu, 2 * f, h, s);
-    bf16_to_f16_t((const uint16_t*)v->w[5], wd, h, f, s);
+    bf16_to_f16_t((const uint16_t*)v->w[1], wqkv, 3 * h, h, 1, 2 * h, cfg->head_dim, s);
+    bf16_to_f16_t((const uint16_t*)v->w[2], wo, h, h, 0, 0, 0, s);
+    bf16_to_f16_t((const uint16_t*)v->w[4], wgu, 2 * f, h, 2, 0, 0, s);
+    bf16_to_f16_t((const uint16_t*)v->w[5], wd, h, f, 0, 0, 0, s);
 
     // attention RMSNorm, QKV projection, RoPE: per token chunk
     for (int64_t t0 = 0; t0 < T; t0 += Tc) {
         const int64_t rows = std::min(Tc, T - t0);
         rmsnorm_fwd2(x + t0 * h, g_attn, sv.n1 + t0 * h, fw.n16, sv.rstd1 + t0, rows, (int)h, cfg->eps, s);
-        GemmDesc d = gd(rows, 3 * h, h, fw.n16, h, true, wqkv, 3 * h, false, 3 * h);
-        d.f16 = true;
-        d.Cf = fw.qkv32;
-        gemm(d, s);
-        qkv_finish(fw.qkv32, nullptr, sv.qkv, cs, sn, t0, rows, S, cfg->heads, cfg->head_dim, s);
+        qkv_project(cfg, fw.n16, wqkv, rows, t0, S, cs, sn, sv.qkv, fw.qkv32, s);
     }
     attention_fwd_ex(sv.qkv, true, sv.o, fw.o16, sv.lse, B, S, cfg->heads, cfg->head_dim, s);
     // output projection + residual, MLP RMSNorm, gate/up, SwiGLU, down + residual: per token chunk
@@ -246,12 +294,8 @@ void layer_forward(const mt_layer_view* v, const mt_model_cfg* cfg, int B, int S
         gemm(d, s);
         rmsnorm_fwd2(sv.xm + t0 * h, g_mlp, sv.n2 ? sv.n2 + t0 * h : nullptr, fw.n16, sv.rstd2 + t0, rows, (int)h,
                      cfg->eps, s);
-        d = gd(rows, 2 * f, h, fw.n16, h, true, wgu, 2 * f, false, 2 * f);
-        d.f16 = true;
-        d.Cf = fw.gu32;
-        d.Cb = sv.gu ? sv.gu + t0 * 2 * f : nullptr;
-        gemm(d, s);
-        swiglu_fwd32(fw.gu32, sv.a ? sv.a + t0 * f : nullptr, fw.a16, rows, (int)f, s);
+        gate_up_project(cfg, fw.n16, wgu, rows, sv.gu ? sv.gu + t0 * 2 * f : nullptr, sv.a ? sv.a + t0 * f : nullptr,
+                        fw.a16, fw.gu32, s);
         d = gd(rows, h, f, fw.a16, f, true, wd, h, false, h);
         d.f16 = true;
         d.R = sv.xm + t0 * h;
@@ -300,17 +344,12 @@ void layer_backward(const mt_layer_view* v, const mt_model_cfg* cfg, const mt_ac
         // them, then its backward; the weight gradients are summed over the
         // chunks in order in fp32 and rounded once.
         const int64_t Tc = fwd_chunk(T);
-        bf16_to_f16_t(wgu, w.mc_wgu, 2 * f, h, s);
+        bf16_to_f16_t(wgu, w.mc_wgu, 2 * f, h, 2, 0, 0, s);
         for (int64_t t0 = 0; t0 < T; t0 += Tc) {
             const int64_t rows = std::min(Tc, T - t0);
             const int acc = t0 > 0;
             rmsnorm_fwd2(sv.xm + t0 * h, g_mlp, w.mc_n2, w.mc_n16, w.mc_rstd, rows, (int)h, cfg->eps, s);
-            d = gd(rows, 2 * f, h, w.mc_n16, h, true, w.mc_wgu, 2 * f, false, 2 * f);
-            d.f16 = true;
-            d.Cf = w.mc_gu32;
-            d.Cb = w.mc_gu;
-            gemm(d, s);
-            swiglu_fwd32(w.mc_gu32, w.mc_a, nullptr, rows, (int)f, s);
+            gate_up_project(cfg, w.mc_n16, w.mc_wgu, rows, w.mc_gu, w.mc_a, nullptr, w.mc_gu32, s);
             // down projection
             d = gd(h, f, rows, dyb + t0 * h, h, false, w.mc_a, f, false, f);
             d.Cf = w.mc_dwd;
