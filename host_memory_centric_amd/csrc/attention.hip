@@ -513,65 +513,83 @@ __global__ __launch_bounds__(ATT_PP_THREADS) __attribute__((amdgpu_waves_per_eu(
 // ---------------------------------------------------------------------------
 // backward: D = rowsum(dO * O)
 // ---------------------------------------------------------------------------
+// Backward pre-passes: LG = HD / 8 lanes per (token, head) row, each lane 8
+// features (16 bytes of every operand), so one load instruction of a wave
+// reads 64 / LG whole rows; the row's sums and maxima are combined over its
+// lanes with shuffles.
+template <int LG>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+    for (int o = LG / 2; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+template <int LG>
+__device__ __forceinline__ float group_max(float v) {
+#pragma unroll
+    for (int o = LG / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+    return v;
+}
+
+// D = rowsum(dO * O) per (token, head), stored [batch, head, seq].
 template <int HD>
 __global__ __launch_bounds__(256) void attn_bwd_pre_kernel(const uint16_t* __restrict__ o, const uint16_t* __restrict__ dout,
                                     float* __restrict__ dvec, int64_t T, int S, int heads) {
-    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (idx >= T * heads) return;
+    constexpr int LG = HD / 8;
+    const int64_t idx = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / LG;
+    const int sub = threadIdx.x % LG;
+    if (idx >= T * heads) return;  // whole groups
     const int64_t t = idx / heads;
     const int head = (int)(idx % heads);
-    const int64_t H = (int64_t)heads * HD;
-    const uint16_t* a = o + t * H + (int64_t)head * HD;
-    const uint16_t* c = dout + t * H + (int64_t)head * HD;
+    const int64_t off = t * (int64_t)heads * HD + (int64_t)head * HD + 8 * sub;
+    const uint4 x = *(const uint4*)(o + off), y = *(const uint4*)(dout + off);
+    const uint32_t xw[4] = {x.x, x.y, x.z, x.w}, yw[4] = {y.x, y.y, y.z, y.w};
     float s = 0.f;
 #pragma unroll
-    for (int i = 0; i < HD; i += 8) {
-        const uint4 x = *(const uint4*)(a + i), y = *(const uint4*)(c + i);
-        const uint32_t xw[4] = {x.x, x.y, x.z, x.w}, yw[4] = {y.x, y.y, y.z, y.w};
-#pragma unroll
-        for (int q = 0; q < 4; ++q) s += bf_lo(xw[q]) * bf_lo(yw[q]) + bf_hi(xw[q]) * bf_hi(yw[q]);
-    }
-    const int64_t b = t / S, sidx = t % S;
-    dvec[(b * heads + head) * S + sidx] = s;
+    for (int q = 0; q < 4; ++q) s += bf_lo(xw[q]) * bf_lo(yw[q]) + bf_hi(xw[q]) * bf_hi(yw[q]);
+    s = group_sum<LG>(s);
+    if (sub == 0) dvec[((t / S) * heads + head) * S + t % S] = s;
 }
 
-// fp16 backward, first pass, one thread per (token, head): D = rowsum(dO * O)
-// and the row statistics that bound the scaled operands: |dO_row|_1,
-// max |dO_row|, max |v_row| (v: the saved fp16 projection).
+// fp16 backward, first pass, per (token, head): D = rowsum(dO * O) and the
+// row statistics that bound the scaled operands: |dO_row|_1, max |dO_row|,
+// max |v_row| (v: the saved fp16 projection).
 template <int HD>
 __global__ __launch_bounds__(256) void attn_bwd_stats_kernel(const uint16_t* __restrict__ qkv16,
                                                              const uint16_t* __restrict__ o,
                                                              const uint16_t* __restrict__ dout,
                                                              float* __restrict__ stats, int64_t T, int S, int heads) {
-    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (idx >= T * heads) return;
+    constexpr int LG = HD / 8;
+    const int64_t idx = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / LG;
+    const int sub = threadIdx.x % LG;
+    if (idx >= T * heads) return;  // whole groups
     const int64_t t = idx / heads;
     const int head = (int)(idx % heads);
     const int64_t H = (int64_t)heads * HD;
-    const uint16_t* a = o + t * H + (int64_t)head * HD;
-    const uint16_t* c = dout + t * H + (int64_t)head * HD;
-    const uint16_t* vv = qkv16 + t * 3 * H + 2 * H + (int64_t)head * HD;
+    const int64_t off = t * H + (int64_t)head * HD + 8 * sub;
+    const uint4 x = *(const uint4*)(o + off), y = *(const uint4*)(dout + off);
+    const uint4 z = *(const uint4*)(qkv16 + t * 3 * H + 2 * H + (int64_t)head * HD + 8 * sub);
+    const uint32_t xw[4] = {x.x, x.y, x.z, x.w}, yw[4] = {y.x, y.y, y.z, y.w}, zw[4] = {z.x, z.y, z.z, z.w};
     float d = 0.f, l1 = 0.f, mdo = 0.f, mv = 0.f;
 #pragma unroll
-    for (int i = 0; i < HD; i += 8) {
-        const uint4 x = *(const uint4*)(a + i), y = *(const uint4*)(c + i), z = *(const uint4*)(vv + i);
-        const uint32_t xw[4] = {x.x, x.y, x.z, x.w}, yw[4] = {y.x, y.y, y.z, y.w}, zw[4] = {z.x, z.y, z.z, z.w};
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const float y0 = bf_lo(yw[q]), y1 = bf_hi(yw[q]);
-            d += bf_lo(xw[q]) * y0 + bf_hi(xw[q]) * y1;
-            l1 += fabsf(y0) + fabsf(y1);
-            mdo = fmaxf(mdo, fmaxf(fabsf(y0), fabsf(y1)));
-            mv = fmaxf(mv, fmaxf(fabsf(h2f((uint16_t)(zw[q] & 0xffff))), fabsf(h2f((uint16_t)(zw[q] >> 16)))));
-        }
+    for (int q = 0; q < 4; ++q) {
+        const float y0 = bf_lo(yw[q]), y1 = bf_hi(yw[q]);
+        d += bf_lo(xw[q]) * y0 + bf_hi(xw[q]) * y1;
+        l1 += fabsf(y0) + fabsf(y1);
+        mdo = fmaxf(mdo, fmaxf(fabsf(y0), fabsf(y1)));
+        mv = fmaxf(mv, fmaxf(fabsf(h2f((uint16_t)(zw[q] & 0xffff))), fabsf(h2f((uint16_t)(zw[q] >> 16)))));
     }
-    const int64_t b = t / S, sidx = t % S;
-    const int64_t r = (b * heads + head) * S + sidx;
-    const int64_t n = T * heads;
-    stats[r] = d;
-    stats[n + r] = l1;
-    stats[2 * n + r] = mdo;
-    stats[3 * n + r] = mv;
+    d = group_sum<LG>(d);
+    l1 = group_sum<LG>(l1);
+    mdo = group_max<LG>(mdo);
+    mv = group_max<LG>(mv);
+    if (sub == 0) {
+        const int64_t r = ((t / S) * heads + head) * S + t % S;
+        const int64_t n = T * heads;
+        stats[r] = d;
+        stats[n + r] = l1;
+        stats[2 * n + r] = mdo;
+        stats[3 * n + r] = mv;
+    }
 }
 
 // 2^k with k an integer such that x * 2^k lies in [2^top, 2^(top+1)); 1 for x == 0.
@@ -989,8 +1007,8 @@ void attention_bwd(const uint16_t* qkv, const uint16_t* o, const float* lse, con
     // kernels execute 16*hd: Q K^T three times and dO V^T twice)
     ProfScope prof(PROF_ATTN_BWD, 10.0 * hd * (double)B * heads * ((double)S * (S + 1) / 2), s);
     if (hd == 128) {
-        hipLaunchKernelGGL(attn_bwd_pre_kernel<128>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, o, dout, dvec,
-                           T, S, heads);
+        hipLaunchKernelGGL(attn_bwd_pre_kernel<128>, dim3((unsigned)((n * 16 + 255) / 256)), dim3(256), 0, s, o, dout,
+                           dvec, T, S, heads);
         hipLaunchKernelGGL((attn_bwd_kv_kernel<128, false>), gk, dim3(ATT_THREADS), 0, s, qkv, lse, dout, dvec, nullptr,
                            dqkv, S, heads, sl2, scale);
         hipLaunchKernelGGL((attn_bwd_kv_kernel<128, true>), gk, dim3(ATT_THREADS), 0, s, qkv, lse, dout, dvec, nullptr,
@@ -998,8 +1016,8 @@ void attention_bwd(const uint16_t* qkv, const uint16_t* o, const float* lse, con
         hipLaunchKernelGGL(attn_bwd_dq_kernel<128>, gq, dim3(ATT_THREADS), 0, s, qkv, lse, dout, dvec, nullptr, dqkv, S,
                            heads, sl2, scale);
     } else {
-        hipLaunchKernelGGL(attn_bwd_pre_kernel<64>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, o, dout, dvec, T,
-                           S, heads);
+        hipLaunchKernelGGL(attn_bwd_pre_kernel<64>, dim3((unsigned)((n * 8 + 255) / 256)), dim3(256), 0, s, o, dout, dvec,
+                           T, S, heads);
         hipLaunchKernelGGL((attn_bwd_kv_kernel<64, false>), gk, dim3(ATT_THREADS), 0, s, qkv, lse, dout, dvec, nullptr,
                            dqkv, S, heads, sl2, scale);
         hipLaunchKernelGGL((attn_bwd_kv_kernel<64, true>), gk, dim3(ATT_THREADS), 0, s, qkv, lse, dout, dvec, nullptr,
@@ -1018,8 +1036,8 @@ static void launch_attn_bwd16(const uint16_t* qkv16, const uint16_t* o, const fl
     float* sc = (float*)(ws + round_up(4 * (size_t)n * 4, 256));
     uint16_t* do16 = (uint16_t*)((char*)sc + round_up((size_t)B * heads * 16, 256));
     const dim3 gq((S + ATT_BQ - 1) / ATT_BQ, B * heads), gk((S + ATT_BK - 1) / ATT_BK, B * heads);
-    hipLaunchKernelGGL(attn_bwd_stats_kernel<HD>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, qkv16, o, dout,
-                       stats, T, S, heads);
+    hipLaunchKernelGGL(attn_bwd_stats_kernel<HD>, dim3((unsigned)((n * (HD / 8) + 255) / 256)), dim3(256), 0, s, qkv16,
+                       o, dout, stats, T, S, heads);
     hipLaunchKernelGGL(attn_bwd_scale_kernel, dim3((unsigned)(B * heads)), dim3(256), 0, s, stats, sc, n, S);
     const int64_t n8 = n * HD / 8;
     hipLaunchKernelGGL(attn_bwd_do16_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s, dout, sc, do16, T, S,

@@ -42,19 +42,39 @@
 namespace mt {
 
 // Sum split-K partials in slice order: out = sum_s part[s] (+R), then the
-// same output semantics as the GEMM epilogue.
+// same output semantics as the GEMM epilogue; 4 consecutive outputs of a row
+// per thread (N is a multiple of 8).
 __global__ void splitk_reduce_kernel(const float* part, int splits, int64_t M, int64_t N, float* Cf,
                                      uint16_t* Cb, const uint16_t* R, int64_t ldc, int accumulate) {
-    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t idx = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
     const int64_t total = M * N;
     if (idx >= total) return;
     const int64_t m = idx / N, n = idx % N;
-    float v = 0.f;
-    for (int s = 0; s < splits; ++s) v += part[(int64_t)s * total + idx];
+    float4 v = *(const float4*)(part + idx);
+    for (int s = 1; s < splits; ++s) {
+        const float4 w = *(const float4*)(part + (int64_t)s * total + idx);
+        v.x += w.x;
+        v.y += w.y;
+        v.z += w.z;
+        v.w += w.w;
+    }
     const int64_t o = m * ldc + n;
-    if (R) v += bf2f(R[o]);
-    if (Cf) Cf[o] = accumulate ? Cf[o] + v : v;
-    if (Cb) Cb[o] = f2bf(v);
+    if (R) {
+        const uint2 r = *(const uint2*)(R + o);
+        v.x += bf_lo(r.x);
+        v.y += bf_hi(r.x);
+        v.z += bf_lo(r.y);
+        v.w += bf_hi(r.y);
+    }
+    if (Cf) {
+        if (accumulate) {
+            const float4 c = *(const float4*)(Cf + o);
+            *(float4*)(Cf + o) = make_float4(c.x + v.x, c.y + v.y, c.z + v.z, c.w + v.w);
+        } else {
+            *(float4*)(Cf + o) = v;
+        }
+    }
+    if (Cb) *(uint2*)(Cb + o) = make_uint2(pack_bf2(v.x, v.y), pack_bf2(v.z, v.w));
 }
 
 static GemmArgs make_args(const GemmDesc& d, float* part, int splits, int64_t kps, int bm, int bn) {
@@ -232,7 +252,7 @@ void gemm(const GemmDesc& d, hipStream_t s) {
         launch_tiles<128, 128, 2, 2>(d, s, part, splits, kps);
     if (splits > 1) {
         const int64_t total = d.M * d.N;
-        hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, part,
+        hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((total / 4 + 255) / 256)), dim3(256), 0, s, part,
                            splits, d.M, d.N, d.Cf, (uint16_t*)d.Cb, (const uint16_t*)d.R, d.ldc, d.accumulate);
     }
     launch_check("gemm");
