@@ -29,6 +29,16 @@
 // holds row 8(e/4) + 4h + e%4 of a 16-row step, so the transposing reads fetch
 // rows 4h..4h+3 and 8+4h..8+4h+3.
 //
+// Every kernel has a bf16 and an fp16 instantiation (F16: v_mfma_f32_32x32x16_f16,
+// same rate).  The layer runs the fp16 ones on the forward's fp16 q, k, v, so
+// that the backward recomputes exactly the forward's scores: the forward's
+// probabilities enter P V as fp16 scaled by 2^14 (the running maximum offset
+// by 14 in the exponent, the log-sum-exp corrected back), and the backward
+// takes dO and dS as fp16 under per-(batch, head) powers of two chosen from
+// bounds of their magnitudes, folded exactly into the exponent of P and
+// divided out in fp32 at the end.  The bf16 instantiations serve the
+// mt_op_attention_* entry points.
+//
 // Layout: qkv is the fused projection output [B*S, 3*H] (q | k | v, head h at
 // columns h*hd .. h*hd + hd - 1 of each third), o is [B*S, H], lse is
 // [B, heads, S] natural-log row logsumexp of the scaled scores.
