@@ -329,10 +329,13 @@ int mt_layer_workspace_bytes(const mt_model_cfg* cfg, int32_t batch, int32_t seq
 /* Layer forward (paper page, section 3, execution workflow: bind streamed
  * weights to a template and compute): RMSNorm, QKV GEMM, RoPE, causal
  * attention, output projection + residual, RMSNorm, gate/up GEMM, SwiGLU,
- * down projection + residual.  x_out = layer(x_in).  When io->saved is
- * non-NULL the internals needed by the backward are stored there; otherwise
- * the workspace holds them as scratch.  Needs x_in, x_out, rope tables,
- * workspace.  MT_E_SHAPE unless head_dim is 64 or 128. */
+ * down projection + residual.  x_out = layer(x_in).  The projections take
+ * fp16 operands (weights converted exactly, activations rounded once from
+ * fp32) and q, k, v and the attention probabilities are kept in fp16; x_out
+ * is bf16.  When io->saved is non-NULL the internals needed by the backward
+ * are stored there; otherwise the workspace holds them as scratch.  Needs
+ * x_in, x_out, rope tables, workspace.  MT_E_SHAPE unless head_dim is 64 or
+ * 128. */
 int mt_layer_fwd(const mt_layer_view* v, const mt_model_cfg* cfg, const mt_act* io, void* stream);
 
 /* Layer backward with recompute (paper page, section 3: block checkpoints,
