@@ -313,8 +313,13 @@ def main():
     ap.add_argument("--mode", default="streamed", choices=["streamed", "resident"])
     ap.add_argument("--slots", type=int, default=5)
     ap.add_argument("--grad-slabs", type=int, default=16)
-    ap.add_argument("--update-order", default="arrival", choices=["arrival", "urgent"],
-                    help="order of the host updates: as gradients arrive, or most urgent for the next step first")
+    ap.add_argument("--grad-slots", type=int, default=2, help="device gradient slots the backward writes in turn")
+    ap.add_argument("--update-order", default="arrival", choices=["arrival", "urgent", "tail"],
+                    help="order of the host updates: as gradients arrive, most urgent for the next step first, "
+                         "or as they arrive until the backward ends and most urgent first after it")
+    ap.add_argument("--carry", type=int, default=0,
+                    help="top layers that keep a device slot of their own across steps, refilled right after "
+                         "their host update (page-locked store only)")
     ap.add_argument("--pageable-store", dest="pinned_store", action="store_false",
                     help="keep the whole store pageable and stream through the packer and the gradient slabs; "
                          "default: the store's W and G regions page-locked, weights and gradients copied directly")
@@ -358,7 +363,8 @@ def main():
     _lib.call("mt_set_optimizer_threads", args.adam_threads)
     tr = Trainer(cfg, adam, mode=args.mode, n_slots=args.slots, n_grad_slabs=args.grad_slabs, device="cuda:0",
                  micro_batches=nmb, master=args.master, pinned_store=args.pinned_store,
-                 update_order=args.update_order, offload_ckpt=args.offload_ckpt)
+                 update_order=args.update_order, offload_ckpt=args.offload_ckpt, carry=args.carry,
+                 grad_slots=args.grad_slots)
 
     if args.progress:
         t_prog = time.perf_counter()
@@ -418,7 +424,8 @@ def main():
     n_loads = tr.n_weight_loads()  # per micro-batch pass
     # (block checkpoints held in host memory go out and come back once per pass)
     ck = nmb * tr.n_host * tr.ckpt_bytes
-    h2d = nmb * ((n_loads - 1) * lay.w_bytes + lay_h.w_bytes) + T * cfg.hidden * 2 + T * 4 + ck
+    h2d = (nmb * ((n_loads - 1) * lay.w_bytes + lay_h.w_bytes) + tr.n_carry_loads() * lay.w_bytes
+           + T * cfg.hidden * 2 + T * 4 + ck)
     d2h = nmb * (cfg.layers * lay.w_bytes + lay_h.w_bytes) + T * cfg.hidden * 4 + ck
     dom = max(prof.items(), key=lambda kv: kv[1][1]) if prof else None
     roof = None
@@ -446,10 +453,14 @@ def main():
                    (f", {nmb} micro-batches per optimizer step" if nmb > 1 else "") +
                    (", fp32 master weights" if args.master else "") +
                    (", host store W/G page-locked (direct copies, no packer)" if args.pinned_store else "") +
-                   (f", checkpoints of the first {tr.n_host} blocks in host memory" if tr.n_host else ""),
+                   (f", checkpoints of the first {tr.n_host} blocks in host memory" if tr.n_host else "") +
+                   (f", top {tr.carry} layers in device slots of their own, refilled after each update"
+                    if tr.carry else "") +
+                   (f", {args.update_order} update order" if args.update_order != "arrival" else ""),
                    "name": cfg.name, "global_batch": cfg.batch * nmb,
                    "seq_len": cfg.seq, "micro_batches": nmb, "master_fp32": bool(args.master),
-                   "mode": args.mode, "slots": tr.n_slots, "ckpt_every": tr.K,
+                   "mode": args.mode, "slots": tr.n_slots, "carried_layers": tr.carry,
+                   "grad_slots": tr.n_gslots, "ckpt_every": tr.K,
                    "host_store": "pinned_dma" if args.pinned_store else "pageable",
                    "update_order": args.update_order, "ckpt_host_blocks": tr.n_host,
                    "parallelism": "none (1 GPU)"},
@@ -459,7 +470,7 @@ def main():
         "mfma_probe_tflops": mfma_probe,
         "pct_probe_exec": round(100 * tflops_exec / mfma_probe, 2),
         "h2d_GBps": round(h2d * args.steps / dt / 1e9, 2), "d2h_GBps": round(d2h * args.steps / dt / 1e9, 2),
-        "weight_loads_per_step": n_loads * nmb, "dev_peak_bytes": dev_peak,
+        "weight_loads_per_step": n_loads * nmb + tr.n_carry_loads(), "dev_peak_bytes": dev_peak,
         "host_store_bytes": int(tr.store.total_bytes()), "loss": round(loss, 5), "kernels": kernels,
         "roofline": roof,
         "overlap": overlap,

@@ -64,25 +64,32 @@ class UpdateScheduler:
 
     Each job carries an event (its gradient copy) and a priority; among the
     jobs whose copy has completed, the thread runs the one with the lowest
-    (priority, submission order).  With equal priorities this is arrival
-    order.  With the order in which the next step's forward needs the units
-    (embedding, then layers bottom-up, then the head) it is most urgent
-    first: the backward produces gradients top-down while the next forward
-    consumes weights bottom-up, so the updates of some upper layers wait and
-    overlap the next step's forward instead of delaying its first layers."""
+    (priority, submission order) when picking by priority, else the first
+    submitted.  With the order in which the next step's forward needs the
+    units (embedding, then layers bottom-up, then the head) this is most
+    urgent first: the backward produces gradients top-down while the next
+    forward consumes weights bottom-up, so the updates of some upper layers
+    wait and overlap the next step's forward instead of delaying its first
+    layers.
 
-    def __init__(self):
+    The events of the jobs are recorded on one in-order stream (the gradient
+    stream) in submission order, so they complete in that order: the thread
+    queries only the first job whose event it has not yet seen complete, and
+    when no job is ready it blocks on that event instead of polling."""
+
+    def __init__(self, by_priority=False):
         self._cv = threading.Condition()
-        self._jobs = []
+        self._jobs = []      # [priority, seq, event, future, fn, args, ready], in submission order
         self._seq = 0
         self._stop = False
+        self._by_priority = bool(by_priority)
         self._thread = threading.Thread(target=self._run, name="mt-adam", daemon=True)
         self._thread.start()
 
     def submit(self, priority, event, fn, *args):
         fut = Future()
         with self._cv:
-            self._jobs.append((priority, self._seq, event, fut, fn, args))
+            self._jobs.append([priority, self._seq, event, fut, fn, args, event is None])
             self._seq += 1
             self._cv.notify()
         return fut
@@ -90,22 +97,41 @@ class UpdateScheduler:
     def _run(self):
         while True:
             with self._cv:
-                while True:
-                    if self._stop and not self._jobs:
-                        return
-                    ready = [j for j in self._jobs if j[2] is None or j[2].query()]
-                    if ready:
-                        job = min(ready, key=lambda j: (j[0], j[1]))
-                        self._jobs.remove(job)
-                        break
-                    self._cv.wait(timeout=2e-4 if self._jobs else None)
-            _, _, _, fut, fn, args = job
+                while not self._jobs and not self._stop:
+                    self._cv.wait()
+                if not self._jobs:
+                    return
+                # readiness in submission order: every job before the first
+                # not-ready one is ready
+                first = next((j for j in self._jobs if not j[6]), None)
+            if first is not None and first[2].query():
+                first[6] = True
+                continue
+            with self._cv:
+                ready = [j for j in self._jobs if j[6]]
+                if ready:
+                    job = min(ready, key=lambda j: (j[0] if self._by_priority else 0, j[1]))
+                    self._jobs.remove(job)
+                else:
+                    job = None
+            if job is None:
+                first[2].synchronize()  # nothing to run before this copy completes
+                first[6] = True
+                continue
+            _, _, _, fut, fn, args, _ = job
             if not fut.set_running_or_notify_cancel():
                 continue
             try:
                 fut.set_result(fn(*args))
             except BaseException as e:  # propagated to whoever waits on the future
                 fut.set_exception(e)
+
+    def set_by_priority(self, on):
+        """Pick ready jobs by (priority, submission order) from now on, or by
+        submission order alone."""
+        with self._cv:
+            self._by_priority = bool(on)
+            self._cv.notify()
 
     def shutdown(self):
         with self._cv:
@@ -154,18 +180,30 @@ def plan_step(L, K, resident):
     return ops
 
 
-def plan_slots(units, n_slots):
+def plan_slots(units, n_slots, fixed=None, preloaded=()):
     """Assign a device slot to every use; returns (slot per use, load flag per use).
 
     A use of a unit already resident is a hit.  Otherwise the load may not go
     into the slot of the op just before it (that copy would have to wait for
     that op, so nothing would overlap); among the other slots an empty one is
     taken, else the one whose unit is next needed furthest in the future
-    (ties: the least recently used)."""
+    (ties: the least recently used).
+
+    fixed: {unit: slot} for units that own a slot of their own (numbered from
+    n_slots on, outside the shared pool): every use of such a unit is in its
+    slot, and only its first use loads, unless the unit is in ``preloaded``
+    (its slot already holds its weights when the step starts)."""
+    fixed = fixed or {}
     content = [None] * n_slots
     last_used = [-1] * n_slots
     slot_of, load = [], []
+    seen_fixed = set(preloaded)
     for i, u in enumerate(units):
+        if u in fixed:
+            slot_of.append(fixed[u])
+            load.append(u not in seen_fixed)
+            seen_fixed.add(u)
+            continue
         if u in content:
             s = content.index(u)
             slot_of.append(s)
@@ -205,11 +243,13 @@ class Trainer:
     gradients the host accumulates (``mt_grad_accumulate``) before one Adam
     step on their mean; master: keep fp32 master weights in the host store;
     update_order: 'arrival' (host updates in the order their gradients
-    arrive) or 'urgent' (most urgent first, see ``UpdateScheduler``).  With
-    'urgent', updates deferred past the end of a step run during the next
-    step's forward; on some machines every gradient copy of that step's
-    backward then ran 4x slower (30.8 instead of 7.5 ms per layer at the 7B
-    shape, one step in two), which arrival order avoids;
+    arrive), 'urgent' (most urgent first, see ``UpdateScheduler``) or 'tail'
+    (arrival order while the backward runs, most urgent first once it has
+    issued its last gradient).  With 'urgent' or 'tail', updates deferred
+    past the end of a step run during the next step's forward; on some
+    machines every gradient copy of that step's backward then ran 4x slower
+    (30.8 instead of 7.5 ms per layer at the 7B shape, one step in two),
+    which arrival order avoids;
     pinned_store: page-lock the store's W and G regions and copy weights to
     the device straight from W and gradients straight into G (no packer
     copy, no gradient slabs; the packer thread only waits for each unit's
@@ -227,6 +267,21 @@ class Trainer:
     device.  Long contexts at full depth need it: a 7B-shaped block input is
     4.3 GB at 512K tokens.  Results are bit-identical to keeping them all on
     the device;
+    grad_slots: device gradient slots the backward writes in turn (a layer's
+    backward waits until the copy out of its slot's previous gradient is
+    done; more slots let the evacuation lag further behind);
+    carry: the top ``carry`` layers each own a device slot of their own (outside
+    the ``n_slots`` pool) that holds their weights from one step to the next
+    (page-locked store only).  Right after the host update of such a layer
+    (whose gradient is among the first of the backward) the optimizer thread
+    enqueues the copy of its new weights into its slot, behind the weight
+    stream's pending loads and after the layer's backward has read the old
+    ones; the next step's forward, recompute and backward of the layer then
+    use the slot without a load.  Each such layer is loaded once per step
+    instead of once per forward and once per recompute, and its load moves
+    out of the link-bound forward into the backward and the update tail.  The
+    device footprint grows by ``carry`` layer slots, a fixed count
+    independent of depth.  Results are bit-identical to ``carry=0``;
     poison (debug): fill every buffer with NaN as soon as the event that
     frees it fires -- a device weight slot after the op that last reads it
     before a reload, a device gradient slot after the copy that evacuates
@@ -238,9 +293,17 @@ class Trainer:
 
     def __init__(self, cfg, adam, mode="streamed", n_slots=2, n_grad_slabs=16, ckpt_every=None, weights=None,
                  device="cuda:0", capture_w32=False, timeline=False, micro_batches=1, master=False,
-                 pinned_store=False, update_order="arrival", offload_ckpt=0, poison=False, delay_seed=None):
-        if update_order not in ("arrival", "urgent"):
-            raise ValueError("update_order must be 'arrival' or 'urgent'")
+                 pinned_store=False, update_order="arrival", offload_ckpt=0, poison=False, delay_seed=None,
+                 carry=0, grad_slots=2):
+        if update_order not in ("arrival", "urgent", "tail"):
+            raise ValueError("update_order must be 'arrival', 'urgent' or 'tail'")
+        self.carry = int(carry)
+        self.n_gslots = int(grad_slots)
+        if self.n_gslots < 1:
+            raise ValueError("grad_slots must be at least 1")
+        if self.carry and (mode == "resident" or not pinned_store or not 0 < self.carry <= cfg.layers):
+            raise ValueError(f"carry must be 0, or with a streamed step and a page-locked store between 1 and "
+                             f"the layer count ({cfg.layers})")
         self.update_order = update_order
         self.poison = bool(poison)
         self._delay_rng = None if delay_seed is None else np.random.default_rng(delay_seed)
@@ -285,12 +348,22 @@ class Trainer:
         self.ops = plan_step(self.L, self.K, mode == "resident")
         units = [MT_UNIT_HEAD if k == "head" else l for (k, l, _) in self.ops]
         self.op_unit = units
-        self.op_slot, self.op_load = plan_slots(units, self.n_slots)
+        # the carried layers' own slots follow the pool's; the plan of a pass
+        # whose carried slots already hold the current weights (every pass
+        # but the first) has no load for them
+        self.carry_slot = {l: self.n_slots + i for i, l in enumerate(range(self.L - self.carry, self.L))}
+        self._plans = {warm: plan_slots(units, self.n_slots, self.carry_slot,
+                                        set(self.carry_slot) if warm else ())
+                       for warm in (False, True)}
+        self.op_slot, self.op_load = self._plans[True]
+        self._carried = False  # the carried slots hold the store's current weights
+        self._carry_ev = {}    # carried layer -> event: its last copy into its slot is done
 
         d, T = self.dev, self.T
         bf, f32 = torch.bfloat16, torch.float32
-        self.slots = [torch.empty(self.slot_bytes, dtype=torch.uint8, device=d) for _ in range(self.n_slots)]
-        self.gslots = [torch.empty(self.lay.w_bytes, dtype=torch.uint8, device=d) for _ in range(2)]
+        self.slots = [torch.empty(self.slot_bytes, dtype=torch.uint8, device=d)
+                      for _ in range(self.n_slots + self.carry)]
+        self.gslots = [torch.empty(self.lay.w_bytes, dtype=torch.uint8, device=d) for _ in range(self.n_gslots)]
         self.head_g = torch.empty(self.lay_head_dev.w_bytes, dtype=torch.uint8, device=d)
         n_ring = self.n_host + 2 if self.n_host else 0  # blocks below n_ring use the two ring buffers
         self.n_ring = n_ring
@@ -342,13 +415,18 @@ class Trainer:
         self.s_h2d = torch.cuda.Stream(device=d)
         self.s_d2h = torch.cuda.Stream(device=d)
         self.packer = ThreadPoolExecutor(1, thread_name_prefix="mt-pack")
-        self.optimizer = UpdateScheduler()
+        # copy issuers: a weight load is enqueued once its slot's last reader
+        # has completed, a gradient copy once its backward has completed, so
+        # that no copy command waits for compute work inside a DMA queue
+        self.h2d_issuer = ThreadPoolExecutor(1, thread_name_prefix="mt-h2d")
+        self.d2h_issuer = ThreadPoolExecutor(1, thread_name_prefix="mt-d2h")
+        self.optimizer = UpdateScheduler(by_priority=update_order == "urgent")
         self.slab_free = queue.Queue()
         for k in range(len(self.gslab)):
             self.slab_free.put(k)
         self.pending = {}              # unit -> future of its host update still running
         self.accum_jobs = {}           # unit -> future of its last micro-batch accumulation
-        self.gslot_d2h = [None, None]  # last copy out of each device gradient slot
+        self.gslot_d2h = [None] * self.n_gslots  # last copy out of each device gradient slot
         self.head_d2h = None           # last copy out of the head's gradient buffer
         self.record_timeline = timeline
         self.progress = None  # optional callable(kind, layer), called as each op is enqueued
@@ -404,6 +482,16 @@ class Trainer:
         store options and batch shape."""
         self.finish()
         self.t = self.store.load(path)
+        self._carried = False  # the carried slots hold the weights before the load
+
+    def store_modified(self):
+        """Declare that the host store was written directly (weights or
+        moments set from elsewhere) after every pending update: the weights
+        the carried layers' slots hold are dropped and loaded again at their
+        next use."""
+        self.finish()
+        self.s_h2d.synchronize()  # no copy out of the store is still reading it
+        self._carried = False
 
     def _wait_unit(self, unit):
         f = self.pending.pop(unit, None)
@@ -421,6 +509,8 @@ class Trainer:
         finally:
             torch.cuda.synchronize(self.dev)
             self.packer.shutdown(wait=True)
+            self.h2d_issuer.shutdown(wait=True)
+            self.d2h_issuer.shutdown(wait=True)
             self.optimizer.shutdown()
             if self.ckpt_io is not None:
                 self.ckpt_io.shutdown(wait=True)
@@ -431,7 +521,13 @@ class Trainer:
         self.store.close()
 
     def n_weight_loads(self):
+        """Weight loads of one pass in the steady state (the carried layers'
+        copies after their updates are counted by n_carry_loads)."""
         return sum(self.op_load)
+
+    def n_carry_loads(self):
+        """Copies of carried layers into their own slots per optimizer step."""
+        return self.carry
 
     def _x(self, l):
         if l == self.L:
@@ -586,15 +682,18 @@ class Trainer:
         if nh:
             ckpt_out(0, inputs_ready)
 
-        # weight loads of this step, in order
-        loads = [i for i, ld in enumerate(self.op_load) if ld]
+        # weight loads of this step, in order (no loads for the carried layers
+        # once their slots hold the current weights)
+        warm = self._carried
+        op_slot, op_load = self._plans[warm]
+        loads = [i for i, ld in enumerate(op_load) if ld]
         load_of_op = {i: j for j, i in enumerate(loads)}
         ready_ev = [torch.cuda.Event(enable_timing=self.record_timeline) for _ in loads]
         op_done = [None] * len(self.ops)
         # previous op that used the same slot (the copy into the slot waits for it)
         slot_prev = [None] * len(self.ops)
         last = {}
-        for i, s in enumerate(self.op_slot):
+        for i, s in enumerate(op_slot):
             slot_prev[i] = last.get(s)
             last[s] = i
 
@@ -624,19 +723,22 @@ class Trainer:
                 call("mt_pack_layer", self.store.ptr, unit, self.wslab[j % 2].ptr, self.slot_bytes)
 
         pack_fut = {j: self.packer.submit(pack, j) for j in range(min(2, len(loads)))}
-        next_load = [0]
+        op_enq = [threading.Event() for _ in self.ops]  # op i enqueued, op_done[i] recorded
+        load_issued = [threading.Event() for _ in loads]
 
         def issue_load(j):
             i = loads[j]
             pack_fut.pop(j).result()
             unit = self.op_unit[i]
             nbytes = (self.lay_head_dev if unit == MT_UNIT_HEAD else self.lay).w_bytes
-            with torch.cuda.stream(hs):
-                if slot_prev[i] is not None:
-                    hs.wait_event(op_done[slot_prev[i]])  # buffer-free
+            pu = slot_prev[i]
+            if pu is not None:
+                op_enq[pu].wait()
+                op_done[pu].synchronize()  # buffer-free: the slot's last reader has completed
+            with torch.cuda.device(self.dev), torch.cuda.stream(hs):
                 if tl is not None:
                     tl["h2d"].append([self._ev(hs), ready_ev[j]])
-                dst = _ptr(self.slots[self.op_slot[i]])
+                dst = _ptr(self.slots[op_slot[i]])
                 if not self.direct:
                     call("mt_copy_h2d", dst, self.wslab[j % 2].ptr, nbytes, sh)
                 elif unit == MT_UNIT_HEAD and self.tied:  # [final gain | embedding matrix as the LM head]
@@ -651,30 +753,44 @@ class Trainer:
             if j + 2 < len(loads):
                 pack_fut[j + 2] = self.packer.submit(pack, j + 2)
 
-        def issue_ready_loads(upto):
-            # prefetch: issue the next loads whose slot is no longer needed by an
-            # op that is still to be enqueued, as long as their packing is done
-            while next_load[0] < len(loads):
-                j = next_load[0]
-                pu = slot_prev[loads[j]]
-                if pu is not None and pu > upto:
-                    break
-                if not pack_fut[j].done():
-                    break
+        def issue_loads():
+            # every load of the pass in order, each as soon as its packing (or
+            # the unit's update) is done and its slot is free
+            for j in range(len(loads)):
                 issue_load(j)
-                next_load[0] += 1
+                load_issued[j].set()
+
+        h2d_fut = self.h2d_issuer.submit(issue_loads) if loads else None
+
+        def wait_load(j):
+            while not load_issued[j].wait(0.05):
+                if h2d_fut.done():
+                    h2d_fut.result()  # the issuer failed: raise its error here
+                    raise RuntimeError("weight load issuer ended early")
+
+        d2h_futs = []
+
+        def wait_copy_out(entry):
+            # (future of the issuer job, event recorded after the copy)
+            if entry is None:
+                return None
+            entry[0].result()
+            return entry[1]
 
         slab_free = self.slab_free
         gslot_d2h = self.gslot_d2h
         cur = 0
         n_bwd = 0
 
-        def adam_layer(ev, unit, src):
-            # src: the pinned slab holding the gradient, or None: already in G
+        def adam_layer(ev, unit, src, after=None):
+            # src: the pinned slab holding the gradient, or None: already in G;
+            # after: a carried layer's backward (its slot's last reader)
             self._debug_delay()
             ev.synchronize()
             if final:
                 call("mt_step", self.store.ptr, unit, src, ctypes.byref(self.madam), t, self._w32_ptr(unit))
+                if after is not None:
+                    self._carry_copy(unit, after, tl)
             else:
                 call("mt_grad_accumulate", self.store.ptr, unit, src)
 
@@ -702,14 +818,20 @@ class Trainer:
 
         jobs = self.pending if final else self.accum_jobs
 
-        issue_ready_loads(-1)
         for i, (kind, l, si) in enumerate(self.ops):
-            if self.op_load[i]:
-                while next_load[0] <= load_of_op[i]:
-                    issue_load(next_load[0])
-                    next_load[0] += 1
+            if op_load[i]:
+                wait_load(load_of_op[i])
                 cs.wait_event(ready_ev[load_of_op[i]])
-            slot = self.op_slot[i]
+                if l in self.carry_slot and kind != "head":
+                    self._carry_ev[l] = ready_ev[load_of_op[i]]
+            elif warm and kind == "fwd" and l in self.carry_slot:
+                # the previous step's update of a carried layer enqueued the
+                # copy of its new weights into the layer's slot before it ended
+                self._wait_unit(l)
+                ev_c = self._carry_ev.get(l)
+                if ev_c is not None:
+                    cs.wait_event(ev_c)
+            slot = op_slot[i]
             if self.progress is not None:
                 self.progress(kind, l)
             # block checkpoints in host memory: the writer of a ring buffer waits for the copy
@@ -726,9 +848,10 @@ class Trainer:
                 if wb is not None and 2 <= wb < self.n_ring:
                     cs.wait_event(ck_d2h[wb - 2])
                 if kind == "head" and self.head_d2h is not None:
-                    cs.wait_event(self.head_d2h)  # previous step's copy out of the head gradient
-                if kind == "bwd" and gslot_d2h[n_bwd % 2] is not None:
-                    cs.wait_event(gslot_d2h[n_bwd % 2])  # buffer-free (gradient slot)
+                    cs.wait_event(wait_copy_out(self.head_d2h))  # previous step's copy out of the head gradient
+                if kind == "bwd" and gslot_d2h[n_bwd % self.n_gslots] is not None:
+                    # buffer-free (gradient slot)
+                    cs.wait_event(wait_copy_out(gslot_d2h[n_bwd % self.n_gslots]))
                 if tl is not None:
                     tl["ops"].append([kind, self._ev(cs), None])
                 if kind == "fwd":
@@ -755,89 +878,125 @@ class Trainer:
                     io.workspace_bytes = self.ws_bytes
                     call("mt_head_fwd_bwd", ctypes.byref(v), ctypes.byref(self.mcfg), ctypes.byref(io), sc)
                 else:  # bwd
-                    g = n_bwd % 2
+                    g = n_bwd % self.n_gslots
                     v = self._bind(slot, self.gslots[g], l)
                     a = self._act(self._x(l), None, self.saved[si], dy=self.dgrad[cur], dyb=self.dgrad_b[cur],
                                   dx=self.dgrad[1 - cur], dxb=self.dgrad_b[1 - cur])
                     call("mt_layer_recompute_bwd", ctypes.byref(v), ctypes.byref(self.mcfg), ctypes.byref(a), sc)
                     cur = 1 - cur
-                if i in poison_slot_after:
+                if i in poison_slot_after or (self.poison and final and kind == "bwd" and l in self.carry_slot):
                     self._poison_dev(self.slots[slot], self.lay_head_dev if kind == "head" else self.lay)
                 ev = torch.cuda.Event(enable_timing=self.record_timeline)
                 ev.record(cs)
                 op_done[i] = ev
                 if tl is not None:
                     tl["ops"][-1][2] = ev
+            op_enq[i].set()
             if wb is not None and wb < nh:
                 ckpt_out(wb, ev)
             if kind == "head":
-                self._wait_unit(MT_UNIT_HEAD)  # the previous update still reads the head's slab
-                self._wait_acc(MT_UNIT_HEAD)   # (or the previous micro-batch's accumulation)
                 d2h = torch.cuda.Event(enable_timing=self.record_timeline)
-                head_dst = self.head_gslab.ptr if self.head_gslab is not None else self.g_addr[MT_UNIT_HEAD]
-                with torch.cuda.stream(ds):
-                    ds.wait_event(ev)
-                    if tl is not None:
-                        tl["d2h"].append([self._ev(ds), d2h])
-                    call("mt_copy_d2h", head_dst, _ptr(self.head_g), self.lay_head_dev.w_bytes, sd)
-                    if self.poison:
-                        self._poison_dev(self.head_g, self.lay_head_dev)
-                    d2h.record(ds)
-                self.head_d2h = d2h
-                jobs[MT_UNIT_HEAD] = self.optimizer.submit(
-                    self._urgency(MT_UNIT_HEAD), d2h, adam_layer, d2h, MT_UNIT_HEAD,
-                    self.head_gslab.ptr if self.head_gslab is not None else None)
-            elif kind == "bwd":
-                g = n_bwd % 2
-                n_bwd += 1
-                self._wait_unit(l)  # (finished long ago: the previous step's update of this layer)
-                if self.direct:
-                    # G is the copy's destination: the previous micro-batch's
-                    # accumulation (long finished) must have read it
-                    self._wait_acc(l)
-                    k, g_dst = None, self.g_addr[l]
-                else:
-                    k = slab_free.get()
-                    g_dst = self.gslab[k].ptr
-                d2h = torch.cuda.Event(enable_timing=self.record_timeline)
-                with torch.cuda.stream(ds):
-                    ds.wait_event(ev)
-                    if tl is not None:
-                        tl["d2h"].append([self._ev(ds), d2h])
-                    call("mt_copy_d2h", g_dst, _ptr(self.gslots[g]), self.lay.w_bytes, sd)
-                    if self.poison:
-                        self._poison_dev(self.gslots[g], self.lay)
-                    d2h.record(ds)
-                    if l == 0:
-                        d2h_x = torch.cuda.Event(enable_timing=self.record_timeline)
+
+                def head_out(ev=ev, d2h=d2h):
+                    self._wait_unit(MT_UNIT_HEAD)  # the previous update still reads the head's slab
+                    self._wait_acc(MT_UNIT_HEAD)   # (or the previous micro-batch's accumulation)
+                    head_dst = self.head_gslab.ptr if self.head_gslab is not None else self.g_addr[MT_UNIT_HEAD]
+                    ev.synchronize()  # the head's gradient is complete
+                    with torch.cuda.device(self.dev), torch.cuda.stream(ds):
                         if tl is not None:
-                            tl["d2h"].append([self._ev(ds), d2h_x])
-                        call("mt_copy_d2h", self.dx0_pin.ptr, _ptr(self.dgrad[cur]), self.T * h * 4, sd)
-                        d2h_x.record(ds)
-                gslot_d2h[g] = d2h
-                if k is None:
-                    jobs[l] = self.optimizer.submit(self._urgency(l), d2h, adam_layer, d2h, l, None)
-                else:
-                    jobs[l] = self.optimizer.submit(self._urgency(l), d2h, adam_layer_slab, d2h, l, k)
-                if l == 0:
-                    jobs[MT_UNIT_EMBED] = self.optimizer.submit(self._urgency(MT_UNIT_EMBED), d2h_x, adam_embed, d2h_x)
-            issue_ready_loads(i)
+                            tl["d2h"].append([self._ev(ds), d2h])
+                        call("mt_copy_d2h", head_dst, _ptr(self.head_g), self.lay_head_dev.w_bytes, sd)
+                        if self.poison:
+                            self._poison_dev(self.head_g, self.lay_head_dev)
+                        d2h.record(ds)
+                    if self.update_order == "tail":
+                        self.optimizer.set_by_priority(False)
+                    jobs[MT_UNIT_HEAD] = self.optimizer.submit(
+                        self._urgency(MT_UNIT_HEAD), d2h, adam_layer, d2h, MT_UNIT_HEAD,
+                        self.head_gslab.ptr if self.head_gslab is not None else None)
+                f = self.d2h_issuer.submit(head_out)
+                d2h_futs.append(f)
+                self.head_d2h = (f, d2h)
+            elif kind == "bwd":
+                g = n_bwd % self.n_gslots
+                n_bwd += 1
+                d2h = torch.cuda.Event(enable_timing=self.record_timeline)
+
+                def grad_out(ev=ev, g=g, l=l, d2h=d2h, dx=self.dgrad[cur]):
+                    self._wait_unit(l)  # (finished long ago: the previous step's update of this layer)
+                    if self.direct:
+                        # G is the copy's destination: the previous micro-batch's
+                        # accumulation (long finished) must have read it
+                        self._wait_acc(l)
+                        k, g_dst = None, self.g_addr[l]
+                    else:
+                        k = slab_free.get()
+                        g_dst = self.gslab[k].ptr
+                    ev.synchronize()  # backward-done: the layer's gradient is complete
+                    with torch.cuda.device(self.dev), torch.cuda.stream(ds):
+                        if tl is not None:
+                            tl["d2h"].append([self._ev(ds), d2h])
+                        call("mt_copy_d2h", g_dst, _ptr(self.gslots[g]), self.lay.w_bytes, sd)
+                        if self.poison:
+                            self._poison_dev(self.gslots[g], self.lay)
+                        d2h.record(ds)
+                        if l == 0:
+                            d2h_x = torch.cuda.Event(enable_timing=self.record_timeline)
+                            if tl is not None:
+                                tl["d2h"].append([self._ev(ds), d2h_x])
+                            call("mt_copy_d2h", self.dx0_pin.ptr, _ptr(dx), self.T * h * 4, sd)
+                            d2h_x.record(ds)
+                    if k is None:
+                        after = ev if (final and l in self.carry_slot) else None
+                        jobs[l] = self.optimizer.submit(self._urgency(l), d2h, adam_layer, d2h, l, None, after)
+                    else:
+                        jobs[l] = self.optimizer.submit(self._urgency(l), d2h, adam_layer_slab, d2h, l, k)
+                    if l == 0:
+                        jobs[MT_UNIT_EMBED] = self.optimizer.submit(self._urgency(MT_UNIT_EMBED), d2h_x, adam_embed,
+                                                                    d2h_x)
+                        if self.update_order == "tail":
+                            self.optimizer.set_by_priority(True)
+                f = self.d2h_issuer.submit(grad_out)
+                d2h_futs.append(f)
+                gslot_d2h[g] = (f, d2h)
             if nh:
                 ckpt_in(i)
 
+        if h2d_fut is not None:
+            h2d_fut.result()
+        for f in d2h_futs:
+            f.result()
         for f in list(pack_fut.values()):
             f.result()
         for f in ck_out:
             if f is not None:
                 f.result()
         cs.synchronize()
+        self._carried = bool(self.carry)
         return float(self.loss_dev.item()), len(loads)
 
+    def _carry_copy(self, unit, after, tl):
+        """Enqueue the copy of a carried layer's updated weights from the store
+        into the layer's own slot, on the weight stream after ``after`` (the
+        layer's backward, the last reader of the old weights).  Runs on the
+        optimizer thread right after the layer's update; the next pass's first
+        use of the layer waits for this copy's event."""
+        hs = self.s_h2d
+        with torch.cuda.device(self.dev):
+            ev = torch.cuda.Event(enable_timing=self.record_timeline)
+            hs.wait_event(after)
+            t0 = self._ev(hs) if tl is not None else None
+            call("mt_copy_h2d", _ptr(self.slots[self.carry_slot[unit]]), self.w_addr[unit], self.lay.w_bytes,
+                 ctypes.c_void_p(hs.cuda_stream))
+            ev.record(hs)
+        if tl is not None:
+            tl["h2d"].append([t0, ev])
+        self._carry_ev[unit] = ev
+
     def _urgency(self, unit):
-        """Scheduling priority of a unit's update: 0 for all in arrival order,
-        else the order in which the next step needs its updated weights."""
-        if self.update_order == "arrival":
-            return 0
+        """Scheduling priority of a unit's update: the order in which the next
+        step needs its updated weights (used by 'urgent' always, by 'tail'
+        once the backward has issued its last gradient)."""
         if unit == MT_UNIT_EMBED:
             return -1
         if unit == MT_UNIT_HEAD:
@@ -859,10 +1018,12 @@ class Trainer:
     def timeline(self):
         """Intervals (ms from the step's start) of the last step recorded with
         timeline=True: {'ops': [(kind, start, end)], 'h2d': [(start, end)],
-        'd2h': [(start, end)]}.  Waits for the step's copies to finish."""
+        'd2h': [(start, end)]}.  Waits for the step's host updates (which
+        enqueue the carried layers' copies) and for its copies to finish."""
         tl = self._tl
         if tl is None:
             return None
+        self.finish()
         for _, _, e in tl["ops"]:
             e.synchronize()
         for _, e in tl["h2d"] + tl["d2h"]:

@@ -146,3 +146,4 @@ def sync_from_oracle(trainer, state, cfg):
                 p = (ms["embed"] if unit == MT_UNIT_EMBED else ms[name] if unit == MT_UNIT_HEAD
                      else ms["layers"][unit][name])
                 st.tensor(unit, name, REGION_P)[...] = p
+    trainer.store_modified()

@@ -50,16 +50,24 @@ def _run(cfg, bits, steps, **kw):
         tr.close()
 
 
-@pytest.mark.parametrize("variant", ["k1_2slot", "k2_1slot", "k2_3slot_1slab", "pinned_k1_2slot",
-                                     "micro_master_k1_2slot", "tied_k2_2slot"])
+VARIANTS = {"k1_2slot": dict(ckpt_every=1, n_slots=2),
+            "k2_1slot": dict(ckpt_every=2, n_slots=1),
+            "k2_3slot_1slab": dict(ckpt_every=2, n_slots=3, n_grad_slabs=1),
+            "pinned_k1_2slot": dict(ckpt_every=1, n_slots=2, pinned_store=True),
+            "micro_master_k1_2slot": dict(ckpt_every=1, n_slots=2, micro_batches=2, master=True),
+            "tied_k2_2slot": dict(ckpt_every=2, n_slots=2),
+            "pinned_carry3_k2_2slot": dict(ckpt_every=2, n_slots=2, pinned_store=True, carry=3),
+            "pinned_carry5_k1_1slot_tail": dict(ckpt_every=1, n_slots=1, pinned_store=True, carry=5,
+                                                update_order="tail"),
+            "pinned_carry2_micro_urgent": dict(ckpt_every=2, n_slots=2, pinned_store=True, carry=2,
+                                               micro_batches=2, update_order="urgent"),
+            "gslots3_k1_3slot_1slab": dict(ckpt_every=1, n_slots=3, n_grad_slabs=1, grad_slots=3)}
+
+
+@pytest.mark.parametrize("variant", list(VARIANTS))
 def test_poison_and_delays_change_no_bit(gpu, variant):
     import dataclasses
-    kw = {"k1_2slot": dict(ckpt_every=1, n_slots=2),
-          "k2_1slot": dict(ckpt_every=2, n_slots=1),
-          "k2_3slot_1slab": dict(ckpt_every=2, n_slots=3, n_grad_slabs=1),
-          "pinned_k1_2slot": dict(ckpt_every=1, n_slots=2, pinned_store=True),
-          "micro_master_k1_2slot": dict(ckpt_every=1, n_slots=2, micro_batches=2, master=True),
-          "tied_k2_2slot": dict(ckpt_every=2, n_slots=2)}[variant]
+    kw = VARIANTS[variant]
     cfg = synth.preset("tiny", layers=5, seq=100)
     if variant.startswith("tied"):
         cfg = dataclasses.replace(cfg, tied=True)
@@ -71,6 +79,23 @@ def test_poison_and_delays_change_no_bit(gpu, variant):
         assert losses == ref_losses, (variant, seed, losses, ref_losses)
         for key, a in ref.items():
             assert np.array_equal(regions[key], a), (variant, seed, key)
+
+
+def test_carried_layers_change_no_bit(gpu):
+    """Carried layers (slots of their own, refilled right after each update)
+    and the update order change no bit: losses and every host region over
+    three steps equal the plain streamed run's, also with micro-batches."""
+    cfg = synth.preset("tiny", layers=5, seq=100)
+    bits = synth.make_weights(cfg)
+    for micro in (1, 2):
+        base = dict(ckpt_every=2, n_slots=2, pinned_store=True, micro_batches=micro)
+        ref_losses, ref = _run(cfg, bits, 3, **base)
+        for extra in (dict(carry=1), dict(carry=3, update_order="tail"), dict(carry=5, n_slots=1),
+                      dict(carry=4, update_order="urgent"), dict(grad_slots=1), dict(grad_slots=3, carry=2)):
+            losses, regions = _run(cfg, bits, 3, **dict(base, **extra))
+            assert losses == ref_losses, (micro, extra)
+            for key, a in ref.items():
+                assert np.array_equal(regions[key], a), (micro, extra, key)
 
 
 def test_device_peak_independent_of_depth(gpu):

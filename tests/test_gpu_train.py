@@ -24,13 +24,14 @@ def _store_regions(tr):
     return {(u, r): tr.store.region(u, r).copy() for u in tr.store.units for r in regions}
 
 
-@pytest.mark.parametrize("mode,pinned", [("streamed", False), ("resident", False), ("streamed", True)])
-def test_tiny_steps_match_oracle(gpu, mode, pinned):
+@pytest.mark.parametrize("mode,pinned,carry", [("streamed", False, 0), ("resident", False, 0), ("streamed", True, 0),
+                                               ("streamed", True, 1)])
+def test_tiny_steps_match_oracle(gpu, mode, pinned, carry):
     cfg = synth.preset("tiny")
     bits = synth.make_weights(cfg)
     adam = synth.AdamCfg()
     st = oracle.HostState(bits)
-    tr = _trainer(cfg, bits, mode=mode, pinned_store=pinned)
+    tr = _trainer(cfg, bits, mode=mode, pinned_store=pinned, carry=carry)
     try:
         for step in range(2):
             tok = synth.make_tokens(cfg, step)
@@ -52,7 +53,11 @@ def test_streamed_equals_resident_bitwise(gpu):
     for name, kw in {"resident": dict(mode="resident"), "k1_2slot": dict(ckpt_every=1, n_slots=2),
                      "k2_2slot": dict(ckpt_every=2, n_slots=2), "k1_3slot": dict(ckpt_every=1, n_slots=3),
                      "k1_1slab": dict(ckpt_every=1, n_grad_slabs=1), "k1_1slot": dict(ckpt_every=1, n_slots=1),
-                     "k2_2slot_urgent": dict(ckpt_every=2, n_slots=2, update_order="urgent")}.items():
+                     "k2_2slot_urgent": dict(ckpt_every=2, n_slots=2, update_order="urgent"),
+                     "k2_2slot_tail": dict(ckpt_every=2, n_slots=2, update_order="tail"),
+                     "k1_2slot_pinned_carry1": dict(ckpt_every=1, n_slots=2, pinned_store=True, carry=1),
+                     "k2_1slot_pinned_carry2_tail": dict(ckpt_every=2, n_slots=1, pinned_store=True, carry=2,
+                                                         update_order="tail")}.items():
         tr = _trainer(cfg, bits, **kw)
         try:
             losses = [tr.step(synth.make_tokens(cfg, s)) for s in range(3)]
@@ -384,6 +389,62 @@ def test_tied_embeddings_match_oracle_and_schedules_agree(gpu):
     assert runs["resident"][0] == runs["k1_2slot"][0]
     for key, a in runs["resident"][1].items():
         assert np.array_equal(runs["k1_2slot"][1][key], a), key
+
+
+def test_carried_slots_across_resume_and_store_writes(gpu, tmp_path):
+    """Carried layers keep device copies of their weights across steps; a
+    checkpoint load or a direct write of the store must drop them.  A run
+    with carried layers that is saved after one step and resumed in a
+    trainer whose carried slots already hold other weights (it ran a step of
+    its own) equals the uninterrupted run without carried layers, losses and
+    every store region bit for bit; so does a run whose store is overwritten
+    with the same run's state between steps."""
+    cfg = synth.preset("tiny", layers=5)
+    bits = synth.make_weights(cfg)
+    kw = dict(ckpt_every=2, n_slots=2, pinned_store=True)
+    ref = _trainer(cfg, bits, **kw)
+    try:
+        lref = [ref.step(synth.make_tokens(cfg, s)) for s in range(3)]
+        rref = _store_regions(ref)
+    finally:
+        ref.close()
+    path = tmp_path / "carry.ckpt"
+    b = _trainer(cfg, bits, carry=3, **kw)
+    try:
+        lb = [b.step(synth.make_tokens(cfg, 0))]
+        b.save(path)
+        mid = _store_regions(b)
+    finally:
+        b.close()
+    c = _trainer(cfg, bits, carry=3, **kw)
+    try:
+        c.step(synth.make_tokens(cfg, 9))
+        c.step(synth.make_tokens(cfg, 8))
+        c.load(path)
+        lb += [c.step(synth.make_tokens(cfg, s)) for s in (1, 2)]
+        rc = _store_regions(c)
+    finally:
+        c.close()
+    assert lb == lref
+    for key, a in rref.items():
+        assert np.array_equal(rc[key], a), key
+    # the same through direct writes of the store (weights, moments, counter)
+    d = _trainer(cfg, bits, carry=3, **kw)
+    try:
+        d.step(synth.make_tokens(cfg, 9))
+        d.step(synth.make_tokens(cfg, 8))
+        d.finish()
+        for (u, r), a in mid.items():
+            d.store.region(u, r)[...] = a
+        d.t = 1
+        d.store_modified()
+        ld = [lb[0]] + [d.step(synth.make_tokens(cfg, s)) for s in (1, 2)]
+        rd = _store_regions(d)
+    finally:
+        d.close()
+    assert ld == lref
+    for key, a in rref.items():
+        assert np.array_equal(rd[key], a), key
 
 
 @pytest.mark.parametrize("variant", ["k1_2slot", "k2_1slot_micro_master", "tied_k1_2slot", "resident"])

@@ -584,6 +584,91 @@ def test_plan_invariants_any_depth(L, K):
                 assert content[slot_of[i]] == u and content.count(u) == 1
 
 
+class _FakeEvent:
+    """A gradient copy's completion event for the scheduler test: completes
+    when the test says so (threading.Event), queried or waited on."""
+
+    def __init__(self):
+        import threading
+        self.done = threading.Event()
+        self.queries = 0
+
+    def query(self):
+        self.queries += 1
+        return self.done.is_set()
+
+    def synchronize(self):
+        self.done.wait()
+
+
+@pytest.mark.parametrize("by_priority", [False, True])
+def test_update_scheduler_order(by_priority):
+    """Jobs run only once their event has completed; events complete in
+    submission order (one in-order stream); among the ready jobs the first
+    submitted runs, or with priorities the lowest priority value; a thread
+    with nothing ready waits on the first pending event instead of polling."""
+    import time
+
+    from host_memory_centric_amd.engine import UpdateScheduler
+    sch = UpdateScheduler(by_priority=by_priority)
+    ran = []
+    evs = [_FakeEvent() for _ in range(6)]
+    prio = [5, 4, 3, 2, 1, 0]  # like gradients of layers 5..0 arriving top-down
+    futs = [sch.submit(prio[i], evs[i], ran.append, i) for i in range(6)]
+    time.sleep(0.05)
+    assert ran == []
+    assert sum(e.queries for e in evs) <= 2  # no polling while nothing is ready
+    # complete events 2, 1, 0 (the waiting thread wakes at 0, the last), then 5, 4, 3
+    for e in reversed(evs[:3]):
+        e.done.set()
+    for f in futs[:3]:
+        f.result(timeout=5)
+    time.sleep(0.05)
+    for e in reversed(evs[3:]):
+        e.done.set()
+    for f in futs:
+        f.result(timeout=5)
+    sch.shutdown()
+    assert sorted(ran) == list(range(6))
+    if not by_priority:
+        assert ran == list(range(6))
+    else:
+        assert ran == [2, 1, 0, 5, 4, 3]
+
+
+@pytest.mark.parametrize("L,K,slots,carry", [(48, 4, 5, 12), (48, 4, 2, 48), (9, 2, 3, 4), (5, 1, 1, 2), (8, 4, 5, 3)])
+def test_carried_layers_plan(L, K, slots, carry):
+    """Layers with slots of their own: every use of a carried layer is in its
+    slot; the first pass loads it once (at its forward), a pass whose carried
+    slots already hold the weights loads it never; the other units stay in
+    the shared pool, and the step loads at least ``carry`` fewer times than
+    without carried layers."""
+    ops = plan_step(L, K, False)
+    units = [-2 if k == "head" else l for k, l, _ in ops]
+    fixed = {l: slots + i for i, l in enumerate(range(L - carry, L))}
+    for warm in (False, True):
+        slot_of, load = plan_slots(units, slots, fixed, set(fixed) if warm else ())
+        for i, u in enumerate(units):
+            if u in fixed:
+                assert slot_of[i] == fixed[u]
+                assert load[i] == (not warm and units.index(u) == i)
+            else:
+                assert slot_of[i] < slots
+    cold = sum(plan_slots(units, slots, fixed)[1])
+    warm = sum(plan_slots(units, slots, fixed, set(fixed))[1])
+    assert cold - warm == carry
+    assert warm <= sum(plan_slots(units, slots)[1]) - carry
+
+
+def test_carry_argument_checked(lib):
+    from host_memory_centric_amd.engine import Trainer
+    cfg = synth.preset("tiny")
+    for kw in (dict(carry=1), dict(carry=3, pinned_store=True), dict(carry=1, mode="resident", pinned_store=True),
+               dict(carry=-1, pinned_store=True)):
+        with pytest.raises(ValueError, match="carry"):
+            Trainer(cfg, synth.AdamCfg(), **kw)
+
+
 @pytest.mark.parametrize("kw", [dict(offload_ckpt=5), dict(offload_ckpt=-1), dict(offload_ckpt=1, mode="resident"),
                                 dict(offload_ckpt=3, ckpt_every=2)])
 def test_offload_ckpt_argument_checked_before_any_allocation(lib, kw):
