@@ -128,10 +128,23 @@ def _inter(u, w):
     return t
 
 
-def overlap_report(tl):
-    """Busy and overlap fractions of one step from its event timeline: the
-    share of host-to-device and device-to-host copy time during which the
-    compute stream is running a layer, head or backward op."""
+def merged_timeline(raws):
+    """One event timeline over consecutive steps (ms from the first step's
+    start): the steps' op, weight-copy and gradient-copy intervals."""
+    rel = raws[0]["ref"].elapsed_time
+    out = {"ops": [], "h2d": [], "d2h": []}
+    for tl in raws:
+        out["ops"] += [(k, rel(a), rel(b)) for k, a, b in tl["ops"]]
+        out["h2d"] += [(rel(a), rel(b)) for a, b in tl["h2d"]]
+        out["d2h"] += [(rel(a), rel(b)) for a, b in tl["d2h"]]
+    return out
+
+
+def overlap_report(tl, n_steps=1):
+    """Busy and overlap fractions over the timed steps from their event
+    timeline: the share of host-to-device and device-to-host copy time during
+    which the compute stream is running a layer, head or backward op.  The
+    window runs from the first step's start to the last copy or op."""
     comp = _union([(a, b) for _, a, b in tl["ops"]])
     h2d, d2h = _union(tl["h2d"]), _union(tl["d2h"])
     copies = _union(tl["h2d"] + tl["d2h"])
@@ -139,12 +152,14 @@ def overlap_report(tl):
 
     def frac(x, y):
         return round(x / y, 4) if y > 0 else None
-    return {"step_ms": round(span, 2), "compute_busy_frac": frac(_total(comp), span),
+    return {"window_ms": round(span, 2), "steps": n_steps, "step_ms": round(span / n_steps, 2),
+            "compute_busy_frac": frac(_total(comp), span),
             "h2d_busy_frac": frac(_total(h2d), span), "d2h_busy_frac": frac(_total(d2h), span),
             "h2d_overlap_frac": frac(_inter(h2d, comp), _total(h2d)),
             "d2h_overlap_frac": frac(_inter(d2h, comp), _total(d2h)),
             "copy_overlap_frac": frac(_inter(copies, comp), _total(copies)),
-            "gpu_idle_ms": round(span - _total(comp), 2)}
+            "gpu_busy_ms_per_step": round(_total(comp) / n_steps, 2),
+            "gpu_idle_ms_per_step": round((span - _total(comp)) / n_steps, 2)}
 
 
 def host_probe(tr, reps=3, master=False):
@@ -307,19 +322,20 @@ def cpu_baseline(cfg):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="14b", choices=WORKLOADS)
     ap.add_argument("--mode", default="streamed", choices=["streamed", "resident"])
     ap.add_argument("--slots", type=int, default=5)
     ap.add_argument("--grad-slabs", type=int, default=16)
-    ap.add_argument("--grad-slots", type=int, default=2, help="device gradient slots the backward writes in turn")
-    ap.add_argument("--update-order", default="arrival", choices=["arrival", "urgent", "tail"],
+    ap.add_argument("--grad-slots", type=int, default=4, help="device gradient slots the backward writes in turn")
+    ap.add_argument("--update-order", default="urgent", choices=["arrival", "urgent", "tail"],
                     help="order of the host updates: as gradients arrive, most urgent for the next step first, "
                          "or as they arrive until the backward ends and most urgent first after it")
-    ap.add_argument("--carry", type=int, default=0,
+    ap.add_argument("--carry", type=int, default=None,
                     help="top layers that keep a device slot of their own across steps, refilled right after "
-                         "their host update (page-locked store only)")
+                         "their host update (page-locked store only); default 36 for the 14B-shaped workload "
+                         "with a page-locked store, else 0")
     ap.add_argument("--pageable-store", dest="pinned_store", action="store_false",
                     help="keep the whole store pageable and stream through the packer and the gradient slabs; "
                          "default: the store's W and G regions page-locked, weights and gradients copied directly")
@@ -332,9 +348,9 @@ def main():
     ap.add_argument("--seq", type=int, default=None, help="override the workload's sequence length")
     ap.add_argument("--layers", type=int, default=None, help="override the workload's layer count")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--timeline-out", default=None, help="write the event timeline of one step as JSON")
+    ap.add_argument("--timeline-out", default=None, help="write the event timeline of the timed steps as JSON")
     ap.add_argument("--no-timeline", action="store_true",
-                    help="skip the extra untimed step that records the copy/compute timeline (long steps)")
+                    help="record no copy/compute event timeline during the timed steps")
     ap.add_argument("--progress", action="store_true",
                     help="print each op as it is enqueued (the enqueue runs a few ops ahead of the GPU)")
     ap.add_argument("--offload-ckpt", type=int, default=0,
@@ -357,6 +373,9 @@ def main():
         cfg = dataclasses.replace(cfg, ckpt_every=args.ckpt_every or cfg.ckpt_every, batch=args.batch or cfg.batch,
                                   seq=args.seq or cfg.seq, layers=args.layers or cfg.layers)
     adam = synth.AdamCfg()
+    if args.carry is None:
+        args.carry = 36 if (cfg.name == "14b" and args.pinned_store and args.mode == "streamed"
+                            and cfg.layers >= 36) else 0
     t_init = time.perf_counter()
     nmb = max(1, args.micro_batches)
     _lib.load()
@@ -386,28 +405,28 @@ def main():
     torch.cuda.synchronize()
     _lib.prof_collect(reset=True)
     _lib.call("mt_prof_enable", 1)
+    # the timed steps record their copy/compute event timeline (events only)
+    tr.record_timeline = not args.no_timeline
+    raws = []
     t0 = time.perf_counter()
     for _ in range(args.steps):
         loss = tr.step(tokens(step))
         step += 1
+        raws.append(tr._tl)
         print(f"[bench] step {step}: loss {loss:.4f} {tr.stats['step_s']:.3f} s", file=sys.stderr, flush=True)
     tr.finish()  # the last step's host updates belong to the timed work
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
+    tr.record_timeline = False
     _lib.call("mt_prof_enable", 0)
     prof = _lib.prof_collect(reset=True)
 
     # the trainer's device footprint: taken before the probes allocate their buffers
     dev_peak = int(torch.cuda.max_memory_allocated())
-    # one more (untimed) step with an event timeline: copy/compute overlap
     overlap = None
     if not args.no_timeline:
-        tr.record_timeline = True
-        tr.step(tokens(step))
-        tr.finish()
-        tl = tr.timeline()
-        tr.record_timeline = False
-        overlap = overlap_report(tl)
+        tl = merged_timeline(raws)
+        overlap = overlap_report(tl, args.steps)
     if args.timeline_out and overlap is not None:
         with open(args.timeline_out, "w") as fh:
             json.dump(tl, fh)
@@ -501,11 +520,11 @@ def main():
     out["host"] = host
     # the three floors of a streamed step: the host link (the step's H2D and
     # D2H bytes at the probed rates), host DRAM (above) and the GPU's own
-    # busy time (compute stream, from the timeline step); the step's time
+    # busy time (compute stream over the timed steps); the step's time
     # against the largest of them
     floors = {"link_ms": round(1e3 * max(h2d / (link["h2d_GBps"] * 1e9), d2h / (link["d2h_GBps"] * 1e9)), 1),
               "host_dram_ms": host["floor_ms"],
-              "gpu_busy_ms": (round(overlap["compute_busy_frac"] * overlap["step_ms"], 1) if overlap else None)}
+              "gpu_busy_ms": overlap["gpu_busy_ms_per_step"] if overlap else None}
     bind = max((k for k in floors if floors[k] is not None), key=lambda k: floors[k])
     floors.update(binding=bind, binding_frac_of_step=round(floors[bind] / ms_step, 3),
                   tflops_exec_at_binding=round(f_exec / (floors[bind] * 1e-3) / 1e12, 1))

@@ -98,12 +98,14 @@ def test_carried_layers_change_no_bit(gpu):
                 assert np.array_equal(regions[key], a), (micro, extra, key)
 
 
-def test_device_peak_independent_of_depth(gpu):
+@pytest.mark.parametrize("carry", [0, 4])
+def test_device_peak_independent_of_depth(gpu, carry):
     """The 7B layer shape (hidden 4096, batch 4 x 2048) streamed with
-    checkpoints every 4 layers and 2 slots, at 8 and at 16 layers: the device
-    peak differs by exactly the two extra block checkpoints ([T, h] bf16,
-    64 MiB each); the weight slots, gradient slots, one block's internals and
-    the workspace are sized per layer."""
+    checkpoints every 4 layers and 2 slots (and, with carried layers, 4 more
+    slots of their own), at 8 and at 16 layers: the device peak differs by
+    exactly the two extra block checkpoints ([T, h] bf16, 64 MiB each); the
+    weight slots, gradient slots, one block's internals and the workspace are
+    sized per layer."""
     import torch
 
     from host_memory_centric_amd.engine import Trainer
@@ -113,9 +115,10 @@ def test_device_peak_independent_of_depth(gpu):
         torch.cuda.empty_cache()
         torch.cuda.reset_peak_memory_stats()
         base = torch.cuda.memory_allocated()
-        tr = Trainer(cfg, synth.AdamCfg(), n_slots=2)
+        tr = Trainer(cfg, synth.AdamCfg(), n_slots=2, carry=carry, pinned_store=carry > 0)
         try:
-            tr.step(synth.make_tokens(cfg, 0))
+            for s in range(2):  # (the second step runs from the carried slots)
+                tr.step(synth.make_tokens(cfg, s))
             tr.finish()
             torch.cuda.synchronize()
             peaks[L] = torch.cuda.max_memory_allocated() - base
