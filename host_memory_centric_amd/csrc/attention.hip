@@ -136,6 +136,29 @@ struct ATile {
     }
 };
 
+// Work order of the causal kernels.  The blocks of a (batch, head) differ in
+// length (the causal prefix), so the launch takes the (batch, head) pairs in
+// groups of G and dispatches each group's blocks longest first: the short
+// blocks fill the end of each group, and at the end of the launch nothing
+// long starts last.  G is chosen so that a group spans about WGS workgroups
+// (several rounds of the machine): at long sequences a group is one or two
+// heads, whose concurrent blocks then share their K/V (or Q/dO) tiles in the
+// L2; at short sequences a group spans many heads.  blockIdx.x + gridDim.x *
+// blockIdx.y is the dispatch order; gridDim.x is the number of (batch, head)
+// pairs and gridDim.y the number of blocks per pair.  rank 0 is the longest
+// block.
+template <int WGS>
+__device__ __forceinline__ void attn_work(int& bh, int& rank) {
+    const int nbh = (int)gridDim.x, nblk = (int)gridDim.y;
+    const int lin = (int)blockIdx.x + nbh * (int)blockIdx.y;
+    const int G = min(nbh, max(1, (WGS + nblk - 1) / nblk));
+    const int per = G * nblk;
+    const int g = lin / per, r = lin - g * per;
+    const int gsz = min(G, nbh - g * G);  // the last group may hold fewer pairs
+    rank = r / gsz;
+    bh = g * G + (r - rank * gsz);
+}
+
 // B-operand fragment from 8 accumulator values (elements r0 .. r0+7 of a
 // tile), rounded to bf16 (F16 = false) or fp16
 template <bool F16 = false>
@@ -186,8 +209,9 @@ __global__ __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(2, 
     __shared__ __attribute__((aligned(1024))) uint16_t kbuf[2][TL::ELEMS];
     __shared__ __attribute__((aligned(1024))) uint16_t vbuf[2][TL::ELEMS];
     const int nqb = (S + ATT_BQ - 1) / ATT_BQ;
-    const int qb = nqb - 1 - (int)blockIdx.x;  // most work first
-    const int bh = blockIdx.y;
+    int bh, rank;
+    attn_work<4096>(bh, rank);
+    const int qb = nqb - 1 - rank;  // the last query block has the most keys
     const int b = bh / heads, head = bh % heads;
     const int lane = threadIdx.x & 63, half = lane >> 5;
     // the wave index is uniform: conditions on it become scalar branches
@@ -341,8 +365,9 @@ __global__ __launch_bounds__(ATT_PP_THREADS) __attribute__((amdgpu_waves_per_eu(
     __shared__ __attribute__((aligned(1024))) uint16_t kbuf[2][TL::ELEMS];
     __shared__ __attribute__((aligned(1024))) uint16_t vbuf[2][TL::ELEMS];
     const int nqb = (S + ATT_PP_BQ - 1) / ATT_PP_BQ;
-    const int qb = nqb - 1 - (int)blockIdx.x;  // most work first
-    const int bh = blockIdx.y;
+    int bh, rank;
+    attn_work<2048>(bh, rank);
+    const int qb = nqb - 1 - rank;  // the last query block has the most keys
     const int b = bh / heads, head = bh % heads;
     const int lane = threadIdx.x & 63, half = lane >> 5;
     // the wave index is uniform: conditions on it become scalar branches
@@ -686,8 +711,9 @@ __global__ __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(2, 
     using TL = ATile<HD>;
     __shared__ __attribute__((aligned(1024))) uint16_t smem[2][2 * TL::ELEMS];  // [buffer][K | V]
     const int nqb = (S + ATT_BQ - 1) / ATT_BQ;
-    const int qb = nqb - 1 - (int)blockIdx.x;
-    const int bh = blockIdx.y;
+    int bh, rank;
+    attn_work<4096>(bh, rank);
+    const int qb = nqb - 1 - rank;  // the last query block has the most keys
     const int b = bh / heads, head = bh % heads;
     const int lane = threadIdx.x & 63, half = lane >> 5;
     // the wave index is uniform: conditions on it become scalar branches
@@ -804,8 +830,8 @@ __global__ __launch_bounds__(ATT_THREADS) __attribute__((amdgpu_waves_per_eu(2, 
     using TL = ATile<HD>;
     __shared__ __attribute__((aligned(1024))) uint16_t smem[2][2 * TL::ELEMS];  // [buffer][Q | dO]
     __shared__ float rs[2][2][ATT_T];  // [buffer][lse*log2(e) | D] of the tile's queries
-    const int kbk = (int)blockIdx.x;  // key block; low blocks (most work) first
-    const int bh = blockIdx.y;
+    int bh, kbk;
+    attn_work<4096>(bh, kbk);  // key block: the first has the most queries
     const int b = bh / heads, head = bh % heads;
     const int lane = threadIdx.x & 63, half = lane >> 5;
     // the wave index is uniform: conditions on it become scalar branches
@@ -944,6 +970,8 @@ static void check_attn(int B, int S, int heads, int hd) {
     if (hd != 64 && hd != 128) MT_FAIL(MT_E_SHAPE, "attention: head_dim %d not in {64, 128}", hd);
     if (B < 1 || S < 1 || heads < 1) MT_FAIL(MT_E_SHAPE, "attention: empty shape");
     if ((int64_t)B * heads > 65535) MT_FAIL(MT_E_SHAPE, "attention: batch*heads too large");
+    if ((S + 127) / 128 > 65535 || (int64_t)B * heads * ((S + 127) / 128) >= (int64_t)1 << 31)
+        MT_FAIL(MT_E_SHAPE, "attention: sequence too long");
 }
 
 size_t attention_fwd_ws_bytes(int, int, int, int) { return 0; }
@@ -961,7 +989,7 @@ template <bool F16>
 static void launch_attn_fwd(const uint16_t* qkv, uint16_t* o, uint16_t* o16, float* lse, int B, int S, int heads,
                             int hd, bool pipe, float sl2, hipStream_t s) {
     if (pipe) {
-        const dim3 grid((S + ATT_BQ - 1) / ATT_BQ, B * heads);
+        const dim3 grid(B * heads, (S + ATT_BQ - 1) / ATT_BQ);
         if (hd == 128)
             hipLaunchKernelGGL((attn_fwd_kernel<128, F16>), grid, dim3(ATT_THREADS), 0, s, qkv, o, o16, lse, S, heads,
                                sl2);
@@ -969,7 +997,7 @@ static void launch_attn_fwd(const uint16_t* qkv, uint16_t* o, uint16_t* o16, flo
             hipLaunchKernelGGL((attn_fwd_kernel<64, F16>), grid, dim3(ATT_THREADS), 0, s, qkv, o, o16, lse, S, heads,
                                sl2);
     } else {
-        const dim3 grid((S + ATT_PP_BQ - 1) / ATT_PP_BQ, B * heads);
+        const dim3 grid(B * heads, (S + ATT_PP_BQ - 1) / ATT_PP_BQ);
         if (hd == 128)
             hipLaunchKernelGGL((attn_fwd_pp_kernel<128, F16>), grid, dim3(ATT_PP_THREADS), 0, s, qkv, o, o16, lse, S,
                                heads, sl2);
@@ -1012,7 +1040,7 @@ void attention_bwd(const uint16_t* qkv, const uint16_t* o, const float* lse, con
     const float sl2 = LOG2E * scale;
     const int64_t T = (int64_t)B * S;
     const int64_t n = T * heads;
-    const dim3 gq((S + ATT_BQ - 1) / ATT_BQ, B * heads), gk((S + ATT_BK - 1) / ATT_BK, B * heads);
+    const dim3 gq(B * heads, (S + ATT_BQ - 1) / ATT_BQ), gk(B * heads, (S + ATT_BK - 1) / ATT_BK);
     // causal entries x (QK^T recompute, dP, dV, dK, dQ) at 2*hd flops each (the
     // kernels execute 16*hd: Q K^T three times and dO V^T twice)
     ProfScope prof(PROF_ATTN_BWD, 10.0 * hd * (double)B * heads * ((double)S * (S + 1) / 2), s);
@@ -1045,7 +1073,7 @@ static void launch_attn_bwd16(const uint16_t* qkv16, const uint16_t* o, const fl
     float* stats = (float*)ws;
     float* sc = (float*)(ws + round_up(4 * (size_t)n * 4, 256));
     uint16_t* do16 = (uint16_t*)((char*)sc + round_up((size_t)B * heads * 16, 256));
-    const dim3 gq((S + ATT_BQ - 1) / ATT_BQ, B * heads), gk((S + ATT_BK - 1) / ATT_BK, B * heads);
+    const dim3 gq(B * heads, (S + ATT_BQ - 1) / ATT_BQ), gk(B * heads, (S + ATT_BK - 1) / ATT_BK);
     hipLaunchKernelGGL(attn_bwd_stats_kernel<HD>, dim3((unsigned)((n * (HD / 8) + 255) / 256)), dim3(256), 0, s, qkv16,
                        o, dout, stats, T, S, heads);
     hipLaunchKernelGGL(attn_bwd_scale_kernel, dim3((unsigned)(B * heads)), dim3(256), 0, s, stats, sc, n, S);
