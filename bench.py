@@ -333,7 +333,7 @@ def main():
                     help="order of the host updates: as gradients arrive, most urgent for the next step first, "
                          "or as they arrive until the backward ends and most urgent first after it")
     ap.add_argument("--carry", type=int, default=None,
-                    help="top layers that keep a device slot of their own across steps, refilled right after "
+                    help="layers that keep a device slot of their own across steps, refilled right after "
                          "their host update (page-locked store only); default 36 for the 14B-shaped workload "
                          "with a page-locked store, else 0")
     ap.add_argument("--pageable-store", dest="pinned_store", action="store_false",
@@ -473,8 +473,8 @@ def main():
                    (", fp32 master weights" if args.master else "") +
                    (", host store W/G page-locked (direct copies, no packer)" if args.pinned_store else "") +
                    (f", checkpoints of the first {tr.n_host} blocks in host memory" if tr.n_host else "") +
-                   (f", top {tr.carry} layers in device slots of their own, refilled after each update"
-                    if tr.carry else "") +
+                   (f", {tr.carry} layers (all but {cfg.layers - tr.carry} evenly spaced) in device slots of their "
+                    f"own, refilled after each update" if tr.carry else "") +
                    (f", {args.update_order} update order" if args.update_order != "arrival" else ""),
                    "name": cfg.name, "global_batch": cfg.batch * nmb,
                    "seq_len": cfg.seq, "micro_batches": nmb, "master_fp32": bool(args.master),

@@ -228,6 +228,17 @@ def plan_slots(units, n_slots, fixed=None, preloaded=()):
     return slot_of, load
 
 
+def carried_layers(L, carry):
+    """The layers that keep slots of their own: all but L - carry evenly
+    spaced ones, which stream.  Streamed layer i (of n = L - carry) is layer
+    (i + 1) * L // n - 1, so each streamed layer follows a run of carried
+    ones whose compute covers its load (at L = 48, carry = 36: layers 3, 7,
+    ..., 47 stream)."""
+    n = L - carry
+    streamed = {(i + 1) * L // n - 1 for i in range(n)} if n > 0 else set()
+    return [l for l in range(L) if l not in streamed]
+
+
 class Trainer:
     """Host-memory-centric trainer on one GPU.
 
@@ -270,18 +281,20 @@ class Trainer:
     grad_slots: device gradient slots the backward writes in turn (a layer's
     backward waits until the copy out of its slot's previous gradient is
     done; more slots let the evacuation lag further behind);
-    carry: the top ``carry`` layers each own a device slot of their own (outside
-    the ``n_slots`` pool) that holds their weights from one step to the next
-    (page-locked store only).  Right after the host update of such a layer
-    (whose gradient is among the first of the backward) the optimizer thread
-    enqueues the copy of its new weights into its slot, behind the weight
-    stream's pending loads and after the layer's backward has read the old
-    ones; the next step's forward, recompute and backward of the layer then
-    use the slot without a load.  Each such layer is loaded once per step
-    instead of once per forward and once per recompute, and its load moves
-    out of the link-bound forward into the backward and the update tail.  The
-    device footprint grows by ``carry`` layer slots, a fixed count
-    independent of depth.  Results are bit-identical to ``carry=0``;
+    carry: ``carry`` layers each own a device slot of their own (outside the
+    ``n_slots`` pool) that holds their weights from one step to the next
+    (page-locked store only); the other layers, evenly spaced (see
+    ``carried_layers``), stream through the pool.  Right after the host
+    update of a carried layer the optimizer thread enqueues the copy of its
+    new weights into its slot, behind the weight stream's pending loads and
+    after the layer's backward has read the old ones; the next step's
+    forward, recompute and backward of the layer then use the slot without a
+    load.  Each carried layer is loaded once per step instead of once per
+    forward and once per recompute, and its load moves out of the link-bound
+    forward into the backward and the update tail; the streamed layers' loads
+    run while the carried layers between them compute.  The device footprint
+    grows by ``carry`` layer slots, a fixed count independent of depth.
+    Results are bit-identical to ``carry=0``;
     poison (debug): fill every buffer with NaN as soon as the event that
     frees it fires -- a device weight slot after the op that last reads it
     before a reload, a device gradient slot after the copy that evacuates
@@ -351,7 +364,7 @@ class Trainer:
         # the carried layers' own slots follow the pool's; the plan of a pass
         # whose carried slots already hold the current weights (every pass
         # but the first) has no load for them
-        self.carry_slot = {l: self.n_slots + i for i, l in enumerate(range(self.L - self.carry, self.L))}
+        self.carry_slot = {l: self.n_slots + i for i, l in enumerate(carried_layers(self.L, self.carry))}
         self._plans = {warm: plan_slots(units, self.n_slots, self.carry_slot,
                                         set(self.carry_slot) if warm else ())
                        for warm in (False, True)}

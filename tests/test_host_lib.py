@@ -660,6 +660,22 @@ def test_carried_layers_plan(L, K, slots, carry):
     assert warm <= sum(plan_slots(units, slots)[1]) - carry
 
 
+@pytest.mark.parametrize("L", [1, 2, 5, 9, 32, 48, 180])
+def test_carried_layers_evenly_spaced(L):
+    """carried_layers(L, c) holds c layers; the L - c streamed ones are spread
+    so that runs of carried layers between them differ by at most one, and the
+    last layer streams whenever any does."""
+    from host_memory_centric_amd.engine import carried_layers
+    for c in range(L + 1):
+        cl = carried_layers(L, c)
+        assert len(cl) == c and cl == sorted(set(cl)) and all(0 <= l < L for l in cl)
+        streamed = [l for l in range(L) if l not in cl]
+        if streamed:
+            assert streamed[-1] == L - 1
+            runs = [b - a - 1 for a, b in zip([-1] + streamed[:-1], streamed)]
+            assert max(runs) - min(runs) <= 1, (L, c, runs)
+
+
 def test_carry_argument_checked(lib):
     from host_memory_centric_amd.engine import Trainer
     cfg = synth.preset("tiny")
