@@ -334,8 +334,8 @@ def main():
                          "or as they arrive until the backward ends and most urgent first after it")
     ap.add_argument("--carry", type=int, default=None,
                     help="layers that keep a device slot of their own across steps, refilled right after "
-                         "their host update (page-locked store only); default 36 for the 14B-shaped workload "
-                         "with a page-locked store, else 0")
+                         "their host update (page-locked store only); default: half the layers for the "
+                         "14B-shaped workload with a page-locked store, else 0")
     ap.add_argument("--pageable-store", dest="pinned_store", action="store_false",
                     help="keep the whole store pageable and stream through the packer and the gradient slabs; "
                          "default: the store's W and G regions page-locked, weights and gradients copied directly")
@@ -373,9 +373,8 @@ def main():
         cfg = dataclasses.replace(cfg, ckpt_every=args.ckpt_every or cfg.ckpt_every, batch=args.batch or cfg.batch,
                                   seq=args.seq or cfg.seq, layers=args.layers or cfg.layers)
     adam = synth.AdamCfg()
-    if args.carry is None:
-        args.carry = 36 if (cfg.name == "14b" and args.pinned_store and args.mode == "streamed"
-                            and cfg.layers >= 36) else 0
+    if args.carry is None:  # 14B-shaped default: every other layer carried, the others stream
+        args.carry = cfg.layers // 2 if (cfg.name == "14b" and args.pinned_store and args.mode == "streamed") else 0
     t_init = time.perf_counter()
     nmb = max(1, args.micro_batches)
     _lib.load()
