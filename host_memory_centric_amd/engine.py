@@ -738,6 +738,7 @@ class Trainer:
         pack_fut = {j: self.packer.submit(pack, j) for j in range(min(2, len(loads)))}
         op_enq = [threading.Event() for _ in self.ops]  # op i enqueued, op_done[i] recorded
         load_issued = [threading.Event() for _ in loads]
+        aborted = [False]  # set when this pass fails: the copy issuers stop waiting for ops
 
         def issue_load(j):
             i = loads[j]
@@ -747,6 +748,8 @@ class Trainer:
             pu = slot_prev[i]
             if pu is not None:
                 op_enq[pu].wait()
+                if aborted[0]:
+                    raise RuntimeError("the pass was abandoned")
                 op_done[pu].synchronize()  # buffer-free: the slot's last reader has completed
             with torch.cuda.device(self.dev), torch.cuda.stream(hs):
                 if tl is not None:
@@ -831,149 +834,160 @@ class Trainer:
 
         jobs = self.pending if final else self.accum_jobs
 
-        for i, (kind, l, si) in enumerate(self.ops):
-            if op_load[i]:
-                wait_load(load_of_op[i])
-                cs.wait_event(ready_ev[load_of_op[i]])
-                if l in self.carry_slot and kind != "head":
-                    self._carry_ev[l] = ready_ev[load_of_op[i]]
-            elif warm and kind == "fwd" and l in self.carry_slot:
-                # the previous step's update of a carried layer enqueued the
-                # copy of its new weights into the layer's slot before it ended
-                self._wait_unit(l)
-                ev_c = self._carry_ev.get(l)
-                if ev_c is not None:
-                    cs.wait_event(ev_c)
-            slot = op_slot[i]
-            if self.progress is not None:
-                self.progress(kind, l)
-            # block checkpoints in host memory: the writer of a ring buffer waits for the copy
-            # out of its previous block; the first reader in the backward for the copy back
-            wb = (l + 1) // K if kind == "fwd" and (l + 1) % K == 0 else None
-            if kind == "head" and nh:
-                ckpt_fetch(nh - 1)
-                if nh >= 2:
-                    ckpt_fetch(nh - 2)
-            if kind == "refwd" and l % K == 0 and l // K < nh:
-                ckpt_in(i - 1, need=l // K)
-                cs.wait_event(ck_h2d[l // K])
-            with torch.cuda.stream(cs):
-                if wb is not None and 2 <= wb < self.n_ring:
-                    cs.wait_event(ck_d2h[wb - 2])
-                if kind == "head" and self.head_d2h is not None:
-                    cs.wait_event(wait_copy_out(self.head_d2h))  # previous step's copy out of the head gradient
-                if kind == "bwd" and gslot_d2h[n_bwd % self.n_gslots] is not None:
-                    # buffer-free (gradient slot)
-                    cs.wait_event(wait_copy_out(gslot_d2h[n_bwd % self.n_gslots]))
-                if tl is not None:
-                    tl["ops"].append([kind, self._ev(cs), None])
-                if kind == "fwd":
-                    v = self._bind(slot, None, l)
-                    # layers before the last block keep nothing: the first saved
-                    # buffer (written again by the last block) is their scratch
-                    a = self._act(self._x(l), self._x(l + 1), self.saved[si if si is not None else 0])
-                    call("mt_layer_fwd", ctypes.byref(v), ctypes.byref(self.mcfg), ctypes.byref(a), sc)
-                elif kind == "refwd":
-                    out = self._x(l + 1) if (l + 1) % self.K != 0 else self.xscratch
-                    v = self._bind(slot, None, l)
-                    a = self._act(self._x(l), out, self.saved[si])
-                    call("mt_layer_fwd", ctypes.byref(v), ctypes.byref(self.mcfg), ctypes.byref(a), sc)
-                elif kind == "head":
-                    v = self._bind(slot, self.head_g, MT_UNIT_HEAD)
-                    io = MtHeadIO()
-                    io.batch, io.seq = self.B, self.S
-                    io.x = self.xL.data_ptr()
-                    io.tokens = self.tok_dev.data_ptr()
-                    io.dx = self.dgrad[cur].data_ptr()
-                    io.dx_bf16 = self.dgrad_b[cur].data_ptr()
-                    io.loss = self.loss_dev.data_ptr()
-                    io.workspace = self.ws.data_ptr()
-                    io.workspace_bytes = self.ws_bytes
-                    call("mt_head_fwd_bwd", ctypes.byref(v), ctypes.byref(self.mcfg), ctypes.byref(io), sc)
-                else:  # bwd
-                    g = n_bwd % self.n_gslots
-                    v = self._bind(slot, self.gslots[g], l)
-                    a = self._act(self._x(l), None, self.saved[si], dy=self.dgrad[cur], dyb=self.dgrad_b[cur],
-                                  dx=self.dgrad[1 - cur], dxb=self.dgrad_b[1 - cur])
-                    call("mt_layer_recompute_bwd", ctypes.byref(v), ctypes.byref(self.mcfg), ctypes.byref(a), sc)
-                    cur = 1 - cur
-                if i in poison_slot_after or (self.poison and final and kind == "bwd" and l in self.carry_slot):
-                    self._poison_dev(self.slots[slot], self.lay_head_dev if kind == "head" else self.lay)
-                ev = torch.cuda.Event(enable_timing=self.record_timeline)
-                ev.record(cs)
-                op_done[i] = ev
-                if tl is not None:
-                    tl["ops"][-1][2] = ev
-            op_enq[i].set()
-            if wb is not None and wb < nh:
-                ckpt_out(wb, ev)
-            if kind == "head":
-                d2h = torch.cuda.Event(enable_timing=self.record_timeline)
+        try:
+            for i, (kind, l, si) in enumerate(self.ops):
+                if op_load[i]:
+                    wait_load(load_of_op[i])
+                    cs.wait_event(ready_ev[load_of_op[i]])
+                    if l in self.carry_slot and kind != "head":
+                        self._carry_ev[l] = ready_ev[load_of_op[i]]
+                elif warm and kind == "fwd" and l in self.carry_slot:
+                    # the previous step's update of a carried layer enqueued the
+                    # copy of its new weights into the layer's slot before it ended
+                    self._wait_unit(l)
+                    ev_c = self._carry_ev.get(l)
+                    if ev_c is not None:
+                        cs.wait_event(ev_c)
+                slot = op_slot[i]
+                if self.progress is not None:
+                    self.progress(kind, l)
+                # block checkpoints in host memory: the writer of a ring buffer waits for the copy
+                # out of its previous block; the first reader in the backward for the copy back
+                wb = (l + 1) // K if kind == "fwd" and (l + 1) % K == 0 else None
+                if kind == "head" and nh:
+                    ckpt_fetch(nh - 1)
+                    if nh >= 2:
+                        ckpt_fetch(nh - 2)
+                if kind == "refwd" and l % K == 0 and l // K < nh:
+                    ckpt_in(i - 1, need=l // K)
+                    cs.wait_event(ck_h2d[l // K])
+                with torch.cuda.stream(cs):
+                    if wb is not None and 2 <= wb < self.n_ring:
+                        cs.wait_event(ck_d2h[wb - 2])
+                    if kind == "head" and self.head_d2h is not None:
+                        cs.wait_event(wait_copy_out(self.head_d2h))  # previous step's copy out of the head gradient
+                    if kind == "bwd" and gslot_d2h[n_bwd % self.n_gslots] is not None:
+                        # buffer-free (gradient slot)
+                        cs.wait_event(wait_copy_out(gslot_d2h[n_bwd % self.n_gslots]))
+                    if tl is not None:
+                        tl["ops"].append([kind, self._ev(cs), None])
+                    if kind == "fwd":
+                        v = self._bind(slot, None, l)
+                        # layers before the last block keep nothing: the first saved
+                        # buffer (written again by the last block) is their scratch
+                        a = self._act(self._x(l), self._x(l + 1), self.saved[si if si is not None else 0])
+                        call("mt_layer_fwd", ctypes.byref(v), ctypes.byref(self.mcfg), ctypes.byref(a), sc)
+                    elif kind == "refwd":
+                        out = self._x(l + 1) if (l + 1) % self.K != 0 else self.xscratch
+                        v = self._bind(slot, None, l)
+                        a = self._act(self._x(l), out, self.saved[si])
+                        call("mt_layer_fwd", ctypes.byref(v), ctypes.byref(self.mcfg), ctypes.byref(a), sc)
+                    elif kind == "head":
+                        v = self._bind(slot, self.head_g, MT_UNIT_HEAD)
+                        io = MtHeadIO()
+                        io.batch, io.seq = self.B, self.S
+                        io.x = self.xL.data_ptr()
+                        io.tokens = self.tok_dev.data_ptr()
+                        io.dx = self.dgrad[cur].data_ptr()
+                        io.dx_bf16 = self.dgrad_b[cur].data_ptr()
+                        io.loss = self.loss_dev.data_ptr()
+                        io.workspace = self.ws.data_ptr()
+                        io.workspace_bytes = self.ws_bytes
+                        call("mt_head_fwd_bwd", ctypes.byref(v), ctypes.byref(self.mcfg), ctypes.byref(io), sc)
+                    else:  # bwd
+                        g = n_bwd % self.n_gslots
+                        v = self._bind(slot, self.gslots[g], l)
+                        a = self._act(self._x(l), None, self.saved[si], dy=self.dgrad[cur], dyb=self.dgrad_b[cur],
+                                      dx=self.dgrad[1 - cur], dxb=self.dgrad_b[1 - cur])
+                        call("mt_layer_recompute_bwd", ctypes.byref(v), ctypes.byref(self.mcfg), ctypes.byref(a), sc)
+                        cur = 1 - cur
+                    if i in poison_slot_after or (self.poison and final and kind == "bwd" and l in self.carry_slot):
+                        self._poison_dev(self.slots[slot], self.lay_head_dev if kind == "head" else self.lay)
+                    ev = torch.cuda.Event(enable_timing=self.record_timeline)
+                    ev.record(cs)
+                    op_done[i] = ev
+                    if tl is not None:
+                        tl["ops"][-1][2] = ev
+                op_enq[i].set()
+                if wb is not None and wb < nh:
+                    ckpt_out(wb, ev)
+                if kind == "head":
+                    d2h = torch.cuda.Event(enable_timing=self.record_timeline)
 
-                def head_out(ev=ev, d2h=d2h):
-                    self._wait_unit(MT_UNIT_HEAD)  # the previous update still reads the head's slab
-                    self._wait_acc(MT_UNIT_HEAD)   # (or the previous micro-batch's accumulation)
-                    head_dst = self.head_gslab.ptr if self.head_gslab is not None else self.g_addr[MT_UNIT_HEAD]
-                    ev.synchronize()  # the head's gradient is complete
-                    with torch.cuda.device(self.dev), torch.cuda.stream(ds):
-                        if tl is not None:
-                            tl["d2h"].append([self._ev(ds), d2h])
-                        call("mt_copy_d2h", head_dst, _ptr(self.head_g), self.lay_head_dev.w_bytes, sd)
-                        if self.poison:
-                            self._poison_dev(self.head_g, self.lay_head_dev)
-                        d2h.record(ds)
-                    if self.update_order == "tail":
-                        self.optimizer.set_by_priority(False)
-                    jobs[MT_UNIT_HEAD] = self.optimizer.submit(
-                        self._urgency(MT_UNIT_HEAD), d2h, adam_layer, d2h, MT_UNIT_HEAD,
-                        self.head_gslab.ptr if self.head_gslab is not None else None)
-                f = self.d2h_issuer.submit(head_out)
-                d2h_futs.append(f)
-                self.head_d2h = (f, d2h)
-            elif kind == "bwd":
-                g = n_bwd % self.n_gslots
-                n_bwd += 1
-                d2h = torch.cuda.Event(enable_timing=self.record_timeline)
-
-                def grad_out(ev=ev, g=g, l=l, d2h=d2h, dx=self.dgrad[cur]):
-                    self._wait_unit(l)  # (finished long ago: the previous step's update of this layer)
-                    if self.direct:
-                        # G is the copy's destination: the previous micro-batch's
-                        # accumulation (long finished) must have read it
-                        self._wait_acc(l)
-                        k, g_dst = None, self.g_addr[l]
-                    else:
-                        k = slab_free.get()
-                        g_dst = self.gslab[k].ptr
-                    ev.synchronize()  # backward-done: the layer's gradient is complete
-                    with torch.cuda.device(self.dev), torch.cuda.stream(ds):
-                        if tl is not None:
-                            tl["d2h"].append([self._ev(ds), d2h])
-                        call("mt_copy_d2h", g_dst, _ptr(self.gslots[g]), self.lay.w_bytes, sd)
-                        if self.poison:
-                            self._poison_dev(self.gslots[g], self.lay)
-                        d2h.record(ds)
-                        if l == 0:
-                            d2h_x = torch.cuda.Event(enable_timing=self.record_timeline)
+                    def head_out(ev=ev, d2h=d2h):
+                        self._wait_unit(MT_UNIT_HEAD)  # the previous update still reads the head's slab
+                        self._wait_acc(MT_UNIT_HEAD)   # (or the previous micro-batch's accumulation)
+                        head_dst = self.head_gslab.ptr if self.head_gslab is not None else self.g_addr[MT_UNIT_HEAD]
+                        ev.synchronize()  # the head's gradient is complete
+                        with torch.cuda.device(self.dev), torch.cuda.stream(ds):
                             if tl is not None:
-                                tl["d2h"].append([self._ev(ds), d2h_x])
-                            call("mt_copy_d2h", self.dx0_pin.ptr, _ptr(dx), self.T * h * 4, sd)
-                            d2h_x.record(ds)
-                    if k is None:
-                        after = ev if (final and l in self.carry_slot) else None
-                        jobs[l] = self.optimizer.submit(self._urgency(l), d2h, adam_layer, d2h, l, None, after)
-                    else:
-                        jobs[l] = self.optimizer.submit(self._urgency(l), d2h, adam_layer_slab, d2h, l, k)
-                    if l == 0:
-                        jobs[MT_UNIT_EMBED] = self.optimizer.submit(self._urgency(MT_UNIT_EMBED), d2h_x, adam_embed,
-                                                                    d2h_x)
+                                tl["d2h"].append([self._ev(ds), d2h])
+                            call("mt_copy_d2h", head_dst, _ptr(self.head_g), self.lay_head_dev.w_bytes, sd)
+                            if self.poison:
+                                self._poison_dev(self.head_g, self.lay_head_dev)
+                            d2h.record(ds)
                         if self.update_order == "tail":
-                            self.optimizer.set_by_priority(True)
-                f = self.d2h_issuer.submit(grad_out)
-                d2h_futs.append(f)
-                gslot_d2h[g] = (f, d2h)
-            if nh:
-                ckpt_in(i)
+                            self.optimizer.set_by_priority(False)
+                        jobs[MT_UNIT_HEAD] = self.optimizer.submit(
+                            self._urgency(MT_UNIT_HEAD), d2h, adam_layer, d2h, MT_UNIT_HEAD,
+                            self.head_gslab.ptr if self.head_gslab is not None else None)
+                    f = self.d2h_issuer.submit(head_out)
+                    d2h_futs.append(f)
+                    self.head_d2h = (f, d2h)
+                elif kind == "bwd":
+                    g = n_bwd % self.n_gslots
+                    n_bwd += 1
+                    d2h = torch.cuda.Event(enable_timing=self.record_timeline)
+
+                    def grad_out(ev=ev, g=g, l=l, d2h=d2h, dx=self.dgrad[cur]):
+                        self._wait_unit(l)  # (finished long ago: the previous step's update of this layer)
+                        if self.direct:
+                            # G is the copy's destination: the previous micro-batch's
+                            # accumulation (long finished) must have read it
+                            self._wait_acc(l)
+                            k, g_dst = None, self.g_addr[l]
+                        else:
+                            k = slab_free.get()
+                            g_dst = self.gslab[k].ptr
+                        ev.synchronize()  # backward-done: the layer's gradient is complete
+                        with torch.cuda.device(self.dev), torch.cuda.stream(ds):
+                            if tl is not None:
+                                tl["d2h"].append([self._ev(ds), d2h])
+                            call("mt_copy_d2h", g_dst, _ptr(self.gslots[g]), self.lay.w_bytes, sd)
+                            if self.poison:
+                                self._poison_dev(self.gslots[g], self.lay)
+                            d2h.record(ds)
+                            if l == 0:
+                                d2h_x = torch.cuda.Event(enable_timing=self.record_timeline)
+                                if tl is not None:
+                                    tl["d2h"].append([self._ev(ds), d2h_x])
+                                call("mt_copy_d2h", self.dx0_pin.ptr, _ptr(dx), self.T * h * 4, sd)
+                                d2h_x.record(ds)
+                        if k is None:
+                            after = ev if (final and l in self.carry_slot) else None
+                            jobs[l] = self.optimizer.submit(self._urgency(l), d2h, adam_layer, d2h, l, None, after)
+                        else:
+                            jobs[l] = self.optimizer.submit(self._urgency(l), d2h, adam_layer_slab, d2h, l, k)
+                        if l == 0:
+                            jobs[MT_UNIT_EMBED] = self.optimizer.submit(self._urgency(MT_UNIT_EMBED), d2h_x, adam_embed,
+                                                                        d2h_x)
+                            if self.update_order == "tail":
+                                self.optimizer.set_by_priority(True)
+                    f = self.d2h_issuer.submit(grad_out)
+                    d2h_futs.append(f)
+                    gslot_d2h[g] = (f, d2h)
+                if nh:
+                    ckpt_in(i)
+        except BaseException:
+            aborted[0] = True
+            for e in op_enq:
+                e.set()
+            for f in ([h2d_fut] if h2d_fut is not None else []) + d2h_futs:
+                try:
+                    f.result()
+                except BaseException:
+                    pass
+            raise
 
         if h2d_fut is not None:
             h2d_fut.result()

@@ -129,3 +129,37 @@ def test_device_peak_independent_of_depth(gpu, carry):
     blocks = {L: (L + 3) // 4 for L in peaks}
     print(f"device peaks: {peaks}, block checkpoint {ckpt} bytes", flush=True)
     assert peaks[16] - peaks[8] == (blocks[16] - blocks[8]) * ckpt, peaks
+
+
+@pytest.mark.parametrize("fail_at", [3, 12])
+def test_failed_pass_releases_the_copy_threads(gpu, fail_at):
+    """An error raised while a pass is being enqueued (here: the bind of the
+    fail_at-th op, a host-side error) propagates from step(); the weight-load
+    and gradient-copy issuer threads, which wait for ops that will never be
+    enqueued, are released, and close() returns.  A new trainer on the same
+    weights then runs its steps normally (losses equal a clean run's)."""
+    import threading
+
+    from host_memory_centric_amd.engine import Trainer
+    cfg = synth.preset("tiny", layers=5, seq=100)
+    bits = synth.make_weights(cfg)
+    kw = dict(ckpt_every=2, n_slots=2, pinned_store=True, carry=2)
+    tr = Trainer(cfg, synth.AdamCfg(), weights=bits, **kw)
+    calls = [0]
+    bind = tr._bind
+
+    def failing_bind(*a):
+        calls[0] += 1
+        if calls[0] == fail_at:
+            raise RuntimeError("planted host-side error")
+        return bind(*a)
+    tr._bind = failing_bind
+    with pytest.raises(RuntimeError, match="planted"):
+        tr.step(synth.make_tokens(cfg, 0))
+    done = threading.Event()
+    th = threading.Thread(target=lambda: (tr.close(), done.set()), daemon=True)
+    th.start()
+    assert done.wait(60), "close() did not return after a failed pass"
+    ref_losses, _ = _run(cfg, bits, 2, **kw)
+    losses, _ = _run(cfg, bits, 2, **kw)
+    assert losses == ref_losses and all(np.isfinite(losses))
