@@ -438,10 +438,14 @@ def test_streamed_step_7b_shape_equals_resident(gpu):
     from host_memory_centric_amd.engine import Trainer
     cfg = synth.preset("7b", layers=8)
     runs = {}
-    # the streamed run as the benchmark launches it (pageable store, packer,
-    # gradient slabs), the same with W and G page-locked and copied directly,
-    # and the resident run
+    # the streamed run (pageable store, packer, gradient slabs), the same with
+    # W and G page-locked and copied directly, the benchmark's schedule (every
+    # other layer carried across steps, most-urgent-first updates, 4 gradient
+    # slots, 5 shared slots; the second step runs from the carried slots) and
+    # the resident run
     for name, kw in (("streamed", dict(mode="streamed")), ("streamed_pinned", dict(mode="streamed", pinned_store=True)),
+                     ("streamed_bench", dict(mode="streamed", pinned_store=True, carry=4, update_order="urgent",
+                                             grad_slots=4, n_slots=5)),
                      ("resident", dict(mode="resident"))):
         _log(f"step 7b-shape 8 layers {name}")
         tr = Trainer(cfg, synth.AdamCfg(), **kw)
@@ -454,6 +458,7 @@ def test_streamed_step_7b_shape_equals_resident(gpu):
     assert ls == lr, (ls, lr)
     assert ds == dr
     assert runs["streamed_pinned"][:2] == (ls, ds)
+    assert runs["streamed_bench"][:2] == (ls, ds)
     assert ns > nr  # the streamed run re-loaded weights for the recompute
     # initial loss in the band of a random model: ln V plus the logits' variance
     lnV = np.log(cfg.vocab)
