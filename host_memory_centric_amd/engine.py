@@ -1004,14 +1004,14 @@ class Trainer:
 
     def _carry_copy(self, unit, after, tl):
         """Enqueue the copy of a carried layer's updated weights from the store
-        into the layer's own slot, on the weight stream after ``after`` (the
-        layer's backward, the last reader of the old weights).  Runs on the
-        optimizer thread right after the layer's update; the next pass's first
-        use of the layer waits for this copy's event."""
+        into the layer's own slot, on the weight stream, once ``after`` (the
+        layer's backward, the last reader of the old weights) has completed.
+        Runs on the optimizer thread right after the layer's update; the next
+        pass's first use of the layer waits for this copy's event."""
         hs = self.s_h2d
+        after.synchronize()  # (long done: the update waited for the gradient copy that followed it)
         with torch.cuda.device(self.dev):
             ev = torch.cuda.Event(enable_timing=self.record_timeline)
-            hs.wait_event(after)
             t0 = self._ev(hs) if tl is not None else None
             call("mt_copy_h2d", _ptr(self.slots[self.carry_slot[unit]]), self.w_addr[unit], self.lay.w_bytes,
                  ctypes.c_void_p(hs.cuda_stream))
