@@ -208,6 +208,55 @@ int gemm_pick_splits(int64_t M, int64_t N, int64_t K) {
     return (int)std::max<int64_t>(1, std::min<int64_t>(s, 16));
 }
 
+// Enqueue one GEMM (checked by gemm()) with the given K slices.
+static void run_gemm(const GemmDesc& d, int splits, int64_t kps, hipStream_t s) {
+    float* part = splits > 1 ? (float*)d.ws : nullptr;
+    if (pipe_ok(d, kps)) {
+        if (use_pp() || d.f16 || d.epi) launch_pp(d, s, part, splits, kps);
+        else launch_pipe(d, s, part, splits, kps);
+    }
+    else if (use_big(d.M, d.N))
+        launch_tiles<256, 256, 2, 4>(d, s, part, splits, kps);
+    else
+        launch_tiles<128, 128, 2, 2>(d, s, part, splits, kps);
+    if (splits > 1) {
+        const int64_t total = d.M * d.N;
+        hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((total / 4 + 255) / 256)), dim3(256), 0, s, part,
+                           splits, d.M, d.N, d.Cf, (uint16_t*)d.Cb, (const uint16_t*)d.R, d.ldc, d.accumulate);
+    }
+}
+
+static int compute_units() {
+    static const int n = [] {
+        int dev = 0, cu = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cu <= 0)
+            cu = 256;
+        return cu;
+    }();
+    return n;
+}
+
+// Tile columns of a GEMM that the last, partly filled round of workgroups
+// holds, when it is worth running them apart; 0 otherwise.  The large-operand
+// kernel runs one 256x256 tile per CU, so 640 tiles on 256 CUs are 2.5 rounds
+// with half the machine idle in the third.  With a long contraction (K >= 8192)
+// the columns of whole rounds go first and the remaining columns run with K
+// split in two, which fills the last round with half-length tiles (-6 % to
+// -12 % at 8192 x 5120 and K = 13824..27648; shorter K loses to the partial
+// sums' extra traffic).  Needs whole tiles, a plain epilogue and a workspace
+// for the partials.
+static int64_t tail_columns(const GemmDesc& d) {
+    if (d.epi || !d.ws || d.M % 256 || d.N % 256 || d.K < 8192 || d.K % (2 * PBK)) return 0;
+    if (gemm_pick_splits(d.M, d.N, d.K) != 1 || !pipe_ok(d, d.K)) return 0;
+    const int64_t tm = d.M / 256, tn = d.N / 256, cu = compute_units();
+    const int64_t rem = (tm * tn) % cu;
+    if (tm * tn < cu || rem == 0 || rem > cu / 2 || rem % tm) return 0;
+    const int64_t nt = rem / tm;
+    if (nt >= tn || d.ws_bytes < (size_t)(2 * d.M * nt * 256 * 4)) return 0;
+    return nt * 256;
+}
+
 void gemm(const GemmDesc& d, hipStream_t s) {
     if (d.M <= 0 || d.N <= 0 || d.K <= 0 || d.M % 8 || d.N % 8 || d.K % 8 || d.lda % 8 || d.ldb % 8 ||
         d.ldc % 8)
@@ -229,6 +278,26 @@ void gemm(const GemmDesc& d, hipStream_t s) {
             MT_FAIL(MT_E_ARG, "gemm: bad RoPE epilogue arguments");
         if (d.epi == 2 && !d.Cb && !d.Ca && !d.Ca16) MT_FAIL(MT_E_ARG, "gemm: SwiGLU epilogue without outputs");
     }
+    if (d.f16 && !d.a_kmajor) MT_FAIL(MT_E_ARG, "gemm: fp16 operands need a K-major A");
+    const ProfClass pc =
+        d.f16 ? PROF_GEMM_FWD16 : d.a_kmajor ? (d.b_kmajor ? PROF_GEMM_NT : PROF_GEMM_NN) : PROF_GEMM_TN;
+    ProfScope prof(pc, 2.0 * (double)d.M * (double)d.N * (double)d.K, s);
+    const int64_t nt = tail_columns(d);
+    if (nt > 0) {
+        // columns [0, N - nt) in whole rounds, then [N - nt, N) with K in two halves
+        GemmDesc head = d, tail = d;
+        const int64_t n0 = d.N - nt;
+        head.N = n0;
+        tail.N = nt;
+        tail.B = (const uint16_t*)d.B + (d.b_kmajor ? n0 * d.ldb : n0);
+        if (d.Cf) tail.Cf = d.Cf + n0;
+        if (d.Cb) tail.Cb = (uint16_t*)d.Cb + n0;
+        if (d.R) tail.R = (const uint16_t*)d.R + n0;
+        run_gemm(head, 1, d.K, s);
+        run_gemm(tail, 2, d.K / 2, s);
+        launch_check("gemm");
+        return;
+    }
     int splits = d.epi ? 1 : gemm_pick_splits(d.M, d.N, d.K);
     if (splits > 1 && (!d.ws || d.ws_bytes < (size_t)splits * d.M * d.N * 4)) splits = 1;
     const int BK = GBK;
@@ -237,24 +306,7 @@ void gemm(const GemmDesc& d, hipStream_t s) {
         kps = ((d.K + splits - 1) / splits + BK - 1) / BK * BK;
         splits = (int)((d.K + kps - 1) / kps);
     }
-    float* part = splits > 1 ? (float*)d.ws : nullptr;
-    const ProfClass pc =
-        d.f16 ? PROF_GEMM_FWD16 : d.a_kmajor ? (d.b_kmajor ? PROF_GEMM_NT : PROF_GEMM_NN) : PROF_GEMM_TN;
-    ProfScope prof(pc, 2.0 * (double)d.M * (double)d.N * (double)d.K, s);
-    if (d.f16 && !d.a_kmajor) MT_FAIL(MT_E_ARG, "gemm: fp16 operands need a K-major A");
-    if (pipe_ok(d, kps)) {
-        if (use_pp() || d.f16 || d.epi) launch_pp(d, s, part, splits, kps);
-        else launch_pipe(d, s, part, splits, kps);
-    }
-    else if (use_big(d.M, d.N))
-        launch_tiles<256, 256, 2, 4>(d, s, part, splits, kps);
-    else
-        launch_tiles<128, 128, 2, 2>(d, s, part, splits, kps);
-    if (splits > 1) {
-        const int64_t total = d.M * d.N;
-        hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((total / 4 + 255) / 256)), dim3(256), 0, s, part,
-                           splits, d.M, d.N, d.Cf, (uint16_t*)d.Cb, (const uint16_t*)d.R, d.ldc, d.accumulate);
-    }
+    run_gemm(d, splits, kps, s);
     launch_check("gemm");
 }
 

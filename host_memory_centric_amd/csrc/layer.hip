@@ -80,6 +80,8 @@ struct FwdWs {
     uint16_t* o16;    // attention output as fp16, whole batch [T, h]
     float* gu32;      // gate | up of a token chunk, fp32 [Tc, 2f]
     uint16_t* a16;    // SwiGLU output of a token chunk, fp16 [Tc, f]
+    void* splitk;     // split-K partials (the backward's buffer, idle during a forward), or NULL
+    size_t splitk_bytes;
 };
 
 FwdWs carve_fwd(Carve& c, const mt_model_cfg* cfg, int64_t T) {
@@ -91,6 +93,8 @@ FwdWs carve_fwd(Carve& c, const mt_model_cfg* cfg, int64_t T) {
     w.o16 = c.take<uint16_t>(T * h);
     w.gu32 = c.take<float>(Tc * 2 * f);
     w.a16 = c.take<uint16_t>(Tc * f);
+    w.splitk = nullptr;
+    w.splitk_bytes = 0;
     return w;
 }
 
@@ -159,6 +163,8 @@ BwdWs carve_ws(Carve& c, const mt_model_cfg* cfg, int64_t B, int64_t S) {
     w.dg_part = c.take<float>(rmsnorm_bwd_blocks(T) * h);
     w.splitk_bytes = splitk_need(cfg, T);
     w.splitk = c.take<char>(w.splitk_bytes);
+    w.fw.splitk = w.splitk;  // outside the forward's transients
+    w.fw.splitk_bytes = w.splitk_bytes;
     w.mc_n2 = w.mc_n16 = w.mc_gu = w.mc_a = w.mc_wgu = nullptr;
     w.mc_rstd = w.mc_gu32 = w.mc_dwd = w.mc_dwgu = nullptr;
     if (mlp_chunked(T)) {
@@ -300,6 +306,8 @@ void layer_forward(const mt_layer_view* v, const mt_model_cfg* cfg, int B, int S
         d.f16 = true;
         d.R = sv.xm + t0 * h;
         d.Cb = y + t0 * h;
+        d.ws = fw.splitk;  // (a ragged last round of tiles may run with K split)
+        d.ws_bytes = fw.splitk_bytes;
         gemm(d, s);
     }
 }
@@ -335,6 +343,8 @@ void layer_backward(const mt_layer_view* v, const mt_model_cfg* cfg, const mt_ac
         gemm(d, s);
         d = gd(T, h, 2 * f, w.dgu, 2 * f, true, wgu, h, false, h);
         d.Cf = w.dn;
+        d.ws = w.splitk;
+        d.ws_bytes = w.splitk_bytes;
         gemm(d, s);
         // MLP RMSNorm (+ residual)
         rmsnorm_bwd(w.dn, sv.xm, sv.rstd2, g_mlp, io->dy, w.dxm, w.dxm_b, w.dg_part, T, (int)h, s);
@@ -370,6 +380,8 @@ void layer_backward(const mt_layer_view* v, const mt_model_cfg* cfg, const mt_ac
             gemm(d, s);
             d = gd(rows, h, 2 * f, w.dgu, 2 * f, true, wgu, h, false, h);
             d.Cf = w.dn + t0 * h;
+            d.ws = w.splitk;
+            d.ws_bytes = w.splitk_bytes;
             gemm(d, s);
             // MLP RMSNorm (+ residual); the chunk's gain partials are row
             // blocks t0 / 16 .. of the whole
@@ -400,6 +412,8 @@ void layer_backward(const mt_layer_view* v, const mt_model_cfg* cfg, const mt_ac
     gemm(d, s);
     d = gd(T, h, 3 * h, w.dqkv, 3 * h, true, wqkv, h, false, h);
     d.Cf = w.dn;
+    d.ws = w.splitk;
+    d.ws_bytes = w.splitk_bytes;
     gemm(d, s);
     // attention RMSNorm (+ residual)
     rmsnorm_bwd(w.dn, (const uint16_t*)io->x_in, sv.rstd1, (const uint16_t*)v->w[0], w.dxm, io->dx,
