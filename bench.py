@@ -130,25 +130,43 @@ def _inter(u, w):
 
 def merged_timeline(raws):
     """One event timeline over consecutive steps (ms from the first step's
-    start): the steps' op, weight-copy and gradient-copy intervals."""
+    start): the steps' op, weight-copy and gradient-copy intervals, and the
+    host updates moved onto the event clock (a backward's end is seen by the
+    host thread that waits for it a little later; the smallest difference
+    gives the shift between the clocks)."""
     rel = raws[0]["ref"].elapsed_time
-    out = {"ops": [], "h2d": [], "d2h": []}
+    t0 = raws[0]["t_host"]
+    out = {"ops": [], "h2d": [], "d2h": [], "host": []}
+    shifts = []
     for tl in raws:
-        out["ops"] += [(k, rel(a), rel(b)) for k, a, b in tl["ops"]]
+        ops = [(k, rel(a), rel(b)) for k, a, b in tl["ops"]]
+        host = [(k, u, 1e3 * (a - t0), 1e3 * (b - t0)) for k, u, a, b in tl["host"]]
+        bwd_end = [e for k, _, e in ops if k == "bwd"]
+        seen = [a for k, _, a, _ in host if k == "bwd_done"]
+        if len(seen) == len(bwd_end):
+            shifts += [a - e for a, e in zip(seen, bwd_end)]
+        out["ops"] += ops
         out["h2d"] += [(rel(a), rel(b)) for a, b in tl["h2d"]]
         out["d2h"] += [(rel(a), rel(b)) for a, b in tl["d2h"]]
+        out["host"] += host
+    shift = min(shifts) if shifts else 0.0
+    out["host"] = [(k, u, a - shift, b - shift) for k, u, a, b in out["host"]]
     return out
 
 
 def overlap_report(tl, n_steps=1):
     """Busy and overlap fractions over the timed steps from their event
     timeline: the share of host-to-device and device-to-host copy time during
-    which the compute stream is running a layer, head or backward op.  The
+    which the compute stream is running a layer, head or backward op, and the
+    share of the window in which the host optimizer thread runs updates.  The
     window runs from the first step's start to the last copy or op."""
     comp = _union([(a, b) for _, a, b in tl["ops"]])
     h2d, d2h = _union(tl["h2d"]), _union(tl["d2h"])
     copies = _union(tl["h2d"] + tl["d2h"])
     span = max([b for _, _, b in tl["ops"]] + [b for _, b in tl["h2d"] + tl["d2h"]])
+    # the host optimizer thread's updates inside the window
+    upd = _union([(max(a, 0.0), min(b, span)) for k, _, a, b in tl.get("host", ())
+                  if k == "update" and b > 0.0 and a < span])
 
     def frac(x, y):
         return round(x / y, 4) if y > 0 else None
@@ -159,7 +177,8 @@ def overlap_report(tl, n_steps=1):
             "d2h_overlap_frac": frac(_inter(d2h, comp), _total(d2h)),
             "copy_overlap_frac": frac(_inter(copies, comp), _total(copies)),
             "gpu_busy_ms_per_step": round(_total(comp) / n_steps, 2),
-            "gpu_idle_ms_per_step": round((span - _total(comp)) / n_steps, 2)}
+            "gpu_idle_ms_per_step": round((span - _total(comp)) / n_steps, 2),
+            "host_update_busy_frac": frac(_total(upd), span) if upd else None}
 
 
 def host_probe(tr, reps=3, master=False):

@@ -685,6 +685,7 @@ class Trainer:
                     hs.wait_event(op_done[last])  # the ring buffer is free
                     if tl is not None:
                         tl["h2d"].append([self._ev(hs), ev])
+                        tl["h2d_tag"][ev] = ("ckpt", b)
                     call("mt_copy_h2d", _ptr(self.ckpt_ring[r]), self.ckpt_slab[r].ptr, ck_bytes, sh)
                     ev.record(hs)
                 ck_h2d[b] = ev
@@ -754,6 +755,7 @@ class Trainer:
             with torch.cuda.device(self.dev), torch.cuda.stream(hs):
                 if tl is not None:
                     tl["h2d"].append([self._ev(hs), ready_ev[j]])
+                    tl["h2d_tag"][ready_ev[j]] = ("load", unit)
                 dst = _ptr(self.slots[op_slot[i]])
                 if not self.direct:
                     call("mt_copy_h2d", dst, self.wslab[j % 2].ptr, nbytes, sh)
@@ -803,12 +805,15 @@ class Trainer:
             # after: a carried layer's backward (its slot's last reader)
             self._debug_delay()
             ev.synchronize()
+            t_a = time.perf_counter()
             if final:
                 call("mt_step", self.store.ptr, unit, src, ctypes.byref(self.madam), t, self._w32_ptr(unit))
                 if after is not None:
                     self._carry_copy(unit, after, tl)
             else:
                 call("mt_grad_accumulate", self.store.ptr, unit, src)
+            if tl is not None:
+                tl["host"].append(("update", unit, t_a, time.perf_counter()))
 
         def adam_layer_slab(ev, unit, k):
             try:
@@ -821,6 +826,7 @@ class Trainer:
         def adam_embed(ev):
             self._debug_delay()
             ev.synchronize()
+            t_a = time.perf_counter()
             if self.tied:  # the shared matrix: the head's gradient (in the head slab) plus the embedding's
                 head_grad = ctypes.c_void_p(self.head_gslab.ptr.value + self.lay_head_dev.tensor_off[1])
                 call("mt_embed_grad_tied", self.store.ptr, self.tok_pin.ptr, self.T, self.dx0_pin.ptr, head_grad)
@@ -831,6 +837,8 @@ class Trainer:
                      self._w32_ptr(MT_UNIT_EMBED))
             else:
                 call("mt_grad_accumulate", self.store.ptr, MT_UNIT_EMBED, None)
+            if tl is not None:
+                tl["host"].append(("update", MT_UNIT_EMBED, t_a, time.perf_counter()))
 
         jobs = self.pending if final else self.accum_jobs
 
@@ -950,6 +958,9 @@ class Trainer:
                             k = slab_free.get()
                             g_dst = self.gslab[k].ptr
                         ev.synchronize()  # backward-done: the layer's gradient is complete
+                        if tl is not None:
+                            t_s = time.perf_counter()
+                            tl["host"].append(("bwd_done", l, t_s, t_s))
                         with torch.cuda.device(self.dev), torch.cuda.stream(ds):
                             if tl is not None:
                                 tl["d2h"].append([self._ev(ds), d2h])
@@ -1018,6 +1029,7 @@ class Trainer:
             ev.record(hs)
         if tl is not None:
             tl["h2d"].append([t0, ev])
+            tl["h2d_tag"][ev] = ("refill", unit)
         self._carry_ev[unit] = ev
 
     def _urgency(self, unit):
@@ -1040,13 +1052,17 @@ class Trainer:
     def _timeline_begin(self, cs):
         ref = torch.cuda.Event(enable_timing=True)
         ref.record(cs)
-        return {"ref": ref, "ops": [], "h2d": [], "d2h": []}
+        return {"ref": ref, "ops": [], "h2d": [], "d2h": [], "host": [], "h2d_tag": {},
+                "t_host": time.perf_counter()}
 
     def timeline(self):
         """Intervals (ms from the step's start) of the last step recorded with
         timeline=True: {'ops': [(kind, start, end)], 'h2d': [(start, end)],
-        'd2h': [(start, end)]}.  Waits for the step's host updates (which
-        enqueue the carried layers' copies) and for its copies to finish."""
+        'd2h': [(start, end)], 'host': [(kind, unit, start, end)]}; 'host' holds
+        the optimizer thread's updates ('update') and the moments the copy
+        thread saw each backward end ('bwd_done'), moved onto the event clock.
+        Waits for the step's host updates (which enqueue the carried layers'
+        copies) and for its copies to finish."""
         tl = self._tl
         if tl is None:
             return None
@@ -1057,9 +1073,17 @@ class Trainer:
             e.synchronize()
         ref = tl["ref"]
         rel = ref.elapsed_time
-        return {"ops": [(k, rel(a), rel(b)) for k, a, b in tl["ops"]],
+        ops = [(k, rel(a), rel(b)) for k, a, b in tl["ops"]]
+        host = [(k, u, 1e3 * (a - tl["t_host"]), 1e3 * (b - tl["t_host"])) for k, u, a, b in tl["host"]]
+        # host clock -> event clock: a backward's end is seen by the thread that
+        # waits for it a little later, so the smallest difference estimates the shift
+        bwd_end = [e for k, _, _, e in ops if k == "bwd"]
+        seen = [a for k, _, a, _ in host if k == "bwd_done"]
+        shift = min((s - e for s, e in zip(seen, bwd_end)), default=0.0) if len(seen) == len(bwd_end) else 0.0
+        return {"ops": ops,
                 "h2d": [(rel(a), rel(b)) for a, b in tl["h2d"]],
-                "d2h": [(rel(a), rel(b)) for a, b in tl["d2h"]]}
+                "d2h": [(rel(a), rel(b)) for a, b in tl["d2h"]],
+                "host": [(k, u, a - shift, b - shift) for k, u, a, b in host]}
 
     # ------------------------------------------------------------------
     def weights(self):

@@ -161,6 +161,10 @@ def test_offloaded_checkpoints_bit_identical(gpu):
             if "timeline" in kw:
                 tl = tr.timeline()
                 assert len(tl["d2h"]) >= cfg.layers + tr.n_host and len(tl["h2d"]) >= tr.n_host
+                # every layer's update, and the moment each backward was seen to end
+                assert sorted(u for k, u, _, _ in tl["host"] if k == "update" and 0 <= u < cfg.layers) \
+                    == list(range(cfg.layers))
+                assert sum(k == "bwd_done" for k, *_ in tl["host"]) == cfg.layers
             runs[name] = (losses, _store_regions(tr))
         finally:
             tr.close()

@@ -754,3 +754,42 @@ def test_device_entries_reject_bad_arguments_before_any_launch(lib):
     out = MtLayerView()
     assert code("mt_bind", ctypes.byref(mc), 0, ctypes.c_void_p(base + 128), None, ctypes.byref(out)) == -3
     assert code("mt_bind", ctypes.byref(mc), 0, None, None, ctypes.byref(out)) == -1
+
+
+class _ClockEvent:
+    """A timing event at a fixed moment of the event clock (ms)."""
+
+    def __init__(self, t):
+        self.t = t
+
+    def elapsed_time(self, other):
+        return other.t - self.t
+
+
+def test_timeline_report_host_updates():
+    """bench.py's merged timeline puts the host updates on the event clock
+    (shifted by the smallest delay between a backward's end and the moment the
+    copy thread saw it) and the report counts the share of the window in which
+    updates run."""
+    import bench
+    E = _ClockEvent
+    # two steps of 100 ms: a forward 0..40, a backward 40..90 (one layer), a
+    # copy out 90..95 and one update; the host clock runs 1000 s ahead and the
+    # copy thread sees each backward 0.5 ms late (2 ms the second time)
+    raws = []
+    for s in range(2):
+        b = 100.0 * s
+        h0 = 1000.0 + b * 1e-3
+        raws.append({"ref": E(b), "ops": [("fwd", E(b), E(b + 40)), ("bwd", E(b + 40), E(b + 90))],
+                     "h2d": [(E(b), E(b + 10))], "d2h": [(E(b + 90), E(b + 95))],
+                     "host": [("bwd_done", 0, h0 + (90.5 + 1.5 * s) * 1e-3, h0 + (90.5 + 1.5 * s) * 1e-3),
+                              ("update", 0, h0 + 95.5e-3, h0 + 120.5e-3)],
+                     "t_host": 1000.0 if s == 0 else 1000.1})
+    tl = bench.merged_timeline(raws)
+    upd = [x for k, _, a, b in tl["host"] if k == "update" for x in (a, b)]
+    assert upd == pytest.approx([95.0, 120.0, 195.0, 220.0])
+    rep = bench.overlap_report(tl, 2)
+    # the window ends with the last op or copy (195 ms): 25 + 0 ms of updates inside it
+    assert rep["window_ms"] == pytest.approx(195.0)
+    assert rep["host_update_busy_frac"] == pytest.approx(25.0 / 195.0, abs=1e-4)
+    assert rep["compute_busy_frac"] == pytest.approx(180.0 / 195.0, abs=1e-4)
