@@ -1077,7 +1077,7 @@ class Trainer:
         host = [(k, u, 1e3 * (a - tl["t_host"]), 1e3 * (b - tl["t_host"])) for k, u, a, b in tl["host"]]
         # host clock -> event clock: a backward's end is seen by the thread that
         # waits for it a little later, so the smallest difference estimates the shift
-        bwd_end = [e for k, _, _, e in ops if k == "bwd"]
+        bwd_end = [e for k, _, e in ops if k == "bwd"]
         seen = [a for k, _, a, _ in host if k == "bwd_done"]
         shift = min((s - e for s, e in zip(seen, bwd_end)), default=0.0) if len(seen) == len(bwd_end) else 0.0
         return {"ops": ops,

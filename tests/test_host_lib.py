@@ -793,3 +793,33 @@ def test_timeline_report_host_updates():
     assert rep["window_ms"] == pytest.approx(195.0)
     assert rep["host_update_busy_frac"] == pytest.approx(25.0 / 195.0, abs=1e-4)
     assert rep["compute_busy_frac"] == pytest.approx(180.0 / 195.0, abs=1e-4)
+
+
+def test_trainer_timeline_conversion():
+    """Trainer.timeline() on a recorded timeline (events of a fixed clock):
+    intervals relative to the step's reference event, host intervals shifted
+    onto the event clock by the smallest delay after a backward's end."""
+    from host_memory_centric_amd.engine import Trainer
+
+    class _Done(_ClockEvent):
+        def synchronize(self):
+            pass
+
+    class _T:
+        def finish(self):
+            pass
+    E = _Done
+    t = _T()
+    t._tl = {"ref": E(10.0), "ops": [("fwd", E(10.0), E(20.0)), ("bwd", E(20.0), E(30.0)),
+                                      ("bwd", E(30.0), E(40.0))],
+             "h2d": [(E(10.0), E(15.0))], "d2h": [(E(30.0), E(35.0)), (E(40.0), E(45.0))],
+             "host": [("bwd_done", 1, 5.0205, 5.0205), ("bwd_done", 0, 5.0312, 5.0312),
+                      ("update", 1, 5.0355, 5.0455)],
+             "t_host": 5.0}
+    tl = Trainer.timeline(t)
+    assert [x for _, a, b in tl["ops"] for x in (a, b)] == pytest.approx([0, 10, 10, 20, 20, 30])
+    assert [x for a, b in tl["d2h"] for x in (a, b)] == pytest.approx([20, 25, 30, 35])
+    # seen 20.5 and 31.2 ms after the step began on the host clock: shift 0.5 ms
+    host = {(k, u): (a, b) for k, u, a, b in tl["host"]}
+    assert host[("bwd_done", 0)] == pytest.approx((30.7, 30.7))
+    assert host[("update", 1)] == pytest.approx((35.0, 45.0))
