@@ -4,8 +4,9 @@ One step = one full training step of the workload (streamed forward, head,
 block recompute + backward, gradient offload, host Adam for every unit) over
 one batch of seeded synthetic tokens.  Prints one JSON line:
 tokens/s (value), executed and model TFLOPS against the bf16 dense MFMA peak,
-host-link GB/s, the live-measured roofline of the dominant kernel, and the
-CPU oracle timed on a bounded sample of the same workload.
+host-link GB/s, the copy/compute overlap of the timed steps, the roofline of
+the dominant kernel (HIP events around its launches in the timed steps), and
+the CPU oracle timed on a bounded sample of the same workload.
 
     python bench.py [--steps K] [--warmup W] [--workload 14b] [--mode streamed]
 """
@@ -348,9 +349,10 @@ def main():
     ap.add_argument("--slots", type=int, default=5)
     ap.add_argument("--grad-slabs", type=int, default=16)
     ap.add_argument("--grad-slots", type=int, default=4, help="device gradient slots the backward writes in turn")
-    ap.add_argument("--update-order", default="urgent", choices=["arrival", "urgent", "tail"],
+    ap.add_argument("--update-order", default="carried", choices=["arrival", "urgent", "tail", "carried"],
                     help="order of the host updates: as gradients arrive, most urgent for the next step first, "
-                         "or as they arrive until the backward ends and most urgent first after it")
+                         "as they arrive until the backward ends and most urgent first after it, or carried "
+                         "layers first during the backward and most urgent first after it")
     ap.add_argument("--carry", type=int, default=None,
                     help="layers that keep a device slot of their own across steps, refilled right after "
                          "their host update (page-locked store only); default: half the layers for the "
@@ -420,6 +422,10 @@ def main():
         loss = tr.step(tokens(step))
         step += 1
         print(f"[bench] warmup step {step}: loss {loss:.4f} {tr.stats['step_s']:.3f} s", file=sys.stderr, flush=True)
+    # the warm-up's host updates (and the weight copies they enqueue) are not
+    # work of the timed steps: they finish before the timed region opens, as
+    # the timed steps' own finish inside it
+    tr.finish()
     torch.cuda.synchronize()
     _lib.prof_collect(reset=True)
     _lib.call("mt_prof_enable", 1)

@@ -29,16 +29,30 @@ std::vector<hipEvent_t> g_pool;
 int64_t g_launches[PROF_N];
 double g_ms[PROF_N], g_flops[PROF_N];
 
+// The timing events skip the system-scope fence that a default event
+// performs when it is recorded (a cache writeback and invalidation): they
+// only order the timestamps around a launch on its own stream, and the
+// fence would perturb the kernels they time and the copies running beside
+// them.
+hipEvent_t new_event() {
+    hipEvent_t e;
+    if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess)
+        MT_FAIL(MT_E_HIP, "hipEventCreateWithFlags failed");
+    return e;
+}
+
 hipEvent_t take_event() {
     if (!g_pool.empty()) {
         hipEvent_t e = g_pool.back();
         g_pool.pop_back();
         return e;
     }
-    hipEvent_t e;
-    if (hipEventCreate(&e) != hipSuccess) MT_FAIL(MT_E_HIP, "hipEventCreate failed");
-    return e;
+    return new_event();
 }
+
+// events created up front when timing is switched on, so that the timed
+// launches do not create events (the pool grows on demand past this)
+constexpr size_t PROF_POOL = 4096;
 }  // namespace
 
 ProfScope::ProfScope(ProfClass c, double flops, hipStream_t st) : s(st) {
@@ -120,7 +134,13 @@ int mt_probe_mfma(int32_t iters, float* sink, void* stream, double* tflops) {
 }
 
 int mt_prof_enable(int on) {
-    return guard([&] { g_on.store(on != 0); });
+    return guard([&] {
+        if (on) {
+            std::lock_guard<std::mutex> lk(g_mu);
+            while (g_pool.size() < PROF_POOL) g_pool.push_back(new_event());
+        }
+        g_on.store(on != 0);
+    });
 }
 
 int mt_prof_collect(mt_prof_entry* out, int max, int* n, int reset) {

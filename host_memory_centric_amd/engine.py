@@ -83,6 +83,7 @@ class UpdateScheduler:
         self._seq = 0
         self._stop = False
         self._by_priority = bool(by_priority)
+        self._key = None  # priority -> sort key (None: the priority itself)
         self._thread = threading.Thread(target=self._run, name="mt-adam", daemon=True)
         self._thread.start()
 
@@ -110,7 +111,8 @@ class UpdateScheduler:
             with self._cv:
                 ready = [j for j in self._jobs if j[6]]
                 if ready:
-                    job = min(ready, key=lambda j: (j[0] if self._by_priority else 0, j[1]))
+                    key = self._key
+                    job = min(ready, key=lambda j: ((key(j[0]) if key else j[0]) if self._by_priority else 0, j[1]))
                     self._jobs.remove(job)
                 else:
                     job = None
@@ -131,6 +133,12 @@ class UpdateScheduler:
         submission order alone."""
         with self._cv:
             self._by_priority = bool(on)
+            self._cv.notify()
+
+    def set_key(self, fn):
+        """Order ready jobs by fn(priority) (None: by the priority) from now on."""
+        with self._cv:
+            self._key = fn
             self._cv.notify()
 
     def shutdown(self):
@@ -308,8 +316,8 @@ class Trainer:
                  device="cuda:0", capture_w32=False, timeline=False, micro_batches=1, master=False,
                  pinned_store=False, update_order="arrival", offload_ckpt=0, poison=False, delay_seed=None,
                  carry=0, grad_slots=2):
-        if update_order not in ("arrival", "urgent", "tail"):
-            raise ValueError("update_order must be 'arrival', 'urgent' or 'tail'")
+        if update_order not in ("arrival", "urgent", "tail", "carried"):
+            raise ValueError("update_order must be 'arrival', 'urgent', 'tail' or 'carried'")
         self.carry = int(carry)
         self.n_gslots = int(grad_slots)
         if self.n_gslots < 1:
@@ -433,7 +441,7 @@ class Trainer:
         # that no copy command waits for compute work inside a DMA queue
         self.h2d_issuer = ThreadPoolExecutor(1, thread_name_prefix="mt-h2d")
         self.d2h_issuer = ThreadPoolExecutor(1, thread_name_prefix="mt-d2h")
-        self.optimizer = UpdateScheduler(by_priority=update_order == "urgent")
+        self.optimizer = UpdateScheduler(by_priority=update_order in ("urgent", "carried"))
         self.slab_free = queue.Queue()
         for k in range(len(self.gslab)):
             self.slab_free.put(k)
@@ -936,6 +944,8 @@ class Trainer:
                             d2h.record(ds)
                         if self.update_order == "tail":
                             self.optimizer.set_by_priority(False)
+                        elif self.update_order == "carried":
+                            self.optimizer.set_key(self._carried_first)
                         jobs[MT_UNIT_HEAD] = self.optimizer.submit(
                             self._urgency(MT_UNIT_HEAD), d2h, adam_layer, d2h, MT_UNIT_HEAD,
                             self.head_gslab.ptr if self.head_gslab is not None else None)
@@ -984,6 +994,8 @@ class Trainer:
                                                                         d2h_x)
                             if self.update_order == "tail":
                                 self.optimizer.set_by_priority(True)
+                            elif self.update_order == "carried":
+                                self.optimizer.set_key(None)
                     f = self.d2h_issuer.submit(grad_out)
                     d2h_futs.append(f)
                     gslot_d2h[g] = (f, d2h)
@@ -1031,6 +1043,13 @@ class Trainer:
             tl["h2d"].append([t0, ev])
             tl["h2d_tag"][ev] = ("refill", unit)
         self._carry_ev[unit] = ev
+
+    def _carried_first(self, priority):
+        """Sort key of the 'carried' order during the backward: the head and
+        the carried layers first (their new weights then travel while the
+        backward runs), then the streamed layers, whose loads go in the next
+        forward anyway; each class by its priority."""
+        return (0 if priority == self.L or priority in self.carry_slot else 1, priority)
 
     def _urgency(self, unit):
         """Scheduling priority of a unit's update: the order in which the next

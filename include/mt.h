@@ -441,7 +441,8 @@ typedef struct mt_prof_entry {
 int mt_probe_mfma(int32_t iters, float* sink, void* stream, double* tflops);
 
 /* on != 0: from now on every launch of a timed class is bracketed by two HIP
- * events recorded on the launch's own stream; on == 0 stops recording. */
+ * events recorded on the launch's own stream (events without the system-scope
+ * fence, taken from a pool that switching on fills); on == 0 stops recording. */
 int mt_prof_enable(int on);
 /* Waits for the recorded events, adds their elapsed times into per-class
  * totals, and copies up to max entries (classes with launches) to out;

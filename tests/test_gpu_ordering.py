@@ -61,7 +61,9 @@ VARIANTS = {"k1_2slot": dict(ckpt_every=1, n_slots=2),
                                                 update_order="tail"),
             "pinned_carry2_micro_urgent": dict(ckpt_every=2, n_slots=2, pinned_store=True, carry=2,
                                                micro_batches=2, update_order="urgent"),
-            "gslots3_k1_3slot_1slab": dict(ckpt_every=1, n_slots=3, n_grad_slabs=1, grad_slots=3)}
+            "gslots3_k1_3slot_1slab": dict(ckpt_every=1, n_slots=3, n_grad_slabs=1, grad_slots=3),
+            "pinned_carry3_k2_2slot_carried": dict(ckpt_every=2, n_slots=2, pinned_store=True, carry=3,
+                                                   update_order="carried")}
 
 
 @pytest.mark.parametrize("variant", list(VARIANTS))

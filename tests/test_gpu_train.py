@@ -57,7 +57,9 @@ def test_streamed_equals_resident_bitwise(gpu):
                      "k2_2slot_tail": dict(ckpt_every=2, n_slots=2, update_order="tail"),
                      "k1_2slot_pinned_carry1": dict(ckpt_every=1, n_slots=2, pinned_store=True, carry=1),
                      "k2_1slot_pinned_carry2_tail": dict(ckpt_every=2, n_slots=1, pinned_store=True, carry=2,
-                                                         update_order="tail")}.items():
+                                                         update_order="tail"),
+                     "k1_2slot_pinned_carry2_carried": dict(ckpt_every=1, n_slots=2, pinned_store=True, carry=2,
+                                                            update_order="carried")}.items():
         tr = _trainer(cfg, bits, **kw)
         try:
             losses = [tr.step(synth.make_tokens(cfg, s)) for s in range(3)]

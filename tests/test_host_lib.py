@@ -823,3 +823,24 @@ def test_trainer_timeline_conversion():
     host = {(k, u): (a, b) for k, u, a, b in tl["host"]}
     assert host[("bwd_done", 0)] == pytest.approx((30.7, 30.7))
     assert host[("update", 1)] == pytest.approx((35.0, 45.0))
+
+
+def test_update_scheduler_key():
+    """With a sort key set, the ready jobs run in the key's order (the
+    'carried' update order during the backward), and after set_key(None) by
+    priority again."""
+    from host_memory_centric_amd.engine import UpdateScheduler
+    sch = UpdateScheduler(by_priority=True)
+    try:
+        for key, want in (((lambda p: (p % 2, p)), [5, 3, 1, 4, 2, 0]), (None, [5, 4, 3, 2, 1, 0])):
+            sch.set_key(key)
+            ran = []
+            evs = [_FakeEvent() for _ in range(6)]
+            futs = [sch.submit(5 - i, evs[i], ran.append, i) for i in range(6)]
+            for e in reversed(evs):  # the waiting thread wakes at the first job's event, the last set
+                e.done.set()
+            for f in futs:
+                f.result(timeout=5)
+            assert ran == want
+    finally:
+        sch.shutdown()
