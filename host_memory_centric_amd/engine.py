@@ -1054,7 +1054,8 @@ class Trainer:
     def _urgency(self, unit):
         """Scheduling priority of a unit's update: the order in which the next
         step needs its updated weights (used by 'urgent' always, by 'tail'
-        once the backward has issued its last gradient)."""
+        and 'carried' once the backward has issued its last gradient, by
+        'carried' within its two classes before)."""
         if unit == MT_UNIT_EMBED:
             return -1
         if unit == MT_UNIT_HEAD:
